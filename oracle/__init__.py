@@ -1,0 +1,55 @@
+"""CPU oracle for the W4A16 group-quantized linear path.
+
+TEST INFRASTRUCTURE ONLY. Nothing in the product path (the HIP library, its
+Python binding, the timed part of ``bench.py``) may import, call or link this
+package. Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.
+
+It is a plain, slow, obviously-correct NumPy float64 restatement of what the
+pages define, written step by step in the pages' order:
+
+* ``channel_scale``   - the AWQ activation statistic s = s_X^alpha (mean |x| per
+  input channel, gathered on calibration tokens).
+* ``scale_input``     - the 1/s that the method folds into the layer input.
+* ``quantize_groups`` - round-to-nearest, min/max zero-point quantization of
+  groups of consecutive input channels.
+* ``pack_codes`` / ``unpack_codes`` - the nibble layout (layout v1).
+* ``quantize_pack``   - all of the above for one weight matrix.
+* ``dequantize`` / ``linear`` - the fused dequantize-then-multiply, in float64.
+
+It shares no code, header, table or constant with the HIP path. The only module
+both sides use is the seeded input generator ``synth``, which holds none of the
+method's arithmetic.
+
+Pins: every function is checked in ``tests/test_oracle*.py`` against closed
+forms, brute force in exact rationals, worked words and invariants (see the
+docstrings). No function here is "parity unpinned".
+"""
+
+from .quant import (
+    channel_scale,
+    scale_input,
+    quantize_groups,
+    pseudo_quantize,
+    quantize_pack,
+    f64_to_f16,
+)
+from .layout import pack_codes, unpack_codes, LAYOUT_VERSION
+from .linear import dequantize, linear, within_tolerance, TOL_REL, TOL_ABS
+
+__all__ = [
+    "channel_scale",
+    "scale_input",
+    "quantize_groups",
+    "pseudo_quantize",
+    "quantize_pack",
+    "f64_to_f16",
+    "pack_codes",
+    "unpack_codes",
+    "LAYOUT_VERSION",
+    "dequantize",
+    "linear",
+    "within_tolerance",
+    "TOL_REL",
+    "TOL_ABS",
+]
