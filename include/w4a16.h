@@ -1,0 +1,160 @@
+/*
+ * w4a16.h - C ABI of the MI355X (gfx950) W4A16 group-quantized linear library.
+ *
+ * What it computes (pages cited by title and section):
+ *   - AWQ, "MIT 6.5940 L13 LLM Deployment" reading guide, AWQ section (slides
+ *     25-28): salient input channels of the weight are multiplied by
+ *     s = s_X^alpha, where s_X is the mean activation magnitude; the matching
+ *     input channel is divided by s (the 1/s is folded into the previous op);
+ *     weights are quantized with Q(w) = Delta * Round(w / Delta), per group of
+ *     128 input channels (QServe table: W4-A16, 4-bit per-group, group 128).
+ *   - Zero-point (asymmetric) form: "CMU 11-868 Model Quantization" guide, L19
+ *     "absmax and zero-point": scale from max - min (a zero range counts as 1),
+ *     an integer zero offset, codes clipped to the integer range.
+ *   - TinyChat, same L13 guide (slides 36-37): 4-bit codes reordered offline so
+ *     that an AND and a shift unpack them, and dequantization fused into the
+ *     matrix multiply so no dequantized weight is written to memory.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers (HIP device memory on the GPU the
+ *     stream belongs to). The caller allocates and owns every buffer; the
+ *     library never allocates, frees or keeps device memory, holds no mutable
+ *     global state, and is safe to call from several host threads.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default stream.
+ *     Calls are asynchronous and stream-ordered. A fault inside a kernel shows up
+ *     at the caller's next synchronization, as for any HIP kernel.
+ *   - Every argument check runs on the host before any HIP call; a failed check
+ *     returns a nonzero status and launches nothing. w4a16_last_error() then
+ *     describes the failure (thread-local text).
+ *   - Outputs must not alias inputs. Inputs are assumed finite.
+ *   - fp16 is IEEE binary16, little-endian; matrices are row-major, dense.
+ *
+ * Packed weight layout, version 1 (w4a16_layout_version() == 1):
+ *   qweight: uint32 [N][K/8], row-major, K-contiguous. Word j of row n holds
+ *   the codes of inputs k = 8j .. 8j+7: nibble i (bits 4i..4i+3, i = 0..3) is
+ *   q[8j+2i] and nibble i+4 (bits 16+4i..16+4i+3) is q[8j+2i+1], so
+ *   (word >> 4i) & 0x000F000F is the pair (q[8j+2i], q[8j+2i+1]) in the low and
+ *   high 16-bit halves. Codes 0,1,...,7 pack to 0x75316420.
+ *   scales, zeros: fp16 [N][K/group], row-major; group g of row n covers
+ *   k = g*group .. g*group+group-1. The dequantized weight is
+ *   w_hat[n][k] = (q[n][k] - zeros[n][g]) * scales[n][g]. Zeros are integers.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_NULL = 1,        /* a required pointer is NULL                                  */
+  W4A16_ERR_SHAPE = 2,       /* a size <= 0, K % group != 0, or a size beyond the limits    */
+  W4A16_ERR_UNSUPPORTED = 3, /* bits != 4 or group != 128, or an unknown path               */
+  W4A16_ERR_ALIGN = 4,       /* a pointer misses its alignment (stated per call)            */
+  W4A16_ERR_HIP = 5,         /* the HIP runtime reported an error at launch                 */
+  W4A16_ERR_ARG = 6          /* another invalid scalar argument (e.g. alpha)                */
+} w4a16_status;
+
+/* Limits (checked): K <= W4A16_MAX_K, N <= 2^24, M <= 2^16, T <= 2^20. */
+#define W4A16_MAX_K 131072
+
+/* Layout version of qweight/scales/zeros written and read by this library: 1. */
+int32_t w4a16_layout_version(void);
+
+/* Static English name of a status code ("ok", "null pointer", ...). */
+const char* w4a16_status_str(int32_t status);
+
+/* Text of the last failure on the calling host thread ("" if none). */
+const char* w4a16_last_error(void);
+
+/*
+ * awq_channel_scale - the AWQ activation statistic (step "s = s_X^alpha").
+ * L13 guide, AWQ section: s = s_X^alpha with s_X the mean magnitude of the
+ * activation per input channel; "MIT 6.5940 Lab 4 + Lab 5" guide, Lab 4 setup:
+ * forward hooks record the mean |input| per channel on calibration tokens.
+ *
+ *   s[k] = float32( (sum_t |x_cal[t][k]| / T) ^ alpha ),  computed in float64;
+ *   a channel whose mean is 0 gets s[k] = 1. alpha = 0.5 uses sqrt.
+ *
+ * x_cal: fp16 [T][K]; s: float32 [K] (output). alpha in [0, 1].
+ * Alignment: x_cal 2 bytes, s 4 bytes. The float64 sum is exact (hence
+ * independent of order) while T * max|x| < 2^29.
+ */
+w4a16_status awq_channel_scale(const void* x_cal, int64_t T, int64_t K, double alpha, float* s,
+                               void* stream);
+
+/*
+ * awq_scale_input - the 1/s folded into the layer input: x_s = f16(x / s).
+ * L13 guide, AWQ section (the scaled channel's input is divided by s);
+ * "Quantization for LLMs" chapter 11, section 11.3: Y = (X diag(s)^-1)(W diag(s))^T.
+ *
+ *   x_s[m][k] = f16_rne( float64(x[m][k]) / float64(s[k]) )   (one rounding)
+ *
+ * x: fp16 [M][K]; s: float32 [K], every s[k] > 0; x_s: fp16 [M][K] (output).
+ * Alignment: x, x_s 2 bytes, s 4 bytes.
+ */
+w4a16_status awq_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* x_s,
+                             void* stream);
+
+/*
+ * awq_quantize_pack - round-to-nearest group quantization and packing.
+ * L13 guide, AWQ section: Q(w) = Delta * Round(w / Delta) on weights already
+ * multiplied by s; CMU L19 zero-point quantizer (range max - min, integer zero,
+ * clipped codes); QServe table: 4-bit weights, group 128; TinyChat packing.
+ *
+ * For every row n and group g (inputs k in [128g, 128g+128)), in float64:
+ *   w   = float64(W[n][k]) * float64(s[k])      (exact; s == NULL means s = 1)
+ *   R   = max w - min w, replaced by 1 when 0
+ *   D   = R / 15                                 (IEEE division)
+ *   z   = rint(-min w / D)                        (round half even, not clamped)
+ *   q   = clamp(rint(w / D) + z, 0, 15)
+ *   scales[n][g] = f16_rne(D), zeros[n][g] = f16_rne(z), qweight = layout v1.
+ * Results are bit-identical to that definition.
+ *
+ * w: fp16 [N][K] (nn.Linear weight: rows are outputs); s: float32 [K] or NULL;
+ * bits must be 4 and group 128. Outputs: qweight uint32 [N][K/8], scales and
+ * zeros fp16 [N][K/128]. Alignment: w and qweight 16 bytes, s 16 bytes,
+ * scales and zeros 2 bytes. K % 128 == 0.
+ */
+w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t K, int32_t bits,
+                               int32_t group, void* qweight, void* scales, void* zeros,
+                               void* stream);
+
+/*
+ * w4a16_linear - the fused dequantize + matrix multiply of a W4A16 layer.
+ * L13 guide, TinyChat kernel fusion (slide 37): dequantize inside the GEMV/GEMM
+ * without writing weights back to memory; CMU guide, "where the speed comes
+ * from": batch-1 decode is a memory-bound GEMV; QServe table: A16 (fp16 inputs).
+ *
+ *   y[m][n] = f16_rne( sum_k x[m][k] * (q[n][k] - zeros[n][g]) * scales[n][g] )
+ *
+ * accumulated in float32 (any summation order). Accuracy contract, with
+ * B = sum_k |x[m][k] * w_hat[n][k]|: |y - exact| <= 1e-3 * B + 1e-5.
+ * x: fp16 [M][K], the input after the 1/s fold; qweight/scales/zeros as written
+ * by awq_quantize_pack; y: fp16 [M][N] (output). group must be 128.
+ * Dispatch: M <= w4a16_gemv_max_m() runs the wave-tile GEMV kernel, larger M
+ * the MFMA kernel. Alignment: x and qweight 16 bytes, scales/zeros/y 2 bytes.
+ */
+w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
+                          int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
+
+/*
+ * w4a16_linear_path - w4a16_linear with the kernel chosen by the caller, for
+ * measuring the GEMV/MFMA hand-off: path 0 = automatic (same as w4a16_linear),
+ * 1 = GEMV kernel (needs M <= 8), 2 = MFMA kernel. Same contract otherwise.
+ */
+w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
+                               const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,
+                               void* y, void* stream);
+
+/* Largest M that w4a16_linear sends to the GEMV kernel. */
+int32_t w4a16_gemv_max_m(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

@@ -32,7 +32,8 @@ DESIGN.md):
 * R2 Round is round-half-to-even (``np.rint``).
 * R3 q = clip(rint(w / Delta) + z, 0, 2^b - 1): round w/Delta first, then add
   the integer zero, so unclamped codes reproduce Delta * Round(w / Delta).
-* R4 z = rint(-min / Delta) is not clamped.
+* R4 z = rint(-min / Delta) is not clamped; a zero offset is +0 (so a group
+  whose minimum is +0 or -0 stores the same zero bits).
 * R5 codes use the float64 Delta; the stored scale is f16(Delta).
 * R6 a constant group (max == min) uses range 1.
 * R7 w / Delta and -min / Delta are IEEE float64 divisions.
@@ -101,7 +102,7 @@ def quantize_groups(w, bits=4, group=128):
     1. per (row, group): mn = min w, mx = max w
     2. range = mx - mn, replaced by 1 when it is 0
     3. Delta = range / (2^b - 1)
-    4. z = rint(-mn / Delta)             (not clamped)
+    4. z = rint(-mn / Delta)             (not clamped; +0 when zero)
     5. q = clip(rint(w / Delta) + z, 0, 2^b - 1)
 
     w: float64 [N][K]. Returns (q int64 [N][K], delta float64 [N][K/g],
@@ -118,7 +119,7 @@ def quantize_groups(w, bits=4, group=128):
     rng = mx - mn
     rng = np.where(rng == 0.0, 1.0, rng)
     delta = rng / qmax
-    z = np.rint(np.negative(mn) / delta)
+    z = np.rint(np.negative(mn) / delta) + 0.0  # a zero offset is stored as +0
     q = np.clip(np.rint(wg / delta[:, :, None]) + z[:, :, None], 0.0, qmax)
     return q.astype(np.int64).reshape(n, k), delta, z
 

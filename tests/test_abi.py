@@ -1,0 +1,130 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every symbol
+declared in include/w4a16.h, and rejects bad arguments before any HIP call."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import w4a16_decode_gemv_amd as w4
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(w4.LIB_PATH), reason="library not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    return sorted({n for n in names if n.startswith(("w4a16_", "awq_"))})
+
+
+def test_header_declares_the_binding_set():
+    assert _declared() == sorted(w4.exported_symbols())
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", w4.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (\w+)$", out, flags=re.M))
+    for name in _declared():
+        assert name in exported, name
+
+
+def test_version_and_status_text():
+    lib = w4.load()
+    assert lib.w4a16_layout_version() == 1
+    assert lib.w4a16_status_str(0) == b"ok"
+    assert lib.w4a16_status_str(5) == b"HIP runtime error"
+    assert lib.w4a16_status_str(99) == b"unknown status"
+    assert lib.w4a16_gemv_max_m() == 8
+
+
+# fake, suitably aligned addresses: the calls must fail before touching them
+A16 = 0x10000
+A2 = 0x10002
+
+
+def _linear(**kw):
+    a = dict(x=A16, q=A16, s=A16, z=A16, M=1, N=64, K=256, group=128, y=A16)
+    a.update(kw)
+    lib = w4.load()
+    return lib.w4a16_linear(a["x"], a["q"], a["s"], a["z"], a["M"], a["N"], a["K"], a["group"], a["y"], None)
+
+
+@pytest.mark.parametrize(
+    "kw,status",
+    [
+        (dict(x=None), w4.ERR_NULL),
+        (dict(q=None), w4.ERR_NULL),
+        (dict(y=None), w4.ERR_NULL),
+        (dict(group=64), w4.ERR_UNSUPPORTED),
+        (dict(M=0), w4.ERR_SHAPE),
+        (dict(N=-1), w4.ERR_SHAPE),
+        (dict(K=200), w4.ERR_SHAPE),
+        (dict(K=131072 + 128), w4.ERR_SHAPE),
+        (dict(M=65537), w4.ERR_SHAPE),
+        (dict(x=A2), w4.ERR_ALIGN),
+        (dict(q=A16 + 4), w4.ERR_ALIGN),
+        (dict(y=A16 + 1), w4.ERR_ALIGN),
+        (dict(s=A16 + 1), w4.ERR_ALIGN),
+    ],
+)
+def test_linear_rejects_before_any_hip_call(kw, status):
+    assert _linear(**kw) == status
+    assert w4.load().w4a16_last_error() != b""
+
+
+def test_linear_path_rejects_unknown_path_and_big_m_on_gemv():
+    lib = w4.load()
+    assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear_path(1, A16, A16, A16, A16, 9, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    # M * ceil(K / 16384) must stay <= 8 on the GEMV path
+    assert lib.w4a16_linear_path(1, A16, A16, A16, A16, 8, 64, 32768, 128, A16, None) == w4.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize(
+    "args,status",
+    [
+        ((None, None, 64, 256, 4, 128, A16, A16, A16), w4.ERR_NULL),
+        ((A16, None, 64, 256, 3, 128, A16, A16, A16), w4.ERR_UNSUPPORTED),
+        ((A16, None, 64, 256, 4, 64, A16, A16, A16), w4.ERR_UNSUPPORTED),
+        ((A16, None, 64, 250, 4, 128, A16, A16, A16), w4.ERR_SHAPE),
+        ((A16, None, 0, 256, 4, 128, A16, A16, A16), w4.ERR_SHAPE),
+        ((A2, None, 64, 256, 4, 128, A16, A16, A16), w4.ERR_ALIGN),
+        ((A16, A16 + 4, 64, 256, 4, 128, A16, A16, A16), w4.ERR_ALIGN),
+        ((A16, None, 64, 256, 4, 128, A16, A16 + 1, A16), w4.ERR_ALIGN),
+    ],
+)
+def test_quantize_pack_rejects(args, status):
+    lib = w4.load()
+    assert lib.awq_quantize_pack(*args, None) == status
+
+
+def test_channel_scale_and_scale_input_reject():
+    lib = w4.load()
+    assert lib.awq_channel_scale(None, 4, 64, 0.5, A16, None) == w4.ERR_NULL
+    assert lib.awq_channel_scale(A16, 0, 64, 0.5, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_channel_scale(A16, 4, 64, 1.5, A16, None) == w4.ERR_ARG
+    assert lib.awq_channel_scale(A16, 4, 64, float("nan"), A16, None) == w4.ERR_ARG
+    assert lib.awq_channel_scale(A16 + 1, 4, 64, 0.5, A16, None) == w4.ERR_ALIGN
+    assert lib.awq_scale_input(A16, None, 1, 64, A16, None) == w4.ERR_NULL
+    assert lib.awq_scale_input(A16, A16, 1, 0, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_scale_input(A16, A16 + 2, 1, 64, A16, None) == w4.ERR_ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    with pytest.raises(ValueError):
+        w4.linear(torch.zeros(1, 256, dtype=torch.float16), torch.zeros(64, 32, dtype=torch.int32),
+                  torch.zeros(64, 2, dtype=torch.float16), torch.zeros(64, 2, dtype=torch.float16))
+
+
+def test_library_links_no_oracle_and_no_torch():
+    out = subprocess.run(["ldd", w4.LIB_PATH], capture_output=True, text=True).stdout
+    assert "torch" not in out and "python" not in out
+    assert ctypes.CDLL(w4.LIB_PATH) is not None

@@ -160,6 +160,16 @@ def test_error_within_half_step_and_code_range(kind):
     assert np.all(np.abs(w - qw) <= d / 2 * (1 + 2.0 ** -40))
 
 
+def test_zero_offset_is_positive_zero():
+    """R4: a group whose minimum is +0 or -0 stores the zero offset as +0."""
+    w = np.zeros((2, 128), dtype=np.float16)
+    w[0, 5] = 0.5
+    w[1, 5] = 0.5
+    w[1, 0] = np.float16(-0.0)
+    _, _, zeros = oracle.quantize_pack(w)
+    assert list(zeros.view(np.uint16)[:, 0]) == [0, 0]
+
+
 def test_constant_group_reading():
     """R6: a constant group uses range 1, so Delta = 1/15; all-zero groups give q = z = 0."""
     w = np.zeros((2, 256))
@@ -333,6 +343,21 @@ def test_within_tolerance_rule():
     b = np.array([10.0, 100.0, 0.0])
     ok = oracle.within_tolerance(np.array([1.0 + 0.0099, -2.0 - 0.11, 1e-5]), y_ref, b)
     assert list(ok) == [True, False, True]
+
+
+def test_tolerance_rule_accepts_fp16_overflow_only_beyond_range():
+    """R11: fp16 outputs saturate to +-inf at 65520; only then is inf acceptable."""
+    inf = np.inf
+    y_ref = np.array([2.0e6, -7.0e4, 65519.0, 1000.0, 2.0e6])
+    b = np.array([3.0e6, 7.0e4, 1.0, 1000.0, 3.0e6])
+    y = np.array([inf, -inf, inf, inf, -inf])
+    assert list(oracle.within_tolerance(y, y_ref, b)) == [True, True, False, False, False]
+    # 65504 + half an ulp (16) is the exact binary16 overflow threshold
+    assert np.float64(65519.99).astype(np.float16) == np.float16(65504)
+    from oracle.linear import F16_OVERFLOW
+
+    with np.errstate(over="ignore"):
+        assert np.isinf(np.float64(F16_OVERFLOW).astype(np.float16))
 
 
 # ---------------------------------------------------------------- a1: AWQ statistic and input fold

@@ -1,0 +1,179 @@
+"""MI355X (gfx950) W4A16 group-quantized linear layers - Python binding.
+
+A thin ctypes layer over ``libw4a16.so`` (C ABI in ``include/w4a16.h``): it
+checks dtypes/devices, allocates outputs with torch on the input's device and
+passes raw device pointers plus torch's current HIP stream. Every step of the
+computation runs in the library's HIP kernels; there is no fallback. If the
+library is missing, every call raises.
+
+    s   = channel_scale(x_cal, alpha=0.5)          # AWQ statistic, float32 [K]
+    x_s = scale_input(x, s)                         # the 1/s fold, fp16 [M][K]
+    qweight, scales, zeros = quantize_pack(W, s)    # RTN 4-bit, group 128
+    y   = linear(x_s, qweight, scales, zeros)       # fused dequant GEMV/GEMM
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4a16.so")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP, ERR_ARG = range(7)
+PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+GROUP = 128
+LAYOUT_VERSION = 1
+
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+def load():
+    """Load the built library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m w4a16_decode_gemv_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    sig = {
+        "w4a16_layout_version": ([], i32),
+        "w4a16_status_str": ([i32], ctypes.c_char_p),
+        "w4a16_last_error": ([], ctypes.c_char_p),
+        "w4a16_gemv_max_m": ([], i32),
+        "awq_channel_scale": ([vp, i64, i64, ctypes.c_double, vp, vp], i32),
+        "awq_scale_input": ([vp, vp, i64, i64, vp, vp], i32),
+        "awq_quantize_pack": ([vp, vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
+        "w4a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
+        "w4a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def exported_symbols():
+    return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
+            "awq_channel_scale", "awq_scale_input", "awq_quantize_pack", "w4a16_linear", "w4a16_linear_path"]
+
+
+def _check(status):
+    if status != OK:
+        lib = load()
+        raise W4A16Error(status, f"{lib.w4a16_status_str(status).decode()}: {lib.w4a16_last_error().decode()}")
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dev_tensor(t, dtype, name, ndim):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got {t.dim()})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream(t):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def channel_scale(x_cal, alpha=0.5, out=None):
+    """AWQ statistic s[k] = (mean_t |x_cal[t, k]|) ** alpha (float32 [K])."""
+    torch = _torch()
+    lib = load()
+    x_cal = _dev_tensor(x_cal, torch.float16, "x_cal", 2)
+    t_, k = x_cal.shape
+    s = torch.empty(k, dtype=torch.float32, device=x_cal.device) if out is None else out
+    _check(lib.awq_channel_scale(x_cal.data_ptr(), t_, k, float(alpha), s.data_ptr(), _stream(x_cal)))
+    return s
+
+
+def scale_input(x, s, out=None):
+    """The 1/s fold: x_s = f16(x / s) (fp16 [M][K])."""
+    torch = _torch()
+    lib = load()
+    x = _dev_tensor(x, torch.float16, "x", 2)
+    s = _dev_tensor(s, torch.float32, "s", 1)
+    m, k = x.shape
+    if s.shape[0] != k:
+        raise ValueError("s must have K entries")
+    xs = torch.empty_like(x) if out is None else out
+    _check(lib.awq_scale_input(x.data_ptr(), s.data_ptr(), m, k, xs.data_ptr(), _stream(x)))
+    return xs
+
+
+def quantize_pack(W, s=None, bits=4, group=GROUP, out=None):
+    """RTN zero-point quantize + pack of an nn.Linear weight fp16 [N][K].
+
+    Returns (qweight int32 [N][K/8] holding layout-v1 uint32 words,
+    scales fp16 [N][K/128], zeros fp16 [N][K/128]).
+    """
+    torch = _torch()
+    lib = load()
+    W = _dev_tensor(W, torch.float16, "W", 2)
+    n, k = W.shape
+    sp = None
+    if s is not None:
+        s = _dev_tensor(s, torch.float32, "s", 1)
+        if s.shape[0] != k:
+            raise ValueError("s must have K entries")
+        sp = s.data_ptr()
+    if out is None:
+        g = max(k // group, 1)
+        qweight = torch.empty((n, max(k // 8, 1)), dtype=torch.int32, device=W.device)
+        scales = torch.empty((n, g), dtype=torch.float16, device=W.device)
+        zeros = torch.empty((n, g), dtype=torch.float16, device=W.device)
+    else:
+        qweight, scales, zeros = out
+    _check(lib.awq_quantize_pack(W.data_ptr(), sp, n, k, bits, group, qweight.data_ptr(), scales.data_ptr(),
+                                 zeros.data_ptr(), _stream(W)))
+    return qweight, scales, zeros
+
+
+def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO):
+    """y = x @ dequant(qweight, scales, zeros)^T, fp16 [M][N] (float32 accumulation)."""
+    torch = _torch()
+    lib = load()
+    x = _dev_tensor(x, torch.float16, "x", 2)
+    qweight = _dev_tensor(qweight, torch.int32, "qweight", 2)
+    scales = _dev_tensor(scales, torch.float16, "scales", 2)
+    zeros = _dev_tensor(zeros, torch.float16, "zeros", 2)
+    m, k = x.shape
+    n = qweight.shape[0]
+    if qweight.shape[1] * 8 != k:
+        raise ValueError("qweight must be [N][K/8]")
+    if scales.shape != zeros.shape or scales.shape[0] != n or scales.shape[1] * group != k:
+        raise ValueError("scales/zeros must be [N][K/group]")
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    if path == PATH_AUTO:
+        status = lib.w4a16_linear(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k,
+                                  group, y.data_ptr(), _stream(x))
+    else:
+        status = lib.w4a16_linear_path(path, x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                                       m, n, k, group, y.data_ptr(), _stream(x))
+    _check(status)
+    return y
+
+
+def gemv_max_m():
+    return int(load().w4a16_gemv_max_m())

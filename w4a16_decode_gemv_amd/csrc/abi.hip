@@ -1,0 +1,155 @@
+// C ABI of the library: argument validation (host only, before any HIP call),
+// status codes and text, and dispatch to the kernel launchers.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "launchers.h"
+#include "w4a16.h"
+
+namespace {
+
+thread_local char g_last_error[512];
+
+w4a16_status fail(w4a16_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+void clear_error() { g_last_error[0] = '\0'; }
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+constexpr int64_t kMaxN = int64_t(1) << 24;
+constexpr int64_t kMaxM = int64_t(1) << 16;
+constexpr int64_t kMaxT = int64_t(1) << 20;
+
+w4a16_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return W4A16_OK;
+}
+
+w4a16_status check_linear(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
+                          int64_t N, int64_t K, int32_t group, const void* y) {
+  if (!x || !qweight || !scales || !zeros || !y) return fail(W4A16_ERR_NULL, "x, qweight, scales, zeros and y are required");
+  if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "group must be 128 (got %d)", (int)group);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "M, N, K must be positive (got %lld, %lld, %lld)",
+                                              (long long)M, (long long)N, (long long)K);
+  if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
+  if (K > W4A16_MAX_K || N > kMaxN || M > kMaxM)
+    return fail(W4A16_ERR_SHAPE, "size beyond the limits (M <= 65536, N <= 2^24, K <= %d)", W4A16_MAX_K);
+  if (!aligned(x, 16) || !aligned(qweight, 16)) return fail(W4A16_ERR_ALIGN, "x and qweight must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(zeros, 2) || !aligned(y, 2))
+    return fail(W4A16_ERR_ALIGN, "scales, zeros and y must be 2-byte aligned");
+  return W4A16_OK;
+}
+
+w4a16_status run_linear(int32_t path, const void* x, const void* qweight, const void* scales, const void* zeros,
+                        int64_t M, int64_t N, int64_t K, void* y, hipStream_t stream) {
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  const uint32_t* qw = static_cast<const uint32_t*>(qweight);
+  const uint16_t* sc = static_cast<const uint16_t*>(scales);
+  const uint16_t* zr = static_cast<const uint16_t*>(zeros);
+  uint16_t* yh = static_cast<uint16_t*>(y);
+  bool use_gemv;
+  if (path == 0)
+    use_gemv = M <= w4a16::gemv_max_m() && w4a16::gemv_supports(M, K);
+  else if (path == 1) {
+    if (!w4a16::gemv_supports(M, K))
+      return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel takes M <= %d (M * ceil(K / 16384) <= 8); got M=%lld K=%lld",
+                  w4a16::gemv_max_m(), (long long)M, (long long)K);
+    use_gemv = true;
+  } else
+    use_gemv = false;
+  if (use_gemv) return hip_result(w4a16::launch_gemv(xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
+  return hip_result(w4a16::launch_mfma(xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t w4a16_layout_version(void) { return 1; }
+
+const char* w4a16_status_str(int32_t status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_NULL: return "null pointer";
+    case W4A16_ERR_SHAPE: return "bad shape";
+    case W4A16_ERR_UNSUPPORTED: return "unsupported configuration";
+    case W4A16_ERR_ALIGN: return "misaligned pointer";
+    case W4A16_ERR_HIP: return "HIP runtime error";
+    case W4A16_ERR_ARG: return "invalid argument";
+    default: return "unknown status";
+  }
+}
+
+const char* w4a16_last_error(void) { return g_last_error; }
+
+int32_t w4a16_gemv_max_m(void) { return w4a16::gemv_max_m(); }
+
+w4a16_status awq_channel_scale(const void* x_cal, int64_t T, int64_t K, double alpha, float* s, void* stream) {
+  clear_error();
+  if (!x_cal || !s) return fail(W4A16_ERR_NULL, "x_cal and s are required");
+  if (T <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "T and K must be positive");
+  if (T > kMaxT || K > W4A16_MAX_K) return fail(W4A16_ERR_SHAPE, "size beyond the limits (T <= 2^20, K <= %d)", W4A16_MAX_K);
+  if (!(alpha >= 0.0 && alpha <= 1.0)) return fail(W4A16_ERR_ARG, "alpha must lie in [0, 1]");
+  if (!aligned(x_cal, 2) || !aligned(s, 4)) return fail(W4A16_ERR_ALIGN, "x_cal must be 2-byte and s 4-byte aligned");
+  return hip_result(w4a16::launch_channel_scale(static_cast<const uint16_t*>(x_cal), T, K, alpha, s,
+                                                static_cast<hipStream_t>(stream)),
+                    "channel-scale launch");
+}
+
+w4a16_status awq_scale_input(const void* x, const float* s, int64_t M, int64_t K, void* x_s, void* stream) {
+  clear_error();
+  if (!x || !s || !x_s) return fail(W4A16_ERR_NULL, "x, s and x_s are required");
+  if (M <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "M and K must be positive");
+  if (M > kMaxM || K > W4A16_MAX_K) return fail(W4A16_ERR_SHAPE, "size beyond the limits (M <= 65536, K <= %d)", W4A16_MAX_K);
+  if (!aligned(x, 2) || !aligned(x_s, 2) || !aligned(s, 4))
+    return fail(W4A16_ERR_ALIGN, "x and x_s must be 2-byte and s 4-byte aligned");
+  return hip_result(w4a16::launch_scale_input(static_cast<const uint16_t*>(x), s, M, K, static_cast<uint16_t*>(x_s),
+                                              static_cast<hipStream_t>(stream)),
+                    "scale-input launch");
+}
+
+w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t K, int32_t bits, int32_t group,
+                               void* qweight, void* scales, void* zeros, void* stream) {
+  clear_error();
+  if (!w || !qweight || !scales || !zeros) return fail(W4A16_ERR_NULL, "w, qweight, scales and zeros are required");
+  if (bits != 4 || group != 128)
+    return fail(W4A16_ERR_UNSUPPORTED, "only bits=4, group=128 is supported (got bits=%d, group=%d)", (int)bits,
+                (int)group);
+  if (N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "N and K must be positive");
+  if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
+  if (K > W4A16_MAX_K || N > kMaxN) return fail(W4A16_ERR_SHAPE, "size beyond the limits (N <= 2^24, K <= %d)", W4A16_MAX_K);
+  if (!aligned(w, 16) || !aligned(qweight, 16) || (s && !aligned(s, 16)))
+    return fail(W4A16_ERR_ALIGN, "w, qweight and s must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(zeros, 2)) return fail(W4A16_ERR_ALIGN, "scales and zeros must be 2-byte aligned");
+  return hip_result(w4a16::launch_quantize_pack(static_cast<const uint16_t*>(w), s, N, K,
+                                                static_cast<uint32_t*>(qweight), static_cast<uint16_t*>(scales),
+                                                static_cast<uint16_t*>(zeros), static_cast<hipStream_t>(stream)),
+                    "quantize-pack launch");
+}
+
+w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
+                          int64_t N, int64_t K, int32_t group, void* y, void* stream) {
+  clear_error();
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  return run_linear(0, x, qweight, scales, zeros, M, N, K, y, static_cast<hipStream_t>(stream));
+}
+
+w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
+                               const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
+                               void* stream) {
+  clear_error();
+  if (path < 0 || path > 2) return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV) or 2 (MFMA)");
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  return run_linear(path, x, qweight, scales, zeros, M, N, K, y, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,160 @@
+// AWQ calibration statistic, the 1/s input fold, and RTN group quantize-pack
+// for gfx950.
+//
+// What is computed follows the "MIT 6.5940 L13 LLM Deployment" guide (AWQ
+// section: s = s_X^alpha, Q(w) = Delta * Round(w / Delta), 1/s folded into the
+// input), the Lab 4 setup of the "MIT 6.5940 Lab 4 + Lab 5" guide (mean |input|
+// per channel), and the "CMU 11-868 Model Quantization" guide, L19 zero-point
+// quantizer (range max - min, zero range counts as 1, integer zero offset,
+// clipped codes). Every quantity that decides a stored bit is computed in
+// float64 with IEEE division and round-half-even, so results are bit-identical
+// to the plain definition.
+#include "device_utils.h"
+#include "launchers.h"
+
+#pragma clang fp contract(off)
+
+namespace w4a16 {
+
+// ---------------------------------------------------------------------------
+// s[k] = (sum_t |x_cal[t][k]| / T)^alpha; one thread per channel, the loop over
+// tokens is coalesced across channels. The float64 sum of fp16 magnitudes is
+// exact (hence order-free) while T * max|x| < 2^29.
+__global__ __launch_bounds__(256) void channel_scale_kernel(const uint16_t* __restrict__ x_cal, int T, int K,
+                                                            double alpha, float* __restrict__ s) {
+  const int k = blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= K) return;
+  double acc0 = 0.0, acc1 = 0.0, acc2 = 0.0, acc3 = 0.0;
+  const uint16_t* p = x_cal + k;
+  int t = 0;
+  for (; t + 4 <= T; t += 4) {
+    acc0 += fabs((double)half_bits_to_float(p[(int64_t)(t + 0) * K]));
+    acc1 += fabs((double)half_bits_to_float(p[(int64_t)(t + 1) * K]));
+    acc2 += fabs((double)half_bits_to_float(p[(int64_t)(t + 2) * K]));
+    acc3 += fabs((double)half_bits_to_float(p[(int64_t)(t + 3) * K]));
+  }
+  for (; t < T; ++t) acc0 += fabs((double)half_bits_to_float(p[(int64_t)t * K]));
+  const double mean = ((acc0 + acc1) + (acc2 + acc3)) / (double)T;
+  double r;
+  if (mean == 0.0)
+    r = 1.0;
+  else if (alpha == 0.5)
+    r = sqrt(mean);
+  else if (alpha == 1.0)
+    r = mean;
+  else if (alpha == 0.0)
+    r = 1.0;
+  else
+    r = pow(mean, alpha);
+  s[k] = (float)r;
+}
+
+hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t T, int64_t K, double alpha, float* s,
+                                hipStream_t stream) {
+  const int block = 256;
+  const int grid = (int)((K + block - 1) / block);
+  hipLaunchKernelGGL(channel_scale_kernel, dim3(grid), dim3(block), 0, stream, x_cal, (int)T, (int)K, alpha, s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// x_s = f16(float64(x) / float64(s)), one correctly rounded division and one
+// round-to-nearest-even to binary16.
+__global__ __launch_bounds__(256) void scale_input_kernel(const uint16_t* __restrict__ x, const float* __restrict__ s,
+                                                          int64_t total, int K, uint16_t* __restrict__ x_s) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total; i += stride) {
+    const int k = (int)(i % K);
+    const double v = (double)half_bits_to_float(x[i]) / (double)s[k];
+    x_s[i] = f64_to_f16_rne(v);
+  }
+}
+
+hipError_t launch_scale_input(const uint16_t* x, const float* s, int64_t M, int64_t K, uint16_t* x_s,
+                              hipStream_t stream) {
+  const int64_t total = M * K;
+  const int block = 256;
+  int64_t grid = (total + block - 1) / block;
+  if (grid > 65536) grid = 65536;
+  hipLaunchKernelGGL(scale_input_kernel, dim3((unsigned)grid), dim3(block), 0, stream, x, s, total, (int)K, x_s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Quantize-pack. One 16-lane DPP row owns one group (128 inputs of one output
+// row): lane j loads the 8 fp16 weights k = 128g + 8j .. +7 (16 bytes, so a
+// wave reads 1 KB contiguous per load), multiplies by s in float64 (exact),
+// takes part in the row's min/max reduction, then writes exactly one packed
+// word (its 8 codes) - layout v1 puts the codes of 8 consecutive inputs in one
+// word. Lane 0 of the row writes the group's fp16 scale and zero.
+__global__ __launch_bounds__(256) void quantize_pack_kernel(const uint4* __restrict__ w, const float4* __restrict__ s,
+                                                            int64_t n_groups, int G, uint32_t* __restrict__ qweight,
+                                                            uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
+  const int64_t gid_raw = (int64_t)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4);
+  const int j = threadIdx.x & 15;
+  const bool valid = gid_raw < n_groups;  // uniform over the 16 lanes of a row
+  const int64_t gid = valid ? gid_raw : 0;
+  const int64_t n = gid / G;
+  const int g = (int)(gid - n * G);
+  const int64_t word_idx = n * ((int64_t)G * 16) + 16 * g + j;  // also the uint4 index of the lane's weights
+
+  const uint4 wv = w[word_idx];
+  const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
+  double v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = (double)half_bits_to_float((uint16_t)(wu[i] & 0xFFFFu));
+    v[2 * i + 1] = (double)half_bits_to_float((uint16_t)(wu[i] >> 16));
+  }
+  if (s != nullptr) {
+    const float4 s0 = s[32 * g + 2 * j];
+    const float4 s1 = s[32 * g + 2 * j + 1];
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * (double)sv[i];  // exact: 11 x 24 significant bits
+  }
+  double mn = v[0], mx = v[0];
+#pragma unroll
+  for (int i = 1; i < 8; ++i) {
+    mn = fmin(mn, v[i]);
+    mx = fmax(mx, v[i]);
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    mn = fmin(mn, __shfl_xor(mn, off, 16));
+    mx = fmax(mx, __shfl_xor(mx, off, 16));
+  }
+  double range = mx - mn;
+  if (range == 0.0) range = 1.0;
+  const double delta = range / 15.0;
+  const double z = rint(-mn / delta) + 0.0;  // + 0.0 makes a zero offset +0
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    double q = rint(v[i] / delta) + z;
+    q = fmin(fmax(q, 0.0), 15.0);
+    const uint32_t c = (uint32_t)q;
+    word |= c << ((i & 1) ? (16 + 4 * (i >> 1)) : (4 * (i >> 1)));
+  }
+  if (valid) {
+    qweight[word_idx] = word;
+    if (j == 0) {
+      scales[gid] = f64_to_f16_rne(delta);
+      zeros[gid] = f64_to_f16_rne(z);
+    }
+  }
+}
+
+hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, uint32_t* qweight,
+                                uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+  const int G = (int)(K / 128);
+  const int64_t n_groups = N * G;
+  const int block = 256;  // 16 groups per block
+  const int64_t grid = (n_groups + 15) / 16;
+  hipLaunchKernelGGL(quantize_pack_kernel, dim3((unsigned)grid), dim3(block), 0, stream,
+                     reinterpret_cast<const uint4*>(w), reinterpret_cast<const float4*>(s), n_groups, G, qweight,
+                     scales, zeros);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16

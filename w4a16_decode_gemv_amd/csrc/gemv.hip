@@ -1,0 +1,283 @@
+// W4A16 GEMV for small batches (M = 1..8) on gfx950.
+//
+// y[m][n] = sum_k x[m][k] * (q[n][k] - z[n][g]) * d[n][g], float32 accumulation.
+// This is TinyChat's fused dequantize + GEMV ("MIT 6.5940 L13 LLM Deployment"
+// guide, TinyChat kernel fusion, slide 37): weights are rebuilt in registers
+// and never written back. Batch-1 decode reads every weight once, so the kernel
+// is bound by HBM bandwidth ("CMU 11-868 Model Quantization" guide, where the
+// speed comes from; "MIT 6.5940 Lab 4 + Lab 5" guide, Lab 4 starting point).
+//
+// Work split
+//   * A workgroup owns R consecutive output rows and spans all of K: thread t
+//     owns the 16-byte code pieces p = t, t + T, ... of every row (a piece is
+//     32 inputs, i.e. 16 bytes of codes). A wave's code load is therefore
+//     1 KB of contiguous HBM per row (eight 128-byte lines).
+//   * Each thread keeps its x pieces in VGPRs for the whole tile (reused by
+//     all R rows) and issues the loads of all R rows before computing, so a
+//     workgroup has R KB per wave in flight.
+//   * The tile's (scale, zero) pairs are staged in LDS; each piece lies inside
+//     one group of 128, so each (row, piece) needs exactly one pair.
+//   * Partial sums are combined through LDS and a 16-lane DPP row sum.
+//
+// Dequantization (layout v1: (word >> 4i) & 0x000F000F is an input pair):
+//   OR-ing a nibble pair into 0x6400 gives the fp16 pair 1024 + q exactly
+//   (0x00F0 nibbles give 1024 + 16q); one v_pk_add_f16 (resp. v_pk_fma_f16 by
+//   1/16) turns that into q exactly. v_dot2_f32_f16 multiplies q pairs by x
+//   pairs into float32 (single rounding per instruction on normal operands).
+//   The zero point is applied once per piece: sum (q - z) x = sum q x - z sum x,
+//   exact in the integer part for any z, so no zero range is special.
+#include "device_utils.h"
+#include "launchers.h"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kMaxThreads = 512;
+constexpr int kMaxM = 8;
+constexpr int kRedPad = 16;  // LDS row padding of the reduction buffer (bank spread)
+
+// Rows per workgroup: R * M * PPT <= 16 keeps the code loads in flight at
+// 16/M KB per wave and the partial sums per thread at R * M <= 16.
+template <int M, int PPT>
+struct Tile {
+  static constexpr int R = (16 / (M * PPT)) > 0 ? (16 / (M * PPT)) : 1;
+  static constexpr int V = R * M;
+};
+
+__device__ __forceinline__ half2_t q_pair_lo(uint32_t w) {  // nibbles at bits 0-3 / 16-19
+  const half2_t b = as_half2(and_or(w, 0x000F000Fu, 0x64006400u));
+  return b - (half2_t){(_Float16)1024.0f, (_Float16)1024.0f};
+}
+
+__device__ __forceinline__ half2_t q_pair_hi(uint32_t w) {  // nibbles at bits 4-7 / 20-23
+  const half2_t b = as_half2(and_or(w, 0x00F000F0u, 0x64006400u));
+  return __builtin_elementwise_fma(b, (half2_t){(_Float16)0.0625f, (_Float16)0.0625f},
+                                   (half2_t){(_Float16)-64.0f, (_Float16)-64.0f});
+}
+
+template <int M, int PPT>
+__global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restrict__ x, const u32x4_t* __restrict__ qw,
+                                                           const uint16_t* __restrict__ scales,
+                                                           const uint16_t* __restrict__ zeros, int N, int K,
+                                                           uint16_t* __restrict__ y) {
+  constexpr int R = Tile<M, PPT>::R;
+  constexpr int V = Tile<M, PPT>::V;
+  constexpr int NS = (R * PPT + 3) / 4;  // staged (scale, zero) pairs per thread (T >= P / PPT)
+  extern __shared__ uint32_t lds[];
+
+  const int T = blockDim.x;
+  const int t = threadIdx.x;
+  const int G = K >> 7;   // groups per row
+  const int P = K >> 5;   // 16-byte code pieces per row
+  const int KX = K >> 3;  // 16-byte x chunks per input row
+  const int row0 = blockIdx.x * R;
+  const int rows = min(R, N - row0);
+  const int n_sz = rows * G;
+
+  // Every load below is unconditional, with indices clamped into the tensors, so
+  // the compiler can count outstanding loads exactly and let each row's compute
+  // start as soon as that row's codes have landed. Lanes past K (the last wave
+  // of a ragged K) compute with a zero scale; rows past N are never stored.
+
+  // (1) scale/zero loads of the tile (contiguous [rows][G] blocks)
+  uint16_t sreg[NS], zreg[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int i = min(t + u * T, n_sz - 1);
+    const int64_t off = (int64_t)row0 * G + i;
+    sreg[u] = scales[off];
+    zreg[u] = zeros[off];
+  }
+
+  // (2) x pieces: 32 inputs = four 16-byte chunks per row of x
+  uint32_t xr[PPT][M][16];
+#pragma unroll
+  for (int pp = 0; pp < PPT; ++pp) {
+    const int p = min(t + pp * T, P - 1);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = x[(int64_t)m * KX + 4 * p + c];
+        xr[pp][m][4 * c + 0] = v.x;
+        xr[pp][m][4 * c + 1] = v.y;
+        xr[pp][m][4 * c + 2] = v.z;
+        xr[pp][m][4 * c + 3] = v.w;
+      }
+    }
+  }
+
+  // (3) code pieces of all rows of the tile
+  u32x4_t cw[R][PPT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = min(row0 + r, N - 1);
+#pragma unroll
+    for (int pp = 0; pp < PPT; ++pp) {
+      const int p = min(t + pp * T, P - 1);
+      cw[r][pp] = __builtin_nontemporal_load(&qw[row * P + p]);
+    }
+  }
+
+  // (4) stage (scale, zero) as one packed word per group
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int i = t + u * T;
+    if (i < n_sz) lds[i] = (uint32_t)sreg[u] | ((uint32_t)zreg[u] << 16);
+  }
+
+  // sum of x over each piece (for the zero-point term)
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float sx[PPT][M];
+#pragma unroll
+  for (int pp = 0; pp < PPT; ++pp)
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = __builtin_amdgcn_fdot2(as_half2(xr[pp][m][j]), ones, a, false);
+      sx[pp][m] = a;
+    }
+
+  __syncthreads();
+
+  // (5) dequantize + multiply, row by row as the loads land
+  float acc[R][M];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int rr = min(r, rows - 1);
+#pragma unroll
+    for (int pp = 0; pp < PPT; ++pp) {
+      const int p_raw = t + pp * T;
+      const int p = min(p_raw, P - 1);
+      const uint32_t sz = lds[rr * G + (p >> 2)];
+      const float d = (p_raw < P) ? half_bits_to_float((uint16_t)(sz & 0xFFFFu)) : 0.f;
+      const float z = half_bits_to_float((uint16_t)(sz >> 16));
+      const uint32_t wd[4] = {cw[r][pp].x, cw[r][pp].y, cw[r][pp].z, cw[r][pp].w};
+      float part[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) part[m] = 0.f;
+#pragma unroll
+      for (int wi = 0; wi < 4; ++wi) {
+        const uint32_t w0 = wd[wi];
+        const uint32_t w8 = w0 >> 8;
+        const half2_t q01 = q_pair_lo(w0);
+        const half2_t q23 = q_pair_hi(w0);
+        const half2_t q45 = q_pair_lo(w8);
+        const half2_t q67 = q_pair_hi(w8);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          float a = part[m];
+          a = __builtin_amdgcn_fdot2(q01, as_half2(xr[pp][m][4 * wi + 0]), a, false);
+          a = __builtin_amdgcn_fdot2(q23, as_half2(xr[pp][m][4 * wi + 1]), a, false);
+          a = __builtin_amdgcn_fdot2(q45, as_half2(xr[pp][m][4 * wi + 2]), a, false);
+          a = __builtin_amdgcn_fdot2(q67, as_half2(xr[pp][m][4 * wi + 3]), a, false);
+          part[m] = a;
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[r][m]);
+    }
+  }
+
+  // (6) reduce the V partials of every thread over the workgroup
+  __syncthreads();  // the LDS region is reused for the reduction
+  float* red = reinterpret_cast<float*>(lds);
+  const int stride = T + kRedPad;
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int m = 0; m < M; ++m) red[(r * M + m) * stride + t] = acc[r][m];
+  __syncthreads();
+  const int j = t & 15;
+  for (int v = t >> 4; v < V; v += (T >> 4)) {
+    float s = 0.f;
+    for (int i = j; i < T; i += 16) s += red[v * stride + i];
+    s = dpp_row_sum16(s);
+    const int r = v / M;
+    const int m = v - r * M;
+    if (j == 0 && r < rows) y[(int64_t)m * N + row0 + r] = float_to_half_bits(s);
+  }
+}
+
+struct Launch {
+  int ppt;
+  int threads;
+};
+
+Launch plan(int64_t K) {
+  const int P = (int)(K >> 5);
+  int ppt = 1;
+  while ((P + ppt - 1) / ppt > kMaxThreads) ppt <<= 1;
+  int t = (P + ppt - 1) / ppt;
+  t = (t + 63) & ~63;
+  return {ppt, t};
+}
+
+template <int M, int PPT>
+hipError_t launch_mp(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                     int64_t N, int64_t K, uint16_t* y, int threads, hipStream_t stream) {
+  constexpr int R = Tile<M, PPT>::R;
+  constexpr int V = Tile<M, PPT>::V;
+  const int G = (int)(K >> 7);
+  const size_t lds_sz = (size_t)R * G * 4;
+  const size_t lds_red = (size_t)V * (threads + kRedPad) * 4;
+  const size_t lds = lds_sz > lds_red ? lds_sz : lds_red;
+  const int grid = (int)((N + R - 1) / R);
+  hipLaunchKernelGGL((gemv_kernel<M, PPT>), dim3(grid), dim3(threads), lds, stream,
+                     reinterpret_cast<const uint4*>(x), reinterpret_cast<const u32x4_t*>(qweight), scales, zeros,
+                     (int)N, (int)K, y);
+  return hipGetLastError();
+}
+
+template <int M>
+hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                    int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  const Launch l = plan(K);
+  switch (l.ppt) {
+    case 1: return launch_mp<M, 1>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+    case 2:
+      if constexpr (M <= 4) return launch_mp<M, 2>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      break;
+    case 4:
+      if constexpr (M <= 2) return launch_mp<M, 4>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      break;
+    case 8:
+      if constexpr (M <= 1) return launch_mp<M, 8>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int gemv_max_m() { return kMaxM; }
+
+bool gemv_supports(int64_t M, int64_t K) {
+  if (M < 1 || M > kMaxM || K <= 0 || K % 128 != 0) return false;
+  return plan(K).ppt * M <= 8;
+}
+
+hipError_t launch_gemv(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                       int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  switch (M) {
+    case 1: return launch_m<1>(x, qweight, scales, zeros, N, K, y, stream);
+    case 2: return launch_m<2>(x, qweight, scales, zeros, N, K, y, stream);
+    case 3: return launch_m<3>(x, qweight, scales, zeros, N, K, y, stream);
+    case 4: return launch_m<4>(x, qweight, scales, zeros, N, K, y, stream);
+    case 5: return launch_m<5>(x, qweight, scales, zeros, N, K, y, stream);
+    case 6: return launch_m<6>(x, qweight, scales, zeros, N, K, y, stream);
+    case 7: return launch_m<7>(x, qweight, scales, zeros, N, K, y, stream);
+    case 8: return launch_m<8>(x, qweight, scales, zeros, N, K, y, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace w4a16

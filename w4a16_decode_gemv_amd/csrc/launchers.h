@@ -1,0 +1,32 @@
+// Internal kernel launchers. Arguments are already validated by the C ABI
+// (abi.hip); each launcher enqueues its kernel(s) on `stream` and returns the
+// HIP status of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t T, int64_t K, double alpha, float* s,
+                                hipStream_t stream);
+
+hipError_t launch_scale_input(const uint16_t* x, const float* s, int64_t M, int64_t K, uint16_t* x_s,
+                              hipStream_t stream);
+
+hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, uint32_t* qweight,
+                                uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+
+// GEMV kernel: needs M <= gemv_max_m() and gemv_supports(M, K).
+int gemv_max_m();
+bool gemv_supports(int64_t M, int64_t K);
+hipError_t launch_gemv(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                       const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                       hipStream_t stream);
+
+// MFMA kernel: any M >= 1.
+hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                       const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                       hipStream_t stream);
+
+}  // namespace w4a16
