@@ -1,0 +1,329 @@
+"""Benchmark of the W4A16 decode GEMV on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--set] [--no-cpu]
+
+One step is one call of the fused dequantize GEMV at M = 1, K = N = 8192 (the
+LLaMA-65B q/k/v/o projection at batch-1 decode), on inputs already resident in
+HBM. The inputs are built by the library itself on the GPU: AWQ channel scale
+from 512 calibration tokens, the 1/s fold of x, and the RTN g128 quantize-pack
+(timed separately as the offline leg). The calls rotate over 16 copies of the
+packed layer (>= 512 MiB) so the 256 MB Infinity Cache cannot serve them.
+
+Prints ONE JSON line (metric, value = achieved GB/s over the timed steps,
+ms_per_step = time per call including launch gaps, roofline of the GEMV kernel,
+CPU-oracle baseline, and extra legs).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A16 GEMV achieved HBM GB/s (% of peak) + µs/call at M=1, K=N=8192"
+HBM_PEAK_GBS = 8000.0
+ROTATE_BYTES = 1 << 29  # two Infinity Caches' worth of distinct buffers
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1_k8192_n8192.json")
+
+
+def algorithmic_bytes(m, n, k, group=128):
+    """Bytes the method must move once: 4-bit codes + fp16 scale and zero per
+    group + fp16 x in + fp16 y out."""
+    return n * k // 2 + 2 * 2 * n * (k // group) + 2 * m * k + 2 * m * n
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "w4a16_decode_gemv_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=2000)
+    p.add_argument("--warmup", type=int, default=200)
+    p.add_argument("--sweep", action="store_true", help="also time the config-4 batch sweep on both kernels")
+    p.add_argument("--set", dest="llama_set", action="store_true", help="also time the 7-projection LLaMA-65B set")
+    p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--only-gemv", action="store_true", help="time the headline GEMV only (for profilers)")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="after the GEMV, run a plain 64 MiB elementwise copy 5 times (counter calibration)")
+    return p.parse_args()
+
+
+class Layer:
+    """One packed layer built on the GPU by the library, replicated `copies` times."""
+
+    def __init__(self, w4, torch, cfg, layer_id, n, k, m, copies):
+        import synth
+
+        dev = "cuda:0"
+        L = synth.layer(cfg, layer_id, n, k, m)
+        self.n, self.k, self.m = n, k, m
+        W = torch.from_numpy(L["W"]).to(dev)
+        xc = torch.from_numpy(L["x_cal"]).to(dev)
+        x = torch.from_numpy(L["x"]).to(dev)
+        self.s = w4.channel_scale(xc, 0.5)
+        self.x = w4.scale_input(x, self.s)
+        qw, sc, zr = w4.quantize_pack(W, self.s)
+        self.W = W
+        self.copies = [(self.x.clone(), qw.clone(), sc.clone(), zr.clone()) for _ in range(copies)]
+        self.y = [torch.empty((m, n), dtype=torch.float16, device=dev) for _ in range(copies)]
+        del qw, sc, zr
+        torch.cuda.synchronize()
+
+    def call(self, w4, i, path=0):
+        x, qw, sc, zr = self.copies[i % len(self.copies)]
+        w4.linear(x, qw, sc, zr, out=self.y[i % len(self.y)], path=path)
+
+
+def copies_for(nbytes):
+    return max(2, -(-ROTATE_BYTES // nbytes))
+
+
+def time_back_to_back(torch, fn, steps, warmup):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps  # ms per call
+
+
+def time_per_launch(torch, fn, steps):
+    """Average of per-launch HIP event pairs (start/end around every launch)."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[i][0].record()
+        fn(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    d = sorted(a.elapsed_time(b) for a, b in ev)
+    return sum(d) / len(d), d[len(d) // 2]
+
+
+def time_graph(torch, fn, steps, reps=5):
+    """Launches captured into one HIP graph; ms per launch over `reps` replays."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn(0)  # warm the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(steps):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * steps)
+
+
+def cpu_baseline(layer, seconds):
+    """The oracle's linear (NumPy float64) on the host, timed on whole-layer calls."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        blas_threads = max([p.get("num_threads", 1) for p in blas] or [1])
+    except Exception:  # threadpoolctl missing: report what numpy would use
+        blas_threads = len(os.sched_getaffinity(0))
+    x = layer.x.cpu().numpy()
+    qw, sc, zr = (t.cpu().numpy() for t in layer.copies[0][1:])
+    qw = qw.view(np.uint32)
+    n_calls, t_total = 0, 0.0
+    t0 = time.perf_counter()
+    while True:
+        a = time.perf_counter()
+        oracle.linear(x, qw, sc, zr)
+        t_total += time.perf_counter() - a
+        n_calls += 1
+        if time.perf_counter() - t0 >= seconds and n_calls >= 2:
+            break
+    us = t_total / n_calls * 1e6
+    nbytes = algorithmic_bytes(layer.m, layer.n, layer.k)
+    return {
+        "value": nbytes / (us * 1e-6) / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{n_calls} whole-layer calls of the float64 NumPy oracle linear (M=1, K=N=8192), "
+                  f"{t_total:.1f} s; {us:.0f} us/call; dequantize is single-threaded NumPy, the matvec uses "
+                  f"{blas_threads} BLAS threads",
+        "us_per_call": us,
+    }
+
+
+def traffic_entry(achieved_bytes_per_launch):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise null."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != source_hash("gemv.hip", "device_utils.h"):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this path has no multi-GPU leg (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        return 2
+    import torch
+
+    import w4a16_decode_gemv_amd as w4
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    w4.load()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+
+    n = k = 8192
+    m = 1
+    nbytes = algorithmic_bytes(m, n, k)
+    layer = Layer(w4, torch, 3, 0, n, k, m, copies_for(nbytes))
+    fn = lambda i: layer.call(w4, i)  # noqa: E731
+
+    # ---- the timed region: exactly `steps` calls, synchronized on both sides
+    ms = time_back_to_back(torch, fn, args.steps, args.warmup)
+    value = nbytes / (ms * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": "W4A16 linear M=1 K=8192 N=8192 (LLaMA-65B q/k/v/o projection, batch-1 decode), "
+                        "4-bit g128 asymmetric, fp16 x/y, fp32 accumulate",
+            "M": m, "K": k, "N": n, "group": 128,
+            "rotating_copies": len(layer.copies),
+            "algorithmic_bytes_per_call": nbytes,
+            "device": props.name, "cus": props.multi_processor_count,
+        },
+    }
+    if args.copy_probe:
+        # a plain read-once/write-once kernel of known size: 64 MiB in, 64 MiB out
+        a = torch.ones(32 << 20, dtype=torch.float16, device="cuda:0")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            torch.mul(a, 1.0, out=b)
+        torch.cuda.synchronize()
+        out["copy_probe_bytes"] = {"read": a.numel() * 2, "write": b.numel() * 2, "kernel": "torch.mul(a, 1.0, out=b)"}
+    if args.only_gemv:
+        print(json.dumps(out), flush=True)
+        return 0
+
+    # ---- kernel duration (HIP events) for the roofline
+    avg_ms, med_ms = time_per_launch(torch, fn, min(args.steps, 400))
+    graph_ms = time_graph(torch, fn, 200)
+    kernel_ms = graph_ms
+    achieved = nbytes / (kernel_ms * 1e-3) / 1e9
+    out["roofline"] = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic_entry(nbytes),
+        "kernel_us": kernel_ms * 1e3,
+        "timing": "HIP events around a replayed HIP graph of 200 back-to-back GEMV launches",
+    }
+    out["timings_us"] = {
+        "eager_back_to_back_per_call": ms * 1e3,
+        "per_launch_event_pair_mean": avg_ms * 1e3,
+        "per_launch_event_pair_median": med_ms * 1e3,
+        "graph_per_launch": graph_ms * 1e3,
+    }
+
+    # ---- offline leg: quantize-pack of the same layer
+    qout = tuple(t.clone() for t in layer.copies[0][1:])
+    qfn = lambda i: w4.quantize_pack(layer.W, layer.s, out=qout)  # noqa: E731
+    q_ms = time_back_to_back(torch, qfn, 20, 3)
+    q_bytes = n * k * 2 + k * 4 + n * k // 2 + 2 * 2 * n * (k // 128)
+    out["quantize_pack"] = {"us_per_call": q_ms * 1e3, "GB_s": q_bytes / (q_ms * 1e-3) / 1e9,
+                            "bytes": q_bytes, "note": "offline: fp16 W + fp32 s in, packed codes/scales/zeros out"}
+
+    if args.llama_set:
+        import synth
+
+        total_bytes, total_us, per = 0, 0.0, []
+        for lid, (name, kk, nn) in enumerate(synth.CONFIGS[3]["layers"]):
+            if name in ("k", "v", "o"):
+                continue
+            b = algorithmic_bytes(1, nn, kk)
+            L = Layer(w4, torch, 3, lid, nn, kk, 1, copies_for(b))
+            t = time_graph(torch, lambda i: L.call(w4, i), 100)
+            reps = 4 if name == "q" else 1
+            per.append({"layer": name, "K": kk, "N": nn, "us": t * 1e3, "GB_s": b / (t * 1e-3) / 1e9, "count": reps})
+            total_bytes += reps * b
+            total_us += reps * t * 1e3
+            del L
+            torch.cuda.empty_cache()
+        out["llama65b_set"] = {"us": total_us, "GB_s": total_bytes / (total_us * 1e-6) / 1e9, "layers": per}
+
+    if args.sweep:
+        import synth
+
+        rows = []
+        for mm in (1, 2, 4, 8, 16, 32):
+            b = algorithmic_bytes(mm, 8192, 8192)
+            L = Layer(w4, torch, 4, 0, 8192, 8192, mm, copies_for(b))
+            for path in (1, 2):
+                if path == 1 and mm > w4.gemv_max_m():
+                    continue
+                t = time_graph(torch, lambda i: L.call(w4, i, path), 100)
+                rows.append({"M": mm, "path": "gemv" if path == 1 else "mfma", "us": t * 1e3,
+                             "GB_s": b / (t * 1e-3) / 1e9, "TFLOP_s": 2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12})
+            del L
+            torch.cuda.empty_cache()
+        out["sweep_k8192_n8192"] = rows
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -14,7 +14,8 @@
 //     1 KB of contiguous HBM per row (eight 128-byte lines).
 //   * Each thread keeps its x pieces in VGPRs for the whole tile (reused by
 //     all R rows) and issues the loads of all R rows before computing, so a
-//     workgroup has R KB per wave in flight.
+//     wave has R KB in flight. Code loads are non-temporal: the weights are
+//     streamed once and should not displace x or the scales in the caches.
 //   * The tile's (scale, zero) pairs are staged in LDS; each piece lies inside
 //     one group of 128, so each (row, piece) needs exactly one pair.
 //   * Partial sums are combined through LDS and a 16-lane DPP row sum.
@@ -37,11 +38,15 @@ constexpr int kMaxThreads = 512;
 constexpr int kMaxM = 8;
 constexpr int kRedPad = 16;  // LDS row padding of the reduction buffer (bank spread)
 
-// Rows per workgroup: R * M * PPT <= 16 keeps the code loads in flight at
-// 16/M KB per wave and the partial sums per thread at R * M <= 16.
+// Rows per workgroup. Measured on MI355X at K = N = 8192: for M = 1, 8 rows
+// per 4-wave workgroup (1024 workgroups, four per CU) streams better than 16
+// rows (512 workgroups) or 4 rows (2048 workgroups, where the per-workgroup x
+// reads double); for M >= 2 the x reads grow with M, and R * M * PPT <= 16
+// keeps more rows sharing them.
 template <int M, int PPT>
 struct Tile {
-  static constexpr int R = (16 / (M * PPT)) > 0 ? (16 / (M * PPT)) : 1;
+  static constexpr int kBudget = (M == 1) ? 8 : 16;
+  static constexpr int R = (kBudget / (M * PPT)) > 0 ? (kBudget / (M * PPT)) : 1;
   static constexpr int V = R * M;
 };
 
