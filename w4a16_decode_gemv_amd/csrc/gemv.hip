@@ -16,9 +16,12 @@
 //     all R rows) and issues the loads of all R rows before computing, so a
 //     wave has R KB in flight. Code loads are non-temporal: the weights are
 //     streamed once and should not displace x or the scales in the caches.
-//   * The tile's (scale, zero) pairs are staged in LDS; each piece lies inside
-//     one group of 128, so each (row, piece) needs exactly one pair.
-//   * Partial sums are combined through LDS and a 16-lane DPP row sum.
+//   * Each piece lies inside one group of 128, so each (row, piece) needs one
+//     (scale, zero) pair; each wave stages the pairs of its own 16 groups in
+//     its own LDS area (no workgroup barrier before compute).
+//   * A row's partial sums are added across the wave with DPP as soon as the
+//     row is computed; one barrier at the end adds the waves' sums in a fixed
+//     order (deterministic).
 //
 // Dequantization (layout v1: (word >> 4i) & 0x000F000F is an input pair):
 //   OR-ing a nibble pair into 0x6400 gives the fp16 pair 1024 + q exactly
@@ -36,7 +39,6 @@ namespace {
 
 constexpr int kMaxThreads = 512;
 constexpr int kMaxM = 8;
-constexpr int kRedPad = 16;  // LDS row padding of the reduction buffer (bank spread)
 
 // Rows per workgroup. Measured on MI355X at K = N = 8192: for M = 1, 8 rows
 // per 4-wave workgroup (1024 workgroups, four per CU) streams better than 16
@@ -68,29 +70,36 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restri
                                                            uint16_t* __restrict__ y) {
   constexpr int R = Tile<M, PPT>::R;
   constexpr int V = Tile<M, PPT>::V;
-  constexpr int NS = (R * PPT + 3) / 4;  // staged (scale, zero) pairs per thread (T >= P / PPT)
-  extern __shared__ uint32_t lds[];
+  constexpr int E = R * PPT * 16;        // (scale, zero) pairs one wave needs: R rows x PPT slots x 16 groups
+  constexpr int NE = (E + 63) / 64;      // ... per lane
+  extern __shared__ uint32_t lds[];      // per wave: E staged pairs, then V partial sums
 
   const int T = blockDim.x;
   const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
   const int G = K >> 7;   // groups per row
   const int P = K >> 5;   // 16-byte code pieces per row
   const int KX = K >> 3;  // 16-byte x chunks per input row
   const int row0 = blockIdx.x * R;
   const int rows = min(R, N - row0);
-  const int n_sz = rows * G;
+  uint32_t* wsz = lds + wave * (E + V);  // this wave's staging area
+  float* wred = reinterpret_cast<float*>(wsz + E);
 
-  // Every load below is unconditional, with indices clamped into the tensors, so
-  // the compiler can count outstanding loads exactly and let each row's compute
-  // start as soon as that row's codes have landed. Lanes past K (the last wave
-  // of a ragged K) compute with a zero scale; rows past N are never stored.
+  // Every load below is unconditional, with indices clamped into the tensors,
+  // so the compiler can count outstanding loads exactly and let each row's
+  // compute start as soon as that row's codes have landed. Lanes past K (the
+  // last wave of a ragged K) compute with a zero scale; rows past N are never
+  // stored.
 
-  // (1) scale/zero loads of the tile (contiguous [rows][G] blocks)
-  uint16_t sreg[NS], zreg[NS];
+  // (1) the (scale, zero) pairs this wave needs: lanes of piece slot pp cover
+  //     16 consecutive groups starting at 16 * wave + pp * T / 4
+  uint16_t sreg[NE], zreg[NE];
 #pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    const int i = min(t + u * T, n_sz - 1);
-    const int64_t off = (int64_t)row0 * G + i;
+  for (int u = 0; u < NE; ++u) {
+    const int e = min(lane + 64 * u, E - 1);
+    const int r = e / (16 * PPT), pp = (e >> 4) % PPT, gl = e & 15;
+    const int g = min(16 * wave + pp * (T >> 2) + gl, G - 1);
+    const int64_t off = (int64_t)min(row0 + r, N - 1) * G + g;
     sreg[u] = scales[off];
     zreg[u] = zeros[off];
   }
@@ -113,7 +122,7 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restri
     }
   }
 
-  // (3) code pieces of all rows of the tile
+  // (3) code pieces of all rows of the tile (non-temporal: read once)
   u32x4_t cw[R][PPT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -125,11 +134,12 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restri
     }
   }
 
-  // (4) stage (scale, zero) as one packed word per group
+  // (4) stage this wave's (scale, zero) pairs; only this wave reads them, and
+  //     a wave sees its own LDS writes in order, so no workgroup barrier
 #pragma unroll
-  for (int u = 0; u < NS; ++u) {
-    const int i = t + u * T;
-    if (i < n_sz) lds[i] = (uint32_t)sreg[u] | ((uint32_t)zreg[u] << 16);
+  for (int u = 0; u < NE; ++u) {
+    const int e = lane + 64 * u;
+    if (e < E) wsz[e] = (uint32_t)sreg[u] | ((uint32_t)zreg[u] << 16);
   }
 
   // sum of x over each piece (for the zero-point term)
@@ -145,25 +155,20 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restri
       sx[pp][m] = a;
     }
 
-  __syncthreads();
-
-  // (5) dequantize + multiply, row by row as the loads land
-  float acc[R][M];
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) acc[r][m] = 0.f;
-
+  // (5) row by row as the loads land: dequantize, multiply, and sum the row's
+  //     partials across the wave at once (the DPP work of early rows overlaps
+  //     the loads of later ones)
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int rr = min(r, rows - 1);
+    float acc[M];
+#pragma unroll
+    for (int m = 0; m < M; ++m) acc[m] = 0.f;
 #pragma unroll
     for (int pp = 0; pp < PPT; ++pp) {
       const int p_raw = t + pp * T;
-      const int p = min(p_raw, P - 1);
-      const uint32_t sz = lds[rr * G + (p >> 2)];
-      const float d = (p_raw < P) ? half_bits_to_float((uint16_t)(sz & 0xFFFFu)) : 0.f;
-      const float z = half_bits_to_float((uint16_t)(sz >> 16));
+      const uint32_t szv = wsz[(r * PPT + pp) * 16 + (lane >> 2)];
+      const float d = (p_raw < P) ? half_bits_to_float((uint16_t)(szv & 0xFFFFu)) : 0.f;
+      const float z = half_bits_to_float((uint16_t)(szv >> 16));
       const uint32_t wd[4] = {cw[r][pp].x, cw[r][pp].y, cw[r][pp].z, cw[r][pp].w};
       float part[M];
 #pragma unroll
@@ -187,27 +192,24 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restri
         }
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m) acc[r][m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[r][m]);
+      for (int m = 0; m < M; ++m) acc[m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float s = wave_sum_lane63(acc[m]);
+      if (lane == 63) wred[r * M + m] = s;
     }
   }
 
-  // (6) reduce the V partials of every thread over the workgroup
-  __syncthreads();  // the LDS region is reused for the reduction
-  float* red = reinterpret_cast<float*>(lds);
-  const int stride = T + kRedPad;
-#pragma unroll
-  for (int r = 0; r < R; ++r)
-#pragma unroll
-    for (int m = 0; m < M; ++m) red[(r * M + m) * stride + t] = acc[r][m];
+  // (6) add the waves' sums in a fixed order and store
   __syncthreads();
-  const int j = t & 15;
-  for (int v = t >> 4; v < V; v += (T >> 4)) {
+  const int nw = T >> 6;
+  for (int v = t; v < rows * M; v += T) {
     float s = 0.f;
-    for (int i = j; i < T; i += 16) s += red[v * stride + i];
-    s = dpp_row_sum16(s);
+    for (int w = 0; w < nw; ++w) s += reinterpret_cast<const float*>(lds + w * (E + V) + E)[v];
     const int r = v / M;
     const int m = v - r * M;
-    if (j == 0 && r < rows) y[(int64_t)m * N + row0 + r] = float_to_half_bits(s);
+    y[(int64_t)m * N + row0 + r] = float_to_half_bits(s);
   }
 }
 
@@ -230,10 +232,8 @@ hipError_t launch_mp(const uint16_t* x, const uint32_t* qweight, const uint16_t*
                      int64_t N, int64_t K, uint16_t* y, int threads, hipStream_t stream) {
   constexpr int R = Tile<M, PPT>::R;
   constexpr int V = Tile<M, PPT>::V;
-  const int G = (int)(K >> 7);
-  const size_t lds_sz = (size_t)R * G * 4;
-  const size_t lds_red = (size_t)V * (threads + kRedPad) * 4;
-  const size_t lds = lds_sz > lds_red ? lds_sz : lds_red;
+  constexpr int E = R * PPT * 16;
+  const size_t lds = (size_t)(threads / 64) * (E + V) * 4;
   const int grid = (int)((N + R - 1) / R);
   hipLaunchKernelGGL((gemv_kernel<M, PPT>), dim3(grid), dim3(threads), lds, stream,
                      reinterpret_cast<const uint4*>(x), reinterpret_cast<const u32x4_t*>(qweight), scales, zeros,
