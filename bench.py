@@ -306,14 +306,15 @@ def main():
         import synth
 
         rows = []
-        for mm in (1, 2, 4, 8, 16, 32):
+        names = {0: "auto", 1: "gemv", 2: "mfma_tiled", 3: "mfma_small_batch"}
+        for mm in (1, 2, 3, 4, 8, 16, 32, 48, 64):
             b = algorithmic_bytes(mm, 8192, 8192)
             L = Layer(w4, torch, 4, 0, 8192, 8192, mm, copies_for(b))
-            for path in (1, 2):
-                if path == 1 and mm > w4.gemv_max_m():
+            for path in (1, 3, 2, 0):
+                if (path == 1 and mm > w4.gemv_max_m()) or (path == 3 and mm > 32):
                     continue
                 t = time_graph(torch, lambda i: L.call(w4, i, path), 100)
-                rows.append({"M": mm, "path": "gemv" if path == 1 else "mfma", "us": t * 1e3,
+                rows.append({"M": mm, "path": names[path], "us": t * 1e3,
                              "GB_s": b / (t * 1e-3) / 1e9, "TFLOP_s": 2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12})
             del L
             torch.cuda.empty_cache()

@@ -135,8 +135,10 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * B = sum_k |x[m][k] * w_hat[n][k]|: |y - exact| <= 1e-3 * B + 1e-5.
  * x: fp16 [M][K], the input after the 1/s fold; qweight/scales/zeros as written
  * by awq_quantize_pack; y: fp16 [M][N] (output). group must be 128.
- * Dispatch: M <= w4a16_gemv_max_m() runs the wave-tile GEMV kernel, larger M
- * the MFMA kernel. Alignment: x and qweight 16 bytes, scales/zeros/y 2 bytes.
+ * Dispatch: M == 1 runs the wave-tile GEMV kernel, 2 <= M <= 32 the
+ * small-batch MFMA kernel (workgroups own whole rows of y, waves split K), and
+ * larger M the tiled MFMA kernel. Alignment: x and qweight 16 bytes,
+ * scales/zeros/y 2 bytes.
  */
 w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
@@ -144,13 +146,16 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
 /*
  * w4a16_linear_path - w4a16_linear with the kernel chosen by the caller, for
  * measuring the GEMV/MFMA hand-off: path 0 = automatic (same as w4a16_linear),
- * 1 = GEMV kernel (needs M <= 8), 2 = MFMA kernel. Same contract otherwise.
+ * 1 = GEMV kernel (needs M <= w4a16_gemv_max_m() and M * ceil(K / 16384) <= 8),
+ * 2 = tiled MFMA kernel (any M), 3 = small-batch MFMA kernel (needs M <= 32).
+ * A path that cannot take the shape returns W4A16_ERR_UNSUPPORTED before any
+ * HIP call. Same contract otherwise.
  */
 w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,
                                void* y, void* stream);
 
-/* Largest M that w4a16_linear sends to the GEMV kernel. */
+/* Largest M that the GEMV kernel (w4a16_linear_path path 1) accepts. */
 int32_t w4a16_gemv_max_m(void);
 
 #ifdef __cplusplus

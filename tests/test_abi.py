@@ -80,8 +80,11 @@ def test_linear_rejects_before_any_hip_call(kw, status):
 
 def test_linear_path_rejects_unknown_path_and_big_m_on_gemv():
     lib = w4.load()
-    assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear_path(4, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear_path(-1, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w4a16_linear_path(1, A16, A16, A16, A16, 9, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    # the small-batch MFMA kernel takes M <= 32
+    assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 33, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     # M * ceil(K / 16384) must stay <= 8 on the GEMV path
     assert lib.w4a16_linear_path(1, A16, A16, A16, A16, 8, 64, 32768, 128, A16, None) == w4.ERR_UNSUPPORTED
 

@@ -66,9 +66,38 @@ def test_mfma_small_shapes(lib, m, n, k):
     _check(lib, xs, qw, sc, zr, path=2, tag="mfma")
 
 
+@pytest.mark.parametrize("m", [1, 2, 3, 7, 16, 17, 31, 32])
+@pytest.mark.parametrize("n,k", [(300, 2048), (97, 11008), (64, 384), (1, 128), (40, 1408), (8200, 1024)])
+def test_skinny_small_shapes(lib, m, n, k):
+    # K = 384 and 128 leave some of the eight K-splitting waves without a group; K = 1408 (11 groups)
+    # and 11008 give uneven splits and half-filled last stages; N = 8200 takes the two-tile-per-wave
+    # variant with a ragged last workgroup
+    xs, qw, sc, zr = _packed(4, 50 + m, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=3, tag="skinny")
+
+
+def test_skinny_long_rows(lib):
+    for m, k in [(2, 22016), (9, 65536), (32, 22016)]:
+        xs, qw, sc, zr = _packed(4, 41, 70, k, m)
+        _check(lib, xs, qw, sc, zr, path=3, tag="skinny-long")
+
+
+def test_skinny_rejects_large_batches(lib):
+    import torch
+
+    from w4a16_decode_gemv_amd import W4A16Error
+
+    g = _gpu()
+    x = torch.zeros((33, 128), dtype=torch.float16, device=g.DEV)
+    qw = torch.zeros((16, 16), dtype=torch.int32, device=g.DEV)
+    sz = torch.zeros((16, 1), dtype=torch.float16, device=g.DEV)
+    with pytest.raises(W4A16Error, match="small-batch"):
+        lib.linear(x, qw, sz, sz, path=3)
+
+
 def test_config1_single_layer(lib):
     xs, qw, sc, zr = _packed(1, 0, 2048, 2048, 1)
-    for path in (0, 1, 2):
+    for path in (0, 1, 2, 3):
         _check(lib, xs, qw, sc, zr, path=path, tag="config1")
 
 
@@ -96,7 +125,7 @@ def test_config3_llama65b_full_size_sampled(lib, layer_id):
 def test_config4_batch_sweep_both_paths(lib, m):
     xs, qw, sc, zr = _packed(4, 0, 8192, 8192, m)
     rows = _sampled_rows(8192, m)
-    paths = (1, 2) if m <= 8 else (2,)
+    paths = (1, 2, 3) if m <= 8 else (2, 3)
     for path in paths:
         _check(lib, xs, qw, sc, zr, path=path, rows=rows, tag="config4")
     _check(lib, xs, qw, sc, zr, path=0, rows=rows, tag="config4-auto")
@@ -111,12 +140,27 @@ def test_config5_batched_serving(lib, m, layer_id):
 
 
 @pytest.mark.parametrize("kind", ["positive", "negative", "constant", "ties", "mixed"])
-@pytest.mark.parametrize("path,m", [(1, 1), (1, 3), (2, 1), (2, 20)])
+@pytest.mark.parametrize("path,m", [(1, 1), (1, 3), (2, 1), (2, 20), (3, 2), (3, 32)])
 def test_edge_weights(lib, kind, path, m):
     n, k = 70, 1024
     W = synth.edge_weights(kind, n, k, seed=11)
     xs, qw, sc, zr = _packed(6, 1, n, k, m, W=W)
     _check(lib, xs, qw, sc, zr, path=path, tag=f"edge-{kind}")
+
+
+@pytest.mark.parametrize("kind", ["positive", "negative", "mixed"])
+@pytest.mark.parametrize("path,m", [(1, 1), (1, 4), (2, 1), (2, 20), (3, 2), (3, 32)])
+def test_zeros_outside_the_exact_fp16_range(lib, kind, path, m):
+    # quantized without the AWQ scale, narrow one-signed groups get |zero| up to ~3400; the MFMA kernels
+    # cannot form (q - z) exactly in fp16 beyond [-2032, 1024] and must take their general route there,
+    # in waves that also hold in-range groups
+    n, k = 70, 1024
+    W = synth.edge_weights(kind, n, k, seed=11)
+    qw, sc, zr = oracle.quantize_pack(W, None)
+    z = zr.astype(np.float64)
+    assert ((z < -2032) | (z > 1024)).any()
+    xs = synth.activations(6, 3, m, k)
+    _check(lib, xs, qw, sc, zr, path=path, tag=f"large-zero-{kind}")
 
 
 def test_all_zero_rows_give_exact_zeros(lib):
@@ -125,14 +169,14 @@ def test_all_zero_rows_give_exact_zeros(lib):
     W = synth.weights(6, 2, n, k)
     W[5] = 0
     W[47] = 0
-    for path, m in [(1, 1), (1, 4), (2, 1), (2, 17)]:
+    for path, m in [(1, 1), (1, 4), (2, 1), (2, 17), (3, 5), (3, 32)]:
         xs, qw, sc, zr = _packed(6, 2, n, k, m, W=W)
         y = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=path))
         assert np.all(y[:, 5] == 0) and np.all(y[:, 47] == 0)
         _check(lib, xs, qw, sc, zr, path=path, tag="zero-rows")
 
 
-@pytest.mark.parametrize("path,m", [(1, 1), (1, 8), (2, 16), (2, 128)])
+@pytest.mark.parametrize("path,m", [(1, 1), (1, 8), (2, 16), (2, 128), (3, 2), (3, 32)])
 def test_deterministic_and_writes_only_its_output(lib, path, m):
     import torch
 

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP, ERR_ARG = range(7)
-PATH_AUTO, PATH_GEMV, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_SKINNY = 0, 1, 2, 3
 GROUP = 128
 LAYOUT_VERSION = 1
 

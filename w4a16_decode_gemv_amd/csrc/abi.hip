@@ -26,6 +26,9 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxM = int64_t(1) << 16;
 constexpr int64_t kMaxT = int64_t(1) << 20;
+// automatic dispatch: the GEMV kernel up to this M, the small-batch MFMA kernel up to
+// skinny_max_m(), the tiled MFMA kernel beyond (hand-off points from the M sweep at K = N = 8192)
+constexpr int64_t kAutoGemvMaxM = 1;
 
 w4a16_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -54,17 +57,24 @@ w4a16_status run_linear(int32_t path, const void* x, const void* qweight, const 
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
   const uint16_t* zr = static_cast<const uint16_t*>(zeros);
   uint16_t* yh = static_cast<uint16_t*>(y);
-  bool use_gemv;
-  if (path == 0)
-    use_gemv = M <= w4a16::gemv_max_m() && w4a16::gemv_supports(M, K);
-  else if (path == 1) {
-    if (!w4a16::gemv_supports(M, K))
-      return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel takes M <= %d (M * ceil(K / 16384) <= 8); got M=%lld K=%lld",
-                  w4a16::gemv_max_m(), (long long)M, (long long)K);
-    use_gemv = true;
-  } else
-    use_gemv = false;
-  if (use_gemv) return hip_result(w4a16::launch_gemv(xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
+  int32_t kernel = path;
+  if (path == 0) {
+    if (M <= kAutoGemvMaxM && w4a16::gemv_supports(M, K))
+      kernel = 1;
+    else if (M <= w4a16::skinny_max_m())
+      kernel = 3;
+    else
+      kernel = 2;
+  } else if (path == 1 && !w4a16::gemv_supports(M, K)) {
+    return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel takes M <= %d (M * ceil(K / 16384) <= 8); got M=%lld K=%lld",
+                w4a16::gemv_max_m(), (long long)M, (long long)K);
+  } else if (path == 3 && M > w4a16::skinny_max_m()) {
+    return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes M <= %d; got M=%lld",
+                w4a16::skinny_max_m(), (long long)M);
+  }
+  if (kernel == 1) return hip_result(w4a16::launch_gemv(xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
+  if (kernel == 3)
+    return hip_result(w4a16::launch_skinny(xh, qw, sc, zr, M, N, K, yh, stream), "small-batch MFMA launch");
   return hip_result(w4a16::launch_mfma(xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
 }
 
@@ -146,7 +156,8 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
                                void* stream) {
   clear_error();
-  if (path < 0 || path > 2) return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV) or 2 (MFMA)");
+  if (path < 0 || path > 3)
+    return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA) or 3 (small-batch MFMA)");
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
   return run_linear(path, x, qweight, scales, zeros, M, N, K, y, static_cast<hipStream_t>(stream));

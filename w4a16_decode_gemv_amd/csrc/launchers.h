@@ -24,7 +24,13 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* qweight, const uint16_
                        const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                        hipStream_t stream);
 
-// MFMA kernel: any M >= 1.
+// Small-batch MFMA kernel: needs M <= skinny_max_m().
+int skinny_max_m();
+hipError_t launch_skinny(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                         const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                         hipStream_t stream);
+
+// Tiled MFMA kernel: any M >= 1.
 hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                        const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                        hipStream_t stream);
