@@ -26,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W4A16 GEMV achieved HBM GB/s (% of peak) + µs/call at M=1, K=N=8192"
 HBM_PEAK_GBS = 8000.0
+PEAK_FP16_TFLOPS = 2500.0  # dense fp16 MFMA peak of MI355X
 ROTATE_BYTES = 1 << 29  # two Infinity Caches' worth of distinct buffers
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1_k8192_n8192.json")
 
@@ -51,9 +52,13 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--sweep", action="store_true", help="also time the config-4 batch sweep on both kernels")
     p.add_argument("--set", dest="llama_set", action="store_true", help="also time the 7-projection LLaMA-65B set")
+    p.add_argument("--serving", action="store_true",
+                   help="also time the batched-serving GEMMs (LLaMA2-7B shapes, M=128/256) against dense fp16")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only-gemv", action="store_true", help="time the headline GEMV only (for profilers)")
+    p.add_argument("--only-m", type=int, default=0,
+                   help="time only the automatic path at this batch M, K = N = 8192 (for profilers)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the GEMV, run a plain 64 MiB elementwise copy 5 times (counter calibration)")
     return p.parse_args()
@@ -140,6 +145,17 @@ def time_graph(torch, fn, steps, reps=5):
     return e0.elapsed_time(e1) / (reps * steps)
 
 
+def copy_probe(torch, out):
+    """A plain read-once/write-once kernel of known size (64 MiB in, 64 MiB out), run five times so
+    that the HBM counters can be scaled to bytes."""
+    a = torch.ones(32 << 20, dtype=torch.float16, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        torch.mul(a, 1.0, out=b)
+    torch.cuda.synchronize()
+    out["copy_probe_bytes"] = {"read": a.numel() * 2, "write": b.numel() * 2, "kernel": "torch.mul(a, 1.0, out=b)"}
+
+
 def cpu_baseline(layer, seconds):
     """The oracle's linear (NumPy float64) on the host, timed on whole-layer calls."""
     import numpy as np
@@ -209,6 +225,18 @@ def main():
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
 
+    if args.only_m:
+        mm = args.only_m
+        b = algorithmic_bytes(mm, 8192, 8192)
+        L = Layer(w4, torch, 4, 0, 8192, 8192, mm, copies_for(b))
+        t = time_back_to_back(torch, lambda i: L.call(w4, i), args.steps, args.warmup)
+        res = {"M": mm, "K": 8192, "N": 8192, "us_per_call": t * 1e3, "GB_s": b / (t * 1e-3) / 1e9,
+               "algorithmic_bytes_per_call": b}
+        if args.copy_probe:
+            copy_probe(torch, res)
+        print(json.dumps(res), flush=True)
+        return 0
+
     n = k = 8192
     m = 1
     nbytes = algorithmic_bytes(m, n, k)
@@ -242,13 +270,7 @@ def main():
         },
     }
     if args.copy_probe:
-        # a plain read-once/write-once kernel of known size: 64 MiB in, 64 MiB out
-        a = torch.ones(32 << 20, dtype=torch.float16, device="cuda:0")
-        b = torch.empty_like(a)
-        for _ in range(5):
-            torch.mul(a, 1.0, out=b)
-        torch.cuda.synchronize()
-        out["copy_probe_bytes"] = {"read": a.numel() * 2, "write": b.numel() * 2, "kernel": "torch.mul(a, 1.0, out=b)"}
+        copy_probe(torch, out)
     if args.only_gemv:
         print(json.dumps(out), flush=True)
         return 0
@@ -319,6 +341,29 @@ def main():
             del L
             torch.cuda.empty_cache()
         out["sweep_k8192_n8192"] = rows
+
+    if args.serving:
+        import synth
+
+        rows = []
+        for lid, (name, kk, nn) in enumerate(synth.CONFIGS[5]["layers"]):
+            for mm in (128, 256):
+                b = algorithmic_bytes(mm, nn, kk)
+                L = Layer(w4, torch, 5, lid, nn, kk, mm, copies_for(b))
+                t = time_graph(torch, lambda i: L.call(w4, i), 50)
+                # dense fp16 reference product of the same shape: y = x @ W^T with W^T stored [K][N]
+                wt = [L.W.t().contiguous() for _ in range(copies_for(nn * kk * 2))]
+                xd = L.x
+                yd = torch.empty((mm, nn), dtype=torch.float16, device=xd.device)
+                td = time_graph(torch, lambda i: torch.matmul(xd, wt[i % len(wt)], out=yd), 50)
+                flop = 2 * mm * nn * kk
+                rows.append({"layer": name, "M": mm, "K": kk, "N": nn, "us": t * 1e3,
+                             "TFLOP_s": flop / (t * 1e-3) / 1e12, "mfma_util": flop / (t * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
+                             "dense_fp16_us": td * 1e3, "dense_fp16_TFLOP_s": flop / (td * 1e-3) / 1e12,
+                             "speedup_vs_dense": td / t})
+                del L, wt
+                torch.cuda.empty_cache()
+        out["serving_llama2_7b"] = rows
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(layer, args.cpu_seconds)
