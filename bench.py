@@ -356,11 +356,21 @@ def main():
                 xd = L.x
                 yd = torch.empty((mm, nn), dtype=torch.float16, device=xd.device)
                 td = time_graph(torch, lambda i: torch.matmul(xd, wt[i % len(wt)], out=yd), 50)
+                td_lt = None
+                try:  # the same product with torch's hipBLASLt backend, where this build has it
+                    prev = torch.backends.cuda.preferred_blas_library()
+                    torch.backends.cuda.preferred_blas_library("cublaslt")
+                    td_lt = time_graph(torch, lambda i: torch.matmul(xd, wt[i % len(wt)], out=yd), 50)
+                    torch.backends.cuda.preferred_blas_library(prev)
+                except (RuntimeError, AttributeError):
+                    pass
                 flop = 2 * mm * nn * kk
                 rows.append({"layer": name, "M": mm, "K": kk, "N": nn, "us": t * 1e3,
                              "TFLOP_s": flop / (t * 1e-3) / 1e12, "mfma_util": flop / (t * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
                              "dense_fp16_us": td * 1e3, "dense_fp16_TFLOP_s": flop / (td * 1e-3) / 1e12,
-                             "speedup_vs_dense": td / t})
+                             "speedup_vs_dense": td / t,
+                             "dense_fp16_hipblaslt_us": None if td_lt is None else td_lt * 1e3,
+                             "speedup_vs_dense_hipblaslt": None if td_lt is None else td_lt / t})
                 del L, wt
                 torch.cuda.empty_cache()
         out["serving_llama2_7b"] = rows
