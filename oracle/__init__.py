@@ -16,6 +16,8 @@ pages define, written step by step in the pages' order:
 * ``pack_codes`` / ``unpack_codes`` - the nibble layout (layout v1).
 * ``quantize_pack``   - all of the above for one weight matrix.
 * ``dequantize`` / ``linear`` - the fused dequantize-then-multiply, in float64.
+* ``rmsnorm_fold``    - the RMSNorm in front of the scaled layers with the 1/s
+  folded into it (the operator that produces x_s in a decoder block).
 
 It shares no code, header, table or constant with the HIP path. The only module
 both sides use is the seeded input generator ``synth``, which holds none of the
@@ -36,6 +38,7 @@ from .quant import (
 )
 from .layout import pack_codes, unpack_codes, LAYOUT_VERSION
 from .linear import dequantize, linear, within_tolerance, TOL_REL, TOL_ABS
+from .norm import rms_factor, rmsnorm_fold
 
 __all__ = [
     "channel_scale",
@@ -52,4 +55,6 @@ __all__ = [
     "within_tolerance",
     "TOL_REL",
     "TOL_ABS",
+    "rms_factor",
+    "rmsnorm_fold",
 ]
