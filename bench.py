@@ -21,6 +21,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -52,6 +54,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--sweep", action="store_true", help="also time the config-4 batch sweep on both kernels")
     p.add_argument("--set", dest="llama_set", action="store_true", help="also time the 7-projection LLaMA-65B set")
+    p.add_argument("--block", action="store_true",
+                   help="also time a LLaMA2-7B decoder block at M=1: separate projections vs q/k/v and gate/up fused")
     p.add_argument("--serving", action="store_true",
                    help="also time the batched-serving GEMMs (LLaMA2-7B shapes, M=128/256) against dense fp16")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
@@ -143,6 +147,78 @@ def time_graph(torch, fn, steps, reps=5):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / (reps * steps)
+
+
+def block_leg(w4, torch):
+    """A LLaMA2-7B decoder block's quantized part at M = 1: RMSNorm (1/s folded) -> q, k, v ->
+    o -> RMSNorm -> gate, up -> down, as 9 launches, against the same with q/k/v and gate/up
+    stacked into single launches (6 launches). Attention itself is not part of this path; the
+    o and down inputs are synthetic activations already divided by their scales (their 1/s
+    folds into the preceding projection's weights)."""
+    import synth
+
+    dev = "cuda:0"
+    layers = synth.CONFIGS[2]["layers"]
+    k = layers[0][1]
+    eps = 1e-5
+    groups = [("qkv", [0, 1, 2]), ("o", [3]), ("gate_up", [4, 5]), ("down", [6])]
+    packed_bytes = sum(n * kk // 2 + 4 * n * (kk // 128) for _, kk, n in layers)
+    copies = max(2, -(-ROTATE_BYTES // packed_bytes))
+    base = {}
+    for gname, ids in groups:
+        kk = layers[ids[0]][1]
+        lead = ids[0]
+        s = w4.channel_scale(torch.from_numpy(synth.calibration(2, lead, kk)).to(dev), 0.5)
+        W = torch.cat([torch.from_numpy(synth.weights(2, i, layers[i][2], kk)).to(dev) for i in ids], dim=0)
+        packed = w4.quantize_pack(W, s)
+        del W
+        bounds, r0 = [], 0
+        for i in ids:
+            bounds.append((r0, r0 + layers[i][2]))
+            r0 += layers[i][2]
+        base[gname] = {"s": s, "packed": packed, "parts": bounds,
+                       "x": w4.scale_input(torch.from_numpy(synth.activations(2, lead, 1, kk)).to(dev), s), "n": r0}
+    h = [torch.from_numpy(synth.activations(2, 10 + j, 1, k)).to(dev) for j in range(2)]
+    gamma = [torch.from_numpy((1.0 + 0.1 * np.random.default_rng(j).standard_normal(k)).astype(np.float16)).to(dev)
+             for j in range(2)]
+    sets = []
+    for c in range(copies):
+        st = {g: {"s": b["s"], "parts": b["parts"], "x": b["x"].clone(),
+                  "packed": tuple(t.clone() for t in b["packed"]),
+                  "y": torch.empty((1, b["n"]), dtype=torch.float16, device=dev)} for g, b in base.items()}
+        st["h"], st["gamma"] = [t.clone() for t in h], gamma
+        sets.append(st)
+    del base
+    torch.cuda.synchronize()
+
+    def lin(g, fused):
+        qw, sc, zr = g["packed"]
+        if fused:
+            w4.linear(g["x"], qw, sc, zr, out=g["y"])
+        else:
+            for a, b in g["parts"]:
+                w4.linear(g["x"], qw[a:b], sc[a:b], zr[a:b], out=g["y"][:, a:b])
+
+    def step(i, fused):
+        st = sets[i % len(sets)]
+        w4.rmsnorm_fold(st["h"][0], st["gamma"][0], st["qkv"]["s"], eps, out=st["qkv"]["x"])
+        lin(st["qkv"], fused)
+        lin(st["o"], fused)
+        w4.rmsnorm_fold(st["h"][1], st["gamma"][1], st["gate_up"]["s"], eps, out=st["gate_up"]["x"])
+        lin(st["gate_up"], fused)
+        lin(st["down"], fused)
+
+    t_norm = time_graph(torch, lambda i: w4.rmsnorm_fold(sets[i % len(sets)]["h"][0], sets[i % len(sets)]["gamma"][0],
+                                                       sets[i % len(sets)]["qkv"]["s"], eps,
+                                                       out=sets[i % len(sets)]["qkv"]["x"]), 50)
+    t_sep = time_graph(torch, lambda i: step(i, False), 20)
+    t_fused = time_graph(torch, lambda i: step(i, True), 20)
+    norm_bytes = 2 * (2 * k * 2 + 2 * k + 4 * k + 2 * k)
+    nbytes = sum(algorithmic_bytes(1, n, kk) for _, kk, n in layers) + norm_bytes
+    return {"launches_separate": 9, "launches_fused": 6, "us_separate": t_sep * 1e3, "us_fused": t_fused * 1e3,
+            "GB_s_separate": nbytes / (t_sep * 1e-3) / 1e9, "GB_s_fused": nbytes / (t_fused * 1e-3) / 1e9,
+            "bytes": nbytes, "rotating_copies": copies, "us_rmsnorm_fold_one_row": t_norm * 1e3,
+            "note": "graph-timed; q/k/v (N=12288) and gate/up (N=22016) stacked row-wise share one launch"}
 
 
 def copy_probe(torch, out):
@@ -341,6 +417,9 @@ def main():
             del L
             torch.cuda.empty_cache()
         out["sweep_k8192_n8192"] = rows
+
+    if args.block:
+        out["llama2_7b_block"] = block_leg(w4, torch)
 
     if args.serving:
         import synth

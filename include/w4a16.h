@@ -100,6 +100,29 @@ w4a16_status awq_scale_input(const void* x, const float* s, int64_t M, int64_t K
                              void* stream);
 
 /*
+ * awq_rmsnorm_fold - the RMSNorm in front of the scaled projections, with the
+ * AWQ 1/s folded into it, so that it writes x_s directly and inference runs no
+ * separate divide. "MIT 6.5940 Lab 4 + Lab 5" guide, AWQ skeleton part 2.3
+ * (the scales are merged into the preceding LayerNorm or linear layer);
+ * "Quantization for LLMs" chapter 11, AWQ section (the division by s is merged
+ * into the LayerNorm in front). The LLaMA-shaped blocks use RMSNorm:
+ *
+ *   r[m]      = 1 / sqrt( sum_k h[m][k]^2 / K + eps )
+ *   x_s[m][k] = f16_rne( ((h[m][k] * r[m]) * gamma[k]) / s[k] )
+ *
+ * every operation in float64 in that order (square root and division correctly
+ * rounded), one float64 -> float16 rounding at the end; the sum of squares in a
+ * fixed order (reproducible). s == NULL gives the plain RMSNorm output.
+ * h: fp16 [M][K]; gamma: fp16 [K]; s: float32 [K] or NULL; eps: finite, > 0;
+ * x_s: fp16 [M][K] (output; must not alias h). K % 8 == 0.
+ * Alignment: h and x_s 16 bytes, gamma 2 bytes, s 4 bytes.
+ * Errors: W4A16_ERR_NULL, W4A16_ERR_SHAPE (M, K <= 0, K % 8, limits),
+ * W4A16_ERR_ARG (eps), W4A16_ERR_ALIGN, W4A16_ERR_HIP; checked before any HIP call.
+ */
+w4a16_status awq_rmsnorm_fold(const void* h, const void* gamma, const float* s, int64_t M, int64_t K,
+                              double eps, void* x_s, void* stream);
+
+/*
  * awq_quantize_pack - round-to-nearest group quantization and packing.
  * L13 guide, AWQ section: Q(w) = Delta * Round(w / Delta) on weights already
  * multiplied by s; CMU L19 zero-point quantizer (range max - min, integer zero,

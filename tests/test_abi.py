@@ -119,6 +119,19 @@ def test_channel_scale_and_scale_input_reject():
     assert lib.awq_scale_input(A16, A16 + 2, 1, 64, A16, None) == w4.ERR_ALIGN
 
 
+def test_rmsnorm_fold_rejects():
+    lib = w4.load()
+    assert lib.awq_rmsnorm_fold(None, A16, A16, 2, 64, 1e-5, A16, None) == w4.ERR_NULL
+    assert lib.awq_rmsnorm_fold(A16, A16, A16, 2, 64, 1e-5, None, None) == w4.ERR_NULL
+    assert lib.awq_rmsnorm_fold(A16, A16, A16, 0, 64, 1e-5, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_rmsnorm_fold(A16, A16, A16, 2, 60, 1e-5, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_rmsnorm_fold(A16, A16, A16, 2, 64, 0.0, A16, None) == w4.ERR_ARG
+    assert lib.awq_rmsnorm_fold(A16, A16, A16, 2, 64, float("inf"), A16, None) == w4.ERR_ARG
+    assert lib.awq_rmsnorm_fold(A16 + 2, A16, A16, 2, 64, 1e-5, A16, None) == w4.ERR_ALIGN
+    assert lib.awq_rmsnorm_fold(A16, A16 + 1, A16, 2, 64, 1e-5, A16, None) == w4.ERR_ALIGN
+    assert lib.awq_rmsnorm_fold(A16, A16, A16 + 2, 2, 64, 1e-5, A16, None) == w4.ERR_ALIGN
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
 

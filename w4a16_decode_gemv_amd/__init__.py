@@ -48,6 +48,7 @@ def load():
         "w4a16_gemv_max_m": ([], i32),
         "awq_channel_scale": ([vp, i64, i64, ctypes.c_double, vp, vp], i32),
         "awq_scale_input": ([vp, vp, i64, i64, vp, vp], i32),
+        "awq_rmsnorm_fold": ([vp, vp, vp, i64, i64, ctypes.c_double, vp, vp], i32),
         "awq_quantize_pack": ([vp, vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
         "w4a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w4a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
@@ -62,7 +63,8 @@ def load():
 
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
-            "awq_channel_scale", "awq_scale_input", "awq_quantize_pack", "w4a16_linear", "w4a16_linear_path"]
+            "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
+            "w4a16_linear_path"]
 
 
 def _check(status):
@@ -119,6 +121,26 @@ def scale_input(x, s, out=None):
         raise ValueError("s must have K entries")
     xs = torch.empty_like(x) if out is None else out
     _check(lib.awq_scale_input(x.data_ptr(), s.data_ptr(), m, k, xs.data_ptr(), _stream(x)))
+    return xs
+
+
+def rmsnorm_fold(h, gamma, s=None, eps=1e-5, out=None):
+    """RMSNorm of h with the 1/s folded in: x_s = f16(((h * r) * gamma) / s), fp16 [M][K]."""
+    torch = _torch()
+    lib = load()
+    h = _dev_tensor(h, torch.float16, "h", 2)
+    gamma = _dev_tensor(gamma, torch.float16, "gamma", 1)
+    m, k = h.shape
+    if gamma.shape[0] != k:
+        raise ValueError("gamma must have K entries")
+    sp = 0
+    if s is not None:
+        s = _dev_tensor(s, torch.float32, "s", 1)
+        if s.shape[0] != k:
+            raise ValueError("s must have K entries")
+        sp = s.data_ptr()
+    xs = torch.empty_like(h) if out is None else out
+    _check(lib.awq_rmsnorm_fold(h.data_ptr(), gamma.data_ptr(), sp, m, k, float(eps), xs.data_ptr(), _stream(h)))
     return xs
 
 

@@ -1,5 +1,6 @@
 // C ABI of the library: argument validation (host only, before any HIP call),
 // status codes and text, and dispatch to the kernel launchers.
+#include <cmath>
 #include <stdarg.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -123,6 +124,20 @@ w4a16_status awq_scale_input(const void* x, const float* s, int64_t M, int64_t K
   return hip_result(w4a16::launch_scale_input(static_cast<const uint16_t*>(x), s, M, K, static_cast<uint16_t*>(x_s),
                                               static_cast<hipStream_t>(stream)),
                     "scale-input launch");
+}
+
+w4a16_status awq_rmsnorm_fold(const void* h, const void* gamma, const float* s, int64_t M, int64_t K, double eps,
+                              void* x_s, void* stream) {
+  clear_error();
+  if (!h || !gamma || !x_s) return fail(W4A16_ERR_NULL, "h, gamma and x_s are required");
+  if (M <= 0 || K <= 0 || K % 8 != 0) return fail(W4A16_ERR_SHAPE, "M, K must be positive and K a multiple of 8");
+  if (M > kMaxT || K > W4A16_MAX_K) return fail(W4A16_ERR_SHAPE, "size beyond the limits (M <= 2^20, K <= %d)", W4A16_MAX_K);
+  if (!(eps > 0.0) || !std::isfinite(eps)) return fail(W4A16_ERR_ARG, "eps must be finite and positive");
+  if (!aligned(h, 16) || !aligned(x_s, 16) || !aligned(gamma, 2) || (s && !aligned(s, 4)))
+    return fail(W4A16_ERR_ALIGN, "h and x_s must be 16-byte, gamma 2-byte and s 4-byte aligned");
+  return hip_result(w4a16::launch_rmsnorm_fold(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(gamma), s,
+                                               M, K, eps, static_cast<uint16_t*>(x_s), static_cast<hipStream_t>(stream)),
+                    "RMSNorm-fold launch");
 }
 
 w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t K, int32_t bits, int32_t group,

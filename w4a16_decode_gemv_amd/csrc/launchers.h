@@ -14,6 +14,9 @@ hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t T, int64_t K, dou
 hipError_t launch_scale_input(const uint16_t* x, const float* s, int64_t M, int64_t K, uint16_t* x_s,
                               hipStream_t stream);
 
+hipError_t launch_rmsnorm_fold(const uint16_t* h, const uint16_t* gamma, const float* s, int64_t M, int64_t K,
+                               double eps, uint16_t* x_s, hipStream_t stream);
+
 hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, uint32_t* qweight,
                                 uint16_t* scales, uint16_t* zeros, hipStream_t stream);
 
