@@ -18,6 +18,8 @@ pages define, written step by step in the pages' order:
 * ``dequantize`` / ``linear`` - the fused dequantize-then-multiply, in float64.
 * ``rmsnorm_fold``    - the RMSNorm in front of the scaled layers with the 1/s
   folded into it (the operator that produces x_s in a decoder block).
+* ``alpha_loss`` / ``search_alpha`` - the AWQ output-error loss and its grid
+  search over alpha.
 
 It shares no code, header, table or constant with the HIP path. The only module
 both sides use is the seeded input generator ``synth``, which holds none of the
@@ -39,6 +41,7 @@ from .quant import (
 from .layout import pack_codes, unpack_codes, LAYOUT_VERSION
 from .linear import dequantize, linear, within_tolerance, TOL_REL, TOL_ABS
 from .norm import rms_factor, rmsnorm_fold
+from .search import GRID as ALPHA_GRID, alpha_loss, search_alpha
 
 __all__ = [
     "channel_scale",
@@ -57,4 +60,7 @@ __all__ = [
     "TOL_ABS",
     "rms_factor",
     "rmsnorm_fold",
+    "ALPHA_GRID",
+    "alpha_loss",
+    "search_alpha",
 ]
