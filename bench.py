@@ -58,6 +58,8 @@ def parse():
                    help="also time a LLaMA2-7B decoder block at M=1: separate projections vs q/k/v and gate/up fused")
     p.add_argument("--serving", action="store_true",
                    help="also time the batched-serving GEMMs (LLaMA2-7B shapes, M=128/256) against dense fp16")
+    p.add_argument("--search", action="store_true",
+                   help="also time the AWQ scale search (loss kernel and grid points) on the LLaMA2-7B block")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only-gemv", action="store_true", help="time the headline GEMV only (for profilers)")
@@ -219,6 +221,47 @@ def block_leg(w4, torch):
             "GB_s_separate": nbytes / (t_sep * 1e-3) / 1e9, "GB_s_fused": nbytes / (t_fused * 1e-3) / 1e9,
             "bytes": nbytes, "rotating_copies": copies, "us_rmsnorm_fold_one_row": t_norm * 1e3,
             "note": "graph-timed; q/k/v (N=12288) and gate/up (N=22016) stacked row-wise share one launch"}
+
+
+def search_leg(w4, torch):
+    """The AWQ scale search on the LLaMA2-7B block's seven projections with 512 calibration
+    tokens: per layer the loss kernel alone (one candidate scale), one grid point (channel
+    scale, input fold, quantize-pack, loss) and the 21-point search, graph-timed."""
+    import synth
+
+    dev = "cuda:0"
+    rows = []
+    total_search_us = 0.0
+    for lid, (name, kk, nn) in enumerate(synth.CONFIGS[2]["layers"]):
+        x_cal = torch.from_numpy(synth.calibration(2, lid, kk)).to(dev)
+        W = torch.from_numpy(synth.weights(2, lid, nn, kk)).to(dev)
+        t_cal = x_cal.shape[0]
+        s = w4.channel_scale(x_cal, 0.5)
+        xs = w4.scale_input(x_cal, s)
+        packed = w4.quantize_pack(W, s)
+        ws = torch.empty(w4.alpha_loss_workspace(t_cal, nn), dtype=torch.float64, device=dev)
+        loss = torch.empty(len(w4.ALPHA_GRID), dtype=torch.float64, device=dev)
+        t_loss = time_graph(torch, lambda i: w4.alpha_loss(x_cal, xs, W, *packed, workspace=ws,
+                                                           out=loss[i % 21:i % 21 + 1]), 21)
+
+        def point(i):
+            a = w4.ALPHA_GRID[i % 21]
+            w4.channel_scale(x_cal, a, out=s)
+            w4.scale_input(x_cal, s, out=xs)
+            w4.quantize_pack(W, s, out=packed)
+            w4.alpha_loss(x_cal, xs, W, *packed, workspace=ws, out=loss[i % 21:i % 21 + 1])
+
+        t_point = time_graph(torch, point, 21)
+        flop = 4 * t_cal * nn * kk  # two products of 2 T N K each
+        rows.append({"layer": name, "T": t_cal, "K": kk, "N": nn, "loss_us": t_loss * 1e3,
+                     "loss_TFLOP_s": flop / (t_loss * 1e-3) / 1e12,
+                     "loss_mfma_util": flop / (t_loss * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
+                     "grid_point_us": t_point * 1e3, "search_21_us": 21 * t_point * 1e3})
+        total_search_us += 21 * t_point * 1e3
+        del x_cal, W, s, xs, packed, ws
+        torch.cuda.empty_cache()
+    return {"layers": rows, "block_search_us": total_search_us,
+            "note": "loss flops = 4 T N K (quantized and fp16 products); graph-timed, inputs resident"}
 
 
 def copy_probe(torch, out):
@@ -420,6 +463,9 @@ def main():
 
     if args.block:
         out["llama2_7b_block"] = block_leg(w4, torch)
+
+    if args.search:
+        out["awq_search_llama2_7b"] = search_leg(w4, torch)
 
     if args.serving:
         import synth

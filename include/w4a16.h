@@ -178,6 +178,45 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,
                                void* y, void* stream);
 
+/*
+ * awq_alpha_loss_workspace - number of float64 values that awq_alpha_loss
+ * needs in its workspace for T calibration rows and N outputs
+ * (ceil(T / 64) * ceil(N / 64)); -1 when T or N is outside the limits.
+ */
+int64_t awq_alpha_loss_workspace(int64_t T, int64_t N);
+
+/*
+ * awq_alpha_loss - the output-error loss that the AWQ scale search minimises,
+ * for one candidate scale s. L13 guide, AWQ section (slide 28): alpha is
+ * chosen by a grid search minimising L(s) = || Q(W s)(s^-1 X) - W X || with
+ * s = s_X^alpha, the error measured on the layer's output; "Quantization for
+ * LLMs" chapter 11, AWQ section. Squared Frobenius norm:
+ *
+ *   loss = sum_{t,n} ( sum_k x_s[t][k] * w_hat[n][k] - sum_k x[t][k] * w[n][k] )^2
+ *
+ * where x_s = f16(x / s) (as awq_scale_input writes it) and w_hat is the
+ * dequantized layout-v1 weight of W * s (as awq_quantize_pack writes it).
+ * Each of the two products is accumulated in float32 (a float32 dot product's
+ * rounding, far below the quantization error being measured); the difference,
+ * its square and the sum over (t, n) are float64, the sum in a fixed order, so
+ * the result is reproducible run to run.
+ * x: fp16 [T][K] calibration activations; x_s: fp16 [T][K]; w: fp16 [N][K];
+ * qweight uint32 [N][K/8], scales and zeros fp16 [N][K/128]; group must be 128.
+ * workspace: float64 [workspace_len], workspace_len >=
+ * awq_alpha_loss_workspace(T, N), overwritten (two calls in flight at once
+ * need two workspaces); loss: one float64 (output, device memory).
+ * Alignment: x, x_s, w and qweight 16 bytes; scales and zeros 2 bytes;
+ * workspace and loss 8 bytes.
+ * Errors: W4A16_ERR_NULL; W4A16_ERR_SHAPE (a size <= 0, K % 128, T > 2^20,
+ * N > 2^24, K > W4A16_MAX_K); W4A16_ERR_UNSUPPORTED (group); W4A16_ERR_ARG
+ * (workspace too small); W4A16_ERR_ALIGN; W4A16_ERR_HIP. Checked before any
+ * HIP call. Launches two kernels (the loss tiles, then the reduction).
+ */
+w4a16_status awq_alpha_loss(const void* x, const void* x_s, const void* w, const void* qweight,
+                            const void* scales, const void* zeros, int64_t T, int64_t N, int64_t K,
+                            int32_t group, double* workspace, int64_t workspace_len, double* loss,
+                            void* stream);
+
 /* Largest M that the GEMV kernel (w4a16_linear_path path 1) accepts. */
 int32_t w4a16_gemv_max_m(void);
 

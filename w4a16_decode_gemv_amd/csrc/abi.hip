@@ -27,6 +27,7 @@ bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxM = int64_t(1) << 16;
 constexpr int64_t kMaxT = int64_t(1) << 20;
+constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;  // one workgroup per loss tile, 1-D grid
 // automatic dispatch: the GEMV kernel up to this M, the small-batch MFMA kernel up to
 // skinny_max_m(), the tiled MFMA kernel beyond (hand-off points from the M sweep at K = N = 8192)
 constexpr int64_t kAutoGemvMaxM = 1;
@@ -176,6 +177,40 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
   return run_linear(path, x, qweight, scales, zeros, M, N, K, y, static_cast<hipStream_t>(stream));
+}
+
+int64_t awq_alpha_loss_workspace(int64_t T, int64_t N) {
+  if (T <= 0 || N <= 0 || T > kMaxT || N > kMaxN) return -1;
+  const int64_t tiles = w4a16::alpha_loss_partials(T, N);
+  return tiles > kMaxTiles ? -1 : tiles;
+}
+
+w4a16_status awq_alpha_loss(const void* x, const void* x_s, const void* w, const void* qweight, const void* scales,
+                            const void* zeros, int64_t T, int64_t N, int64_t K, int32_t group, double* workspace,
+                            int64_t workspace_len, double* loss, void* stream) {
+  clear_error();
+  if (!x || !x_s || !w || !qweight || !scales || !zeros || !workspace || !loss)
+    return fail(W4A16_ERR_NULL, "x, x_s, w, qweight, scales, zeros, workspace and loss are required");
+  if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "group must be 128 (got %d)", (int)group);
+  if (T <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "T, N, K must be positive (got %lld, %lld, %lld)",
+                                              (long long)T, (long long)N, (long long)K);
+  if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
+  const int64_t need = awq_alpha_loss_workspace(T, N);
+  if (K > W4A16_MAX_K || need < 0)
+    return fail(W4A16_ERR_SHAPE, "size beyond the limits (T <= 2^20, N <= 2^24, K <= %d, ceil(T/64) * ceil(N/64) < 2^31)",
+                W4A16_MAX_K);
+  if (workspace_len < need)
+    return fail(W4A16_ERR_ARG, "workspace holds %lld float64 values, %lld needed", (long long)workspace_len,
+                (long long)need);
+  if (!aligned(x, 16) || !aligned(x_s, 16) || !aligned(w, 16) || !aligned(qweight, 16))
+    return fail(W4A16_ERR_ALIGN, "x, x_s, w and qweight must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(zeros, 2) || !aligned(workspace, 8) || !aligned(loss, 8))
+    return fail(W4A16_ERR_ALIGN, "scales and zeros must be 2-byte, workspace and loss 8-byte aligned");
+  return hip_result(w4a16::launch_alpha_loss(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x_s),
+                                             static_cast<const uint16_t*>(w), static_cast<const uint32_t*>(qweight),
+                                             static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
+                                             T, N, K, workspace, loss, static_cast<hipStream_t>(stream)),
+                    "alpha-loss launch");
 }
 
 }  // extern "C"

@@ -44,7 +44,6 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;          // output columns per workgroup (4 waves x 16)
-constexpr int GK = 128;         // inputs per group = one stage
 constexpr int kThreads = 256;
 
 __device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
