@@ -225,8 +225,9 @@ def block_leg(w4, torch):
 
 def search_leg(w4, torch):
     """The AWQ scale search on the LLaMA2-7B block's seven projections with 512 calibration
-    tokens: per layer the loss kernel alone (one candidate scale), one grid point (channel
-    scale, input fold, quantize-pack, loss) and the 21-point search, graph-timed."""
+    tokens: per layer the original output (once per search), the loss kernel alone (one
+    candidate scale), one grid point (channel scale, input fold, quantize-pack, loss) and the
+    21-point search, graph-timed."""
     import synth
 
     dev = "cuda:0"
@@ -241,7 +242,9 @@ def search_leg(w4, torch):
         packed = w4.quantize_pack(W, s)
         ws = torch.empty(w4.alpha_loss_workspace(t_cal, nn), dtype=torch.float64, device=dev)
         loss = torch.empty(len(w4.ALPHA_GRID), dtype=torch.float64, device=dev)
-        t_loss = time_graph(torch, lambda i: w4.alpha_loss(x_cal, xs, W, *packed, workspace=ws,
+        y_ref = torch.empty((t_cal, nn), dtype=torch.float32, device=dev)
+        t_ref = time_graph(torch, lambda i: w4.output_reference(x_cal, W, out=y_ref), 10)
+        t_loss = time_graph(torch, lambda i: w4.alpha_loss(xs, *packed, y_ref, workspace=ws,
                                                            out=loss[i % 21:i % 21 + 1]), 21)
 
         def point(i):
@@ -249,19 +252,22 @@ def search_leg(w4, torch):
             w4.channel_scale(x_cal, a, out=s)
             w4.scale_input(x_cal, s, out=xs)
             w4.quantize_pack(W, s, out=packed)
-            w4.alpha_loss(x_cal, xs, W, *packed, workspace=ws, out=loss[i % 21:i % 21 + 1])
+            w4.alpha_loss(xs, *packed, y_ref, workspace=ws, out=loss[i % 21:i % 21 + 1])
 
         t_point = time_graph(torch, point, 21)
-        flop = 4 * t_cal * nn * kk  # two products of 2 T N K each
-        rows.append({"layer": name, "T": t_cal, "K": kk, "N": nn, "loss_us": t_loss * 1e3,
-                     "loss_TFLOP_s": flop / (t_loss * 1e-3) / 1e12,
+        flop = 2 * t_cal * nn * kk  # one product of 2 T N K
+        search_us = (t_ref + 21 * t_point) * 1e3
+        rows.append({"layer": name, "T": t_cal, "K": kk, "N": nn, "reference_us": t_ref * 1e3,
+                     "reference_TFLOP_s": flop / (t_ref * 1e-3) / 1e12,
+                     "loss_us": t_loss * 1e3, "loss_TFLOP_s": flop / (t_loss * 1e-3) / 1e12,
                      "loss_mfma_util": flop / (t_loss * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
-                     "grid_point_us": t_point * 1e3, "search_21_us": 21 * t_point * 1e3})
-        total_search_us += 21 * t_point * 1e3
-        del x_cal, W, s, xs, packed, ws
+                     "grid_point_us": t_point * 1e3, "search_21_us": search_us})
+        total_search_us += search_us
+        del x_cal, W, s, xs, packed, ws, y_ref
         torch.cuda.empty_cache()
     return {"layers": rows, "block_search_us": total_search_us,
-            "note": "loss flops = 4 T N K (quantized and fp16 products); graph-timed, inputs resident"}
+            "note": "flops = 2 T N K per product; a search = one reference output + 21 grid points; "
+                    "graph-timed, inputs resident"}
 
 
 def copy_probe(torch, out):

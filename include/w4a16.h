@@ -180,10 +180,28 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
 
 /*
  * awq_alpha_loss_workspace - number of float64 values that awq_alpha_loss
- * needs in its workspace for T calibration rows and N outputs
- * (ceil(T / 64) * ceil(N / 64)); -1 when T or N is outside the limits.
+ * needs in its workspace for T calibration rows and N outputs (one per 64 x 128
+ * tile of the (t, n) plane); -1 when T or N is outside the limits.
  */
 int64_t awq_alpha_loss_workspace(int64_t T, int64_t N);
+
+/*
+ * awq_output_reference - the original layer's output on the calibration
+ * activations, the W X term of the AWQ scale-search loss. L13 guide, AWQ
+ * section (slide 28): the loss compares the quantized layer's output with W X;
+ * "Quantization for LLMs" chapter 11, AWQ section. It does not depend on the
+ * candidate scale, so a search computes it once:
+ *
+ *   y_ref[t][n] = sum_k x[t][k] * w[n][k]      (float32 accumulation)
+ *
+ * x: fp16 [T][K]; w: fp16 [N][K] (nn.Linear weight); y_ref: float32 [T][N]
+ * (output). K % 128 == 0. Alignment: x and w 16 bytes, y_ref 4 bytes.
+ * Errors: W4A16_ERR_NULL; W4A16_ERR_SHAPE (a size <= 0, K % 128, T > 2^20,
+ * N > 2^24, K > W4A16_MAX_K); W4A16_ERR_ALIGN; W4A16_ERR_HIP. Checked before
+ * any HIP call.
+ */
+w4a16_status awq_output_reference(const void* x, const void* w, int64_t T, int64_t N, int64_t K,
+                                  float* y_ref, void* stream);
 
 /*
  * awq_alpha_loss - the output-error loss that the AWQ scale search minimises,
@@ -192,30 +210,30 @@ int64_t awq_alpha_loss_workspace(int64_t T, int64_t N);
  * s = s_X^alpha, the error measured on the layer's output; "Quantization for
  * LLMs" chapter 11, AWQ section. Squared Frobenius norm:
  *
- *   loss = sum_{t,n} ( sum_k x_s[t][k] * w_hat[n][k] - sum_k x[t][k] * w[n][k] )^2
+ *   loss = sum_{t,n} ( sum_k x_s[t][k] * w_hat[n][k] - y_ref[t][n] )^2
  *
- * where x_s = f16(x / s) (as awq_scale_input writes it) and w_hat is the
- * dequantized layout-v1 weight of W * s (as awq_quantize_pack writes it).
- * Each of the two products is accumulated in float32 (a float32 dot product's
- * rounding, far below the quantization error being measured); the difference,
- * its square and the sum over (t, n) are float64, the sum in a fixed order, so
- * the result is reproducible run to run.
- * x: fp16 [T][K] calibration activations; x_s: fp16 [T][K]; w: fp16 [N][K];
- * qweight uint32 [N][K/8], scales and zeros fp16 [N][K/128]; group must be 128.
- * workspace: float64 [workspace_len], workspace_len >=
- * awq_alpha_loss_workspace(T, N), overwritten (two calls in flight at once
- * need two workspaces); loss: one float64 (output, device memory).
- * Alignment: x, x_s, w and qweight 16 bytes; scales and zeros 2 bytes;
- * workspace and loss 8 bytes.
+ * where x_s = f16(x / s) (as awq_scale_input writes it), w_hat is the
+ * dequantized layout-v1 weight of W * s (as awq_quantize_pack writes it) and
+ * y_ref the original output (as awq_output_reference writes it). The product
+ * is accumulated in float32 (a float32 dot product's rounding, far below the
+ * quantization error being measured); the residual, its square and the sum
+ * over (t, n) are float64, the sum in a fixed order, so the result is
+ * reproducible run to run.
+ * x_s: fp16 [T][K]; qweight uint32 [N][K/8], scales and zeros fp16 [N][K/128];
+ * y_ref: float32 [T][N]; group must be 128. workspace: float64
+ * [workspace_len], workspace_len >= awq_alpha_loss_workspace(T, N),
+ * overwritten (two calls in flight at once need two workspaces); loss: one
+ * float64 (output, device memory).
+ * Alignment: x_s and qweight 16 bytes; scales and zeros 2 bytes; y_ref 4
+ * bytes; workspace and loss 8 bytes.
  * Errors: W4A16_ERR_NULL; W4A16_ERR_SHAPE (a size <= 0, K % 128, T > 2^20,
  * N > 2^24, K > W4A16_MAX_K); W4A16_ERR_UNSUPPORTED (group); W4A16_ERR_ARG
  * (workspace too small); W4A16_ERR_ALIGN; W4A16_ERR_HIP. Checked before any
  * HIP call. Launches two kernels (the loss tiles, then the reduction).
  */
-w4a16_status awq_alpha_loss(const void* x, const void* x_s, const void* w, const void* qweight,
-                            const void* scales, const void* zeros, int64_t T, int64_t N, int64_t K,
-                            int32_t group, double* workspace, int64_t workspace_len, double* loss,
-                            void* stream);
+w4a16_status awq_alpha_loss(const void* x_s, const void* qweight, const void* scales, const void* zeros,
+                            const float* y_ref, int64_t T, int64_t N, int64_t K, int32_t group,
+                            double* workspace, int64_t workspace_len, double* loss, void* stream);
 
 /* Largest M that the GEMV kernel (w4a16_linear_path path 1) accepts. */
 int32_t w4a16_gemv_max_m(void);

@@ -134,16 +134,18 @@ def test_rmsnorm_fold_rejects():
 
 def test_alpha_loss_workspace_and_rejects():
     lib = w4.load()
-    assert lib.awq_alpha_loss_workspace(512, 4096) == 8 * 64
+    assert lib.awq_alpha_loss_workspace(512, 4096) == 8 * 32  # 64 x 128 tiles
     assert lib.awq_alpha_loss_workspace(65, 63) == 2
     assert lib.awq_alpha_loss_workspace(0, 64) == -1
     assert lib.awq_alpha_loss_workspace(64, (1 << 24) + 1) == -1
     assert lib.awq_alpha_loss_workspace(1 << 20, 1 << 24) == -1  # more than 2^31 - 1 tiles
 
-    def call(x=A16, xs=A16, w=A16, q=A16, sc=A16, z=A16, T=100, N=200, K=256, group=128, ws=A16, wl=8, loss=A16):
-        return lib.awq_alpha_loss(x, xs, w, q, sc, z, T, N, K, group, ws, wl, loss, None)
+    def call(xs=A16, q=A16, sc=A16, z=A16, y=A16, T=100, N=200, K=256, group=128, ws=A16, wl=8, loss=A16):
+        return lib.awq_alpha_loss(xs, q, sc, z, y, T, N, K, group, ws, wl, loss, None)
 
-    assert call(x=None) == w4.ERR_NULL
+    assert lib.awq_alpha_loss_workspace(100, 200) == 2 * 2
+    assert call(xs=None) == w4.ERR_NULL
+    assert call(y=None) == w4.ERR_NULL
     assert call(ws=None) == w4.ERR_NULL
     assert call(loss=None) == w4.ERR_NULL
     assert call(group=64) == w4.ERR_UNSUPPORTED
@@ -151,12 +153,24 @@ def test_alpha_loss_workspace_and_rejects():
     assert call(K=200) == w4.ERR_SHAPE
     assert call(K=131072 + 128) == w4.ERR_SHAPE
     assert call(T=(1 << 20) + 1) == w4.ERR_SHAPE
-    assert call(wl=7) == w4.ERR_ARG
+    assert call(wl=3) == w4.ERR_ARG
     assert call(xs=A16 + 2) == w4.ERR_ALIGN
-    assert call(w=A16 + 8) == w4.ERR_ALIGN
+    assert call(q=A16 + 8) == w4.ERR_ALIGN
     assert call(sc=A16 + 1) == w4.ERR_ALIGN
+    assert call(y=A16 + 2) == w4.ERR_ALIGN
     assert call(ws=A16 + 4) == w4.ERR_ALIGN
     assert call(loss=A16 + 4) == w4.ERR_ALIGN
+
+
+def test_output_reference_rejects():
+    lib = w4.load()
+    assert lib.awq_output_reference(None, A16, 4, 4, 128, A16, None) == w4.ERR_NULL
+    assert lib.awq_output_reference(A16, A16, 4, 4, 128, None, None) == w4.ERR_NULL
+    assert lib.awq_output_reference(A16, A16, 0, 4, 128, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_output_reference(A16, A16, 4, 4, 100, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_output_reference(A16, A16, 4, (1 << 24) + 1, 128, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_output_reference(A16 + 8, A16, 4, 4, 128, A16, None) == w4.ERR_ALIGN
+    assert lib.awq_output_reference(A16, A16, 4, 4, 128, A16 + 2, None) == w4.ERR_ALIGN
 
 
 def test_binding_refuses_cpu_tensors():

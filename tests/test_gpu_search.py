@@ -1,5 +1,8 @@
-"""GPU parity of the AWQ scale search (awq_alpha_loss and the device grid search) against
-the float64 oracle (oracle/search.py).
+"""GPU parity of the AWQ scale search (awq_output_reference, awq_alpha_loss and the device
+grid search) against the float64 oracle (oracle/search.py).
+
+* The original output y_ref = x W^T is accumulated in float32: each entry within
+  1e-5 * sum_k |x w| of the float64 value.
 
 * The loss kernel is fed the oracle's own s, x_s and packed weights, so both sides
   measure the same quantized layer; the device accumulates each product in float32, the
@@ -39,8 +42,23 @@ def _kernel_loss(lib, x_cal, W, alpha):
     s = oracle.channel_scale(x_cal, alpha)
     xs = oracle.scale_input(x_cal, s)
     q, sc, z = oracle.quantize_pack(W, s)
-    out = lib.alpha_loss(g.dev(x_cal), g.dev(xs), g.dev(W), g.dev(q), g.dev(sc), g.dev(z))
+    y_ref = lib.output_reference(g.dev(x_cal), g.dev(W))
+    out = lib.alpha_loss(g.dev(xs), g.dev(q), g.dev(sc), g.dev(z), y_ref)
     return float(g.host(out)[0])
+
+
+@pytest.mark.parametrize("t_cal,n,k", [(64, 128, 128), (100, 200, 384), (7, 130, 11008), (512, 4096, 4096),
+                                       (65, 129, 256), (1, 1, 128)])
+def test_output_reference_matches_oracle(lib, t_cal, n, k):
+    g = _gpu()
+    W = synth.weights(2, 4, n, k)
+    x_cal = synth.calibration(2, 4, k, t_cal)
+    print(f"output-reference T={t_cal} N={n} K={k}", flush=True)
+    got = g.host(lib.output_reference(g.dev(x_cal), g.dev(W))).astype(np.float64)
+    x64, w64 = x_cal.astype(np.float64), W.astype(np.float64)
+    want = x64 @ w64.T
+    bound = DELTA * (np.abs(x64) @ np.abs(w64).T)
+    assert np.all(np.abs(got - want) <= bound), float(np.max(np.abs(got - want) / np.maximum(bound, 1e-300)))
 
 
 def _loss_bound(x_cal, W, alpha):
@@ -115,7 +133,8 @@ def test_alpha_loss_is_reproducible_and_zero_for_exact_weights(lib):
     qp, sc, z = oracle.quantize_pack(w_grid, None)
     assert np.array_equal(oracle.dequantize(qp, sc, z, k), w_grid.astype(np.float64))
     xs = oracle.scale_input(x_cal, np.ones(k, np.float32))
-    out = lib.alpha_loss(g.dev(x_cal), g.dev(xs), g.dev(w_grid), g.dev(qp), g.dev(sc), g.dev(z))
+    y_ref = lib.output_reference(g.dev(x_cal), g.dev(w_grid))
+    out = lib.alpha_loss(g.dev(xs), g.dev(qp), g.dev(sc), g.dev(z), y_ref)
     loss0 = float(g.host(out)[0])
     y = x_cal.astype(np.float64) @ w_grid.astype(np.float64).T
     assert loss0 <= 1e-9 * float((y * y).sum()), loss0

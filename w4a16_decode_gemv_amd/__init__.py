@@ -53,7 +53,8 @@ def load():
         "w4a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w4a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_alpha_loss_workspace": ([i64, i64], i64),
-        "awq_alpha_loss": ([vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
+        "awq_output_reference": ([vp, vp, i64, i64, i64, vp, vp], i32),
+        "awq_alpha_loss": ([vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -66,7 +67,8 @@ def load():
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
-            "w4a16_linear_path", "awq_alpha_loss_workspace", "awq_alpha_loss"]
+            "w4a16_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
+            "awq_alpha_loss"]
 
 
 def _check(status):
@@ -207,29 +209,43 @@ def alpha_loss_workspace(T, N):
     return n
 
 
-def alpha_loss(x, x_s, W, qweight, scales, zeros, group=GROUP, workspace=None, out=None):
-    """Output-error loss of one candidate scale, float64 [1] on the device:
-    sum_{t,n} (x_s @ w_hat^T - x @ W^T)^2 with w_hat the dequantized (qweight, scales, zeros)."""
+def output_reference(x, W, out=None):
+    """The original layer's output on the calibration activations, float32 [T][N]: x @ W^T."""
     torch = _torch()
     lib = load()
     x = _dev_tensor(x, torch.float16, "x", 2)
-    x_s = _dev_tensor(x_s, torch.float16, "x_s", 2)
     W = _dev_tensor(W, torch.float16, "W", 2)
+    t_, k = x.shape
+    n = W.shape[0]
+    if W.shape[1] != k:
+        raise ValueError("x must be [T][K] and W [N][K]")
+    y = torch.empty((t_, n), dtype=torch.float32, device=x.device) if out is None else out
+    _check(lib.awq_output_reference(x.data_ptr(), W.data_ptr(), t_, n, k, y.data_ptr(), _stream(x)))
+    return y
+
+
+def alpha_loss(x_s, qweight, scales, zeros, y_ref, group=GROUP, workspace=None, out=None):
+    """Output-error loss of one candidate scale, float64 [1] on the device:
+    sum_{t,n} (x_s @ w_hat^T - y_ref)^2 with w_hat the dequantized (qweight, scales, zeros)."""
+    torch = _torch()
+    lib = load()
+    x_s = _dev_tensor(x_s, torch.float16, "x_s", 2)
     qweight = _dev_tensor(qweight, torch.int32, "qweight", 2)
     scales = _dev_tensor(scales, torch.float16, "scales", 2)
     zeros = _dev_tensor(zeros, torch.float16, "zeros", 2)
-    t_, k = x.shape
-    n = W.shape[0]
-    if x_s.shape != x.shape or W.shape[1] != k:
-        raise ValueError("x and x_s must be [T][K] and W [N][K]")
+    y_ref = _dev_tensor(y_ref, torch.float32, "y_ref", 2)
+    t_, k = x_s.shape
+    n = qweight.shape[0]
     if tuple(qweight.shape) != (n, k // 8) or scales.shape != zeros.shape or tuple(scales.shape) != (n, k // group):
         raise ValueError("qweight must be [N][K/8] and scales/zeros [N][K/group]")
+    if tuple(y_ref.shape) != (t_, n):
+        raise ValueError("y_ref must be [T][N]")
     if workspace is None:
-        workspace = torch.empty(alpha_loss_workspace(t_, n), dtype=torch.float64, device=x.device)
-    loss = torch.empty(1, dtype=torch.float64, device=x.device) if out is None else out
-    _check(lib.awq_alpha_loss(x.data_ptr(), x_s.data_ptr(), W.data_ptr(), qweight.data_ptr(), scales.data_ptr(),
-                              zeros.data_ptr(), t_, n, k, group, workspace.data_ptr(), workspace.numel(),
-                              loss.data_ptr(), _stream(x)))
+        workspace = torch.empty(alpha_loss_workspace(t_, n), dtype=torch.float64, device=x_s.device)
+    loss = torch.empty(1, dtype=torch.float64, device=x_s.device) if out is None else out
+    _check(lib.awq_alpha_loss(x_s.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
+                              y_ref.data_ptr(), t_, n, k, group, workspace.data_ptr(), workspace.numel(),
+                              loss.data_ptr(), _stream(x_s)))
     return loss
 
 
@@ -237,8 +253,8 @@ ALPHA_GRID = tuple(i / 20 for i in range(21))
 
 
 def search_alpha(x_cal, W, grid=ALPHA_GRID):
-    """The AWQ grid search on the device: for every alpha, s = channel_scale(x_cal, alpha), x_s = scale_input,
-    quantize_pack(W, s) and the output-error loss. Returns (losses float64 [len(grid)] on the device, the alpha
+    """The AWQ grid search on the device: the original output once, then for every alpha
+    s = channel_scale(x_cal, alpha), x_s = scale_input, quantize_pack(W, s) and the output-error loss. Returns (losses float64 [len(grid)] on the device, the alpha
     of the first minimum)."""
     torch = _torch()
     x_cal = _dev_tensor(x_cal, torch.float16, "x_cal", 2)
@@ -253,11 +269,12 @@ def search_alpha(x_cal, W, grid=ALPHA_GRID):
               torch.empty((n, k // GROUP), dtype=torch.float16, device=dev))
     workspace = torch.empty(alpha_loss_workspace(t_, n), dtype=torch.float64, device=dev)
     losses = torch.empty(len(grid), dtype=torch.float64, device=dev)
+    y_ref = output_reference(x_cal, W)  # independent of alpha: once per search
     for i, a in enumerate(grid):
         channel_scale(x_cal, a, out=s)
         scale_input(x_cal, s, out=xs)
         quantize_pack(W, s, out=packed)
-        alpha_loss(x_cal, xs, W, *packed, workspace=workspace, out=losses[i:i + 1])
+        alpha_loss(xs, *packed, y_ref, workspace=workspace, out=losses[i:i + 1])
     host = losses.cpu().tolist()
     best = min(range(len(host)), key=lambda i: (host[i], i))  # the first index of the minimum
     return losses, grid[best]

@@ -185,31 +185,45 @@ int64_t awq_alpha_loss_workspace(int64_t T, int64_t N) {
   return tiles > kMaxTiles ? -1 : tiles;
 }
 
-w4a16_status awq_alpha_loss(const void* x, const void* x_s, const void* w, const void* qweight, const void* scales,
-                            const void* zeros, int64_t T, int64_t N, int64_t K, int32_t group, double* workspace,
+w4a16_status awq_output_reference(const void* x, const void* w, int64_t T, int64_t N, int64_t K, float* y_ref,
+                                  void* stream) {
+  clear_error();
+  if (!x || !w || !y_ref) return fail(W4A16_ERR_NULL, "x, w and y_ref are required");
+  if (T <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "T, N, K must be positive (got %lld, %lld, %lld)",
+                                              (long long)T, (long long)N, (long long)K);
+  if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
+  if (K > W4A16_MAX_K || awq_alpha_loss_workspace(T, N) < 0)
+    return fail(W4A16_ERR_SHAPE, "size beyond the limits (T <= 2^20, N <= 2^24, K <= %d)", W4A16_MAX_K);
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y_ref, 4))
+    return fail(W4A16_ERR_ALIGN, "x and w must be 16-byte, y_ref 4-byte aligned");
+  return hip_result(w4a16::launch_output_reference(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w),
+                                                   T, N, K, y_ref, static_cast<hipStream_t>(stream)),
+                    "output-reference launch");
+}
+
+w4a16_status awq_alpha_loss(const void* x_s, const void* qweight, const void* scales, const void* zeros,
+                            const float* y_ref, int64_t T, int64_t N, int64_t K, int32_t group, double* workspace,
                             int64_t workspace_len, double* loss, void* stream) {
   clear_error();
-  if (!x || !x_s || !w || !qweight || !scales || !zeros || !workspace || !loss)
-    return fail(W4A16_ERR_NULL, "x, x_s, w, qweight, scales, zeros, workspace and loss are required");
+  if (!x_s || !qweight || !scales || !zeros || !y_ref || !workspace || !loss)
+    return fail(W4A16_ERR_NULL, "x_s, qweight, scales, zeros, y_ref, workspace and loss are required");
   if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "group must be 128 (got %d)", (int)group);
   if (T <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "T, N, K must be positive (got %lld, %lld, %lld)",
                                               (long long)T, (long long)N, (long long)K);
   if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
   const int64_t need = awq_alpha_loss_workspace(T, N);
   if (K > W4A16_MAX_K || need < 0)
-    return fail(W4A16_ERR_SHAPE, "size beyond the limits (T <= 2^20, N <= 2^24, K <= %d, ceil(T/64) * ceil(N/64) < 2^31)",
-                W4A16_MAX_K);
+    return fail(W4A16_ERR_SHAPE, "size beyond the limits (T <= 2^20, N <= 2^24, K <= %d)", W4A16_MAX_K);
   if (workspace_len < need)
     return fail(W4A16_ERR_ARG, "workspace holds %lld float64 values, %lld needed", (long long)workspace_len,
                 (long long)need);
-  if (!aligned(x, 16) || !aligned(x_s, 16) || !aligned(w, 16) || !aligned(qweight, 16))
-    return fail(W4A16_ERR_ALIGN, "x, x_s, w and qweight must be 16-byte aligned");
-  if (!aligned(scales, 2) || !aligned(zeros, 2) || !aligned(workspace, 8) || !aligned(loss, 8))
-    return fail(W4A16_ERR_ALIGN, "scales and zeros must be 2-byte, workspace and loss 8-byte aligned");
-  return hip_result(w4a16::launch_alpha_loss(static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(x_s),
-                                             static_cast<const uint16_t*>(w), static_cast<const uint32_t*>(qweight),
+  if (!aligned(x_s, 16) || !aligned(qweight, 16))
+    return fail(W4A16_ERR_ALIGN, "x_s and qweight must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(zeros, 2) || !aligned(y_ref, 4) || !aligned(workspace, 8) || !aligned(loss, 8))
+    return fail(W4A16_ERR_ALIGN, "scales and zeros must be 2-byte, y_ref 4-byte, workspace and loss 8-byte aligned");
+  return hip_result(w4a16::launch_alpha_loss(static_cast<const uint16_t*>(x_s), static_cast<const uint32_t*>(qweight),
                                              static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
-                                             T, N, K, workspace, loss, static_cast<hipStream_t>(stream)),
+                                             y_ref, T, N, K, workspace, loss, static_cast<hipStream_t>(stream)),
                     "alpha-loss launch");
 }
 

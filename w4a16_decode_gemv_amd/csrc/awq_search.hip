@@ -1,33 +1,49 @@
-// The output-error loss of the AWQ scale search, for one candidate scale.
+// The output-error loss of the AWQ scale search.
 //
-//   L(s) = sum_{t,n} ( sum_k x_s[t][k] * w_hat[n][k]  -  sum_k x[t][k] * w[n][k] )^2
+//   loss(s) = sum_{t,n} ( sum_k x_s[t][k] * w_hat[n][k]  -  y_ref[t][n] )^2,
+//   y_ref[t][n] = sum_k x[t][k] * w[n][k]
 //
 // "MIT 6.5940 L13 LLM Deployment" guide, AWQ section (slide 28): the scale is
-// chosen by a grid search over alpha on L(s) = ||Q(W s)(s^-1 X) - W X|| with
-// s = s_X^alpha, the error measured on the layer's output; chapter 11, AWQ
-// section, the same. Here x_s = f16(x / s) is the input the deployed kernel
-// consumes and w_hat = (q - z) * d is rebuilt from the packed codes and the stored
-// fp16 scale and zero of W * s (both produced by this library's own kernels), so
-// the loss is the one of the layer as it would run.
+// picked by a grid search over alpha that minimises the distance between the
+// quantized layer's output on (s^-1 X) and the original layer's output W X,
+// with s = s_X^alpha; "Quantization for LLMs" chapter 11, AWQ section, the same.
+// x_s = f16(x / s) is the input the deployed kernel consumes and w_hat =
+// (q - z) * d is rebuilt from the packed codes and the stored fp16 scale and zero
+// of W * s, so the loss is that of the layer as it would run.
 //
-// One fused tiled MFMA pass computes both products for a 64 x 64 (t, n) tile,
-// one quantization group (128 inputs) per step:
-//   * the quantized product takes exact fp16 q in the B operand and applies each
-//     group as d * (sum_k x_s q - z * sum_k x_s): exact q - z for every storable
-//     zero; sum_k x_s per (row, group) is formed once while the tile is staged;
-//   * the reference product takes the fp16 weights directly;
-// both accumulate in float32. x and x_s are shared by the four waves and staged
-// through LDS (double-buffered, the next group's global loads in flight while the
-// current one is computed); the weights, codes and (scale, zero) of a wave's 16
-// output rows are its own and go straight to registers. The tile's squared
-// differences are summed in float64 in a fixed order into one partial; a second
-// one-workgroup kernel adds the partials in index order into the loss, so the
-// result is reproducible run to run.
+// The original layer's output does not depend on the candidate scale, so it is
+// computed once per search (output_reference_kernel) and every grid point runs
+// only the quantized product (alpha_loss_kernel), whose epilogue subtracts the
+// stored reference, squares and sums.
 //
-// Fragments as in the tiled linear kernel (v_mfma_f32_16x16x32_f16): at step st
-// of a group, slot group j holds the 8 inputs of chunk 4j + st, so lane (j, c)
-// reads 64 contiguous bytes of its weight row and one 16-byte code chunk per
-// group.
+// Both kernels tile the (t, n) plane in BM x BN = 64 x 128 tiles, one workgroup of
+// eight waves per tile, each wave owning 16 output rows n and all 64 rows t, one
+// quantization group (128 inputs) per stage:
+//   * the 64 x 128 input tile (x or x_s) is shared by the eight waves and passes
+//     through LDS; the weights of a wave's 16 rows (codes with (scale, zero), or
+//     the fp16 weights) are its own and stay in registers;
+//   * loads run R = 2 stages ahead of the compute in register sets that are
+//     written to LDS one stage ahead; every load is a buffer load, so rows past T
+//     or N and stages past the last group read as zero with no memory traffic and
+//     the pipeline has no data-dependent branch; the workgroup barrier orders LDS
+//     only, so loads stay in flight across it;
+//   * the quantized product takes exact fp16 (q - z) in the B operand while the
+//     zero lies in [-2032, 1024] (OR-ing a nibble pair into 0x6400 gives 1024 + q;
+//     a packed add, or a packed FMA by 1/16 for the high nibbles, with -(1024 + z)
+//     or -(64 + z) gives q - z without rounding), and acc += d * sum; a wave that
+//     meets a zero outside that range (only one-signed groups have one) takes the
+//     general route for that stage: exact q, and the zero applied as
+//     z * sum_k x_s with sum_k x_s from an MFMA of the same fragment against ones;
+//   * products accumulate in float32; the loss epilogue forms each residual, its
+//     square and the tile's sum in float64 in a fixed order and writes one partial;
+//     a one-workgroup kernel adds the partials in index order, so the loss is
+//     reproducible run to run.
+//
+// Fragments (v_mfma_f32_16x16x32_f16): lane (j, c) = (l / 16, l % 16) holds
+// A[m = c][8 k-slots of slot group j] and B[the same slots][n = c]; D[m = 4 j + i]
+// [n = c]. At step st of a stage, slot group j takes the 8 inputs of chunk
+// 4 j + st, so a lane reads 64 contiguous weight bytes, or one 16-byte chunk of
+// codes, per stage of its row.
 #include "device_utils.h"
 #include "launchers.h"
 
@@ -38,18 +54,24 @@ namespace {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 64;   // calibration rows t per tile (4 MFMA tiles of 16)
-constexpr int BN = 64;   // output rows n per tile (4 waves x 16)
-constexpr int kThreads = 256;
-constexpr int XP = 17;   // x tiles: 16 chunks of 16 bytes per row, padded to 17
+constexpr int MT = 4;                 // 16-row MFMA tiles of t per workgroup
+constexpr int WAVES = 8;
+constexpr int BM = 16 * MT;           // 64 rows t
+constexpr int BN = 16 * WAVES;        // 128 rows n
+constexpr int kThreads = 64 * WAVES;
+constexpr int XU = BM * 16 / kThreads;  // 16-byte input chunks per thread per stage
+constexpr int R = 2;                  // stages of loads in flight ahead of the compute
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: raw 32-bit data, range-checked
+constexpr int kOutOfRange = 1 << 30;      // added to an offset: past every range used here
+
+static_assert(R % 2 == 0, "the LDS buffer of each unrolled stage must be fixed");
 
 __device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
 
-// the eight codes q of one code word as exact fp16, in k order
-__device__ __forceinline__ half8_t codes_word(uint32_t w) {
+// exact fp16 pairs of one code word (8 codes in k order) minus the zero:
+// c_lo = -(1024 + z), c_hi = -(64 + z); z = 0 gives the codes q themselves
+__device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t c_lo, half2_t c_hi) {
   const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const half2_t c_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const half2_t c_hi = {(_Float16)-64.0f, (_Float16)-64.0f};
   const uint32_t w8 = w >> 8;
   const half2_t p0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + c_lo;
   const half2_t p1 = __builtin_elementwise_fma(as_half2(and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
@@ -60,185 +82,300 @@ __device__ __forceinline__ half8_t codes_word(uint32_t w) {
   return __builtin_bit_cast(half8_t, v);
 }
 
-// sum of the eight fp16 values of one 16-byte chunk, float32, in k order
-__device__ __forceinline__ float chunk_sum(u32x4_t v) {
-  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s += half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
-    s += half_bits_to_float((uint16_t)(w[i] >> 16));
-  }
-  return s;
-}
-
-struct Smem {
-  u32x4_t xs[2][BM][XP];  // x_s tile of the group
-  u32x4_t x[2][BM][XP];   // x tile of the group
-  float sxs[2][BM];       // sum over the group's 128 inputs of x_s, per row
-};
-
-// Tiles are numbered so that the eight XCDs (workgroups go to them round-robin)
-// each take a contiguous run of output-row tiles, all calibration tiles of one
-// output-row tile back to back: a weight tile is fetched by one XCD's L2.
+// Tiles are numbered so that each of the eight XCDs (workgroups are dealt to them
+// round-robin) takes a contiguous run: the calibration tiles of one weight tile
+// run on one XCD, which then fetches that weight tile into its L2 once.
 __device__ __forceinline__ int tile_of_block(int id, int nb) {
   const int xcd = id & 7, slot = id >> 3;
   const int per = nb >> 3, rem = nb & 7;
   return xcd * per + min(xcd, rem) + slot;
 }
 
-__global__ __launch_bounds__(kThreads) void alpha_loss_kernel(const u32x4_t* __restrict__ x, const u32x4_t* __restrict__ xs,
-                                                             const u32x4_t* __restrict__ w, const u32x4_t* __restrict__ qw,
+// workgroup barrier that orders LDS only: global loads stay in flight across it
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Loads of one stage's input tile into registers, and their store into LDS (rows
+// XOR-free: the row pitch of 17 chunks keeps the 16 lanes of a read on distinct banks).
+struct InputTile {
+  int off[XU];
+  __device__ InputTile(int t, int K) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) off[u] = ((t >> 4) + (kThreads / 16) * u) * K * 2 + (t & 15) * 16;
+  }
+};
+
+struct Lds {
+  u32x4_t x[2][BM][17];
+};
+
+__device__ __forceinline__ void store_tile(Lds& lds, int b, const u32x4_t (&v)[XU], int t) {
+#pragma unroll
+  for (int u = 0; u < XU; ++u) lds.x[b][(t >> 4) + (kThreads / 16) * u][t & 15] = v[u];
+}
+
+// ---------------------------------------------------------------- the quantized product
+
+struct QuantStage {
+  u32x4_t x[XU];
+  u32x4_t q;
+  uint16_t s, z;
+};
+
+__global__ __launch_bounds__(kThreads) void alpha_loss_kernel(const uint16_t* __restrict__ xs,
+                                                             const uint32_t* __restrict__ qw,
                                                              const uint16_t* __restrict__ scales,
-                                                             const uint16_t* __restrict__ zeros, int T, int N, int K,
+                                                             const uint16_t* __restrict__ zeros,
+                                                             const float* __restrict__ yref, int T, int N, int K,
                                                              int GT, double* __restrict__ partials) {
-  __shared__ Smem sm;
-  __shared__ double wsum[kThreads / 64];
+  __shared__ Lds lds;
+  __shared__ double wsum[WAVES];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
   const int tile = tile_of_block(blockIdx.x, gridDim.x);
   const int m0 = (tile % GT) * BM, n0 = (tile / GT) * BN;
-  const int G = K >> 7, KX = K >> 3, KQ = K >> 5;
+  const int G = K >> 7;
+  const int nl = wave * 16 + c;  // this lane's output row within the tile
 
-  // staging of x and x_s: chunk i = t + 256 u -> row (t >> 4) + 16 u, chunk t & 15; the
-  // 16 lanes of a row form one DPP row
-  const int ch = t & 15;
-  int64_t xoff[4];
-#pragma unroll
-  for (int u = 0; u < 4; ++u) xoff[u] = (int64_t)min(m0 + (t >> 4) + 16 * u, T - 1) * KX + ch;
-  // this lane's output row
-  const int nl = wave * 16 + c;
-  const int nrow = min(n0 + nl, N - 1);
-  const u32x4_t* wrow = w + (int64_t)nrow * KX + 4 * j;
-  const u32x4_t* qrow = qw + (int64_t)nrow * KQ + j;
-  const int64_t szrow = (int64_t)nrow * G;
+  // each resource spans only this tile's rows (at most 32 MiB), so an offset plus
+  // kOutOfRange always lies past it
+  const int64_t rows_t = min(T - m0, BM), rows_n = min(N - n0, BN);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(xs + (int64_t)m0 * K, rows_t * K * 2);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qw + (int64_t)n0 * (K >> 3), rows_n * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rs = rsrc(scales + (int64_t)n0 * G, rows_n * G * 2);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(zeros + (int64_t)n0 * G, rows_n * G * 2);
+  const InputTile xin(t, K);
+  const int qo = nl * (K >> 1) + j * 16;
+  const int so = nl * G * 2;
 
-  u32x4_t rxs[4], rx[4];
-  u32x4_t wn[4], qn;
-  uint16_t sn, zn;
-  auto load_stage = [&](int g) {
+  QuantStage set[R];
+  auto issue = [&](int g, QuantStage& r) {
+    const int past = (int)(g >= G) * kOutOfRange;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      rxs[u] = xs[xoff[u] + 16 * g];
-      rx[u] = x[xoff[u] + 16 * g];
-    }
-#pragma unroll
-    for (int st = 0; st < 4; ++st) wn[st] = wrow[16 * g + st];
-    qn = qrow[4 * g];
-    sn = scales[szrow + g];
-    zn = zeros[szrow + g];
-  };
-  auto store_stage = [&](int b) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = (t >> 4) + 16 * u;
-      sm.xs[b][r][ch] = rxs[u];
-      sm.x[b][r][ch] = rx[u];
-      const float sr = dpp_row_sum16(chunk_sum(rxs[u]));
-      if (ch == 0) sm.sxs[b][r] = sr;
-    }
+    for (int u = 0; u < XU; ++u) r.x[u] = load16(rx, xin.off[u] + g * 256 + past);
+    r.q = load16(rq, qo + g * 64 + past);
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, so + g * 2 + past, 0, 0);
+    r.z = __builtin_amdgcn_raw_buffer_load_b16(rz, so + g * 2 + past, 0, 0);
   };
 
-  float4_t dq[4], dr[4];  // quantized and reference products, per MFMA tile of rows
+  float4_t acc[MT];
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-    dq[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    dr[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  }
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0);
-  store_stage(0);
-  u32x4_t wc[4] = {wn[0], wn[1], wn[2], wn[3]};
-  u32x4_t qc = qn;
-  uint16_t sc = sn, zc = zn;
-  __syncthreads();
-  for (int g = 0; g < G; ++g) {
-    const int b = g & 1;
-    if (g + 1 < G) load_stage(g + 1);
-    const half8_t bq[4] = {codes_word(qc.x), codes_word(qc.y), codes_word(qc.z), codes_word(qc.w)};
-    const float d = half_bits_to_float(sc);
-    const float zf = half_bits_to_float(zc);
+  auto compute = [&](const QuantStage& r, int b) {
+    const float d = half_bits_to_float(r.s);
+    const _Float16 zh = __builtin_bit_cast(_Float16, r.z);
+    const float zf = (float)zh;
+    const bool exact = zf >= -2032.0f && zf <= 1024.0f;
+    if (__builtin_amdgcn_ballot_w64(!exact) == 0) {
+      const _Float16 clo = -((_Float16)1024.0f + zh), chi = -((_Float16)64.0f + zh);
+      const half2_t c_lo = {clo, clo}, c_hi = {chi, chi};
+      const half8_t bq[4] = {dequant_word(r.q.x, c_lo, c_hi), dequant_word(r.q.y, c_lo, c_hi),
+                             dequant_word(r.q.z, c_lo, c_hi), dequant_word(r.q.w, c_lo, c_hi)};
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-      const int row = 16 * mt + c;
-      float4_t a = {0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < MT; ++mt) {
+        float4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        a = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(sm.xs[b][row][4 * j + st]), bq[st], a, 0, 0, 0);
-        dr[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(sm.x[b][row][4 * j + st]), as_half8(wc[st]), dr[mt],
-                                                        0, 0, 0);
+        for (int st = 0; st < 4; ++st)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(lds.x[b][16 * mt + c][4 * j + st]), bq[st], a, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, a[i], acc[mt][i]);
       }
-      const float4_t sx = *reinterpret_cast<const float4_t*>(&sm.sxs[b][16 * mt + 4 * j]);
+    } else {
+      const half2_t c_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+      const half2_t c_hi = {(_Float16)-64.0f, (_Float16)-64.0f};
+      const u32x4_t ones_bits = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+      const half8_t ones = as_half8(ones_bits);
+      const half8_t bq[4] = {dequant_word(r.q.x, c_lo, c_hi), dequant_word(r.q.y, c_lo, c_hi),
+                             dequant_word(r.q.z, c_lo, c_hi), dequant_word(r.q.w, c_lo, c_hi)};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dq[mt][i] = __builtin_fmaf(d, __builtin_fmaf(-zf, sx[i], a[i]), dq[mt][i]);
-    }
-    if (g + 1 < G) {
-      store_stage(b ^ 1);  // the buffer every wave finished reading before the last barrier
+      for (int mt = 0; mt < MT; ++mt) {
+        float4_t a = {0.f, 0.f, 0.f, 0.f}, sx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int st = 0; st < 4; ++st) wc[st] = wn[st];
-      qc = qn;
-      sc = sn;
-      zc = zn;
+        for (int st = 0; st < 4; ++st) {
+          const half8_t xa = as_half8(lds.x[b][16 * mt + c][4 * j + st]);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bq[st], a, 0, 0, 0);
+          sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ones, sx, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, __builtin_fmaf(-zf, sx[i], a[i]), acc[mt][i]);
+      }
     }
-    __syncthreads();
-  }
+  };
 
-  // squared differences of this tile's valid outputs, float64, fixed order
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    issue(r, set[r]);
+    __builtin_amdgcn_sched_barrier(0);  // stages stay in issue order: the waits count on it
+  }
+  store_tile(lds, 0, set[0].x, t);
+  lds_barrier();
+  for (int g0 = 0; g0 < G; g0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int g = g0 + r;
+      if (g < G) compute(set[r], r & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(g + R, set[r]);  // this set's stage is computed: refill it
+      __builtin_amdgcn_sched_barrier(0);
+      store_tile(lds, (r + 1) & 1, set[(r + 1) % R].x, t);  // the buffer every wave left at the last barrier
+      lds_barrier();
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load in flight at exit
+
+  // the reference entries of this lane's 16 outputs, loaded together (indices clamped
+  // into the matrix, invalid outputs masked afterwards)
+  const int n = n0 + nl;
+  const int64_t ncol = min(n, N - 1);
+  float yr[MT][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yr[mt][i] = yref[(int64_t)min(m0 + 16 * mt + 4 * j + i, T - 1) * N + ncol];
+  double e2 = 0.0;
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool valid = m0 + 16 * mt + 4 * j + i < T && n < N;
+      const double e = valid ? (double)acc[mt][i] - (double)yr[mt][i] : 0.0;
+      e2 += e * e;
+    }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) e2 += __shfl_xor(e2, off, 64);
+  if (lane == 0) wsum[wave] = e2;
+  __syncthreads();
+  if (t == 0) {
+    double sum = 0.0;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) sum += wsum[w];
+    partials[tile] = sum;
+  }
+}
+
+__global__ __launch_bounds__(256) void sum_partials_kernel(const double* __restrict__ partials, int64_t count,
+                                                          double* __restrict__ loss) {
+  __shared__ double wsum[4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   double acc = 0.0;
+  for (int64_t i = t; i < count; i += 256) acc += partials[i];
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+  if (lane == 0) wsum[wave] = acc;
+  __syncthreads();
+  if (t == 0) *loss = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+}
+
+// ---------------------------------------------------------------- the original layer's output
+
+struct DenseStage {
+  u32x4_t x[XU];
+  u32x4_t w[4];
+};
+
+__global__ __launch_bounds__(kThreads) void output_reference_kernel(const uint16_t* __restrict__ x,
+                                                                   const uint16_t* __restrict__ w, int T, int N,
+                                                                   int K, int GT, float* __restrict__ y) {
+  __shared__ Lds lds;
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j = lane >> 4, c = lane & 15;
+  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  const int m0 = (tile % GT) * BM, n0 = (tile / GT) * BN;
+  const int G = K >> 7;
+  const int nl = wave * 16 + c;
+
+  const int64_t rows_t = min(T - m0, BM), rows_n = min(N - n0, BN);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x + (int64_t)m0 * K, rows_t * K * 2);
+  const __amdgpu_buffer_rsrc_t rw = rsrc(w + (int64_t)n0 * K, rows_n * K * 2);
+  const InputTile xin(t, K);
+  const int wo = nl * K * 2 + j * 64;
+
+  DenseStage set[R];
+  auto issue = [&](int g, DenseStage& r) {
+    const int past = (int)(g >= G) * kOutOfRange;
+#pragma unroll
+    for (int u = 0; u < XU; ++u) r.x[u] = load16(rx, xin.off[u] + g * 256 + past);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) r.w[st] = load16(rw, wo + g * 256 + st * 16 + past);
+  };
+
+  float4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const DenseStage& r, int b) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int st = 0; st < 4; ++st)
+        acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(lds.x[b][16 * mt + c][4 * j + st]),
+                                                         as_half8(r.w[st]), acc[mt], 0, 0, 0);
+  };
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    issue(r, set[r]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  store_tile(lds, 0, set[0].x, t);
+  lds_barrier();
+  for (int g0 = 0; g0 < G; g0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int g = g0 + r;
+      if (g < G) compute(set[r], r & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(g + R, set[r]);
+      __builtin_amdgcn_sched_barrier(0);
+      store_tile(lds, (r + 1) & 1, set[(r + 1) % R].x, t);
+      lds_barrier();
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
   const int n = n0 + nl;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
+  for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = m0 + 16 * mt + 4 * j + i;
-      const double e = (double)dq[mt][i] - (double)dr[mt][i];
-      if (m < T && n < N) acc += e * e;
+      if (m < T && n < N) y[(int64_t)m * N + n] = acc[mt][i];
     }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) wsum[wave] = acc;
-  __syncthreads();
-  if (t == 0) {
-    double s = 0.0;
-#pragma unroll
-    for (int ww = 0; ww < kThreads / 64; ++ww) s += wsum[ww];
-    partials[tile] = s;
-  }
 }
 
-__global__ __launch_bounds__(kThreads) void sum_partials_kernel(const double* __restrict__ partials, int64_t count,
-                                                               double* __restrict__ loss) {
-  __shared__ double wsum[kThreads / 64];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  double acc = 0.0;
-  for (int64_t i = t; i < count; i += kThreads) acc += partials[i];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-  if (lane == 0) wsum[wave] = acc;
-  __syncthreads();
-  if (t == 0) {
-    double s = 0.0;
-#pragma unroll
-    for (int ww = 0; ww < kThreads / 64; ++ww) s += wsum[ww];
-    *loss = s;
-  }
-}
+int64_t tiles(int64_t T, int64_t N) { return ((T + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
 }  // namespace
 
-int64_t alpha_loss_partials(int64_t T, int64_t N) { return ((T + BM - 1) / BM) * ((N + BN - 1) / BN); }
+int64_t alpha_loss_partials(int64_t T, int64_t N) { return tiles(T, N); }
 
-hipError_t launch_alpha_loss(const uint16_t* x, const uint16_t* x_s, const uint16_t* w, const uint32_t* qweight,
-                             const uint16_t* scales, const uint16_t* zeros, int64_t T, int64_t N, int64_t K,
+hipError_t launch_output_reference(const uint16_t* x, const uint16_t* w, int64_t T, int64_t N, int64_t K, float* y,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(output_reference_kernel, dim3((unsigned)tiles(T, N)), dim3(kThreads), 0, stream, x, w, (int)T,
+                     (int)N, (int)K, (int)((T + BM - 1) / BM), y);
+  return hipGetLastError();
+}
+
+hipError_t launch_alpha_loss(const uint16_t* x_s, const uint32_t* qweight, const uint16_t* scales,
+                             const uint16_t* zeros, const float* y_ref, int64_t T, int64_t N, int64_t K,
                              double* partials, double* loss, hipStream_t stream) {
-  const int64_t tiles = alpha_loss_partials(T, N);
-  hipLaunchKernelGGL(alpha_loss_kernel, dim3((unsigned)tiles), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const u32x4_t*>(x), reinterpret_cast<const u32x4_t*>(x_s),
-                     reinterpret_cast<const u32x4_t*>(w), reinterpret_cast<const u32x4_t*>(qweight), scales, zeros,
-                     (int)T, (int)N, (int)K, (int)((T + BM - 1) / BM), partials);
+  const int64_t nt = tiles(T, N);
+  hipLaunchKernelGGL(alpha_loss_kernel, dim3((unsigned)nt), dim3(kThreads), 0, stream, x_s, qweight, scales, zeros,
+                     y_ref, (int)T, (int)N, (int)K, (int)((T + BM - 1) / BM), partials);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(kThreads), 0, stream, partials, tiles, loss);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3(1), dim3(256), 0, stream, partials, nt, loss);
   return hipGetLastError();
 }
 

@@ -38,11 +38,14 @@ hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_
                        const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                        hipStream_t stream);
 
-// Loss of the AWQ scale search for one candidate scale: number of float64
-// partials it writes, and the launch (loss kernel + fixed-order reduction).
+// AWQ scale search: the original layer's output (float32), and the loss of one
+// candidate scale (number of float64 partials it writes; loss kernel + fixed-order
+// reduction).
+hipError_t launch_output_reference(const uint16_t* x, const uint16_t* w, int64_t T, int64_t N, int64_t K, float* y,
+                                   hipStream_t stream);
 int64_t alpha_loss_partials(int64_t T, int64_t N);
-hipError_t launch_alpha_loss(const uint16_t* x, const uint16_t* x_s, const uint16_t* w, const uint32_t* qweight,
-                             const uint16_t* scales, const uint16_t* zeros, int64_t T, int64_t N, int64_t K,
+hipError_t launch_alpha_loss(const uint16_t* x_s, const uint32_t* qweight, const uint16_t* scales,
+                             const uint16_t* zeros, const float* y_ref, int64_t T, int64_t N, int64_t K,
                              double* partials, double* loss, hipStream_t stream);
 
 }  // namespace w4a16
