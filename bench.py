@@ -255,13 +255,18 @@ def search_leg(w4, torch):
             w4.alpha_loss(xs, *packed, y_ref, workspace=ws, out=loss[i % 21:i % 21 + 1])
 
         t_point = time_graph(torch, point, 21)
+        t_scale = time_graph(torch, lambda i: w4.channel_scale(x_cal, w4.ALPHA_GRID[i % 21], out=s), 21)
+        t_fold = time_graph(torch, lambda i: w4.scale_input(x_cal, s, out=xs), 21)
+        t_quant = time_graph(torch, lambda i: w4.quantize_pack(W, s, out=packed), 21)
         flop = 2 * t_cal * nn * kk  # one product of 2 T N K
         search_us = (t_ref + 21 * t_point) * 1e3
         rows.append({"layer": name, "T": t_cal, "K": kk, "N": nn, "reference_us": t_ref * 1e3,
                      "reference_TFLOP_s": flop / (t_ref * 1e-3) / 1e12,
                      "loss_us": t_loss * 1e3, "loss_TFLOP_s": flop / (t_loss * 1e-3) / 1e12,
                      "loss_mfma_util": flop / (t_loss * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
-                     "grid_point_us": t_point * 1e3, "search_21_us": search_us})
+                     "grid_point_us": t_point * 1e3, "channel_scale_us": t_scale * 1e3,
+                     "scale_input_us": t_fold * 1e3, "quantize_pack_us": t_quant * 1e3,
+                     "search_21_us": search_us})
         total_search_us += search_us
         del x_cal, W, s, xs, packed, ws, y_ref
         torch.cuda.empty_cache()

@@ -82,6 +82,28 @@ def test_channel_scale_bit_exact(lib, alpha, cfg, k):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), g.report_mismatch("s", got, want)
 
 
+@pytest.mark.parametrize("t_cal,k,misalign", [(7, 4096, False), (100, 37, False), (513, 136, False), (1, 8, False),
+                                              (64, 1024, True), (33, 120, True)])
+def test_channel_scale_token_split_and_fallback(lib, t_cal, k, misalign):
+    # K % 8 == 0 with 16-byte alignment takes the token-split kernel, anything else the
+    # per-channel kernel; the float64 sum is exact, so both must give identical bits
+    import torch
+
+    g = _gpu()
+    xc = synth.calibration(1, 4, k, t_cal)
+    if misalign:
+        flat = torch.empty(t_cal * k + 1, dtype=torch.float16, device=g.DEV)
+        xd = flat[1:].view(t_cal, k)
+        xd.copy_(torch.from_numpy(xc))
+        assert xd.data_ptr() % 16 != 0
+    else:
+        xd = g.dev(xc)
+    for alpha in (0.5, 1.0):
+        got = g.host(lib.channel_scale(xd, alpha))
+        want = oracle.channel_scale(xc, alpha)
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), g.report_mismatch("s", got, want)
+
+
 def test_channel_scale_general_alpha_within_an_ulp(lib):
     g = _gpu()
     xc = synth.calibration(1, 1, 2048)

@@ -17,9 +17,28 @@
 namespace w4a16 {
 
 // ---------------------------------------------------------------------------
-// s[k] = (sum_t |x_cal[t][k]| / T)^alpha; one thread per channel, the loop over
-// tokens is coalesced across channels. The float64 sum of fp16 magnitudes is
-// exact (hence order-free) while T * max|x| < 2^29.
+// s[k] = (sum_t |x_cal[t][k]| / T)^alpha. The float64 sum of fp16 magnitudes is
+// exact while T * max|x| < 2^29 (every fp16 value is a multiple of 2^-24), so it
+// does not depend on the order of the additions: the tokens can be split freely.
+
+__device__ __forceinline__ float channel_power(double sum, int T, double alpha) {
+  const double mean = sum / (double)T;
+  double r;
+  if (mean == 0.0)
+    r = 1.0;
+  else if (alpha == 0.5)
+    r = sqrt(mean);
+  else if (alpha == 1.0)
+    r = mean;
+  else if (alpha == 0.0)
+    r = 1.0;
+  else
+    r = pow(mean, alpha);
+  return (float)r;
+}
+
+// Any K and alignment: one thread per channel, the loop over tokens coalesced
+// across channels.
 __global__ __launch_bounds__(256) void channel_scale_kernel(const uint16_t* __restrict__ x_cal, int T, int K,
                                                             double alpha, float* __restrict__ s) {
   const int k = blockIdx.x * blockDim.x + threadIdx.x;
@@ -34,26 +53,75 @@ __global__ __launch_bounds__(256) void channel_scale_kernel(const uint16_t* __re
     acc3 += fabs((double)half_bits_to_float(p[(int64_t)(t + 3) * K]));
   }
   for (; t < T; ++t) acc0 += fabs((double)half_bits_to_float(p[(int64_t)t * K]));
-  const double mean = ((acc0 + acc1) + (acc2 + acc3)) / (double)T;
-  double r;
-  if (mean == 0.0)
-    r = 1.0;
-  else if (alpha == 0.5)
-    r = sqrt(mean);
-  else if (alpha == 1.0)
-    r = mean;
-  else if (alpha == 0.0)
-    r = 1.0;
-  else
-    r = pow(mean, alpha);
-  s[k] = (float)r;
+  s[k] = channel_power((acc0 + acc1) + (acc2 + acc3), T, alpha);
+}
+
+// K % 8 == 0 and x_cal 16-byte aligned: a workgroup owns 128 channels; its 16
+// rows of 16 threads split the tokens (thread (ty, tx) reads the 16 bytes of
+// channels 8tx .. 8tx+7 of tokens ty, ty + 16, ...), and the 16 partial sums of
+// each channel meet in LDS.
+constexpr int kScaleRows = 16;
+
+__global__ __launch_bounds__(256) void channel_scale_wide_kernel(const uint4* __restrict__ x_cal, int T, int K,
+                                                                 double alpha, float* __restrict__ s) {
+  __shared__ double part[kScaleRows][129];
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
+  const int k0 = blockIdx.x * 128 + 8 * tx;  // first of this thread's 8 channels
+  const bool active = k0 < K;                // K % 8 == 0: all 8 channels exist
+  const int KC = K >> 3;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+  if (active) {
+    const uint4* p = x_cal + (k0 >> 3);
+    int t = ty;
+    for (; t + 3 * kScaleRows < T; t += 4 * kScaleRows) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = p[(int64_t)(t + u * kScaleRows) * KC];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[2 * i] += fabs((double)half_bits_to_float((uint16_t)(w[i] & 0xFFFFu)));
+          acc[2 * i + 1] += fabs((double)half_bits_to_float((uint16_t)(w[i] >> 16)));
+        }
+      }
+    }
+    for (; t < T; t += kScaleRows) {
+      const uint4 v = p[(int64_t)t * KC];
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] += fabs((double)half_bits_to_float((uint16_t)(w[i] & 0xFFFFu)));
+        acc[2 * i + 1] += fabs((double)half_bits_to_float((uint16_t)(w[i] >> 16)));
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) part[ty][8 * tx + i] = acc[i];
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    const int k = blockIdx.x * 128 + threadIdx.x;
+    if (k < K) {
+      double sum = 0.0;
+#pragma unroll
+      for (int r = 0; r < kScaleRows; ++r) sum += part[r][threadIdx.x];
+      s[k] = channel_power(sum, T, alpha);
+    }
+  }
 }
 
 hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t T, int64_t K, double alpha, float* s,
                                 hipStream_t stream) {
-  const int block = 256;
-  const int grid = (int)((K + block - 1) / block);
-  hipLaunchKernelGGL(channel_scale_kernel, dim3(grid), dim3(block), 0, stream, x_cal, (int)T, (int)K, alpha, s);
+  if (K % 8 == 0 && (reinterpret_cast<uintptr_t>(x_cal) & 15) == 0) {
+    const int grid = (int)((K + 127) / 128);
+    hipLaunchKernelGGL(channel_scale_wide_kernel, dim3(grid), dim3(256), 0, stream,
+                       reinterpret_cast<const uint4*>(x_cal), (int)T, (int)K, alpha, s);
+  } else {
+    const int block = 256;
+    const int grid = (int)((K + block - 1) / block);
+    hipLaunchKernelGGL(channel_scale_kernel, dim3(grid), dim3(block), 0, stream, x_cal, (int)T, (int)K, alpha, s);
+  }
   return hipGetLastError();
 }
 
