@@ -38,7 +38,7 @@ from .quant import (
     quantize_pack,
     f64_to_f16,
 )
-from .layout import pack_codes, unpack_codes, LAYOUT_VERSION
+from .layout import pack_codes, unpack_codes, pack_codes3, unpack_codes3, LAYOUT_VERSION
 from .linear import dequantize, linear, within_tolerance, TOL_REL, TOL_ABS
 from .norm import rms_factor, rmsnorm_fold
 from .search import GRID as ALPHA_GRID, alpha_loss, search_alpha

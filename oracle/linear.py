@@ -23,7 +23,7 @@ acceptance rule for any device result y is
 
 import numpy as np
 
-from .layout import unpack_codes
+from .layout import unpack_codes, unpack_codes3
 
 TOL_REL = 1e-3
 TOL_ABS = 1e-5
@@ -31,9 +31,14 @@ TOL_ABS = 1e-5
 _ROW_BLOCK = 512
 
 
-def dequantize(qweight, scales, zeros, k, group=128):
-    """w_hat[n, k] = (q[n, k] - zero[n, g]) * scale[n, g], float64 [N][K]."""
-    q = unpack_codes(qweight, k).astype(np.float64)
+def dequantize(qweight, scales, zeros, k, group=128, bits=4):
+    """w_hat[n, k] = (q[n, k] - zero[n, g]) * scale[n, g], float64 [N][K].
+
+    qweight is in layout v1 (bits = 4) or the 3-bit bit-plane layout (bits = 3).
+    """
+    if bits not in (3, 4):
+        raise ValueError("bits must be 3 or 4")
+    q = (unpack_codes(qweight, k) if bits == 4 else unpack_codes3(qweight, k)).astype(np.float64)
     n = q.shape[0]
     s = np.asarray(scales, dtype=np.float16).astype(np.float64)
     z = np.asarray(zeros, dtype=np.float16).astype(np.float64)
@@ -44,7 +49,7 @@ def dequantize(qweight, scales, zeros, k, group=128):
     return w.reshape(n, k)
 
 
-def linear(x, qweight, scales, zeros, group=128, rows=None):
+def linear(x, qweight, scales, zeros, group=128, rows=None, bits=4):
     """y_ref = x @ w_hat^T and B = |x| @ |w_hat|^T, both float64 [M][N].
 
     x: float16 [M][K] (the input after the 1/s fold). ``rows`` optionally
@@ -67,7 +72,7 @@ def linear(x, qweight, scales, zeros, group=128, rows=None):
     ax = np.abs(x64)
     for r0 in range(0, n, _ROW_BLOCK):
         r1 = min(n, r0 + _ROW_BLOCK)
-        w = dequantize(qweight[r0:r1], scales[r0:r1], zeros[r0:r1], k, group)
+        w = dequantize(qweight[r0:r1], scales[r0:r1], zeros[r0:r1], k, group, bits)
         y[:, r0:r1] = x64 @ w.T
         b[:, r0:r1] = ax @ np.abs(w).T
     return y, b

@@ -142,19 +142,23 @@ def quantize_pack(W, s=None, bits=4, group=128):
 
     w = float64(W) * float64(s) (exact: 11-bit times 24-bit significands), then
     ``quantize_groups``, then storage: scales = f16(Delta), zeros = f16(z),
-    qweight = layout-v1 nibble words. Returns (qweight uint32 [N][K/8],
-    scales float16 [N][K/g], zeros float16 [N][K/g]).
+    qweight = layout-v1 nibble words (bits = 4) or the 3-bit bit-plane words
+    (bits = 3). Returns (qweight uint32 [N][K/8] or [N][3K/32], scales float16
+    [N][K/g], zeros float16 [N][K/g]).
     """
-    from .layout import pack_codes
+    from .layout import pack_codes, pack_codes3
 
     W = np.asarray(W, dtype=np.float16)
     n, k = W.shape
-    if bits != 4:
-        raise ValueError("layout v1 stores 4-bit codes")
+    if bits not in (3, 4):
+        raise ValueError("the packed layouts store 3-bit or 4-bit codes")
     if k % group != 0:
         raise ValueError("K must be a multiple of the group size")
+    if bits == 3 and k % 32 != 0:
+        raise ValueError("the 3-bit layout packs blocks of 32 inputs")
+    pack = pack_codes if bits == 4 else pack_codes3
     s64 = None if s is None else np.asarray(s, dtype=np.float32).astype(np.float64)
-    qweight = np.empty((n, k // 8), dtype=np.uint32)
+    qweight = np.empty((n, k // 8 if bits == 4 else 3 * (k // 32)), dtype=np.uint32)
     scales = np.empty((n, k // group), dtype=np.float16)
     zeros = np.empty((n, k // group), dtype=np.float16)
     for r0 in range(0, n, _ROW_BLOCK):
@@ -163,7 +167,7 @@ def quantize_pack(W, s=None, bits=4, group=128):
         if s64 is not None:
             w = w * s64[None, :]
         q, delta, z = quantize_groups(w, bits, group)
-        qweight[r0:r1] = pack_codes(q)
+        qweight[r0:r1] = pack(q)
         scales[r0:r1] = f64_to_f16(delta)
         zeros[r0:r1] = f64_to_f16(z)
     return qweight, scales, zeros

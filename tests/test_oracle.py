@@ -78,15 +78,16 @@ def test_f64_to_f16_matches_exact_rational_rne():
 
 
 # ---------------------------------------------------------------- P1: brute force nearest level
-@pytest.mark.parametrize("group", [4, 8, 16])
-def test_rtn_picks_nearest_level_brute_force(group):
+@pytest.mark.parametrize("bits,group", [(4, 4), (4, 8), (4, 16), (3, 4), (3, 8), (3, 16)])
+def test_rtn_picks_nearest_level_brute_force(bits, group):
     n, g = 24, 6
     w = RNG.standard_normal((n, g * group)) * 0.02
     w[0, :group] = np.linspace(-1, 1, group)          # hand-built group
     w[1, :group] = np.arange(group) * 0.125 - 0.25     # dyadic, exact halves possible
     w[2, :group] = 0.3                                  # constant
     w[3, :group] = np.abs(w[3, :group]) + 0.5          # one-signed
-    q, delta, z = oracle.quantize_groups(w, bits=4, group=group)
+    q, delta, z = oracle.quantize_groups(w, bits=bits, group=group)
+    levels = 2 ** bits
     for r in range(n):
         for gi in range(g):
             d = Fraction(float(delta[r, gi]))
@@ -94,9 +95,9 @@ def test_rtn_picks_nearest_level_brute_force(group):
             for c in range(group):
                 k = gi * group + c
                 x = Fraction(float(w[r, k]))
-                dist = [abs(x - (qq - zz) * d) for qq in range(16)]
+                dist = [abs(x - (qq - zz) * d) for qq in range(levels)]
                 best = min(dist)
-                winners = [qq for qq in range(16) if dist[qq] == best]
+                winners = [qq for qq in range(levels) if dist[qq] == best]
                 qo = int(q[r, k])
                 if qo in winners:
                     continue
@@ -143,8 +144,9 @@ def test_round_half_to_even_and_round_before_adding_zero():
 
 
 # ---------------------------------------------------------------- P2/P3: invariants
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 64), (4, 32), (3, 128), (3, 32)])
 @pytest.mark.parametrize("kind", ["normal", "ties", "constant", "positive", "negative", "subnormal", "wide", "mixed"])
-def test_error_within_half_step_and_code_range(kind):
+def test_error_within_half_step_and_code_range(kind, bits, group):
     import synth
 
     if kind == "normal":
@@ -152,12 +154,22 @@ def test_error_within_half_step_and_code_range(kind):
     else:
         W = synth.edge_weights(kind, 64, 1024, seed=3)
     w = W.astype(np.float64)
-    q, delta, z = oracle.quantize_groups(w, 4, 128)
-    assert q.min() >= 0 and q.max() <= 15
+    q, delta, z = oracle.quantize_groups(w, bits, group)
+    assert q.min() >= 0 and q.max() <= 2 ** bits - 1
     assert np.all(z == np.rint(z))
-    qw = oracle.pseudo_quantize(w, 4, 128)
-    d = np.repeat(delta, 128, axis=1)
+    qw = oracle.pseudo_quantize(w, bits, group)
+    d = np.repeat(delta, group, axis=1)
     assert np.all(np.abs(w - qw) <= d / 2 * (1 + 2.0 ** -40))
+    # the group's minimum maps to code 0 exactly (rint(-a) = -rint(a)); its maximum to the top
+    # code, or one below where -min/Delta sits at a rounding tie
+    wg = w.reshape(64, -1, group)
+    qg = q.reshape(64, -1, group)
+    spread = wg.max(axis=2) > wg.min(axis=2)
+    assert np.all(np.take_along_axis(qg, wg.argmin(axis=2)[:, :, None], 2)[:, :, 0][spread] == 0)
+    top = np.take_along_axis(qg, wg.argmax(axis=2)[:, :, None], 2)[:, :, 0][spread]
+    assert np.all(top >= 2 ** bits - 2)
+    if kind == "normal":
+        assert np.mean(top == 2 ** bits - 1) > 0.9
 
 
 def test_zero_offset_is_positive_zero():
@@ -181,15 +193,16 @@ def test_constant_group_reading():
 
 
 # ---------------------------------------------------------------- P4: the pages' error statistic
-def test_mean_round_error_is_a_quarter_step():
+@pytest.mark.parametrize("bits,group", [(4, 128), (3, 128), (4, 32)])
+def test_mean_round_error_is_a_quarter_step(bits, group):
     """L13 AWQ slides 26/28: the expected rounding error is about 0.25 (in steps)."""
     import synth
 
     W = synth.weights(9, 0, 1024, 1024)
     w = W.astype(np.float64)
-    _, delta, _ = oracle.quantize_groups(w, 4, 128)
-    err = np.abs(w - oracle.pseudo_quantize(w, 4, 128)) / np.repeat(delta, 128, axis=1)
-    assert abs(err.mean() - 0.25) < 0.005
+    _, delta, _ = oracle.quantize_groups(w, bits, group)
+    err = np.abs(w - oracle.pseudo_quantize(w, bits, group)) / np.repeat(delta, group, axis=1)
+    assert abs(err.mean() - 0.25) < 0.01
 
 
 def test_scaling_a_salient_channel_divides_its_error():
@@ -288,30 +301,31 @@ def test_eight_bit_case_matches_page_two_zero_point_quantizer():
 
 
 # ---------------------------------------------------------------- P8: linear exactness
-def _exact_linear(x, qw, sc, zr, k):
-    codes = oracle.unpack_codes(qw, k)
+def _exact_linear(x, qw, sc, zr, k, bits=4, group=128):
+    codes = oracle.unpack_codes(qw, k) if bits == 4 else oracle.unpack_codes3(qw, k)
     m, n = x.shape[0], qw.shape[0]
     out = np.empty((m, n), dtype=object)
     for i in range(m):
         for r in range(n):
             acc = Fraction(0)
             for c in range(k):
-                g = c // 128
+                g = c // group
                 wv = (codes[r, c] - Fraction(float(zr[r, g]))) * Fraction(float(sc[r, g]))
                 acc += Fraction(float(x[i, c])) * wv
             out[i, r] = acc
     return out
 
 
-def test_linear_matches_exact_rationals():
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 32), (3, 128), (3, 64)])
+def test_linear_matches_exact_rationals(bits, group):
     import synth
 
     k, n, m = 256, 5, 2
     W = synth.weights(1, 7, n, k)
     x = synth.activations(1, 7, m, k)
-    qw, sc, zr = oracle.quantize_pack(W)
-    y, b = oracle.linear(x, qw, sc, zr)
-    ex = _exact_linear(x, qw, sc, zr, k)
+    qw, sc, zr = oracle.quantize_pack(W, bits=bits, group=group)
+    y, b = oracle.linear(x, qw, sc, zr, group=group, bits=bits)
+    ex = _exact_linear(x, qw, sc, zr, k, bits, group)
     for i in range(m):
         for r in range(n):
             assert abs(Fraction(float(y[i, r])) - ex[i, r]) <= Fraction(k) * Fraction(2) ** -52 * Fraction(float(b[i, r]))
