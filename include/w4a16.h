@@ -38,6 +38,21 @@
  *   scales, zeros: fp16 [N][K/group], row-major; group g of row n covers
  *   k = g*group .. g*group+group-1. The dequantized weight is
  *   w_hat[n][k] = (q[n][k] - zeros[n][g]) * scales[n][g]. Zeros are integers.
+ *
+ * Packed 3-bit layout (codes 0..7; "MIT 6.5940 Lab 4 + Lab 5" guide, Lab 4
+ * setup: 3-bit weights with groups of 128; L13 AWQ section: INT3 g128):
+ *   qweight: uint32 [N][3K/32]. The 32 inputs k = 32b .. 32b+31 of row n own
+ *   words 3b, 3b+1, 3b+2. Word 3b+h (h = 0, 1) holds the low two bits of the
+ *   codes of inputs 32b+16h .. 32b+16h+15: bits 2i..2i+1 (i = 0..7) are
+ *   q[32b+16h+2i] & 3 and bits 16+2i..16+2i+1 are q[32b+16h+2i+1] & 3. Word
+ *   3b+2 holds the high bits: bit i (i = 0..15) is q[32b+2i] >> 2 and bit 16+i
+ *   is q[32b+2i+1] >> 2. So a pair of codes still ORs into an fp16 pair:
+ *   ((lo >> 2i) & 0x00030003) | (((hi >> j) & 0x00010001) << 2), j = 8h + i.
+ *   Codes 0..7, 0..7, 0..7, 0..7 pack to 0xDDDD8888, 0xDDDD8888, 0xCCCCCCCC.
+ *   scales and zeros as above.
+ *
+ * Group sizes: 128 (the default; QServe table), 64 and 32 (Lab 5's kernel uses
+ * groups of 32). Group 64 is this library's reading of the range between them.
  */
 #ifndef W4A16_H
 #define W4A16_H
@@ -52,7 +67,7 @@ typedef enum {
   W4A16_OK = 0,
   W4A16_ERR_NULL = 1,        /* a required pointer is NULL                                  */
   W4A16_ERR_SHAPE = 2,       /* a size <= 0, K % group != 0, or a size beyond the limits    */
-  W4A16_ERR_UNSUPPORTED = 3, /* bits != 4 or group != 128, or an unknown path               */
+  W4A16_ERR_UNSUPPORTED = 3, /* an unsupported bits/group, or an unknown or unfit path        */
   W4A16_ERR_ALIGN = 4,       /* a pointer misses its alignment (stated per call)            */
   W4A16_ERR_HIP = 5,         /* the HIP runtime reported an error at launch                 */
   W4A16_ERR_ARG = 6          /* another invalid scalar argument (e.g. alpha)                */
@@ -126,21 +141,25 @@ w4a16_status awq_rmsnorm_fold(const void* h, const void* gamma, const float* s, 
  * awq_quantize_pack - round-to-nearest group quantization and packing.
  * L13 guide, AWQ section: Q(w) = Delta * Round(w / Delta) on weights already
  * multiplied by s; CMU L19 zero-point quantizer (range max - min, integer zero,
- * clipped codes); QServe table: 4-bit weights, group 128; TinyChat packing.
+ * clipped codes); QServe table: 4-bit weights, group 128; Lab 4 setup: 3-bit,
+ * group 128; TinyChat packing.
  *
- * For every row n and group g (inputs k in [128g, 128g+128)), in float64:
+ * For every row n and group g (inputs k in [Gs g, Gs g + Gs), Gs = group), in
+ * float64, with Q = 2^bits - 1:
  *   w   = float64(W[n][k]) * float64(s[k])      (exact; s == NULL means s = 1)
  *   R   = max w - min w, replaced by 1 when 0
- *   D   = R / 15                                 (IEEE division)
+ *   D   = R / Q                                  (IEEE division)
  *   z   = rint(-min w / D)                        (round half even, not clamped)
- *   q   = clamp(rint(w / D) + z, 0, 15)
- *   scales[n][g] = f16_rne(D), zeros[n][g] = f16_rne(z), qweight = layout v1.
+ *   q   = clamp(rint(w / D) + z, 0, Q)
+ *   scales[n][g] = f16_rne(D), zeros[n][g] = f16_rne(z), qweight = layout v1
+ *   (bits 4) or the 3-bit layout (bits 3).
  * Results are bit-identical to that definition.
  *
  * w: fp16 [N][K] (nn.Linear weight: rows are outputs); s: float32 [K] or NULL;
- * bits must be 4 and group 128. Outputs: qweight uint32 [N][K/8], scales and
- * zeros fp16 [N][K/128]. Alignment: w and qweight 16 bytes, s 16 bytes,
- * scales and zeros 2 bytes. K % 128 == 0.
+ * bits 3 or 4; group 32, 64 or 128; K % group == 0. Outputs: qweight uint32
+ * [N][K/8] (bits 4) or [N][3K/32] (bits 3), scales and zeros fp16
+ * [N][K/group]. Alignment: w and qweight 16 bytes, s 16 bytes, scales and
+ * zeros 2 bytes.
  */
 w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t K, int32_t bits,
                                int32_t group, void* qweight, void* scales, void* zeros,
@@ -157,11 +176,14 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * accumulated in float32 (any summation order). Accuracy contract, with
  * B = sum_k |x[m][k] * w_hat[n][k]|: |y - exact| <= 1e-3 * B + 1e-5.
  * x: fp16 [M][K], the input after the 1/s fold; qweight/scales/zeros as written
- * by awq_quantize_pack; y: fp16 [M][N] (output). group must be 128.
- * Dispatch: M == 1 runs the wave-tile GEMV kernel, 2 <= M <= 32 the
+ * by awq_quantize_pack with bits 4; y: fp16 [M][N] (output). group 32, 64 or
+ * 128 (as quantized); K % 128 == 0.
+ * Dispatch, group 128: M == 1 runs the wave-tile GEMV kernel, 2 <= M <= 32 the
  * small-batch MFMA kernel (workgroups own whole rows of y, waves split K), and
- * larger M the tiled MFMA kernel. Alignment: x and qweight 16 bytes,
- * scales/zeros/y 2 bytes.
+ * larger M the tiled MFMA kernel. Groups of 32 and 64: M <= 8 (M <= 4 above
+ * K = 16384) runs the GEMV kernel's variant, larger M the tiled MFMA kernel's
+ * variant (one (scale, zero) per 32-input MFMA step). Alignment: x and qweight
+ * 16 bytes, scales/zeros/y 2 bytes.
  */
 w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
@@ -172,9 +194,30 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
  * 1 = GEMV kernel (needs M <= w4a16_gemv_max_m() and M * ceil(K / 16384) <= 8),
  * 2 = tiled MFMA kernel (any M), 3 = small-batch MFMA kernel (needs M <= 32).
  * A path that cannot take the shape returns W4A16_ERR_UNSUPPORTED before any
- * HIP call. Same contract otherwise.
+ * HIP call (path 3 takes groups of 128 only). Same contract otherwise.
  */
 w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
+                               const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,
+                               void* y, void* stream);
+
+/*
+ * w3a16_linear - the fused dequantize + matrix multiply for 3-bit codes in the
+ * packed 3-bit layout (awq_quantize_pack with bits 3). Lab 4 setup: 3-bit
+ * weights, groups of 128; L13 TinyChat kernel fusion. Same formula, accuracy
+ * contract, arguments and alignment as w4a16_linear; group 32, 64 or 128;
+ * K % 128 == 0. Dispatch: M <= 8 (M <= 4 above K = 16384) the GEMV kernel's
+ * 3-bit variant, larger M the tiled MFMA kernel's 3-bit variant.
+ */
+w4a16_status w3a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
+                          int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
+
+/*
+ * w3a16_linear_path - w3a16_linear with the kernel chosen by the caller: path
+ * 0 = automatic, 1 = GEMV variant (needs M <= 8, and M <= 4 above K = 16384,
+ * K <= 32768), 2 = tiled MFMA variant (any M). Other paths, or a shape the
+ * chosen kernel cannot take, return W4A16_ERR_UNSUPPORTED before any HIP call.
+ */
+w4a16_status w3a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,
                                void* y, void* stream);
 

@@ -20,7 +20,7 @@ def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
-    return sorted({n for n in names if n.startswith(("w4a16_", "awq_"))})
+    return sorted({n for n in names if n.startswith(("w4a16_", "w3a16_", "awq_"))})
 
 
 def test_header_declares_the_binding_set():
@@ -61,7 +61,7 @@ def _linear(**kw):
         (dict(x=None), w4.ERR_NULL),
         (dict(q=None), w4.ERR_NULL),
         (dict(y=None), w4.ERR_NULL),
-        (dict(group=64), w4.ERR_UNSUPPORTED),
+        (dict(group=16), w4.ERR_UNSUPPORTED),
         (dict(M=0), w4.ERR_SHAPE),
         (dict(N=-1), w4.ERR_SHAPE),
         (dict(K=200), w4.ERR_SHAPE),
@@ -93,8 +93,12 @@ def test_linear_path_rejects_unknown_path_and_big_m_on_gemv():
     "args,status",
     [
         ((None, None, 64, 256, 4, 128, A16, A16, A16), w4.ERR_NULL),
-        ((A16, None, 64, 256, 3, 128, A16, A16, A16), w4.ERR_UNSUPPORTED),
-        ((A16, None, 64, 256, 4, 64, A16, A16, A16), w4.ERR_UNSUPPORTED),
+        ((A16, None, 64, 256, 2, 128, A16, A16, A16), w4.ERR_UNSUPPORTED),
+        ((A16, None, 64, 256, 5, 128, A16, A16, A16), w4.ERR_UNSUPPORTED),
+        ((A16, None, 64, 256, 4, 16, A16, A16, A16), w4.ERR_UNSUPPORTED),
+        ((A16, None, 64, 256, 3, 256, A16, A16, A16), w4.ERR_UNSUPPORTED),
+        ((A16, None, 64, 96, 4, 64, A16, A16, A16), w4.ERR_SHAPE),
+        ((A16, None, 64, 48, 3, 32, A16, A16, A16), w4.ERR_SHAPE),
         ((A16, None, 64, 250, 4, 128, A16, A16, A16), w4.ERR_SHAPE),
         ((A16, None, 0, 256, 4, 128, A16, A16, A16), w4.ERR_SHAPE),
         ((A2, None, 64, 256, 4, 128, A16, A16, A16), w4.ERR_ALIGN),
@@ -160,6 +164,21 @@ def test_alpha_loss_workspace_and_rejects():
     assert call(y=A16 + 2) == w4.ERR_ALIGN
     assert call(ws=A16 + 4) == w4.ERR_ALIGN
     assert call(loss=A16 + 4) == w4.ERR_ALIGN
+
+
+def test_format_variants_reject():
+    lib = w4.load()
+    # groups other than 32/64/128; K not a multiple of 128; small-batch path with other formats
+    assert lib.w4a16_linear(A16, A16, A16, A16, 1, 64, 256, 16, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear(A16, A16, A16, A16, 1, 64, 96, 32, A16, None) == w4.ERR_SHAPE
+    assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 4, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w3a16_linear(A16, A16, A16, A16, 1, 64, 256, 256, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w3a16_linear(None, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_NULL
+    assert lib.w3a16_linear(A16, A16, A16, A16, 1, 64, 200, 128, A16, None) == w4.ERR_SHAPE
+    assert lib.w3a16_linear(A16 + 8, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_ALIGN
+    assert lib.w3a16_linear_path(3, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w3a16_linear_path(1, A16, A16, A16, A16, 9, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w3a16_linear_path(1, A16, A16, A16, A16, 8, 64, 32768 + 128, 128, A16, None) == w4.ERR_UNSUPPORTED
 
 
 def test_output_reference_rejects():

@@ -1,0 +1,150 @@
+"""GPU parity of the other code formats: 3-bit codes (packed 3-bit layout) and groups of
+32 and 64, against the float64 oracle.
+
+* quantize-pack: codes, scales and zeros bit-identical to the oracle's for bits 3/4 and
+  groups 32/64/128, on ragged and full-size layers and on the edge tensors;
+* the linear layer: every output within 1e-3 * sum_k |x * w_hat| + 1e-5 of the oracle, on
+  both kernels (the GEMV variant for M <= 8, the tiled MFMA variant for any M), fed the
+  oracle's packed weights.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+FORMATS = [(4, 64), (4, 32), (3, 128), (3, 64), (3, 32)]
+
+
+def _gpu():
+    from tests import _gpu
+
+    return _gpu
+
+
+def _qp_compare(lib, W, s, bits, group, tag):
+    g = _gpu()
+    print(f"quantize-pack {tag} bits={bits} group={group} N={W.shape[0]} K={W.shape[1]}", flush=True)
+    got = lib.quantize_pack(g.dev(W), None if s is None else g.dev(s), bits=bits, group=group)
+    want = oracle.quantize_pack(W, s, bits=bits, group=group)
+    gq = g.host_u32(got[0])
+    assert np.array_equal(gq, want[0]), g.report_mismatch("qweight", gq, want[0])
+    for name, a, b in (("scales", got[1], want[1]), ("zeros", got[2], want[2])):
+        ab = g.bits16(g.host(a))
+        bb = g.bits16(b)
+        assert np.array_equal(ab, bb), g.report_mismatch(name, ab, bb)
+
+
+@pytest.mark.parametrize("bits,group", FORMATS + [(4, 128)])
+@pytest.mark.parametrize("n,k", [(37, 384), (300, 2048), (64, 11008)])
+def test_quantize_pack_bit_exact(lib, bits, group, n, k):
+    W = synth.weights(2, 3, n, k)
+    s = oracle.channel_scale(synth.calibration(2, 3, k))
+    _qp_compare(lib, W, s, bits, group, "scaled")
+    _qp_compare(lib, W, None, bits, group, "plain")
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("kind", ["ties", "constant", "positive", "negative", "subnormal", "wide", "mixed"])
+def test_quantize_pack_edge_tensors(lib, bits, group, kind):
+    W = synth.edge_weights(kind, 40, 512, seed=5)
+    _qp_compare(lib, W, None, bits, group, kind)
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_quantize_pack_full_layer_sampled_rows(lib, bits, group):
+    # LLaMA-65B q projection, 8192 x 8192: packed on the device in full, 64 rows compared
+    g = _gpu()
+    W = synth.weights(3, 0, 8192, 8192)
+    s = oracle.channel_scale(synth.calibration(3, 0, 8192))
+    print(f"quantize-pack full bits={bits} group={group}", flush=True)
+    got = lib.quantize_pack(g.dev(W), g.dev(s), bits=bits, group=group)
+    rows = np.linspace(0, 8191, 64).astype(int)
+    want = oracle.quantize_pack(W[rows], s, bits=bits, group=group)
+    assert np.array_equal(g.host_u32(got[0])[rows], want[0])
+    assert np.array_equal(g.bits16(g.host(got[1])[rows]), g.bits16(want[1]))
+    assert np.array_equal(g.bits16(g.host(got[2])[rows]), g.bits16(want[2]))
+
+
+def _linear_check(lib, x, packed, bits, group, path, tag, rows=None):
+    g = _gpu()
+    m, k = x.shape
+    print(f"linear {tag} bits={bits} group={group} path={path} M={m} N={packed[0].shape[0]} K={k}", flush=True)
+    y = g.host(lib.linear(g.dev(x), *[g.dev(t) for t in packed], group=group, path=path, bits=bits))
+    y_ref, b = oracle.linear(x, *packed, group=group, rows=rows, bits=bits)
+    if rows is not None:
+        y = y[:, rows]
+    ok = oracle.within_tolerance(y.astype(np.float64), y_ref, b)
+    assert np.all(ok), (tag, np.argwhere(~ok)[:3])
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("m", [1, 2, 3, 5, 8])
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 384), (300, 2048), (97, 11008), (64, 22016), (40, 32768)])
+def test_gemv_variant(lib, bits, group, m, n, k):
+    if k > 16384 and m > 4:
+        pytest.skip("the GEMV variant takes M <= 4 above K = 16384")
+    x_cal = synth.calibration(2, 5, k)
+    s = oracle.channel_scale(x_cal)
+    packed = oracle.quantize_pack(synth.weights(2, 5, n, k), s, bits=bits, group=group)
+    x = oracle.scale_input(synth.activations(2, 5, m, k), s)
+    _linear_check(lib, x, packed, bits, group, 1, "gemv")
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("m", [1, 9, 17, 33, 100])
+@pytest.mark.parametrize("n,k", [(37, 384), (300, 2048), (130, 11008)])
+def test_mfma_variant(lib, bits, group, m, n, k):
+    x_cal = synth.calibration(4, 6, k)
+    s = oracle.channel_scale(x_cal)
+    packed = oracle.quantize_pack(synth.weights(4, 6, n, k), s, bits=bits, group=group)
+    x = oracle.scale_input(synth.activations(4, 6, m, k), s)
+    _linear_check(lib, x, packed, bits, group, 2, "mfma")
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("kind", ["positive", "negative", "mixed", "wide"])
+def test_variants_on_edge_weights(lib, bits, group, kind):
+    # one-signed groups quantized without the AWQ scale give zeros far outside the exact
+    # fp16 (q - z) range, mixed with ordinary groups: the tiled kernel's general route
+    W = synth.edge_weights(kind, 96, 1024, seed=7)
+    packed = oracle.quantize_pack(W, None, bits=bits, group=group)
+    x = synth.activations(1, 8, 40, 1024)
+    for path, m in ((1, 1), (1, 8), (2, 3), (2, 40)):
+        _linear_check(lib, x[:m], packed, bits, group, path, kind)
+
+
+@pytest.mark.parametrize("bits,group", [(3, 128), (4, 32)])
+@pytest.mark.parametrize("m", [1, 4, 64])
+def test_full_size_layers_sampled(lib, bits, group, m):
+    # LLaMA-65B projections: 8192 -> 8192 and 8192 -> 22016, 256 sampled output rows
+    g = _gpu()
+    for lid, (name, k, n) in enumerate(synth.CONFIGS[3]["layers"][3:5]):
+        x_cal = synth.calibration(3, lid, k)
+        s = oracle.channel_scale(x_cal)
+        W = synth.weights(3, lid, n, k)
+        packed = tuple(g.host(t) for t in lib.quantize_pack(g.dev(W), g.dev(s), bits=bits, group=group))
+        packed = (packed[0].view(np.uint32), packed[1], packed[2])
+        x = oracle.scale_input(synth.activations(3, lid, m, k), s)
+        rows = np.linspace(0, n - 1, 256).astype(int)
+        _linear_check(lib, x, packed, bits, group, 0, f"full-{name}", rows=rows)
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+def test_auto_dispatch_and_determinism(lib, bits, group):
+    g = _gpu()
+    k, n = 4096, 512
+    s = oracle.channel_scale(synth.calibration(2, 9, k))
+    packed = oracle.quantize_pack(synth.weights(2, 9, n, k), s, bits=bits, group=group)
+    dev = [g.dev(t) for t in packed]
+    for m in (1, 8, 9, 128):
+        x = oracle.scale_input(synth.activations(2, 9, m, k), s)
+        xd = g.dev(x)
+        y1 = g.host(lib.linear(xd, *dev, group=group, bits=bits))
+        y2 = g.host(lib.linear(xd, *dev, group=group, bits=bits))
+        assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+        y_ref, b = oracle.linear(x, *packed, group=group, bits=bits)
+        assert np.all(oracle.within_tolerance(y1.astype(np.float64), y_ref, b))

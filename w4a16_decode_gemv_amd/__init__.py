@@ -53,6 +53,8 @@ def load():
         "w4a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w4a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_alpha_loss_workspace": ([i64, i64], i64),
+        "w3a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
+        "w3a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_output_reference": ([vp, vp, i64, i64, i64, vp, vp], i32),
         "awq_alpha_loss": ([vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
     }
@@ -67,7 +69,7 @@ def load():
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
-            "w4a16_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
+            "w4a16_linear_path", "w3a16_linear", "w3a16_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
             "awq_alpha_loss"]
 
 
@@ -166,7 +168,8 @@ def quantize_pack(W, s=None, bits=4, group=GROUP, out=None):
         sp = s.data_ptr()
     if out is None:
         g = max(k // group, 1)
-        qweight = torch.empty((n, max(k // 8, 1)), dtype=torch.int32, device=W.device)
+        words = k // 8 if bits == 4 else 3 * (k // 32)
+        qweight = torch.empty((n, max(words, 1)), dtype=torch.int32, device=W.device)
         scales = torch.empty((n, g), dtype=torch.float16, device=W.device)
         zeros = torch.empty((n, g), dtype=torch.float16, device=W.device)
     else:
@@ -176,8 +179,10 @@ def quantize_pack(W, s=None, bits=4, group=GROUP, out=None):
     return qweight, scales, zeros
 
 
-def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO):
-    """y = x @ dequant(qweight, scales, zeros)^T, fp16 [M][N] (float32 accumulation)."""
+def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO, bits=4):
+    """y = x @ dequant(qweight, scales, zeros)^T, fp16 [M][N] (float32 accumulation).
+
+    bits 4: qweight in layout v1 [N][K/8]; bits 3: the 3-bit layout [N][3K/32]."""
     torch = _torch()
     lib = load()
     x = _dev_tensor(x, torch.float16, "x", 2)
@@ -186,17 +191,19 @@ def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO):
     zeros = _dev_tensor(zeros, torch.float16, "zeros", 2)
     m, k = x.shape
     n = qweight.shape[0]
-    if qweight.shape[1] * 8 != k:
-        raise ValueError("qweight must be [N][K/8]")
+    if bits not in (3, 4):
+        raise ValueError("bits must be 3 or 4")
+    if (bits == 4 and qweight.shape[1] * 8 != k) or (bits == 3 and qweight.shape[1] * 32 != 3 * k):
+        raise ValueError("qweight must be [N][K/8] (4-bit) or [N][3K/32] (3-bit)")
     if scales.shape != zeros.shape or scales.shape[0] != n or scales.shape[1] * group != k:
         raise ValueError("scales/zeros must be [N][K/group]")
     y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
-    if path == PATH_AUTO:
-        status = lib.w4a16_linear(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k,
-                                  group, y.data_ptr(), _stream(x))
+    args = (x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k, group, y.data_ptr(),
+            _stream(x))
+    if bits == 4:
+        status = lib.w4a16_linear(*args) if path == PATH_AUTO else lib.w4a16_linear_path(path, *args)
     else:
-        status = lib.w4a16_linear_path(path, x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
-                                       m, n, k, group, y.data_ptr(), _stream(x))
+        status = lib.w3a16_linear(*args) if path == PATH_AUTO else lib.w3a16_linear_path(path, *args)
     _check(status)
     return y
 

@@ -40,7 +40,8 @@ w4a16_status hip_result(hipError_t e, const char* what) {
 w4a16_status check_linear(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
                           int64_t N, int64_t K, int32_t group, const void* y) {
   if (!x || !qweight || !scales || !zeros || !y) return fail(W4A16_ERR_NULL, "x, qweight, scales, zeros and y are required");
-  if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "group must be 128 (got %d)", (int)group);
+  if (group != 128 && group != 64 && group != 32)
+    return fail(W4A16_ERR_UNSUPPORTED, "group must be 32, 64 or 128 (got %d)", (int)group);
   if (M <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "M, N, K must be positive (got %lld, %lld, %lld)",
                                               (long long)M, (long long)N, (long long)K);
   if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
@@ -52,13 +53,30 @@ w4a16_status check_linear(const void* x, const void* qweight, const void* scales
   return W4A16_OK;
 }
 
-w4a16_status run_linear(int32_t path, const void* x, const void* qweight, const void* scales, const void* zeros,
-                        int64_t M, int64_t N, int64_t K, void* y, hipStream_t stream) {
+// bits 4 with group 128 runs the tuned kernels; every other format the variant kernels
+w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* qweight, const void* scales,
+                        const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
+                        hipStream_t stream) {
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   const uint32_t* qw = static_cast<const uint32_t*>(qweight);
   const uint16_t* sc = static_cast<const uint16_t*>(scales);
   const uint16_t* zr = static_cast<const uint16_t*>(zeros);
   uint16_t* yh = static_cast<uint16_t*>(y);
+  if (bits != 4 || group != 128) {
+    const bool gemv_ok = w4a16::gemv_variant_supports(M, K, group);
+    int32_t kernel = path;
+    if (path == 0) {
+      kernel = gemv_ok ? 1 : 2;
+    } else if (path == 1 && !gemv_ok) {
+      return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel for this format takes M <= %d and K <= 32768 "
+                  "(M <= 4 above K = 16384); got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
+    } else if (path == 3) {
+      return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes 4-bit codes with groups of 128 only");
+    }
+    if (kernel == 1)
+      return hip_result(w4a16::launch_gemv_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
+    return hip_result(w4a16::launch_mfma_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
+  }
   int32_t kernel = path;
   if (path == 0) {
     if (M <= kAutoGemvMaxM && w4a16::gemv_supports(M, K))
@@ -145,16 +163,17 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
                                void* qweight, void* scales, void* zeros, void* stream) {
   clear_error();
   if (!w || !qweight || !scales || !zeros) return fail(W4A16_ERR_NULL, "w, qweight, scales and zeros are required");
-  if (bits != 4 || group != 128)
-    return fail(W4A16_ERR_UNSUPPORTED, "only bits=4, group=128 is supported (got bits=%d, group=%d)", (int)bits,
-                (int)group);
+  if ((bits != 4 && bits != 3) || (group != 128 && group != 64 && group != 32))
+    return fail(W4A16_ERR_UNSUPPORTED, "bits must be 3 or 4 and group 32, 64 or 128 (got bits=%d, group=%d)",
+                (int)bits, (int)group);
   if (N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "N and K must be positive");
-  if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
+  if (K % group != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of the group (got K=%lld, group=%d)",
+                                  (long long)K, (int)group);
   if (K > W4A16_MAX_K || N > kMaxN) return fail(W4A16_ERR_SHAPE, "size beyond the limits (N <= 2^24, K <= %d)", W4A16_MAX_K);
   if (!aligned(w, 16) || !aligned(qweight, 16) || (s && !aligned(s, 16)))
     return fail(W4A16_ERR_ALIGN, "w, qweight and s must be 16-byte aligned");
   if (!aligned(scales, 2) || !aligned(zeros, 2)) return fail(W4A16_ERR_ALIGN, "scales and zeros must be 2-byte aligned");
-  return hip_result(w4a16::launch_quantize_pack(static_cast<const uint16_t*>(w), s, N, K,
+  return hip_result(w4a16::launch_quantize_pack(static_cast<const uint16_t*>(w), s, N, K, bits, group,
                                                 static_cast<uint32_t*>(qweight), static_cast<uint16_t*>(scales),
                                                 static_cast<uint16_t*>(zeros), static_cast<hipStream_t>(stream)),
                     "quantize-pack launch");
@@ -165,7 +184,7 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
   clear_error();
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
-  return run_linear(0, x, qweight, scales, zeros, M, N, K, y, static_cast<hipStream_t>(stream));
+  return run_linear(4, 0, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
 }
 
 w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
@@ -176,7 +195,25 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
     return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA) or 3 (small-batch MFMA)");
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
-  return run_linear(path, x, qweight, scales, zeros, M, N, K, y, static_cast<hipStream_t>(stream));
+  return run_linear(4, path, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
+}
+
+w4a16_status w3a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
+                          int64_t N, int64_t K, int32_t group, void* y, void* stream) {
+  clear_error();
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  return run_linear(3, 0, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
+}
+
+w4a16_status w3a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
+                               const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
+                               void* stream) {
+  clear_error();
+  if (path < 0 || path > 2) return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV) or 2 (tiled MFMA)");
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  return run_linear(3, path, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
 }
 
 int64_t awq_alpha_loss_workspace(int64_t T, int64_t N) {

@@ -149,24 +149,30 @@ hipError_t launch_scale_input(const uint16_t* x, const float* s, int64_t M, int6
 }
 
 // ---------------------------------------------------------------------------
-// Quantize-pack. One 16-lane DPP row owns one group (128 inputs of one output
-// row): lane j loads the 8 fp16 weights k = 128g + 8j .. +7 (16 bytes, so a
-// wave reads 1 KB contiguous per load), multiplies by s in float64 (exact),
-// takes part in the row's min/max reduction, then writes exactly one packed
-// word (its 8 codes) - layout v1 puts the codes of 8 consecutive inputs in one
-// word. Lane 0 of the row writes the group's fp16 scale and zero.
+// Quantize-pack. A group of GROUP inputs of one output row belongs to GROUP / 8
+// consecutive lanes: lane j of the group loads the 8 fp16 weights
+// k = GROUP g + 8j .. +7 (16 bytes, so a wave reads 1 KB contiguous per load),
+// multiplies by s in float64 (exact), takes part in the group's min/max
+// reduction, and computes its 8 codes. 4-bit codes: the lane writes exactly one
+// layout-v1 word (the codes of 8 consecutive inputs). 3-bit codes: the four
+// lanes of a 32-input block OR their bits into the block's three bit-plane words
+// (two low-bit words, one high-bit word) and three of them write one word each.
+// Lane 0 of the group writes the fp16 scale and zero.
+template <int BITS, int GROUP>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(const uint4* __restrict__ w, const float4* __restrict__ s,
                                                             int64_t n_groups, int G, uint32_t* __restrict__ qweight,
                                                             uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
-  const int64_t gid_raw = (int64_t)blockIdx.x * (blockDim.x >> 4) + (threadIdx.x >> 4);
-  const int j = threadIdx.x & 15;
-  const bool valid = gid_raw < n_groups;  // uniform over the 16 lanes of a row
+  constexpr int LPG = GROUP / 8;  // lanes per group
+  constexpr double kQmax = (double)((1 << BITS) - 1);
+  const int64_t gid_raw = (int64_t)blockIdx.x * (blockDim.x / LPG) + (threadIdx.x / LPG);
+  const int j = threadIdx.x % LPG;
+  const bool valid = gid_raw < n_groups;  // uniform over the lanes of a group
   const int64_t gid = valid ? gid_raw : 0;
   const int64_t n = gid / G;
   const int g = (int)(gid - n * G);
-  const int64_t word_idx = n * ((int64_t)G * 16) + 16 * g + j;  // also the uint4 index of the lane's weights
+  const int64_t chunk = n * ((int64_t)G * LPG) + (int64_t)LPG * g + j;  // the lane's 16-byte weight chunk
 
-  const uint4 wv = w[word_idx];
+  const uint4 wv = w[chunk];
   const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
   double v[8];
 #pragma unroll
@@ -175,8 +181,9 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const uint4* __restr
     v[2 * i + 1] = (double)half_bits_to_float((uint16_t)(wu[i] >> 16));
   }
   if (s != nullptr) {
-    const float4 s0 = s[32 * g + 2 * j];
-    const float4 s1 = s[32 * g + 2 * j + 1];
+    const int64_t kc = (int64_t)GROUP * g + 8 * j;  // first input of the chunk
+    const float4 s0 = s[kc / 4];
+    const float4 s1 = s[kc / 4 + 1];
     const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = v[i] * (double)sv[i];  // exact: 11 x 24 significant bits
@@ -188,41 +195,81 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const uint4* __restr
     mx = fmax(mx, v[i]);
   }
 #pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    mn = fmin(mn, __shfl_xor(mn, off, 16));
-    mx = fmax(mx, __shfl_xor(mx, off, 16));
+  for (int off = 1; off < LPG; off <<= 1) {
+    mn = fmin(mn, __shfl_xor(mn, off, LPG));
+    mx = fmax(mx, __shfl_xor(mx, off, LPG));
   }
   double range = mx - mn;
   if (range == 0.0) range = 1.0;
-  const double delta = range / 15.0;
+  const double delta = range / kQmax;
   const double z = rint(-mn / delta) + 0.0;  // + 0.0 makes a zero offset +0
-  uint32_t word = 0;
+  uint32_t c[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     double q = rint(v[i] / delta) + z;
-    q = fmin(fmax(q, 0.0), 15.0);
-    const uint32_t c = (uint32_t)q;
-    word |= c << ((i & 1) ? (16 + 4 * (i >> 1)) : (4 * (i >> 1)));
+    q = fmin(fmax(q, 0.0), kQmax);
+    c[i] = (uint32_t)q;
   }
-  if (valid) {
-    qweight[word_idx] = word;
-    if (j == 0) {
-      scales[gid] = f64_to_f16_rne(delta);
-      zeros[gid] = f64_to_f16_rne(z);
+  if constexpr (BITS == 4) {
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) word |= c[i] << ((i & 1) ? (16 + 4 * (i >> 1)) : (4 * (i >> 1)));
+    if (valid) qweight[chunk] = word;
+  } else {
+    // position of this lane's 8 inputs in its 32-input block: quarter jb = j & 3
+    const int jb = j & 3;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int pl = 4 * (jb & 1) + (i >> 1);  // pair index within the 16-input half
+      const int ph = 4 * jb + (i >> 1);        // pair index within the block
+      lo |= (c[i] & 3u) << ((i & 1) ? (16 + 2 * pl) : (2 * pl));
+      hi |= (c[i] >> 2) << ((i & 1) ? (16 + ph) : ph);
     }
+    lo |= __shfl_xor(lo, 1, LPG);  // quarters 0|1 and 2|3 share a low-bit word
+    hi |= __shfl_xor(hi, 1, LPG);
+    hi |= __shfl_xor(hi, 2, LPG);
+    // block index within the row, and its three words
+    const int64_t block = (int64_t)(GROUP / 32) * g + (j >> 2);
+    const int64_t base = n * ((int64_t)G * (GROUP / 32) * 3) + 3 * block;
+    if (valid) {
+      if (jb == 0) qweight[base] = lo;      // quarters 0, 1
+      if (jb == 2) qweight[base + 1] = lo;  // quarters 2, 3
+      if (jb == 1) qweight[base + 2] = hi;
+    }
+  }
+  if (valid && j == 0) {
+    scales[gid] = f64_to_f16_rne(delta);
+    zeros[gid] = f64_to_f16_rne(z);
   }
 }
 
-hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, uint32_t* qweight,
-                                uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
-  const int G = (int)(K / 128);
+template <int BITS, int GROUP>
+hipError_t launch_qp(const uint16_t* w, const float* s, int64_t N, int64_t K, uint32_t* qweight, uint16_t* scales,
+                     uint16_t* zeros, hipStream_t stream) {
+  const int G = (int)(K / GROUP);
   const int64_t n_groups = N * G;
-  const int block = 256;  // 16 groups per block
-  const int64_t grid = (n_groups + 15) / 16;
-  hipLaunchKernelGGL(quantize_pack_kernel, dim3((unsigned)grid), dim3(block), 0, stream,
+  const int block = 256;
+  const int per_block = block / (GROUP / 8);
+  const int64_t grid = (n_groups + per_block - 1) / per_block;
+  hipLaunchKernelGGL((quantize_pack_kernel<BITS, GROUP>), dim3((unsigned)grid), dim3(block), 0, stream,
                      reinterpret_cast<const uint4*>(w), reinterpret_cast<const float4*>(s), n_groups, G, qweight,
                      scales, zeros);
   return hipGetLastError();
+}
+
+hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, int bits, int group,
+                                uint32_t* qweight, uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+  if (bits == 4) {
+    if (group == 128) return launch_qp<4, 128>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 64) return launch_qp<4, 64>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 32) return launch_qp<4, 32>(w, s, N, K, qweight, scales, zeros, stream);
+  } else if (bits == 3) {
+    if (group == 128) return launch_qp<3, 128>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 64) return launch_qp<3, 64>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 32) return launch_qp<3, 32>(w, s, N, K, qweight, scales, zeros, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w4a16

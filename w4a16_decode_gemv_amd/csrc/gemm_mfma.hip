@@ -208,6 +208,199 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
   }
 }
 
+// ---------------------------------------------------------------------------
+// Variants: 3-bit codes and groups of 32 or 64 (and 3-bit with groups of 128).
+// A stage is still 128 inputs, but MFMA step st covers exactly the 32 inputs
+// 32 st .. 32 st + 31 (lane (j, c) takes inputs 32 st + 8 j .. + 7), so every
+// step lies inside one group and gets its own (scale, zero): acc += d_st * step.
+// The LDS code rows are laid out so that a lane reads the words of its four
+// steps with one 16-byte read: 4-bit, position 4 j + st holds word 4 st + j (the
+// lane's 8 inputs of step st); 3-bit, positions 0..3 / 4..7 / 8..11 hold the
+// low-bit word of inputs 0..15, of inputs 16..31, and the high-bit word, of
+// pieces 0..3.
+
+template <int MB, int BITS>
+struct VarSmem {
+  uint4 a[2][16 * MB][17];
+  uint32_t b[2][BN][20];
+  uint32_t sz[2][BN][4];  // (scale | zero << 16) per row and step
+};
+
+// exact fp16 pairs (q - z) of lane j's 8 inputs of a 3-bit piece
+__device__ __forceinline__ half8_t dequant3(uint32_t lo, uint32_t hi, int j, half2_t c) {
+  const int i0 = 4 * (j & 1), p0 = 4 * j;
+  uint32_t v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    // bits p and 16 + p of hi (p = p0 + e) rotated to bits 2 and 18
+    const uint32_t hp = __builtin_amdgcn_alignbit(hi, hi, (uint32_t)(p0 + e + 30) & 31u);
+    const uint32_t t = and_or(hp, 0x00040004u, 0x64006400u);
+    v[e] = __builtin_bit_cast(uint32_t, as_half2(and_or(lo >> (2 * (i0 + e)), 0x00030003u, t)) + c);
+  }
+  return as_half8(v[0], v[1], v[2], v[3]);
+}
+
+template <int MB, int BITS>
+__global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restrict__ x, const uint32_t* __restrict__ qw,
+                                                            const uint16_t* __restrict__ scales,
+                                                            const uint16_t* __restrict__ zeros, int M, int N, int K,
+                                                            int gsh, uint16_t* __restrict__ y) {
+  constexpr int BM = 16 * MB;
+  constexpr int AU = (BM * 16 + kThreads - 1) / kThreads;
+  constexpr int WPS = BITS == 4 ? 16 : 12;  // code words per row per stage
+  __shared__ VarSmem<MB, BITS> sm;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int j = lane >> 4, c = lane & 15;
+  const int m0 = blockIdx.y * BM;
+  const int n0 = blockIdx.x * BN;
+  const int S = K >> 7;            // stages
+  const int G = K >> (5 + gsh);    // groups per row
+  const int KX = K >> 3;
+  const int64_t row_words = (int64_t)(K >> 7) * WPS;
+
+  // codes staging: 4-bit, thread t < 256 copies words 4q..4q+3 of row t / 4; 3-bit, thread t < 192
+  // copies words 4q..4q+3 (q = t % 3) of row t / 3
+  const int b_row = BITS == 4 ? (t >> 2) : (t / 3);
+  const int b_q = BITS == 4 ? (t & 3) : (t % 3);
+  const bool b_act = BITS == 4 || t < 192;
+  const int64_t b_src = (int64_t)min(n0 + b_row, N - 1) * row_words + 4 * b_q;
+  // (scale, zero) staging: thread t -> row t / 4, step t % 4
+  const int s_row = min(n0 + (t >> 2), N - 1), s_st = t & 3;
+
+  uint4 areg[AU];
+  uint4 breg = {0u, 0u, 0u, 0u};
+  uint16_t sreg, zreg;
+  auto load_stage = [&](int g) {
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      const int i = t + u * kThreads;
+      const int r = i >> 4, ch = i & 15;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (i < BM * 16 && m0 + r < M) v = x[(int64_t)(m0 + r) * KX + g * 16 + ch];
+      areg[u] = v;
+    }
+    if (b_act) breg = *reinterpret_cast<const uint4*>(qw + b_src + (int64_t)g * WPS);
+    const int64_t off = (int64_t)s_row * G + (((g << 2) + s_st) >> gsh);
+    sreg = scales[off];
+    zreg = zeros[off];
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < AU; ++u) {
+      const int i = t + u * kThreads;
+      if (i < BM * 16) sm.a[buf][i >> 4][i & 15] = areg[u];
+    }
+    if (b_act) {
+      const uint32_t wv[4] = {breg.x, breg.y, breg.z, breg.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int w = 4 * b_q + e;  // word of the stage
+        const int pos = BITS == 4 ? (4 * (w & 3) + (w >> 2))    // word 4 st + j -> 4 j + st
+                                  : (4 * (w % 3) + w / 3);      // piece w / 3, kind w % 3 -> 4 kind + piece
+        sm.b[buf][b_row][pos] = wv[e];
+      }
+    }
+    sm.sz[buf][t >> 2][s_st] = (uint32_t)sreg | ((uint32_t)zreg << 16);
+  };
+
+  float4_t acc[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) acc[mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  load_stage(0);
+  store_stage(0);
+  __syncthreads();
+
+  const int n_loc = wave * 16 + c;
+  const half8_t ones = as_half8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
+  for (int g = 0; g < S; ++g) {
+    const int buf = g & 1;
+    if (g + 1 < S) load_stage(g + 1);
+
+    const uint4 szq = *reinterpret_cast<const uint4*>(&sm.sz[buf][n_loc][0]);
+    const uint32_t szs[4] = {szq.x, szq.y, szq.z, szq.w};
+    float d[4], zf[4];
+    _Float16 zh[4];
+    bool ok = true;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      d[st] = half_bits_to_float((uint16_t)(szs[st] & 0xFFFFu));
+      zh[st] = __builtin_bit_cast(_Float16, (uint16_t)(szs[st] >> 16));
+      zf[st] = (float)zh[st];
+      ok = ok && zf[st] >= -2032.0f && zf[st] <= 1024.0f;
+    }
+    const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
+    // B fragments of the four steps: exact (q - z) on the fast route, exact q otherwise
+    half8_t bfrag[4];
+    if constexpr (BITS == 4) {
+      const uint4 wq = *reinterpret_cast<const uint4*>(&sm.b[buf][n_loc][4 * j]);
+      const uint32_t words[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const _Float16 zz = fast ? zh[st] : (_Float16)0.0f;
+        const _Float16 clo = -((_Float16)1024.0f + zz), chi = -((_Float16)64.0f + zz);
+        bfrag[st] = dequant_word(words[st], (half2_t){clo, clo}, (half2_t){chi, chi});
+      }
+    } else {
+      const uint4 lo = *reinterpret_cast<const uint4*>(&sm.b[buf][n_loc][4 * (j >> 1)]);
+      const uint4 hi = *reinterpret_cast<const uint4*>(&sm.b[buf][n_loc][8]);
+      const uint32_t los[4] = {lo.x, lo.y, lo.z, lo.w}, his[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const _Float16 zz = fast ? zh[st] : (_Float16)0.0f;
+        const _Float16 cc = -((_Float16)1024.0f + zz);
+        bfrag[st] = dequant3(los[st], his[st], j, (half2_t){cc, cc});
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const uint4 av = sm.a[buf][16 * mb + c][4 * st + j];
+        const half8_t a = as_half8(av.x, av.y, av.z, av.w);
+        const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+        const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bfrag[st], zero4, 0, 0, 0);
+        if (fast) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][i] = __builtin_fmaf(d[st], p[i], acc[mb][i]);
+        } else {
+          const float4_t sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, zero4, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mb][i] = __builtin_fmaf(d[st], __builtin_fmaf(-zf[st], sx[i], p[i]), acc[mb][i]);
+        }
+      }
+    }
+
+    if (g + 1 < S) {
+      __syncthreads();
+      store_stage(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  const int n = n0 + n_loc;
+  if (n < N) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * mb + 4 * j + i;
+        if (m < M) y[(int64_t)m * N + n] = float_to_half_bits(acc[mb][i]);
+      }
+  }
+}
+
+template <int MB, int BITS>
+hipError_t launch_var(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                      int64_t M, int64_t N, int64_t K, int gsh, uint16_t* y, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
+  hipLaunchKernelGGL((mfma_var_kernel<MB, BITS>), grid, dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(x),
+                     qweight, scales, zeros, (int)M, (int)N, (int)K, gsh, y);
+  return hipGetLastError();
+}
+
 template <int MB>
 hipError_t launch_mb(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                      int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
@@ -224,6 +417,20 @@ hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_
   if (M <= 16) return launch_mb<1>(x, qweight, scales, zeros, M, N, K, y, stream);
   if (M <= 32) return launch_mb<2>(x, qweight, scales, zeros, M, N, K, y, stream);
   return launch_mb<4>(x, qweight, scales, zeros, M, N, K, y, stream);
+}
+
+hipError_t launch_mfma_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                               const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                               hipStream_t stream) {
+  const int gsh = group == 32 ? 0 : group == 64 ? 1 : 2;
+  if (bits == 4) {
+    if (M <= 16) return launch_var<1, 4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+    if (M <= 32) return launch_var<2, 4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+    return launch_var<4, 4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+  }
+  if (M <= 16) return launch_var<1, 3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+  if (M <= 32) return launch_var<2, 3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+  return launch_var<4, 3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
 }
 
 }  // namespace w4a16

@@ -213,6 +213,191 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restri
   }
 }
 
+// ---------------------------------------------------------------------------
+// Variants: 3-bit codes, and groups of 32 or 64 (the same work split; the batch
+// size M is a runtime value up to the template's MT, rows past M are loaded as
+// copies of row M - 1 and never stored; the group size is a runtime shift).
+//
+// 3-bit pieces are the 12 bytes of one 32-input block of the bit-plane layout:
+// low-bit words lo0 (inputs 0..15), lo1 (16..31) and the high-bit word hi. The
+// pair of inputs (2j, 2j+1) is rebuilt as the fp16 pair 1024 + q by OR-ing
+// ((lo >> 2i) & 0x00030003) and the high bits moved to bits 2 and 18 into 0x6400.
+
+template <int BITS>
+struct Piece;
+template <>
+struct Piece<4> {
+  u32x4_t w;
+};
+template <>
+struct Piece<3> {
+  uint32_t lo0, lo1, hi;
+};
+
+__device__ __forceinline__ Piece<4> load_piece(const uint32_t* qw, int64_t row, int P, int p, Piece<4>*) {
+  Piece<4> r;
+  r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(qw) + row * P + p);
+  return r;
+}
+
+__device__ __forceinline__ Piece<3> load_piece(const uint32_t* qw, int64_t row, int P, int p, Piece<3>*) {
+  const uint32_t* b = qw + (row * P + p) * 3;
+  Piece<3> r;
+  r.lo0 = __builtin_nontemporal_load(b);
+  r.lo1 = __builtin_nontemporal_load(b + 1);
+  r.hi = __builtin_nontemporal_load(b + 2);
+  return r;
+}
+
+// the 16 exact fp16 code pairs of a piece, pair j = inputs (2j, 2j+1)
+__device__ __forceinline__ void piece_pairs(const Piece<4>& pc, half2_t (&q)[16]) {
+  const uint32_t wd[4] = {pc.w.x, pc.w.y, pc.w.z, pc.w.w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    const uint32_t w8 = wd[wi] >> 8;
+    q[4 * wi + 0] = q_pair_lo(wd[wi]);
+    q[4 * wi + 1] = q_pair_hi(wd[wi]);
+    q[4 * wi + 2] = q_pair_lo(w8);
+    q[4 * wi + 3] = q_pair_hi(w8);
+  }
+}
+
+__device__ __forceinline__ void piece_pairs(const Piece<3>& pc, half2_t (&q)[16]) {
+  const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t lo = (j < 8) ? pc.lo0 : pc.lo1;
+    // bits j and 16 + j of hi moved to bits 2 and 18
+    const uint32_t hj = j >= 2 ? (pc.hi >> (j - 2)) : (pc.hi << (2 - j));
+    const uint32_t t = and_or(hj, 0x00040004u, 0x64006400u);
+    q[j] = as_half2(and_or(lo >> (2 * (j & 7)), 0x00030003u, t)) + m1024;
+  }
+}
+
+template <int MT, int PPT, int BITS>
+__global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __restrict__ x, const uint32_t* __restrict__ qw,
+                                                               const uint16_t* __restrict__ scales,
+                                                               const uint16_t* __restrict__ zeros, int M, int N, int K,
+                                                               int gsh, uint16_t* __restrict__ y) {
+  constexpr int R = Tile<MT, PPT>::R;
+  constexpr int V = Tile<MT, PPT>::V;
+  constexpr int E = R * PPT * 64;        // staged (scale, zero) pairs per wave, enough for groups of 32
+  constexpr int NE = E / 64;
+  extern __shared__ uint32_t lds[];
+
+  const int T = blockDim.x;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int G = K >> (5 + gsh);  // groups per row
+  const int P = K >> 5;          // 32-input pieces per row
+  const int KX = K >> 3;
+  const int row0 = blockIdx.x * R;
+  const int rows = min(R, N - row0);
+  uint32_t* wsz = lds + wave * (E + V);
+  float* wred = reinterpret_cast<float*>(wsz + E);
+
+  // (1) (scale, zero) pairs: slot pp of this wave covers 64 >> gsh groups from (64 wave + pp T) >> gsh
+  uint16_t sreg[NE], zreg[NE];
+#pragma unroll
+  for (int u = 0; u < NE; ++u) {
+    const int e = lane + 64 * u;
+    const int r = e / (64 * PPT), pp = (e >> 6) % PPT, gl = e & 63;
+    const int g = min(((64 * wave + pp * T) >> gsh) + gl, G - 1);
+    const int64_t off = (int64_t)min(row0 + r, N - 1) * G + g;
+    sreg[u] = scales[off];
+    zreg[u] = zeros[off];
+  }
+
+  // (2) x pieces (rows past M repeat row M - 1)
+  uint32_t xr[PPT][MT][16];
+#pragma unroll
+  for (int pp = 0; pp < PPT; ++pp) {
+    const int p = min(t + pp * T, P - 1);
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const int mr = min(m, M - 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = x[(int64_t)mr * KX + 4 * p + c];
+        xr[pp][m][4 * c + 0] = v.x;
+        xr[pp][m][4 * c + 1] = v.y;
+        xr[pp][m][4 * c + 2] = v.z;
+        xr[pp][m][4 * c + 3] = v.w;
+      }
+    }
+  }
+
+  // (3) code pieces of all rows of the tile
+  Piece<BITS> cw[R][PPT];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int64_t row = min(row0 + r, N - 1);
+#pragma unroll
+    for (int pp = 0; pp < PPT; ++pp)
+      cw[r][pp] = load_piece(qw, row, P, min(t + pp * T, P - 1), (Piece<BITS>*)nullptr);
+  }
+
+  // (4) stage this wave's pairs (read by this wave only)
+#pragma unroll
+  for (int u = 0; u < NE; ++u) wsz[lane + 64 * u] = (uint32_t)sreg[u] | ((uint32_t)zreg[u] << 16);
+
+  const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
+  float sx[PPT][MT];
+#pragma unroll
+  for (int pp = 0; pp < PPT; ++pp)
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      float a = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) a = __builtin_amdgcn_fdot2(as_half2(xr[pp][m][j]), ones, a, false);
+      sx[pp][m] = a;
+    }
+
+  // (5) per row: dequantize, multiply, wave sum
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    float acc[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int pp = 0; pp < PPT; ++pp) {
+      const int p_raw = t + pp * T;
+      const uint32_t szv = wsz[(r * PPT + pp) * 64 + (lane >> gsh)];
+      const float d = (p_raw < P) ? half_bits_to_float((uint16_t)(szv & 0xFFFFu)) : 0.f;
+      const float z = half_bits_to_float((uint16_t)(szv >> 16));
+      half2_t q[16];
+      piece_pairs(cw[r][pp], q);
+      float part[MT];
+#pragma unroll
+      for (int m = 0; m < MT; ++m) {
+        float a = 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a = __builtin_amdgcn_fdot2(q[j], as_half2(xr[pp][m][j]), a, false);
+        part[m] = a;
+      }
+#pragma unroll
+      for (int m = 0; m < MT; ++m) acc[m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < MT; ++m) {
+      const float sum = wave_sum_lane63(acc[m]);
+      if (lane == 63) wred[r * MT + m] = sum;
+    }
+  }
+
+  // (6) the waves' sums in a fixed order
+  __syncthreads();
+  const int nw = T >> 6;
+  for (int v = t; v < rows * MT; v += T) {
+    const int r = v / MT;
+    const int m = v - r * MT;
+    if (m >= M) continue;
+    float sum = 0.f;
+    for (int w = 0; w < nw; ++w) sum += reinterpret_cast<const float*>(lds + w * (E + V) + E)[v];
+    y[(int64_t)m * N + row0 + r] = float_to_half_bits(sum);
+  }
+}
+
 struct Launch {
   int ppt;
   int threads;
@@ -261,9 +446,60 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const uint16_t* 
   return hipErrorInvalidValue;
 }
 
+template <int MT, int PPT, int BITS>
+hipError_t launch_var(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                      int64_t M, int64_t N, int64_t K, int gsh, uint16_t* y, int threads, hipStream_t stream) {
+  constexpr int R = Tile<MT, PPT>::R;
+  constexpr int V = Tile<MT, PPT>::V;
+  constexpr int E = R * PPT * 64;
+  const size_t lds = (size_t)(threads / 64) * (E + V) * 4;
+  const int grid = (int)((N + R - 1) / R);
+  hipLaunchKernelGGL((gemv_var_kernel<MT, PPT, BITS>), dim3(grid), dim3(threads), lds, stream,
+                     reinterpret_cast<const uint4*>(x), qweight, scales, zeros, (int)M, (int)N, (int)K, gsh, y);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_var_bits(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                           int64_t M, int64_t N, int64_t K, int gsh, uint16_t* y, hipStream_t stream) {
+  const Launch l = plan(K);
+  const int mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+  if (l.ppt == 1) {
+    switch (mt) {
+      case 1: return launch_var<1, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      case 2: return launch_var<2, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      case 4: return launch_var<4, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      default: return launch_var<8, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+    }
+  }
+  if (l.ppt == 2) {
+    switch (mt) {
+      case 1: return launch_var<1, 2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      case 2: return launch_var<2, 2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      case 4: return launch_var<4, 2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 int gemv_max_m() { return kMaxM; }
+
+bool gemv_variant_supports(int64_t M, int64_t K, int group) {
+  if (M < 1 || M > kMaxM || K <= 0 || K % group != 0) return false;
+  const int ppt = plan(K).ppt;
+  const int mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
+  return ppt == 1 || (ppt == 2 && mt <= 4);
+}
+
+hipError_t launch_gemv_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                               const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  const int gsh = group == 32 ? 0 : group == 64 ? 1 : 2;
+  if (bits == 4) return launch_var_bits<4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+  return launch_var_bits<3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+}
 
 bool gemv_supports(int64_t M, int64_t K) {
   if (M < 1 || M > kMaxM || K <= 0 || K % 128 != 0) return false;

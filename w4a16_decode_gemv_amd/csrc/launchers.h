@@ -17,8 +17,9 @@ hipError_t launch_scale_input(const uint16_t* x, const float* s, int64_t M, int6
 hipError_t launch_rmsnorm_fold(const uint16_t* h, const uint16_t* gamma, const float* s, int64_t M, int64_t K,
                                double eps, uint16_t* x_s, hipStream_t stream);
 
-hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, uint32_t* qweight,
-                                uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+// bits 3 or 4, group 32, 64 or 128 (validated by the caller)
+hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, int bits, int group,
+                                uint32_t* qweight, uint16_t* scales, uint16_t* zeros, hipStream_t stream);
 
 // GEMV kernel: needs M <= gemv_max_m() and gemv_supports(M, K).
 int gemv_max_m();
@@ -26,6 +27,13 @@ bool gemv_supports(int64_t M, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                        const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                        hipStream_t stream);
+
+// GEMV for the other code formats (bits 3 or 4, group 32, 64 or 128): needs
+// gemv_variant_supports(M, K, group).
+bool gemv_variant_supports(int64_t M, int64_t K, int group);
+hipError_t launch_gemv_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                               const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                               hipStream_t stream);
 
 // Small-batch MFMA kernel: needs M <= skinny_max_m().
 int skinny_max_m();
@@ -47,5 +55,10 @@ int64_t alpha_loss_partials(int64_t T, int64_t N);
 hipError_t launch_alpha_loss(const uint16_t* x_s, const uint32_t* qweight, const uint16_t* scales,
                              const uint16_t* zeros, const float* y_ref, int64_t T, int64_t N, int64_t K,
                              double* partials, double* loss, hipStream_t stream);
+
+// Tiled MFMA kernel for the other code formats (bits 3 or 4, group 32, 64 or 128); any M >= 1.
+hipError_t launch_mfma_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                               const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                               hipStream_t stream);
 
 }  // namespace w4a16
