@@ -33,10 +33,10 @@ ROTATE_BYTES = 1 << 29  # two Infinity Caches' worth of distinct buffers
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemv_m1_k8192_n8192.json")
 
 
-def algorithmic_bytes(m, n, k, group=128):
-    """Bytes the method must move once: 4-bit codes + fp16 scale and zero per
-    group + fp16 x in + fp16 y out."""
-    return n * k // 2 + 2 * 2 * n * (k // group) + 2 * m * k + 2 * m * n
+def algorithmic_bytes(m, n, k, group=128, bits=4):
+    """Bytes the method must move once: the packed codes (bits / 8 per weight) + fp16 scale
+    and zero per group + fp16 x in + fp16 y out."""
+    return n * k * bits // 8 + 2 * 2 * n * (k // group) + 2 * m * k + 2 * m * n
 
 
 def source_hash(*names):
@@ -60,6 +60,8 @@ def parse():
                    help="also time the batched-serving GEMMs (LLaMA2-7B shapes, M=128/256) against dense fp16")
     p.add_argument("--search", action="store_true",
                    help="also time the AWQ scale search (loss kernel and grid points) on the LLaMA2-7B block")
+    p.add_argument("--formats", action="store_true",
+                   help="also time the 3-bit and group-32/64 formats at K = N = 8192 (GEMV M=1, MFMA M=128)")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only-gemv", action="store_true", help="time the headline GEMV only (for profilers)")
@@ -73,7 +75,7 @@ def parse():
 class Layer:
     """One packed layer built on the GPU by the library, replicated `copies` times."""
 
-    def __init__(self, w4, torch, cfg, layer_id, n, k, m, copies):
+    def __init__(self, w4, torch, cfg, layer_id, n, k, m, copies, bits=4, group=128):
         import synth
 
         dev = "cuda:0"
@@ -84,7 +86,8 @@ class Layer:
         x = torch.from_numpy(L["x"]).to(dev)
         self.s = w4.channel_scale(xc, 0.5)
         self.x = w4.scale_input(x, self.s)
-        qw, sc, zr = w4.quantize_pack(W, self.s)
+        qw, sc, zr = w4.quantize_pack(W, self.s, bits=bits, group=group)
+        self.bits, self.group = bits, group
         self.W = W
         self.copies = [(self.x.clone(), qw.clone(), sc.clone(), zr.clone()) for _ in range(copies)]
         self.y = [torch.empty((m, n), dtype=torch.float16, device=dev) for _ in range(copies)]
@@ -93,7 +96,7 @@ class Layer:
 
     def call(self, w4, i, path=0):
         x, qw, sc, zr = self.copies[i % len(self.copies)]
-        w4.linear(x, qw, sc, zr, out=self.y[i % len(self.y)], path=path)
+        w4.linear(x, qw, sc, zr, out=self.y[i % len(self.y)], path=path, group=self.group, bits=self.bits)
 
 
 def copies_for(nbytes):
@@ -477,6 +480,19 @@ def main():
 
     if args.search:
         out["awq_search_llama2_7b"] = search_leg(w4, torch)
+
+    if args.formats:
+        rows = []
+        for bits, group in ((4, 128), (4, 64), (4, 32), (3, 128), (3, 64), (3, 32)):
+            for mm in (1, 4, 128):
+                b = algorithmic_bytes(mm, 8192, 8192, group, bits)
+                L = Layer(w4, torch, 3, 0, 8192, 8192, mm, copies_for(b), bits=bits, group=group)
+                t = time_graph(torch, lambda i: L.call(w4, i), 100)
+                rows.append({"bits": bits, "group": group, "M": mm, "us": t * 1e3, "bytes": b,
+                             "GB_s": b / (t * 1e-3) / 1e9, "TFLOP_s": 2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12})
+                del L
+                torch.cuda.empty_cache()
+        out["formats_k8192_n8192"] = rows
 
     if args.serving:
         import synth
