@@ -20,6 +20,10 @@ pages define, written step by step in the pages' order:
   folded into it (the operator that produces x_s in a decoder block).
 * ``alpha_loss`` / ``search_alpha`` - the AWQ output-error loss and its grid
   search over alpha.
+* ``quantize_groups_sym`` / ``quantize_pack_sym`` - symmetric absmax codes (the
+  same packed layouts, a fixed zero).
+* ``nf4_levels`` / ``quantize_nf4`` / ``dequantize_nf4`` / ``linear_nf4`` - the
+  NormalFloat-4 codebook and blockwise absmax NF4 quantization.
 
 It shares no code, header, table or constant with the HIP path. The only module
 both sides use is the seeded input generator ``synth``, which holds none of the
@@ -42,6 +46,17 @@ from .layout import pack_codes, unpack_codes, pack_codes3, unpack_codes3, LAYOUT
 from .linear import dequantize, linear, within_tolerance, TOL_REL, TOL_ABS
 from .norm import rms_factor, rmsnorm_fold
 from .search import GRID as ALPHA_GRID, alpha_loss, search_alpha
+from .sym import quantize_groups_sym, quantize_pack_sym
+from .nf4 import (
+    LEVELS as NF4_LEVELS,
+    LEVELS_F16 as NF4_LEVELS_F16,
+    nf4_levels,
+    nf4_codes,
+    quantize_nf4,
+    quantize_pack_nf4,
+    dequantize_nf4,
+    linear_nf4,
+)
 
 __all__ = [
     "channel_scale",
