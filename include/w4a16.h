@@ -278,6 +278,77 @@ w4a16_status awq_alpha_loss(const void* x_s, const void* qweight, const void* sc
                             const float* y_ref, int64_t T, int64_t N, int64_t K, int32_t group,
                             double* workspace, int64_t workspace_len, double* loss, void* stream);
 
+/*
+ * awq_quantize_pack_sym - symmetric absmax group quantization into the same
+ * packed layouts. "CMU 11-868 Model Quantization" guide, L19 "absmax and
+ * zero-point" (the absmax quantizer: scale from the largest magnitude, values
+ * mapped onto the symmetric integer range and rounded); L13 guide, AWQ section
+ * (Q(w) = Delta * Round(w / Delta), Delta from max |w|). For every row n and
+ * group g, in float64, with H = 2^(bits-1) - 1:
+ *   w     = float64(W[n][k]) * float64(s[k])     (exact; s == NULL means s = 1)
+ *   m     = max |w|, replaced by 1 when 0
+ *   D     = m / H                                 (IEEE division)
+ *   q     = clamp(rint(w / D), -H, H)
+ *   stored code q + 2^(bits-1); scales[n][g] = f16_rne(D); zeros[n][g] = 2^(bits-1).
+ * So w4a16_linear (bits 4) or w3a16_linear (bits 3) computes with these weights
+ * unchanged. Arguments, layouts, alignment and errors as awq_quantize_pack.
+ */
+w4a16_status awq_quantize_pack_sym(const void* w, const float* s, int64_t N, int64_t K, int32_t bits,
+                                   int32_t group, void* qweight, void* scales, void* zeros,
+                                   void* stream);
+
+/*
+ * nf4_codebook - the 16 NormalFloat-4 levels as fp16 bit patterns, ascending
+ * (host only; levels[7] is 0). "Quantization for LLMs" chapter 11, section 11.5:
+ * 8 positive levels at standard normal quantiles of OFFSET - i (OFFSET - 1/2) / 8
+ * (i = 0..7), 7 negative levels mirrored from OFFSET - i (OFFSET - 1/2) / 7
+ * (i = 0..6), and 0, all divided by the largest; OFFSET = 0.9677083. Each level
+ * is rounded once to fp16; these are the values the NF4 kernels multiply with.
+ * levels: host array of 16 (NULL is ignored).
+ */
+void nf4_codebook(uint16_t* levels);
+
+/*
+ * nf4_quantize_pack - blockwise absmax NF4 quantization (chapter 11, section
+ * 11.5: each block of 64 weights is divided by its largest magnitude and mapped
+ * to the nearest of the 16 levels; the block keeps a float32 absmax). For every
+ * row n and block b of `block` inputs:
+ *   w = float64(W[n][k]) * float64(s[k])   (s == NULL means s = 1)
+ *   a = f32_rne(max |w|)                    -> absmax[n][b]
+ *   code = the index of the fp16 level nearest to w / float64(a) (the count of
+ *          level midpoints at or below it, so an exact midpoint goes up); a
+ *          block with a = 0 takes the code of level 0.
+ * Codes are packed in layout v1. Bit-identical to that definition.
+ * w: fp16 [N][K]; s: float32 [K] or NULL; block 32, 64 or 128 (64 on the page);
+ * K % block == 0. Outputs: qweight uint32 [N][K/8], absmax float32 [N][K/block].
+ * Alignment: w, qweight and s 16 bytes, absmax 4 bytes.
+ * Errors: W4A16_ERR_NULL, W4A16_ERR_UNSUPPORTED (block), W4A16_ERR_SHAPE,
+ * W4A16_ERR_ALIGN, W4A16_ERR_HIP; checked before any HIP call.
+ */
+w4a16_status nf4_quantize_pack(const void* w, const float* s, int64_t N, int64_t K, int32_t block,
+                               void* qweight, float* absmax, void* stream);
+
+/*
+ * nf4_linear - the fused dequantize + matrix multiply for NF4 weights (chapter
+ * 11, section 11.5: the NF4 weights are dequantized just before the multiply;
+ * L13 TinyChat kernel fusion: in registers, never written back):
+ *
+ *   y[m][n] = f16_rne( sum_k x[m][k] * level[q[n][k]] * absmax[n][b] )
+ *
+ * with the fp16 codebook of nf4_codebook, float32 accumulation, and the
+ * accuracy contract of w4a16_linear (B = sum_k |x * w_hat|). x: fp16 [M][K];
+ * qweight, absmax as nf4_quantize_pack writes them; y: fp16 [M][N]; block 32,
+ * 64 or 128; K % 128 == 0. Dispatch: M <= 8 (M <= 4 above K = 16384, K <=
+ * 32768) the GEMV kernel's NF4 variant (the codebook in LDS), larger M the
+ * tiled MFMA kernel's. Alignment: x and qweight 16 bytes, absmax 4, y 2.
+ */
+w4a16_status nf4_linear(const void* x, const void* qweight, const float* absmax, int64_t M, int64_t N,
+                        int64_t K, int32_t block, void* y, void* stream);
+
+/* nf4_linear_path - nf4_linear with the kernel chosen: 0 auto, 1 GEMV, 2 tiled MFMA. */
+w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, const float* absmax,
+                             int64_t M, int64_t N, int64_t K, int32_t block, void* y, void* stream);
+
 /* Largest M that the GEMV kernel (w4a16_linear_path path 1) accepts. */
 int32_t w4a16_gemv_max_m(void);
 

@@ -20,7 +20,7 @@ def _declared():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
-    return sorted({n for n in names if n.startswith(("w4a16_", "w3a16_", "awq_"))})
+    return sorted({n for n in names if n.startswith(("w4a16_", "w3a16_", "awq_", "nf4_"))})
 
 
 def test_header_declares_the_binding_set():
@@ -179,6 +179,32 @@ def test_format_variants_reject():
     assert lib.w3a16_linear_path(3, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w3a16_linear_path(1, A16, A16, A16, A16, 9, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w3a16_linear_path(1, A16, A16, A16, A16, 8, 64, 32768 + 128, 128, A16, None) == w4.ERR_UNSUPPORTED
+
+
+def test_nf4_codebook_is_the_oracles_fp16_codebook():
+    # the library derives its codebook itself (its own normal quantiles); both must round to
+    # the same fp16 levels
+    import numpy as np
+
+    import oracle
+
+    assert w4.nf4_codebook() == [int(b) for b in oracle.NF4_LEVELS_F16.view(np.uint16)]
+
+
+def test_nf4_and_sym_reject():
+    lib = w4.load()
+    assert lib.nf4_quantize_pack(None, None, 4, 128, 64, A16, A16, None) == w4.ERR_NULL
+    assert lib.nf4_quantize_pack(A16, None, 4, 128, 16, A16, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.nf4_quantize_pack(A16, None, 4, 96, 64, A16, A16, None) == w4.ERR_SHAPE
+    assert lib.nf4_quantize_pack(A16, None, 4, 128, 64, A16, A16 + 2, None) == w4.ERR_ALIGN
+    assert lib.nf4_linear(A16, A16, A16, 1, 64, 256, 48, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.nf4_linear(A16, A16, A16, 1, 64, 192, 64, A16, None) == w4.ERR_SHAPE
+    assert lib.nf4_linear(A16, A16, A16 + 2, 1, 64, 256, 64, A16, None) == w4.ERR_ALIGN
+    assert lib.nf4_linear_path(3, A16, A16, A16, 1, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.nf4_linear_path(1, A16, A16, A16, 9, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.awq_quantize_pack_sym(A16, None, 4, 256, 2, 128, A16, A16, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.awq_quantize_pack_sym(A16, None, 4, 200, 4, 128, A16, A16, A16, None) == w4.ERR_SHAPE
+    assert lib.awq_quantize_pack_sym(None, None, 4, 256, 4, 128, A16, A16, A16, None) == w4.ERR_NULL
 
 
 def test_output_reference_rejects():

@@ -1,0 +1,151 @@
+"""GPU parity of the symmetric absmax and NF4 variants against the float64 oracle
+(oracle/sym.py, oracle/nf4.py).
+
+* quantize-pack: codes, scales/absmax and zeros bit-identical to the oracle's;
+* the linear layer: every output within 1e-3 * sum_k |x * w_hat| + 1e-5 of the oracle, on
+  the GEMV and tiled MFMA kernels, fed the oracle's packed weights. Symmetric weights run
+  through the ordinary linear entry points (their zero is fixed); NF4 through nf4_linear.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu():
+    from tests import _gpu
+
+    return _gpu
+
+
+# ---------------------------------------------------------------- symmetric absmax
+def _sym_compare(lib, W, s, bits, group, tag):
+    g = _gpu()
+    print(f"sym quantize-pack {tag} bits={bits} group={group} N={W.shape[0]} K={W.shape[1]}", flush=True)
+    got = lib.quantize_pack_sym(g.dev(W), None if s is None else g.dev(s), bits=bits, group=group)
+    want = oracle.quantize_pack_sym(W, s, bits=bits, group=group)
+    assert np.array_equal(g.host_u32(got[0]), want[0])
+    assert np.array_equal(g.bits16(g.host(got[1])), g.bits16(want[1]))
+    assert np.array_equal(g.bits16(g.host(got[2])), g.bits16(want[2]))
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 64), (4, 32), (3, 128), (3, 32)])
+@pytest.mark.parametrize("n,k", [(37, 384), (256, 4096)])
+def test_sym_quantize_pack_bit_exact(lib, bits, group, n, k):
+    W = synth.weights(2, 7, n, k)
+    s = oracle.channel_scale(synth.calibration(2, 7, k))
+    _sym_compare(lib, W, s, bits, group, "scaled")
+    _sym_compare(lib, W, None, bits, group, "plain")
+
+
+@pytest.mark.parametrize("kind", ["ties", "constant", "positive", "negative", "subnormal", "wide", "mixed"])
+def test_sym_quantize_pack_edge_tensors(lib, kind):
+    W = synth.edge_weights(kind, 40, 512, seed=9)
+    W[3, :128] = 0  # an all-zero group
+    for bits, group in ((4, 128), (3, 64)):
+        _sym_compare(lib, W, None, bits, group, kind)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 32), (3, 128)])
+@pytest.mark.parametrize("m", [1, 3, 8, 17, 64])
+def test_sym_linear_all_paths(lib, bits, group, m):
+    g = _gpu()
+    k, n = 2048, 300
+    s = oracle.channel_scale(synth.calibration(2, 8, k))
+    packed = oracle.quantize_pack_sym(synth.weights(2, 8, n, k), s, bits=bits, group=group)
+    x = oracle.scale_input(synth.activations(2, 8, m, k), s)
+    y_ref, b = oracle.linear(x, *packed, group=group, bits=bits)
+    paths = [0, 2] + ([1] if m <= 8 else []) + ([3] if bits == 4 and group == 128 and m <= 32 else [])
+    for path in paths:
+        print(f"sym linear bits={bits} group={group} M={m} path={path}", flush=True)
+        y = g.host(lib.linear(g.dev(x), *[g.dev(t) for t in packed], group=group, path=path, bits=bits))
+        assert np.all(oracle.within_tolerance(y.astype(np.float64), y_ref, b)), path
+
+
+# ---------------------------------------------------------------- NF4
+def _nf4_compare(lib, W, s, block, tag):
+    g = _gpu()
+    print(f"nf4 quantize-pack {tag} block={block} N={W.shape[0]} K={W.shape[1]}", flush=True)
+    qw, a = lib.nf4_quantize_pack(g.dev(W), None if s is None else g.dev(s), block=block)
+    want_q, want_a = oracle.quantize_pack_nf4(W, s, block)
+    gq = g.host_u32(qw)
+    assert np.array_equal(gq, want_q), g.report_mismatch("qweight", gq, want_q)
+    ga = g.host(a)
+    assert np.array_equal(ga.view(np.uint32), want_a.view(np.uint32)), g.report_mismatch("absmax", ga, want_a)
+
+
+@pytest.mark.parametrize("block", [64, 32, 128])
+@pytest.mark.parametrize("n,k", [(37, 384), (300, 2048), (64, 11008)])
+def test_nf4_quantize_pack_bit_exact(lib, block, n, k):
+    W = synth.weights(3, 2, n, k)
+    _nf4_compare(lib, W, None, block, "plain")
+    s = oracle.channel_scale(synth.calibration(3, 2, k))
+    _nf4_compare(lib, W, s, block, "scaled")
+
+
+@pytest.mark.parametrize("kind", ["ties", "constant", "positive", "negative", "subnormal", "wide", "mixed"])
+def test_nf4_quantize_pack_edge_tensors(lib, kind):
+    W = synth.edge_weights(kind, 40, 512, seed=11)
+    W[5, 64:128] = 0  # an all-zero block
+    _nf4_compare(lib, W, None, 64, kind)
+
+
+def test_nf4_quantize_pack_codebook_levels_exactly(lib):
+    # weights that are codebook levels times powers of two: every code must come back
+    rng = np.random.default_rng(4)
+    c = rng.integers(0, 16, size=(64, 1024))
+    c[:, ::64] = 0  # level -1 in every block
+    scale = 2.0 ** rng.integers(-9, -3, size=(64, 16))
+    W = (oracle.NF4_LEVELS_F16.astype(np.float64)[c] * np.repeat(scale, 64, axis=1)).astype(np.float16)
+    _nf4_compare(lib, W, None, 64, "levels")
+
+
+def _nf4_linear_check(lib, x, qw, a, block, path, tag, rows=None):
+    g = _gpu()
+    print(f"nf4 linear {tag} block={block} path={path} M={x.shape[0]} N={qw.shape[0]} K={x.shape[1]}", flush=True)
+    y = g.host(lib.nf4_linear(g.dev(x), g.dev(qw), g.dev(a), block=block, path=path))
+    y_ref, b = oracle.linear_nf4(x, qw, a, block, rows=rows)
+    if rows is not None:
+        y = y[:, rows]
+    ok = oracle.within_tolerance(y.astype(np.float64), y_ref, b)
+    assert np.all(ok), (tag, np.argwhere(~ok)[:3])
+
+
+@pytest.mark.parametrize("block", [64, 32, 128])
+@pytest.mark.parametrize("m", [1, 2, 5, 8])
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 384), (300, 2048), (97, 11008), (64, 22016)])
+def test_nf4_gemv(lib, block, m, n, k):
+    if k > 16384 and m > 4:
+        pytest.skip("the GEMV variant takes M <= 4 above K = 16384")
+    qw, a = oracle.quantize_pack_nf4(synth.weights(3, 4, n, k), None, block)
+    x = synth.activations(3, 4, m, k)
+    _nf4_linear_check(lib, x, qw, a, block, 1, "gemv")
+
+
+@pytest.mark.parametrize("block", [64, 32])
+@pytest.mark.parametrize("m", [1, 9, 33, 100])
+@pytest.mark.parametrize("n,k", [(37, 384), (300, 2048), (130, 11008)])
+def test_nf4_mfma(lib, block, m, n, k):
+    qw, a = oracle.quantize_pack_nf4(synth.weights(3, 5, n, k), None, block)
+    x = synth.activations(3, 5, m, k)
+    _nf4_linear_check(lib, x, qw, a, block, 2, "mfma")
+
+
+@pytest.mark.parametrize("m", [1, 4, 128])
+def test_nf4_full_size_sampled_and_deterministic(lib, m):
+    # LLaMA-65B q projection 8192 x 8192, packed on the device, 256 sampled rows
+    g = _gpu()
+    W = synth.weights(3, 0, 8192, 8192)
+    qw_d, a_d = lib.nf4_quantize_pack(g.dev(W), None, block=64)
+    x = synth.activations(3, 0, m, 8192)
+    xd = g.dev(x)
+    y1 = g.host(lib.nf4_linear(xd, qw_d, a_d, block=64))
+    y2 = g.host(lib.nf4_linear(xd, qw_d, a_d, block=64))
+    assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+    rows = np.linspace(0, 8191, 256).astype(int)
+    y_ref, b = oracle.linear_nf4(x, g.host_u32(qw_d), g.host(a_d), 64, rows=rows)
+    assert np.all(oracle.within_tolerance(y1[:, rows].astype(np.float64), y_ref, b))

@@ -55,6 +55,11 @@ def load():
         "awq_alpha_loss_workspace": ([i64, i64], i64),
         "w3a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w3a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
+        "awq_quantize_pack_sym": ([vp, vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
+        "nf4_codebook": ([vp], None),
+        "nf4_quantize_pack": ([vp, vp, i64, i64, i32, vp, vp, vp], i32),
+        "nf4_linear": ([vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
+        "nf4_linear_path": ([i32, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_output_reference": ([vp, vp, i64, i64, i64, vp, vp], i32),
         "awq_alpha_loss": ([vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
     }
@@ -69,7 +74,8 @@ def load():
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
-            "w4a16_linear_path", "w3a16_linear", "w3a16_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
+            "w4a16_linear_path", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
+            "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
             "awq_alpha_loss"]
 
 
@@ -177,6 +183,81 @@ def quantize_pack(W, s=None, bits=4, group=GROUP, out=None):
     _check(lib.awq_quantize_pack(W.data_ptr(), sp, n, k, bits, group, qweight.data_ptr(), scales.data_ptr(),
                                  zeros.data_ptr(), _stream(W)))
     return qweight, scales, zeros
+
+
+def quantize_pack_sym(W, s=None, bits=4, group=GROUP, out=None):
+    """Symmetric absmax quantize-pack: codes q + 2^(b-1) in the packed layouts, fp16 scales,
+    zeros 2^(b-1) (so ``linear`` computes with them unchanged)."""
+    torch = _torch()
+    lib = load()
+    W = _dev_tensor(W, torch.float16, "W", 2)
+    n, k = W.shape
+    sp = None
+    if s is not None:
+        s = _dev_tensor(s, torch.float32, "s", 1)
+        if s.shape[0] != k:
+            raise ValueError("s must have K entries")
+        sp = s.data_ptr()
+    if out is None:
+        words = k // 8 if bits == 4 else 3 * (k // 32)
+        qweight = torch.empty((n, max(words, 1)), dtype=torch.int32, device=W.device)
+        scales = torch.empty((n, max(k // group, 1)), dtype=torch.float16, device=W.device)
+        zeros = torch.empty((n, max(k // group, 1)), dtype=torch.float16, device=W.device)
+    else:
+        qweight, scales, zeros = out
+    _check(lib.awq_quantize_pack_sym(W.data_ptr(), sp, n, k, bits, group, qweight.data_ptr(), scales.data_ptr(),
+                                     zeros.data_ptr(), _stream(W)))
+    return qweight, scales, zeros
+
+
+NF4_BLOCK = 64
+
+
+def nf4_codebook():
+    """The library's 16 fp16 NF4 levels (bit patterns, ascending), as a list of ints."""
+    buf = (ctypes.c_uint16 * 16)()
+    load().nf4_codebook(buf)
+    return list(buf)
+
+
+def nf4_quantize_pack(W, s=None, block=NF4_BLOCK, out=None):
+    """NF4 quantize-pack: (qweight int32 [N][K/8] in layout v1, absmax float32 [N][K/block])."""
+    torch = _torch()
+    lib = load()
+    W = _dev_tensor(W, torch.float16, "W", 2)
+    n, k = W.shape
+    sp = None
+    if s is not None:
+        s = _dev_tensor(s, torch.float32, "s", 1)
+        if s.shape[0] != k:
+            raise ValueError("s must have K entries")
+        sp = s.data_ptr()
+    if out is None:
+        qweight = torch.empty((n, max(k // 8, 1)), dtype=torch.int32, device=W.device)
+        absmax = torch.empty((n, max(k // block, 1)), dtype=torch.float32, device=W.device)
+    else:
+        qweight, absmax = out
+    _check(lib.nf4_quantize_pack(W.data_ptr(), sp, n, k, block, qweight.data_ptr(), absmax.data_ptr(), _stream(W)))
+    return qweight, absmax
+
+
+def nf4_linear(x, qweight, absmax, block=NF4_BLOCK, out=None, path=PATH_AUTO):
+    """y = x @ (codebook[q] * absmax)^T, fp16 [M][N] (float32 accumulation)."""
+    torch = _torch()
+    lib = load()
+    x = _dev_tensor(x, torch.float16, "x", 2)
+    qweight = _dev_tensor(qweight, torch.int32, "qweight", 2)
+    absmax = _dev_tensor(absmax, torch.float32, "absmax", 2)
+    m, k = x.shape
+    n = qweight.shape[0]
+    if qweight.shape[1] * 8 != k:
+        raise ValueError("qweight must be [N][K/8]")
+    if tuple(absmax.shape) != (n, k // block):
+        raise ValueError("absmax must be [N][K/block]")
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    _check(lib.nf4_linear_path(path, x.data_ptr(), qweight.data_ptr(), absmax.data_ptr(), m, n, k, block,
+                               y.data_ptr(), _stream(x)))
+    return y
 
 
 def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO, bits=4):

@@ -53,6 +53,60 @@ w4a16_status check_linear(const void* x, const void* qweight, const void* scales
   return W4A16_OK;
 }
 
+// The NF4 codebook ("Quantization for LLMs", chapter 11, section 11.5): 8 positive
+// levels at the standard normal quantiles of OFFSET - i (OFFSET - 1/2) / 8 (i = 0..7),
+// 7 negative levels mirrored from OFFSET - i (OFFSET - 1/2) / 7 (i = 0..6), and 0, all
+// divided by the largest; OFFSET = 0.9677083. The quantiles come from bisection on
+// the normal CDF 1/2 erfc(-x / sqrt 2) to double precision; each level is then
+// rounded once to fp16. Built once per process (thread-safe static init).
+double normal_cdf(double x) { return 0.5 * std::erfc(-x / std::sqrt(2.0)); }
+
+double normal_quantile_upper(double p) {  // p in (1/2, 1)
+  double lo = 0.0, hi = 40.0;
+  for (int i = 0; i < 400 && lo < hi; ++i) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    if (normal_cdf(mid) < p)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  return 0.5 * (lo + hi);
+}
+
+const w4a16::Nf4Table& nf4_table() {
+  static const w4a16::Nf4Table table = [] {
+    constexpr double kOffset = 0.9677083;
+    const double span = kOffset - 0.5;
+    const double top = normal_quantile_upper(kOffset);
+    double levels[16];
+    for (int i = 0; i < 7; ++i) levels[i] = -normal_quantile_upper(kOffset - i * span / 7.0) / top;
+    levels[7] = 0.0;
+    for (int i = 0; i < 8; ++i) levels[15 - i] = normal_quantile_upper(kOffset - i * span / 8.0) / top;
+    w4a16::Nf4Table t;
+    for (int i = 0; i < 8; ++i)
+      t.pairs[i] = (uint32_t)w4a16::f64_to_f16_rne(levels[2 * i]) |
+                   ((uint32_t)w4a16::f64_to_f16_rne(levels[2 * i + 1]) << 16);
+    return t;
+  }();
+  return table;
+}
+
+w4a16_status check_nf4_linear(const void* x, const void* qweight, const void* absmax, int64_t M, int64_t N, int64_t K,
+                              int32_t block, const void* y) {
+  if (!x || !qweight || !absmax || !y) return fail(W4A16_ERR_NULL, "x, qweight, absmax and y are required");
+  if (block != 64 && block != 32 && block != 128)
+    return fail(W4A16_ERR_UNSUPPORTED, "block must be 32, 64 or 128 (got %d)", (int)block);
+  if (M <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "M, N, K must be positive (got %lld, %lld, %lld)",
+                                              (long long)M, (long long)N, (long long)K);
+  if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
+  if (K > W4A16_MAX_K || N > kMaxN || M > kMaxM)
+    return fail(W4A16_ERR_SHAPE, "size beyond the limits (M <= 65536, N <= 2^24, K <= %d)", W4A16_MAX_K);
+  if (!aligned(x, 16) || !aligned(qweight, 16)) return fail(W4A16_ERR_ALIGN, "x and qweight must be 16-byte aligned");
+  if (!aligned(absmax, 4) || !aligned(y, 2)) return fail(W4A16_ERR_ALIGN, "absmax must be 4-byte and y 2-byte aligned");
+  return W4A16_OK;
+}
+
 // bits 4 with group 128 runs the tuned kernels; every other format the variant kernels
 w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* qweight, const void* scales,
                         const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
@@ -220,6 +274,77 @@ int64_t awq_alpha_loss_workspace(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0 || T > kMaxT || N > kMaxN) return -1;
   const int64_t tiles = w4a16::alpha_loss_partials(T, N);
   return tiles > kMaxTiles ? -1 : tiles;
+}
+
+void nf4_codebook(uint16_t* levels) {
+  if (!levels) return;
+  const w4a16::Nf4Table& t = nf4_table();
+  for (int i = 0; i < 8; ++i) {
+    levels[2 * i] = (uint16_t)(t.pairs[i] & 0xFFFFu);
+    levels[2 * i + 1] = (uint16_t)(t.pairs[i] >> 16);
+  }
+}
+
+w4a16_status nf4_quantize_pack(const void* w, const float* s, int64_t N, int64_t K, int32_t block, void* qweight,
+                               float* absmax, void* stream) {
+  clear_error();
+  if (!w || !qweight || !absmax) return fail(W4A16_ERR_NULL, "w, qweight and absmax are required");
+  if (block != 64 && block != 32 && block != 128)
+    return fail(W4A16_ERR_UNSUPPORTED, "block must be 32, 64 or 128 (got %d)", (int)block);
+  if (N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "N and K must be positive");
+  if (K % block != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of the block (got K=%lld)", (long long)K);
+  if (K > W4A16_MAX_K || N > kMaxN) return fail(W4A16_ERR_SHAPE, "size beyond the limits (N <= 2^24, K <= %d)", W4A16_MAX_K);
+  if (!aligned(w, 16) || !aligned(qweight, 16) || (s && !aligned(s, 16)))
+    return fail(W4A16_ERR_ALIGN, "w, qweight and s must be 16-byte aligned");
+  if (!aligned(absmax, 4)) return fail(W4A16_ERR_ALIGN, "absmax must be 4-byte aligned");
+  return hip_result(w4a16::launch_nf4_quantize_pack(static_cast<const uint16_t*>(w), s, N, K, block,
+                                                    nf4_table().pairs, static_cast<uint32_t*>(qweight), absmax,
+                                                    static_cast<hipStream_t>(stream)),
+                    "NF4 quantize-pack launch");
+}
+
+w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, const float* absmax, int64_t M,
+                             int64_t N, int64_t K, int32_t block, void* y, void* stream) {
+  clear_error();
+  if (path < 0 || path > 2) return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV) or 2 (tiled MFMA)");
+  const w4a16_status st = check_nf4_linear(x, qweight, absmax, M, N, K, block, y);
+  if (st != W4A16_OK) return st;
+  const bool gemv_ok = w4a16::gemv_variant_supports(M, K, block);
+  if (path == 1 && !gemv_ok)
+    return fail(W4A16_ERR_UNSUPPORTED, "the NF4 GEMV kernel takes M <= %d and K <= 32768 (M <= 4 above K = 16384); "
+                "got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  const uint32_t* qw = static_cast<const uint32_t*>(qweight);
+  uint16_t* yh = static_cast<uint16_t*>(y);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (path == 1 || (path == 0 && gemv_ok))
+    return hip_result(w4a16::launch_gemv_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs), "NF4 GEMV launch");
+  return hip_result(w4a16::launch_mfma_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs), "NF4 MFMA launch");
+}
+
+w4a16_status nf4_linear(const void* x, const void* qweight, const float* absmax, int64_t M, int64_t N, int64_t K,
+                        int32_t block, void* y, void* stream) {
+  return nf4_linear_path(0, x, qweight, absmax, M, N, K, block, y, stream);
+}
+
+w4a16_status awq_quantize_pack_sym(const void* w, const float* s, int64_t N, int64_t K, int32_t bits, int32_t group,
+                                   void* qweight, void* scales, void* zeros, void* stream) {
+  clear_error();
+  if (!w || !qweight || !scales || !zeros) return fail(W4A16_ERR_NULL, "w, qweight, scales and zeros are required");
+  if ((bits != 4 && bits != 3) || (group != 128 && group != 64 && group != 32))
+    return fail(W4A16_ERR_UNSUPPORTED, "bits must be 3 or 4 and group 32, 64 or 128 (got bits=%d, group=%d)",
+                (int)bits, (int)group);
+  if (N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "N and K must be positive");
+  if (K % group != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of the group (got K=%lld, group=%d)",
+                                  (long long)K, (int)group);
+  if (K > W4A16_MAX_K || N > kMaxN) return fail(W4A16_ERR_SHAPE, "size beyond the limits (N <= 2^24, K <= %d)", W4A16_MAX_K);
+  if (!aligned(w, 16) || !aligned(qweight, 16) || (s && !aligned(s, 16)))
+    return fail(W4A16_ERR_ALIGN, "w, qweight and s must be 16-byte aligned");
+  if (!aligned(scales, 2) || !aligned(zeros, 2)) return fail(W4A16_ERR_ALIGN, "scales and zeros must be 2-byte aligned");
+  return hip_result(w4a16::launch_quantize_pack_sym(static_cast<const uint16_t*>(w), s, N, K, bits, group,
+                                                    static_cast<uint32_t*>(qweight), static_cast<uint16_t*>(scales),
+                                                    static_cast<uint16_t*>(zeros), static_cast<hipStream_t>(stream)),
+                    "symmetric quantize-pack launch");
 }
 
 w4a16_status awq_output_reference(const void* x, const void* w, int64_t T, int64_t N, int64_t K, float* y_ref,

@@ -158,7 +158,7 @@ hipError_t launch_scale_input(const uint16_t* x, const float* s, int64_t M, int6
 // lanes of a 32-input block OR their bits into the block's three bit-plane words
 // (two low-bit words, one high-bit word) and three of them write one word each.
 // Lane 0 of the group writes the fp16 scale and zero.
-template <int BITS, int GROUP>
+template <int BITS, int GROUP, bool SYM>
 __global__ __launch_bounds__(256) void quantize_pack_kernel(const uint4* __restrict__ w, const float4* __restrict__ s,
                                                             int64_t n_groups, int G, uint32_t* __restrict__ qweight,
                                                             uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros) {
@@ -188,27 +188,47 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const uint4* __restr
 #pragma unroll
     for (int i = 0; i < 8; ++i) v[i] = v[i] * (double)sv[i];  // exact: 11 x 24 significant bits
   }
-  double mn = v[0], mx = v[0];
-#pragma unroll
-  for (int i = 1; i < 8; ++i) {
-    mn = fmin(mn, v[i]);
-    mx = fmax(mx, v[i]);
-  }
-#pragma unroll
-  for (int off = 1; off < LPG; off <<= 1) {
-    mn = fmin(mn, __shfl_xor(mn, off, LPG));
-    mx = fmax(mx, __shfl_xor(mx, off, LPG));
-  }
-  double range = mx - mn;
-  if (range == 0.0) range = 1.0;
-  const double delta = range / kQmax;
-  const double z = rint(-mn / delta) + 0.0;  // + 0.0 makes a zero offset +0
+  double delta, z;
   uint32_t c[8];
+  if constexpr (!SYM) {
+    double mn = v[0], mx = v[0];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    double q = rint(v[i] / delta) + z;
-    q = fmin(fmax(q, 0.0), kQmax);
-    c[i] = (uint32_t)q;
+    for (int i = 1; i < 8; ++i) {
+      mn = fmin(mn, v[i]);
+      mx = fmax(mx, v[i]);
+    }
+#pragma unroll
+    for (int off = 1; off < LPG; off <<= 1) {
+      mn = fmin(mn, __shfl_xor(mn, off, LPG));
+      mx = fmax(mx, __shfl_xor(mx, off, LPG));
+    }
+    double range = mx - mn;
+    if (range == 0.0) range = 1.0;
+    delta = range / kQmax;
+    z = rint(-mn / delta) + 0.0;  // + 0.0 makes a zero offset +0
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      double q = rint(v[i] / delta) + z;
+      q = fmin(fmax(q, 0.0), kQmax);
+      c[i] = (uint32_t)q;
+    }
+  } else {
+    // symmetric absmax: Delta = max|w| / (2^(b-1) - 1), codes rint(w / Delta) clipped to
+    // the symmetric range, stored with the fixed zero 2^(b-1)
+    constexpr double kHalf = (double)((1 << (BITS - 1)) - 1);
+    double m = fabs(v[0]);
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = fmax(m, fabs(v[i]));
+#pragma unroll
+    for (int off = 1; off < LPG; off <<= 1) m = fmax(m, __shfl_xor(m, off, LPG));
+    if (m == 0.0) m = 1.0;
+    delta = m / kHalf;
+    z = (double)(1 << (BITS - 1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const double q = fmin(fmax(rint(v[i] / delta), -kHalf), kHalf);
+      c[i] = (uint32_t)(q + z);
+    }
   }
   if constexpr (BITS == 4) {
     uint32_t word = 0;
@@ -244,7 +264,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(const uint4* __restr
   }
 }
 
-template <int BITS, int GROUP>
+template <int BITS, int GROUP, bool SYM>
 hipError_t launch_qp(const uint16_t* w, const float* s, int64_t N, int64_t K, uint32_t* qweight, uint16_t* scales,
                      uint16_t* zeros, hipStream_t stream) {
   const int G = (int)(K / GROUP);
@@ -252,23 +272,128 @@ hipError_t launch_qp(const uint16_t* w, const float* s, int64_t N, int64_t K, ui
   const int block = 256;
   const int per_block = block / (GROUP / 8);
   const int64_t grid = (n_groups + per_block - 1) / per_block;
-  hipLaunchKernelGGL((quantize_pack_kernel<BITS, GROUP>), dim3((unsigned)grid), dim3(block), 0, stream,
+  hipLaunchKernelGGL((quantize_pack_kernel<BITS, GROUP, SYM>), dim3((unsigned)grid), dim3(block), 0, stream,
                      reinterpret_cast<const uint4*>(w), reinterpret_cast<const float4*>(s), n_groups, G, qweight,
                      scales, zeros);
   return hipGetLastError();
 }
 
+template <bool SYM>
+hipError_t launch_qp_any(const uint16_t* w, const float* s, int64_t N, int64_t K, int bits, int group,
+                         uint32_t* qweight, uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+  if (bits == 4) {
+    if (group == 128) return launch_qp<4, 128, SYM>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 64) return launch_qp<4, 64, SYM>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 32) return launch_qp<4, 32, SYM>(w, s, N, K, qweight, scales, zeros, stream);
+  } else if (bits == 3) {
+    if (group == 128) return launch_qp<3, 128, SYM>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 64) return launch_qp<3, 64, SYM>(w, s, N, K, qweight, scales, zeros, stream);
+    if (group == 32) return launch_qp<3, 32, SYM>(w, s, N, K, qweight, scales, zeros, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, int bits, int group,
                                 uint32_t* qweight, uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
-  if (bits == 4) {
-    if (group == 128) return launch_qp<4, 128>(w, s, N, K, qweight, scales, zeros, stream);
-    if (group == 64) return launch_qp<4, 64>(w, s, N, K, qweight, scales, zeros, stream);
-    if (group == 32) return launch_qp<4, 32>(w, s, N, K, qweight, scales, zeros, stream);
-  } else if (bits == 3) {
-    if (group == 128) return launch_qp<3, 128>(w, s, N, K, qweight, scales, zeros, stream);
-    if (group == 64) return launch_qp<3, 64>(w, s, N, K, qweight, scales, zeros, stream);
-    if (group == 32) return launch_qp<3, 32>(w, s, N, K, qweight, scales, zeros, stream);
+  return launch_qp_any<false>(w, s, N, K, bits, group, qweight, scales, zeros, stream);
+}
+
+hipError_t launch_quantize_pack_sym(const uint16_t* w, const float* s, int64_t N, int64_t K, int bits, int group,
+                                    uint32_t* qweight, uint16_t* scales, uint16_t* zeros, hipStream_t stream) {
+  return launch_qp_any<true>(w, s, N, K, bits, group, qweight, scales, zeros, stream);
+}
+
+// ---------------------------------------------------------------------------
+// NF4 quantize-pack. A block of BLOCK inputs of one row belongs to BLOCK / 8
+// lanes (8 weights each, as above); a = f32(max |w|) of the block, and each
+// weight's code is the index of the nearest fp16 codebook level to w / a
+// (float64 division): the number of level midpoints at or below it, so an
+// exact midpoint goes to the larger level. A block with a = 0 stores a = 0 and
+// the code of level 0. Codes are packed in layout v1.
+template <int BLOCK>
+__global__ __launch_bounds__(256) void nf4_quantize_kernel(const uint4* __restrict__ w, const float4* __restrict__ s,
+                                                           int64_t n_blocks, int G, Nf4Table table,
+                                                           uint32_t* __restrict__ qweight, float* __restrict__ absmax) {
+  constexpr int LPB = BLOCK / 8;
+  const int64_t bid_raw = (int64_t)blockIdx.x * (blockDim.x / LPB) + (threadIdx.x / LPB);
+  const int j = threadIdx.x % LPB;
+  const bool valid = bid_raw < n_blocks;
+  const int64_t bid = valid ? bid_raw : 0;
+  const int64_t n = bid / G;
+  const int g = (int)(bid - n * G);
+  const int64_t chunk = n * ((int64_t)G * LPB) + (int64_t)LPB * g + j;
+
+  const uint4 wv = w[chunk];
+  const uint32_t wu[4] = {wv.x, wv.y, wv.z, wv.w};
+  double v[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = (double)half_bits_to_float((uint16_t)(wu[i] & 0xFFFFu));
+    v[2 * i + 1] = (double)half_bits_to_float((uint16_t)(wu[i] >> 16));
   }
+  if (s != nullptr) {
+    const int64_t kc = (int64_t)BLOCK * g + 8 * j;
+    const float4 s0 = s[kc / 4];
+    const float4 s1 = s[kc / 4 + 1];
+    const float sv[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = v[i] * (double)sv[i];
+  }
+  double m = fabs(v[0]);
+#pragma unroll
+  for (int i = 1; i < 8; ++i) m = fmax(m, fabs(v[i]));
+#pragma unroll
+  for (int off = 1; off < LPB; off <<= 1) m = fmax(m, __shfl_xor(m, off, LPB));
+  const float a = (float)m;  // round to nearest even
+  // midpoints of consecutive fp16 levels (exact in float64); the level-0 code
+  double mid[15];
+  int zero_code = 0;
+#pragma unroll
+  for (int i = 0; i < 15; ++i) {
+    const uint32_t w0 = table.pairs[i >> 1], w1 = table.pairs[(i + 1) >> 1];
+    const double l0 = (double)half_bits_to_float((uint16_t)((i & 1) ? (w0 >> 16) : (w0 & 0xFFFFu)));
+    const double l1 = (double)half_bits_to_float((uint16_t)(((i + 1) & 1) ? (w1 >> 16) : (w1 & 0xFFFFu)));
+    mid[i] = (l0 + l1) * 0.5;
+    if (l1 == 0.0) zero_code = i + 1;
+  }
+  uint32_t word = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t c = (uint32_t)zero_code;
+    if (a != 0.0f) {
+      const double x = v[i] / (double)a;
+      c = 0;
+#pragma unroll
+      for (int t = 0; t < 15; ++t) c += (mid[t] <= x) ? 1u : 0u;
+    }
+    word |= c << ((i & 1) ? (16 + 4 * (i >> 1)) : (4 * (i >> 1)));
+  }
+  if (valid) {
+    qweight[chunk] = word;
+    if (j == 0) absmax[bid] = a;
+  }
+}
+
+template <int BLOCK>
+hipError_t launch_nf4q(const uint16_t* w, const float* s, int64_t N, int64_t K, const uint32_t* lut,
+                       uint32_t* qweight, float* absmax, hipStream_t stream) {
+  const int G = (int)(K / BLOCK);
+  const int64_t n_blocks = N * G;
+  const int per_block = 256 / (BLOCK / 8);
+  const int64_t grid = (n_blocks + per_block - 1) / per_block;
+  Nf4Table t;
+  for (int i = 0; i < 8; ++i) t.pairs[i] = lut[i];
+  hipLaunchKernelGGL((nf4_quantize_kernel<BLOCK>), dim3((unsigned)grid), dim3(256), 0, stream,
+                     reinterpret_cast<const uint4*>(w), reinterpret_cast<const float4*>(s), n_blocks, G, t, qweight,
+                     absmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_nf4_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, int block,
+                                    const uint32_t* lut, uint32_t* qweight, float* absmax, hipStream_t stream) {
+  if (block == 64) return launch_nf4q<64>(w, s, N, K, lut, qweight, absmax, stream);
+  if (block == 32) return launch_nf4q<32>(w, s, N, K, lut, qweight, absmax, stream);
+  if (block == 128) return launch_nf4q<128>(w, s, N, K, lut, qweight, absmax, stream);
   return hipErrorInvalidValue;
 }
 

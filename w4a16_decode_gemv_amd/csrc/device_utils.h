@@ -21,8 +21,8 @@ __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_c
 
 // float64 -> binary16 with a single round-to-nearest-even step (no float32
 // intermediate, which would round twice). Handles signed zero, subnormal
-// results, overflow to infinity and NaN.
-__device__ __forceinline__ uint16_t f64_to_f16_rne(double d) {
+// results, overflow to infinity and NaN. Host and device.
+__host__ __device__ inline uint16_t f64_to_f16_rne(double d) {
   const uint64_t b = __builtin_bit_cast(uint64_t, d);
   const uint16_t sign = (uint16_t)((b >> 48) & 0x8000u);
   const uint64_t a = b & 0x7FFFFFFFFFFFFFFFull;
@@ -53,6 +53,12 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(bits));
   return d;
 }
+
+// The NF4 codebook as kernels take it: the 16 fp16 levels in ascending order, two per
+// word (low half first).
+struct Nf4Table {
+  uint32_t pairs[8];
+};
 
 // Sum over the 16 lanes of a DPP row; every lane of the row receives the sum.
 __device__ __forceinline__ float dpp_row_sum16(float v) {

@@ -209,7 +209,8 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Variants: 3-bit codes and groups of 32 or 64 (and 3-bit with groups of 128).
+// Variants: 3-bit codes and groups of 32 or 64 (and 3-bit with groups of 128), and
+// NF4 codes (layout v1 codes into the 16-level codebook, a float32 absmax per block).
 // A stage is still 128 inputs, but MFMA step st covers exactly the 32 inputs
 // 32 st .. 32 st + 31 (lane (j, c) takes inputs 32 st + 8 j .. + 7), so every
 // step lies inside one group and gets its own (scale, zero): acc += d_st * step.
@@ -218,6 +219,8 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
 // lane's 8 inputs of step st); 3-bit, positions 0..3 / 4..7 / 8..11 hold the
 // low-bit word of inputs 0..15, of inputs 16..31, and the high-bit word, of
 // pieces 0..3.
+
+constexpr int kNF4 = 16;
 
 template <int MB, int BITS>
 struct VarSmem {
@@ -242,13 +245,18 @@ __device__ __forceinline__ half8_t dequant3(uint32_t lo, uint32_t hi, int j, hal
 
 template <int MB, int BITS>
 __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restrict__ x, const uint32_t* __restrict__ qw,
-                                                            const uint16_t* __restrict__ scales,
+                                                            const void* __restrict__ scales,
                                                             const uint16_t* __restrict__ zeros, int M, int N, int K,
-                                                            int gsh, uint16_t* __restrict__ y) {
+                                                            int gsh, Nf4Table table, uint16_t* __restrict__ y) {
   constexpr int BM = 16 * MB;
   constexpr int AU = (BM * 16 + kThreads - 1) / kThreads;
-  constexpr int WPS = BITS == 4 ? 16 : 12;  // code words per row per stage
+  constexpr bool NF4 = BITS == kNF4;
+  constexpr int WPS = BITS == 3 ? 12 : 16;  // code words per row per stage
   __shared__ VarSmem<MB, BITS> sm;
+  __shared__ __align__(16) _Float16 lut[16];
+  if constexpr (NF4) {
+    if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(lut)[threadIdx.x] = table.pairs[threadIdx.x];
+  }
 
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
@@ -262,16 +270,16 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
 
   // codes staging: 4-bit, thread t < 256 copies words 4q..4q+3 of row t / 4; 3-bit, thread t < 192
   // copies words 4q..4q+3 (q = t % 3) of row t / 3
-  const int b_row = BITS == 4 ? (t >> 2) : (t / 3);
-  const int b_q = BITS == 4 ? (t & 3) : (t % 3);
-  const bool b_act = BITS == 4 || t < 192;
+  const int b_row = BITS != 3 ? (t >> 2) : (t / 3);
+  const int b_q = BITS != 3 ? (t & 3) : (t % 3);
+  const bool b_act = BITS != 3 || t < 192;
   const int64_t b_src = (int64_t)min(n0 + b_row, N - 1) * row_words + 4 * b_q;
   // (scale, zero) staging: thread t -> row t / 4, step t % 4
   const int s_row = min(n0 + (t >> 2), N - 1), s_st = t & 3;
 
   uint4 areg[AU];
   uint4 breg = {0u, 0u, 0u, 0u};
-  uint16_t sreg, zreg;
+  uint32_t szreg;
   auto load_stage = [&](int g) {
 #pragma unroll
     for (int u = 0; u < AU; ++u) {
@@ -283,8 +291,10 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
     }
     if (b_act) breg = *reinterpret_cast<const uint4*>(qw + b_src + (int64_t)g * WPS);
     const int64_t off = (int64_t)s_row * G + (((g << 2) + s_st) >> gsh);
-    sreg = scales[off];
-    zreg = zeros[off];
+    if constexpr (NF4)
+      szreg = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
+    else
+      szreg = (uint32_t)static_cast<const uint16_t*>(scales)[off] | ((uint32_t)zeros[off] << 16);
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
@@ -297,12 +307,12 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int w = 4 * b_q + e;  // word of the stage
-        const int pos = BITS == 4 ? (4 * (w & 3) + (w >> 2))    // word 4 st + j -> 4 j + st
+        const int pos = BITS != 3 ? (4 * (w & 3) + (w >> 2))    // word 4 st + j -> 4 j + st
                                   : (4 * (w % 3) + w / 3);      // piece w / 3, kind w % 3 -> 4 kind + piece
         sm.b[buf][b_row][pos] = wv[e];
       }
     }
-    sm.sz[buf][t >> 2][s_st] = (uint32_t)sreg | ((uint32_t)zreg << 16);
+    sm.sz[buf][t >> 2][s_st] = szreg;
   };
 
   float4_t acc[MB];
@@ -311,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
 
   load_stage(0);
   store_stage(0);
-  __syncthreads();
+  __syncthreads();  // also publishes the codebook
 
   const int n_loc = wave * 16 + c;
   const half8_t ones = as_half8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
@@ -326,15 +336,34 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
     bool ok = true;
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
-      d[st] = half_bits_to_float((uint16_t)(szs[st] & 0xFFFFu));
-      zh[st] = __builtin_bit_cast(_Float16, (uint16_t)(szs[st] >> 16));
+      if constexpr (NF4) {
+        d[st] = __builtin_bit_cast(float, szs[st]);
+        zh[st] = (_Float16)0.0f;
+      } else {
+        d[st] = half_bits_to_float((uint16_t)(szs[st] & 0xFFFFu));
+        zh[st] = __builtin_bit_cast(_Float16, (uint16_t)(szs[st] >> 16));
+      }
       zf[st] = (float)zh[st];
       ok = ok && zf[st] >= -2032.0f && zf[st] <= 1024.0f;
     }
-    const bool fast = __builtin_amdgcn_ballot_w64(!ok) == 0;
-    // B fragments of the four steps: exact (q - z) on the fast route, exact q otherwise
+    const bool fast = NF4 || __builtin_amdgcn_ballot_w64(!ok) == 0;
+    // B fragments of the four steps: exact (q - z) on the fast route, exact q otherwise;
+    // NF4: the codebook levels
     half8_t bfrag[4];
-    if constexpr (BITS == 4) {
+    if constexpr (NF4) {
+      const uint4 wq = *reinterpret_cast<const uint4*>(&sm.b[buf][n_loc][4 * j]);
+      const uint32_t words[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        uint32_t v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint32_t n = words[st] >> (4 * i);
+          v[i] = __builtin_bit_cast(uint32_t, (half2_t){lut[n & 15u], lut[(n >> 16) & 15u]});
+        }
+        bfrag[st] = as_half8(v[0], v[1], v[2], v[3]);
+      }
+    } else if constexpr (BITS == 4) {
       const uint4 wq = *reinterpret_cast<const uint4*>(&sm.b[buf][n_loc][4 * j]);
       const uint32_t words[4] = {wq.x, wq.y, wq.z, wq.w};
 #pragma unroll
@@ -393,12 +422,22 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
 }
 
 template <int MB, int BITS>
-hipError_t launch_var(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                      int64_t M, int64_t N, int64_t K, int gsh, uint16_t* y, hipStream_t stream) {
+hipError_t launch_var(const uint16_t* x, const uint32_t* qweight, const void* scales, const uint16_t* zeros,
+                      int64_t M, int64_t N, int64_t K, int gsh, const Nf4Table& table, uint16_t* y,
+                      hipStream_t stream) {
   const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
   hipLaunchKernelGGL((mfma_var_kernel<MB, BITS>), grid, dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(x),
-                     qweight, scales, zeros, (int)M, (int)N, (int)K, gsh, y);
+                     qweight, scales, zeros, (int)M, (int)N, (int)K, gsh, table, y);
   return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_var_m(const uint16_t* x, const uint32_t* qweight, const void* scales, const uint16_t* zeros,
+                        int64_t M, int64_t N, int64_t K, int gsh, const Nf4Table& table, uint16_t* y,
+                        hipStream_t stream) {
+  if (M <= 16) return launch_var<1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, table, y, stream);
+  if (M <= 32) return launch_var<2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, table, y, stream);
+  return launch_var<4, BITS>(x, qweight, scales, zeros, M, N, K, gsh, table, y, stream);
 }
 
 template <int MB>
@@ -423,14 +462,15 @@ hipError_t launch_mfma_variant(int bits, int group, const uint16_t* x, const uin
                                const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream) {
   const int gsh = group == 32 ? 0 : group == 64 ? 1 : 2;
-  if (bits == 4) {
-    if (M <= 16) return launch_var<1, 4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
-    if (M <= 32) return launch_var<2, 4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
-    return launch_var<4, 4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
-  }
-  if (M <= 16) return launch_var<1, 3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
-  if (M <= 32) return launch_var<2, 3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
-  return launch_var<4, 3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+  const Nf4Table none = {};
+  if (bits == 4) return launch_var_m<4>(x, qweight, scales, zeros, M, N, K, gsh, none, y, stream);
+  return launch_var_m<3>(x, qweight, scales, zeros, M, N, K, gsh, none, y, stream);
+}
+
+hipError_t launch_mfma_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
+                           const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  const int gsh = block == 32 ? 0 : block == 64 ? 1 : 2;
+  return launch_var_m<kNF4>(x, qweight, absmax, nullptr, M, N, K, gsh, table, y, stream);
 }
 
 }  // namespace w4a16

@@ -223,19 +223,23 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restri
 // pair of inputs (2j, 2j+1) is rebuilt as the fp16 pair 1024 + q by OR-ing
 // ((lo >> 2i) & 0x00030003) and the high bits moved to bits 2 and 18 into 0x6400.
 
-template <int BITS>
-struct Piece;
-template <>
-struct Piece<4> {
-  u32x4_t w;
+// code formats of the variant kernels: 4-bit and 3-bit integer codes with a
+// (scale, zero) per group, and NF4 (4-bit codes into the 16-level codebook, layout
+// v1) with a float32 absmax per block
+constexpr int kNF4 = 16;
+
+template <int FMT>
+struct Piece {
+  u32x4_t w;  // layout v1: 4-bit integer codes and NF4 codes
 };
 template <>
 struct Piece<3> {
   uint32_t lo0, lo1, hi;
 };
 
-__device__ __forceinline__ Piece<4> load_piece(const uint32_t* qw, int64_t row, int P, int p, Piece<4>*) {
-  Piece<4> r;
+template <int FMT>
+__device__ __forceinline__ Piece<FMT> load_piece(const uint32_t* qw, int64_t row, int P, int p, Piece<FMT>*) {
+  Piece<FMT> r;
   r.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(qw) + row * P + p);
   return r;
 }
@@ -250,7 +254,19 @@ __device__ __forceinline__ Piece<3> load_piece(const uint32_t* qw, int64_t row, 
 }
 
 // the 16 exact fp16 code pairs of a piece, pair j = inputs (2j, 2j+1)
-__device__ __forceinline__ void piece_pairs(const Piece<4>& pc, half2_t (&q)[16]) {
+// NF4: pair i of word wi is (codebook[(w >> 4i) & 15], codebook[(w >> 16 + 4i) & 15])
+__device__ __forceinline__ void piece_pairs(const Piece<kNF4>& pc, half2_t (&q)[16], const _Float16* lut) {
+  const uint32_t wd[4] = {pc.w.x, pc.w.y, pc.w.z, pc.w.w};
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t n = wd[wi] >> (4 * i);
+      q[4 * wi + i] = (half2_t){lut[n & 15u], lut[(n >> 16) & 15u]};
+    }
+}
+
+__device__ __forceinline__ void piece_pairs(const Piece<4>& pc, half2_t (&q)[16], const _Float16*) {
   const uint32_t wd[4] = {pc.w.x, pc.w.y, pc.w.z, pc.w.w};
 #pragma unroll
   for (int wi = 0; wi < 4; ++wi) {
@@ -262,7 +278,7 @@ __device__ __forceinline__ void piece_pairs(const Piece<4>& pc, half2_t (&q)[16]
   }
 }
 
-__device__ __forceinline__ void piece_pairs(const Piece<3>& pc, half2_t (&q)[16]) {
+__device__ __forceinline__ void piece_pairs(const Piece<3>& pc, half2_t (&q)[16], const _Float16*) {
   const half2_t m1024 = {(_Float16)-1024.0f, (_Float16)-1024.0f};
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
@@ -274,11 +290,11 @@ __device__ __forceinline__ void piece_pairs(const Piece<3>& pc, half2_t (&q)[16]
   }
 }
 
-template <int MT, int PPT, int BITS>
+template <int MT, int PPT, int FMT>
 __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __restrict__ x, const uint32_t* __restrict__ qw,
-                                                               const uint16_t* __restrict__ scales,
+                                                               const void* __restrict__ scales,
                                                                const uint16_t* __restrict__ zeros, int M, int N, int K,
-                                                               int gsh, uint16_t* __restrict__ y) {
+                                                               int gsh, Nf4Table table, uint16_t* __restrict__ y) {
   constexpr int R = Tile<MT, PPT>::R;
   constexpr int V = Tile<MT, PPT>::V;
   constexpr int E = R * PPT * 64;        // staged (scale, zero) pairs per wave, enough for groups of 32
@@ -296,16 +312,24 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
   uint32_t* wsz = lds + wave * (E + V);
   float* wred = reinterpret_cast<float*>(wsz + E);
 
-  // (1) (scale, zero) pairs: slot pp of this wave covers 64 >> gsh groups from (64 wave + pp T) >> gsh
-  uint16_t sreg[NE], zreg[NE];
+  __shared__ __align__(16) _Float16 lut[16];
+  if constexpr (FMT == kNF4) {
+    if (t < 8) reinterpret_cast<uint32_t*>(lut)[t] = table.pairs[t];
+  }
+
+  // (1) (scale, zero) pairs, or NF4 absmax: slot pp of this wave covers 64 >> gsh groups from
+  //     (64 wave + pp T) >> gsh
+  uint32_t sz[NE];
 #pragma unroll
   for (int u = 0; u < NE; ++u) {
     const int e = lane + 64 * u;
     const int r = e / (64 * PPT), pp = (e >> 6) % PPT, gl = e & 63;
     const int g = min(((64 * wave + pp * T) >> gsh) + gl, G - 1);
     const int64_t off = (int64_t)min(row0 + r, N - 1) * G + g;
-    sreg[u] = scales[off];
-    zreg[u] = zeros[off];
+    if constexpr (FMT == kNF4)
+      sz[u] = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
+    else
+      sz[u] = (uint32_t)static_cast<const uint16_t*>(scales)[off] | ((uint32_t)zeros[off] << 16);
   }
 
   // (2) x pieces (rows past M repeat row M - 1)
@@ -328,18 +352,19 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
   }
 
   // (3) code pieces of all rows of the tile
-  Piece<BITS> cw[R][PPT];
+  Piece<FMT> cw[R][PPT];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int64_t row = min(row0 + r, N - 1);
 #pragma unroll
     for (int pp = 0; pp < PPT; ++pp)
-      cw[r][pp] = load_piece(qw, row, P, min(t + pp * T, P - 1), (Piece<BITS>*)nullptr);
+      cw[r][pp] = load_piece(qw, row, P, min(t + pp * T, P - 1), (Piece<FMT>*)nullptr);
   }
 
   // (4) stage this wave's pairs (read by this wave only)
 #pragma unroll
-  for (int u = 0; u < NE; ++u) wsz[lane + 64 * u] = (uint32_t)sreg[u] | ((uint32_t)zreg[u] << 16);
+  for (int u = 0; u < NE; ++u) wsz[lane + 64 * u] = sz[u];
+  if constexpr (FMT == kNF4) __syncthreads();  // the codebook is visible to every wave
 
   const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
   float sx[PPT][MT];
@@ -363,10 +388,16 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
     for (int pp = 0; pp < PPT; ++pp) {
       const int p_raw = t + pp * T;
       const uint32_t szv = wsz[(r * PPT + pp) * 64 + (lane >> gsh)];
-      const float d = (p_raw < P) ? half_bits_to_float((uint16_t)(szv & 0xFFFFu)) : 0.f;
-      const float z = half_bits_to_float((uint16_t)(szv >> 16));
+      float d, z;
+      if constexpr (FMT == kNF4) {
+        d = (p_raw < P) ? __builtin_bit_cast(float, szv) : 0.f;
+        z = 0.f;
+      } else {
+        d = (p_raw < P) ? half_bits_to_float((uint16_t)(szv & 0xFFFFu)) : 0.f;
+        z = half_bits_to_float((uint16_t)(szv >> 16));
+      }
       half2_t q[16];
-      piece_pairs(cw[r][pp], q);
+      piece_pairs(cw[r][pp], q, lut);
       float part[MT];
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -376,7 +407,12 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
         part[m] = a;
       }
 #pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[m]);
+      for (int m = 0; m < MT; ++m) {
+        if constexpr (FMT == kNF4)
+          acc[m] = __builtin_fmaf(d, part[m], acc[m]);
+        else
+          acc[m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[m]);
+      }
     }
 #pragma unroll
     for (int m = 0; m < MT; ++m) {
@@ -446,37 +482,39 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const uint16_t* 
   return hipErrorInvalidValue;
 }
 
-template <int MT, int PPT, int BITS>
-hipError_t launch_var(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                      int64_t M, int64_t N, int64_t K, int gsh, uint16_t* y, int threads, hipStream_t stream) {
+template <int MT, int PPT, int FMT>
+hipError_t launch_var(const uint16_t* x, const uint32_t* qweight, const void* scales, const uint16_t* zeros,
+                      int64_t M, int64_t N, int64_t K, int gsh, const Nf4Table& table, uint16_t* y, int threads,
+                      hipStream_t stream) {
   constexpr int R = Tile<MT, PPT>::R;
   constexpr int V = Tile<MT, PPT>::V;
   constexpr int E = R * PPT * 64;
   const size_t lds = (size_t)(threads / 64) * (E + V) * 4;
   const int grid = (int)((N + R - 1) / R);
-  hipLaunchKernelGGL((gemv_var_kernel<MT, PPT, BITS>), dim3(grid), dim3(threads), lds, stream,
-                     reinterpret_cast<const uint4*>(x), qweight, scales, zeros, (int)M, (int)N, (int)K, gsh, y);
+  hipLaunchKernelGGL((gemv_var_kernel<MT, PPT, FMT>), dim3(grid), dim3(threads), lds, stream,
+                     reinterpret_cast<const uint4*>(x), qweight, scales, zeros, (int)M, (int)N, (int)K, gsh, table, y);
   return hipGetLastError();
 }
 
-template <int BITS>
-hipError_t launch_var_bits(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                           int64_t M, int64_t N, int64_t K, int gsh, uint16_t* y, hipStream_t stream) {
+template <int FMT>
+hipError_t launch_var_fmt(const uint16_t* x, const uint32_t* qweight, const void* scales, const uint16_t* zeros,
+                          int64_t M, int64_t N, int64_t K, int gsh, const Nf4Table& table, uint16_t* y,
+                          hipStream_t stream) {
   const Launch l = plan(K);
   const int mt = M <= 1 ? 1 : M <= 2 ? 2 : M <= 4 ? 4 : 8;
   if (l.ppt == 1) {
     switch (mt) {
-      case 1: return launch_var<1, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
-      case 2: return launch_var<2, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
-      case 4: return launch_var<4, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
-      default: return launch_var<8, 1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      case 1: return launch_var<1, 1, FMT>(x, qweight, scales, zeros, M, N, K, gsh, table, y, l.threads, stream);
+      case 2: return launch_var<2, 1, FMT>(x, qweight, scales, zeros, M, N, K, gsh, table, y, l.threads, stream);
+      case 4: return launch_var<4, 1, FMT>(x, qweight, scales, zeros, M, N, K, gsh, table, y, l.threads, stream);
+      default: return launch_var<8, 1, FMT>(x, qweight, scales, zeros, M, N, K, gsh, table, y, l.threads, stream);
     }
   }
   if (l.ppt == 2) {
     switch (mt) {
-      case 1: return launch_var<1, 2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
-      case 2: return launch_var<2, 2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
-      case 4: return launch_var<4, 2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, y, l.threads, stream);
+      case 1: return launch_var<1, 2, FMT>(x, qweight, scales, zeros, M, N, K, gsh, table, y, l.threads, stream);
+      case 2: return launch_var<2, 2, FMT>(x, qweight, scales, zeros, M, N, K, gsh, table, y, l.threads, stream);
+      case 4: return launch_var<4, 2, FMT>(x, qweight, scales, zeros, M, N, K, gsh, table, y, l.threads, stream);
       default: break;
     }
   }
@@ -497,8 +535,15 @@ bool gemv_variant_supports(int64_t M, int64_t K, int group) {
 hipError_t launch_gemv_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                                const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const int gsh = group == 32 ? 0 : group == 64 ? 1 : 2;
-  if (bits == 4) return launch_var_bits<4>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
-  return launch_var_bits<3>(x, qweight, scales, zeros, M, N, K, gsh, y, stream);
+  const Nf4Table none = {};
+  if (bits == 4) return launch_var_fmt<4>(x, qweight, scales, zeros, M, N, K, gsh, none, y, stream);
+  return launch_var_fmt<3>(x, qweight, scales, zeros, M, N, K, gsh, none, y, stream);
+}
+
+hipError_t launch_gemv_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
+                           const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  const int gsh = block == 32 ? 0 : block == 64 ? 1 : 2;
+  return launch_var_fmt<kNF4>(x, qweight, absmax, nullptr, M, N, K, gsh, table, y, stream);
 }
 
 bool gemv_supports(int64_t M, int64_t K) {

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "device_utils.h"
+
 namespace w4a16 {
 
 hipError_t launch_channel_scale(const uint16_t* x_cal, int64_t T, int64_t K, double alpha, float* s,
@@ -20,6 +22,15 @@ hipError_t launch_rmsnorm_fold(const uint16_t* h, const uint16_t* gamma, const f
 // bits 3 or 4, group 32, 64 or 128 (validated by the caller)
 hipError_t launch_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, int bits, int group,
                                 uint32_t* qweight, uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+
+// Symmetric absmax quantize-pack (codes q + 2^(b-1), zeros 2^(b-1)); bits 3 or 4, group 32, 64, 128.
+hipError_t launch_quantize_pack_sym(const uint16_t* w, const float* s, int64_t N, int64_t K, int bits, int group,
+                                    uint32_t* qweight, uint16_t* scales, uint16_t* zeros, hipStream_t stream);
+
+// NF4 quantize-pack with the 16 fp16 codebook levels (ascending, two per word) in lut[8];
+// block 32, 64 or 128; codes in layout v1, float32 absmax [N][K/block].
+hipError_t launch_nf4_quantize_pack(const uint16_t* w, const float* s, int64_t N, int64_t K, int block,
+                                    const uint32_t* lut, uint32_t* qweight, float* absmax, hipStream_t stream);
 
 // GEMV kernel: needs M <= gemv_max_m() and gemv_supports(M, K).
 int gemv_max_m();
@@ -60,5 +71,12 @@ hipError_t launch_alpha_loss(const uint16_t* x_s, const uint32_t* qweight, const
 hipError_t launch_mfma_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                                const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream);
+
+// NF4 linear (codes in layout v1, float32 absmax per block of 32, 64 or 128): the GEMV kernel's
+// NF4 variant (needs gemv_variant_supports(M, K, block)) and the tiled MFMA kernel's (any M).
+hipError_t launch_gemv_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
+                           const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
+hipError_t launch_mfma_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
+                           const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
 }  // namespace w4a16
