@@ -492,6 +492,22 @@ def main():
                              "GB_s": b / (t * 1e-3) / 1e9, "TFLOP_s": 2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12})
                 del L
                 torch.cuda.empty_cache()
+        # NF4 (blocks of 64, float32 absmax) on the same layer
+        import synth
+
+        W = torch.from_numpy(synth.weights(3, 0, 8192, 8192)).to("cuda:0")
+        for mm in (1, 4, 128):
+            b = 8192 * 8192 // 2 + 4 * 8192 * (8192 // 64) + 2 * mm * 8192 * 2
+            copies = copies_for(b)
+            packs = [w4.nf4_quantize_pack(W, None, block=64) for _ in range(copies)]
+            xq = torch.from_numpy(synth.activations(3, 0, mm, 8192)).to("cuda:0")
+            yq = torch.empty((mm, 8192), dtype=torch.float16, device="cuda:0")
+            t = time_graph(torch, lambda i: w4.nf4_linear(xq, *packs[i % copies], block=64, out=yq), 100)
+            rows.append({"format": "nf4", "group": 64, "M": mm, "us": t * 1e3, "bytes": b,
+                         "GB_s": b / (t * 1e-3) / 1e9, "TFLOP_s": 2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12})
+            del packs
+            torch.cuda.empty_cache()
+        del W
         out["formats_k8192_n8192"] = rows
 
     if args.serving:

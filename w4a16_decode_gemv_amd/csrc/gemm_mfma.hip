@@ -243,6 +243,27 @@ __device__ __forceinline__ half8_t dequant3(uint32_t lo, uint32_t hi, int j, hal
   return as_half8(v[0], v[1], v[2], v[3]);
 }
 
+// fast route of one stage: SPG consecutive steps share a group (SPG = group / 32) and
+// chain into one MFMA accumulator, which is scaled once by that group's scale
+template <int MB, int SPG>
+__device__ __forceinline__ void fast_steps(const uint4 (&a_tile)[16 * MB][17], const half8_t (&bfrag)[4],
+                                           const float (&d)[4], int c, int j, float4_t (&acc)[MB]) {
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+    for (int g0 = 0; g0 < 4; g0 += SPG) {
+      float4_t p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = g0; st < g0 + SPG; ++st) {
+        const uint4 av = a_tile[16 * mb + c][4 * st + j];
+        p = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(av.x, av.y, av.z, av.w), bfrag[st], p, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[mb][i] = __builtin_fmaf(d[g0], p[i], acc[mb][i]);
+    }
+  }
+}
+
 template <int MB, int BITS>
 __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restrict__ x, const uint32_t* __restrict__ qw,
                                                             const void* __restrict__ scales,
@@ -279,7 +300,10 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
 
   uint4 areg[AU];
   uint4 breg = {0u, 0u, 0u, 0u};
-  uint32_t szreg;
+  // scale and zero stay in separate registers until the LDS store: combining them at
+  // load time would make the wave wait for those loads at once
+  uint32_t sreg = 0;
+  uint16_t zreg = 0;
   auto load_stage = [&](int g) {
 #pragma unroll
     for (int u = 0; u < AU; ++u) {
@@ -291,10 +315,12 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
     }
     if (b_act) breg = *reinterpret_cast<const uint4*>(qw + b_src + (int64_t)g * WPS);
     const int64_t off = (int64_t)s_row * G + (((g << 2) + s_st) >> gsh);
-    if constexpr (NF4)
-      szreg = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
-    else
-      szreg = (uint32_t)static_cast<const uint16_t*>(scales)[off] | ((uint32_t)zeros[off] << 16);
+    if constexpr (NF4) {
+      sreg = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
+    } else {
+      sreg = static_cast<const uint16_t*>(scales)[off];
+      zreg = zeros[off];
+    }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
@@ -312,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
         sm.b[buf][b_row][pos] = wv[e];
       }
     }
-    sm.sz[buf][t >> 2][s_st] = szreg;
+    sm.sz[buf][t >> 2][s_st] = NF4 ? sreg : (sreg | ((uint32_t)zreg << 16));
   };
 
   float4_t acc[MB];
@@ -383,18 +409,23 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
         bfrag[st] = dequant3(los[st], his[st], j, (half2_t){cc, cc});
       }
     }
+    if (fast) {
+      // the steps of one group chain into one accumulator, scaled once
+      if (gsh == 2)
+        fast_steps<MB, 4>(sm.a[buf], bfrag, d, c, j, acc);
+      else if (gsh == 1)
+        fast_steps<MB, 2>(sm.a[buf], bfrag, d, c, j, acc);
+      else
+        fast_steps<MB, 1>(sm.a[buf], bfrag, d, c, j, acc);
+    } else {
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        const uint4 av = sm.a[buf][16 * mb + c][4 * st + j];
-        const half8_t a = as_half8(av.x, av.y, av.z, av.w);
-        const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
-        const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bfrag[st], zero4, 0, 0, 0);
-        if (fast) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mb][i] = __builtin_fmaf(d[st], p[i], acc[mb][i]);
-        } else {
+        for (int st = 0; st < 4; ++st) {
+          const uint4 av = sm.a[buf][16 * mb + c][4 * st + j];
+          const half8_t a = as_half8(av.x, av.y, av.z, av.w);
+          const float4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+          const float4_t p = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bfrag[st], zero4, 0, 0, 0);
           const float4_t sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, ones, zero4, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mb][i] = __builtin_fmaf(d[st], __builtin_fmaf(-zf[st], sx[i], p[i]), acc[mb][i]);
