@@ -276,7 +276,9 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
   __shared__ VarSmem<MB, BITS> sm;
   __shared__ __align__(16) _Float16 lut[16];
   if constexpr (NF4) {
-    if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(lut)[threadIdx.x] = table.pairs[threadIdx.x];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (threadIdx.x == i) reinterpret_cast<uint32_t*>(lut)[i] = table.pairs[i];
   }
 
   const int t = threadIdx.x;

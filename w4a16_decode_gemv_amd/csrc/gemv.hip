@@ -314,22 +314,30 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
 
   __shared__ __align__(16) _Float16 lut[16];
   if constexpr (FMT == kNF4) {
-    if (t < 8) reinterpret_cast<uint32_t*>(lut)[t] = table.pairs[t];
+    // constant indices keep the codebook words in scalar registers (no memory round trip)
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (t == i) reinterpret_cast<uint32_t*>(lut)[i] = table.pairs[i];
   }
 
   // (1) (scale, zero) pairs, or NF4 absmax: slot pp of this wave covers 64 >> gsh groups from
-  //     (64 wave + pp T) >> gsh
-  uint32_t sz[NE];
+  //     (64 wave + pp T) >> gsh. Scale and zero stay in separate registers until they are
+  //     staged, so no wait on these loads comes before the weight loads are issued.
+  uint32_t sreg[NE];
+  uint16_t zreg[NE];
 #pragma unroll
   for (int u = 0; u < NE; ++u) {
     const int e = lane + 64 * u;
     const int r = e / (64 * PPT), pp = (e >> 6) % PPT, gl = e & 63;
     const int g = min(((64 * wave + pp * T) >> gsh) + gl, G - 1);
     const int64_t off = (int64_t)min(row0 + r, N - 1) * G + g;
-    if constexpr (FMT == kNF4)
-      sz[u] = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
-    else
-      sz[u] = (uint32_t)static_cast<const uint16_t*>(scales)[off] | ((uint32_t)zeros[off] << 16);
+    if constexpr (FMT == kNF4) {
+      sreg[u] = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
+      zreg[u] = 0;
+    } else {
+      sreg[u] = static_cast<const uint16_t*>(scales)[off];
+      zreg[u] = zeros[off];
+    }
   }
 
   // (2) x pieces (rows past M repeat row M - 1)
@@ -360,11 +368,18 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
     for (int pp = 0; pp < PPT; ++pp)
       cw[r][pp] = load_piece(qw, row, P, min(t + pp * T, P - 1), (Piece<FMT>*)nullptr);
   }
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before anything waits on one
 
   // (4) stage this wave's pairs (read by this wave only)
 #pragma unroll
-  for (int u = 0; u < NE; ++u) wsz[lane + 64 * u] = sz[u];
-  if constexpr (FMT == kNF4) __syncthreads();  // the codebook is visible to every wave
+  for (int u = 0; u < NE; ++u) wsz[lane + 64 * u] = sreg[u] | ((uint32_t)zreg[u] << 16);
+  if constexpr (FMT == kNF4) {
+    // the codebook written by wave 0 becomes visible to every wave; the barrier orders LDS
+    // only, so the weight loads stay in flight across it
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  }
 
   const half2_t ones = {(_Float16)1.0f, (_Float16)1.0f};
   float sx[PPT][MT];
