@@ -533,13 +533,26 @@ def main():
                 except (RuntimeError, AttributeError):
                     pass
                 flop = 2 * mm * nn * kk
+                ws = torch.empty(w4.splitk_workspace_bytes(mm, nn, kk, 16) // 4, dtype=torch.float32,
+                                 device=xd.device)
+                split_rows = {}
+                for sp in (0, 2, 4, 8, 16):
+                    if sp > kk // 128:
+                        continue
+                    ts = time_graph(torch, lambda i: w4.linear_splitk(*L.copies[i % len(L.copies)], splits=sp,
+                                                                       workspace=ws, out=L.y[i % len(L.y)]), 50)
+                    split_rows["auto" if sp == 0 else str(sp)] = ts * 1e3
+                t_split = split_rows["auto"]
                 rows.append({"layer": name, "M": mm, "K": kk, "N": nn, "us": t * 1e3,
+                             "splitk_us": t_split, "splitk_TFLOP_s": flop / (t_split * 1e-6) / 1e12,
+                             "splitk_mfma_util": flop / (t_split * 1e-6) / 1e12 / PEAK_FP16_TFLOPS,
+                             "splitk_by_splits_us": split_rows,
                              "TFLOP_s": flop / (t * 1e-3) / 1e12, "mfma_util": flop / (t * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
                              "dense_fp16_us": td * 1e3, "dense_fp16_TFLOP_s": flop / (td * 1e-3) / 1e12,
                              "speedup_vs_dense": td / t,
                              "dense_fp16_hipblaslt_us": None if td_lt is None else td_lt * 1e3,
                              "speedup_vs_dense_hipblaslt": None if td_lt is None else td_lt / t})
-                del L, wt
+                del L, wt, ws
                 torch.cuda.empty_cache()
         out["serving_llama2_7b"] = rows
 

@@ -201,6 +201,33 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
                                void* y, void* stream);
 
 /*
+ * w4a16_linear_splitk_workspace - bytes of float32 workspace that
+ * w4a16_linear_splitk needs for this shape and split count (splits 0 = the
+ * library's choice); -1 when the shape or split count is not accepted.
+ */
+int64_t w4a16_linear_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t splits);
+
+/*
+ * w4a16_linear_splitk - w4a16_linear (4-bit, groups of 128) on the split-K
+ * MFMA kernel, for batches whose output has too few tiles to fill the chip
+ * (CMU guide: at large batch the layer is compute-bound; L13 TinyChat kernel
+ * fusion). The K groups are split into `splits` contiguous ranges (0 = the
+ * library's choice, else 1 <= splits <= min(16, K/128)); each range's float32
+ * partial of every output goes to `workspace`, and a second kernel adds the
+ * partials in index order and rounds once to fp16, so results are reproducible.
+ * Same formula, accuracy contract, arguments and alignment as w4a16_linear,
+ * plus workspace: device memory of workspace_bytes >=
+ * w4a16_linear_splitk_workspace(M, N, K, splits) bytes, 16-byte aligned,
+ * overwritten (two calls in flight at once need two workspaces).
+ * Errors: those of w4a16_linear; W4A16_ERR_UNSUPPORTED (group != 128);
+ * W4A16_ERR_NULL (workspace); W4A16_ERR_ARG (splits, workspace too small);
+ * W4A16_ERR_ALIGN (workspace). Launches two kernels.
+ */
+w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
+                                 int64_t M, int64_t N, int64_t K, int32_t group, int32_t splits,
+                                 void* workspace, int64_t workspace_bytes, void* y, void* stream);
+
+/*
  * w3a16_linear - the fused dequantize + matrix multiply for 3-bit codes in the
  * packed 3-bit layout (awq_quantize_pack with bits 3). Lab 4 setup: 3-bit
  * weights, groups of 128; L13 TinyChat kernel fusion. Same formula, accuracy

@@ -207,6 +207,27 @@ def test_nf4_and_sym_reject():
     assert lib.awq_quantize_pack_sym(None, None, 4, 256, 4, 128, A16, A16, A16, None) == w4.ERR_NULL
 
 
+def test_splitk_workspace_and_rejects():
+    lib = w4.load()
+    assert lib.w4a16_linear_splitk_workspace(128, 4096, 4096, 4) == 4 * 128 * 4096 * 4
+    assert lib.w4a16_linear_splitk_workspace(128, 4096, 4096, 0) > 0
+    assert lib.w4a16_linear_splitk_workspace(128, 4096, 256, 3) == -1   # more splits than groups
+    assert lib.w4a16_linear_splitk_workspace(128, 4096, 4096, 17) == -1
+    assert lib.w4a16_linear_splitk_workspace(0, 4096, 4096, 2) == -1
+
+    def call(group=128, splits=2, ws=A16, wb=1 << 30, M=128, K=4096):
+        return lib.w4a16_linear_splitk(A16, A16, A16, A16, M, 4096, K, group, splits, ws, wb, A16, None)
+
+    assert call(group=64) == w4.ERR_UNSUPPORTED
+    assert call(ws=None) == w4.ERR_NULL
+    assert call(splits=-1) == w4.ERR_ARG
+    assert call(splits=17) == w4.ERR_ARG
+    assert call(splits=3, K=256) == w4.ERR_ARG
+    assert call(wb=100) == w4.ERR_ARG
+    assert call(ws=A16 + 8) == w4.ERR_ALIGN
+    assert call(K=200) == w4.ERR_SHAPE
+
+
 def test_output_reference_rejects():
     lib = w4.load()
     assert lib.awq_output_reference(None, A16, 4, 4, 128, A16, None) == w4.ERR_NULL

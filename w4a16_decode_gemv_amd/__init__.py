@@ -53,6 +53,8 @@ def load():
         "w4a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w4a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_alpha_loss_workspace": ([i64, i64], i64),
+        "w4a16_linear_splitk_workspace": ([i64, i64, i64, i32], i64),
+        "w4a16_linear_splitk": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, i64, vp, vp], i32),
         "w3a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w3a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_quantize_pack_sym": ([vp, vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
@@ -74,7 +76,7 @@ def load():
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
-            "w4a16_linear_path", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
+            "w4a16_linear_path", "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
             "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
             "awq_alpha_loss"]
 
@@ -183,6 +185,35 @@ def quantize_pack(W, s=None, bits=4, group=GROUP, out=None):
     _check(lib.awq_quantize_pack(W.data_ptr(), sp, n, k, bits, group, qweight.data_ptr(), scales.data_ptr(),
                                  zeros.data_ptr(), _stream(W)))
     return qweight, scales, zeros
+
+
+def splitk_workspace_bytes(M, N, K, splits=0):
+    n = int(load().w4a16_linear_splitk_workspace(int(M), int(N), int(K), int(splits)))
+    if n < 0:
+        raise ValueError(f"shape M={M} N={N} K={K} with splits={splits} is not accepted by the split-K kernel")
+    return n
+
+
+def linear_splitk(x, qweight, scales, zeros, splits=0, workspace=None, out=None, group=GROUP):
+    """``linear`` (4-bit, groups of 128) on the split-K MFMA kernel; workspace: a float32 device
+    tensor of at least splitk_workspace_bytes(M, N, K, splits) bytes (allocated when omitted)."""
+    torch = _torch()
+    lib = load()
+    x = _dev_tensor(x, torch.float16, "x", 2)
+    qweight = _dev_tensor(qweight, torch.int32, "qweight", 2)
+    scales = _dev_tensor(scales, torch.float16, "scales", 2)
+    zeros = _dev_tensor(zeros, torch.float16, "zeros", 2)
+    m, k = x.shape
+    n = qweight.shape[0]
+    if qweight.shape[1] * 8 != k or scales.shape != zeros.shape or tuple(scales.shape) != (n, k // group):
+        raise ValueError("qweight must be [N][K/8] and scales/zeros [N][K/group]")
+    if workspace is None:
+        workspace = torch.empty(splitk_workspace_bytes(m, n, k, splits) // 4, dtype=torch.float32, device=x.device)
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    _check(lib.w4a16_linear_splitk(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k,
+                                   group, splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   y.data_ptr(), _stream(x)))
+    return y
 
 
 def quantize_pack_sym(W, s=None, bits=4, group=GROUP, out=None):

@@ -270,6 +270,36 @@ w4a16_status w3a16_linear_path(int32_t path, const void* x, const void* qweight,
   return run_linear(3, path, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
 }
 
+int64_t w4a16_linear_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t splits) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
+  if (splits < 0 || splits > w4a16::splitk_max_splits()) return -1;
+  int s = splits == 0 ? w4a16::splitk_default_splits(M, N, K) : splits;
+  if (s > K / 128) return -1;
+  return w4a16::splitk_workspace_floats(M, N, s) * 4;
+}
+
+w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
+                                 int64_t N, int64_t K, int32_t group, int32_t splits, void* workspace,
+                                 int64_t workspace_bytes, void* y, void* stream) {
+  clear_error();
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "the split-K kernel takes groups of 128 (got %d)", (int)group);
+  if (!workspace) return fail(W4A16_ERR_NULL, "workspace is required");
+  if (splits < 0 || splits > w4a16::splitk_max_splits() || splits > K / 128)
+    return fail(W4A16_ERR_ARG, "splits must lie in [0, min(%d, K/128)] (got %d)", w4a16::splitk_max_splits(), (int)splits);
+  const int s = splits == 0 ? w4a16::splitk_default_splits(M, N, K) : splits;
+  const int64_t need = w4a16::splitk_workspace_floats(M, N, s) * 4;
+  if (workspace_bytes < need)
+    return fail(W4A16_ERR_ARG, "workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+  if (!aligned(workspace, 16)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
+  return hip_result(w4a16::launch_splitk(static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
+                                         static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), M,
+                                         N, K, s, static_cast<float*>(workspace), static_cast<uint16_t*>(y),
+                                         static_cast<hipStream_t>(stream)),
+                    "split-K launch");
+}
+
 int64_t awq_alpha_loss_workspace(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0 || T > kMaxT || N > kMaxN) return -1;
   const int64_t tiles = w4a16::alpha_loss_partials(T, N);

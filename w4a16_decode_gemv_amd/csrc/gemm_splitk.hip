@@ -1,0 +1,282 @@
+// W4A16 GEMM with K split across workgroups, for batches whose output has too few
+// tiles to fill the chip (M = 128..256 against N = 4096..11008: 64-172 tiles of
+// 64 x 128 for 256 CUs).
+//
+// y[m][n] = f16( sum_s P_s[m][n] ),  P_s[m][n] = sum_{g in split s} d[n][g] * sum_{k in g} x[m][k] (q[n][k] - z[n][g])
+//
+// The same fused dequantize + multiply as the other kernels ("MIT 6.5940 L13 LLM
+// Deployment" guide, TinyChat kernel fusion; "CMU 11-868 Model Quantization"
+// guide: at large batch the layer is compute-bound and belongs on the matrix
+// cores). The K groups are split into S contiguous ranges; workgroup (tile, s)
+// computes the float32 partial P_s of its 64 x 128 tile over range s and writes
+// it to the caller's workspace; a second kernel adds the S partials of every
+// output in index order (reproducible) and rounds once to fp16.
+//
+// Partial kernel (same structure as the AWQ-search loss kernel): eight waves,
+// each owning 16 output rows n and all 64 rows m, one group per stage; the x tile
+// is shared through LDS, a wave's codes and (scale, zero) stay in its registers;
+// loads run two stages ahead in register sets, as buffer loads (rows past M or N
+// and stages past the range read as zero, with no traffic), with an LDS-only
+// barrier so loads stay in flight across it. B fragments are exact fp16 (q - z)
+// while z lies in [-2032, 1024] (one FMA by the scale per output and group); a
+// wave meeting another zero takes the general route for that stage (exact q and
+// z * sum_k x with sum_k x from an MFMA against ones).
+#include <algorithm>
+
+#include "device_utils.h"
+#include "launchers.h"
+
+namespace w4a16 {
+
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int MT = 4;                  // 16-row MFMA tiles of m per workgroup
+constexpr int WAVES = 8;
+constexpr int BM = 16 * MT;            // 64 rows m
+constexpr int BN = 16 * WAVES;         // 128 rows n
+constexpr int kThreads = 64 * WAVES;
+constexpr int XU = BM * 16 / kThreads;  // 16-byte x chunks per thread per stage
+constexpr int R = 2;                   // stages of loads in flight
+constexpr int kBufferFlags = 0x00020000;
+constexpr int kOutOfRange = 1 << 30;
+constexpr int kMaxSplits = 16;
+
+__device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
+
+__device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t c_lo, half2_t c_hi) {
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t w8 = w >> 8;
+  const half2_t p0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + c_lo;
+  const half2_t p1 = __builtin_elementwise_fma(as_half2(and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
+  const half2_t p2 = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) + c_lo;
+  const half2_t p3 = __builtin_elementwise_fma(as_half2(and_or(w8, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
+  const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+  return __builtin_bit_cast(half8_t, v);
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+// Workgroups are dealt to the eight XCDs round-robin; numbering them so that each
+// XCD takes a contiguous run keeps the m-tiles and splits of one weight tile on one L2.
+__device__ __forceinline__ int item_of_block(int id, int nb) {
+  const int xcd = id & 7, slot = id >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return xcd * per + min(xcd, rem) + slot;
+}
+
+struct Stage {
+  u32x4_t x[XU];
+  u32x4_t q;
+  uint16_t s, z;
+};
+
+// grid: tiles_m * tiles_n * S items; item = (n-tile, split, m-tile) with m-tile fastest
+__global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint32_t* __restrict__ qw,
+                                                                 const uint16_t* __restrict__ scales,
+                                                                 const uint16_t* __restrict__ zeros, int M, int N,
+                                                                 int K, int S, int TM, float* __restrict__ part) {
+  __shared__ u32x4_t lx[2][BM][17];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j = lane >> 4, c = lane & 15;
+  const int item = item_of_block(blockIdx.x, gridDim.x);
+  const int tm = item % TM;
+  const int rest = item / TM;
+  const int split = rest % S;
+  const int tn = rest / S;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int G = K >> 7;
+  // this split's groups [g_begin, g_end): the first G % S splits take one more
+  const int base = G / S, extra = G % S;
+  const int g_begin = split * base + min(split, extra);
+  const int gcount = base + (split < extra ? 1 : 0);
+  const int nl = wave * 16 + c;
+
+  const int64_t rows_m = min(M - m0, BM), rows_n = min(N - n0, BN);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x + (int64_t)m0 * K + (int64_t)g_begin * 128, rows_m * K * 2 - (int64_t)g_begin * 256);
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qw + (int64_t)n0 * (K >> 3) + (int64_t)g_begin * 16, rows_n * (K >> 1) - (int64_t)g_begin * 64);
+  const __amdgpu_buffer_rsrc_t rs = rsrc(scales + (int64_t)n0 * G + g_begin, rows_n * G * 2 - (int64_t)g_begin * 2);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(zeros + (int64_t)n0 * G + g_begin, rows_n * G * 2 - (int64_t)g_begin * 2);
+  int xoff[XU];
+#pragma unroll
+  for (int u = 0; u < XU; ++u) xoff[u] = ((t >> 4) + (kThreads / 16) * u) * K * 2 + (t & 15) * 16;
+  const int qo = nl * (K >> 1) + j * 16;
+  const int so = nl * G * 2;
+
+  Stage set[R];
+  // stage g of this split (0 .. gcount-1); stages past the split read as zero
+  auto issue = [&](int g, Stage& r) {
+    const int past = (int)(g >= gcount) * kOutOfRange;
+#pragma unroll
+    for (int u = 0; u < XU; ++u) r.x[u] = load16(rx, xoff[u] + g * 256 + past);
+    r.q = load16(rq, qo + g * 64 + past);
+    r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, so + g * 2 + past, 0, 0);
+    r.z = __builtin_amdgcn_raw_buffer_load_b16(rz, so + g * 2 + past, 0, 0);
+  };
+  auto store = [&](const Stage& r, int b) {
+#pragma unroll
+    for (int u = 0; u < XU; ++u) lx[b][(t >> 4) + (kThreads / 16) * u][t & 15] = r.x[u];
+  };
+
+  float4_t acc[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage& r, int b) {
+    const float d = half_bits_to_float(r.s);
+    const _Float16 zh = __builtin_bit_cast(_Float16, r.z);
+    const float zf = (float)zh;
+    const bool exact = zf >= -2032.0f && zf <= 1024.0f;
+    if (__builtin_amdgcn_ballot_w64(!exact) == 0) {
+      const _Float16 clo = -((_Float16)1024.0f + zh), chi = -((_Float16)64.0f + zh);
+      const half2_t c_lo = {clo, clo}, c_hi = {chi, chi};
+      const half8_t bq[4] = {dequant_word(r.q.x, c_lo, c_hi), dequant_word(r.q.y, c_lo, c_hi),
+                             dequant_word(r.q.z, c_lo, c_hi), dequant_word(r.q.w, c_lo, c_hi)};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(lx[b][16 * mt + c][4 * j + st]), bq[st], a, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, a[i], acc[mt][i]);
+      }
+    } else {
+      const half2_t c_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+      const half2_t c_hi = {(_Float16)-64.0f, (_Float16)-64.0f};
+      const u32x4_t ones_bits = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+      const half8_t ones = as_half8(ones_bits);
+      const half8_t bq[4] = {dequant_word(r.q.x, c_lo, c_hi), dequant_word(r.q.y, c_lo, c_hi),
+                             dequant_word(r.q.z, c_lo, c_hi), dequant_word(r.q.w, c_lo, c_hi)};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float4_t a = {0.f, 0.f, 0.f, 0.f}, sx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+          const half8_t xa = as_half8(lx[b][16 * mt + c][4 * j + st]);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, bq[st], a, 0, 0, 0);
+          sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa, ones, sx, 0, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, __builtin_fmaf(-zf, sx[i], a[i]), acc[mt][i]);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    issue(r, set[r]);
+    __builtin_amdgcn_sched_barrier(0);  // stages stay in issue order: the waits count on it
+  }
+  store(set[0], 0);
+  lds_barrier();
+  for (int g0 = 0; g0 < gcount; g0 += R) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int g = g0 + r;
+      if (g < gcount) compute(set[r], r & 1);
+      __builtin_amdgcn_sched_barrier(0);
+      issue(g + R, set[r]);
+      __builtin_amdgcn_sched_barrier(0);
+      store(set[(r + 1) % R], (r + 1) & 1);
+      lds_barrier();
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load in flight at exit
+
+  // the partial of this split: part[split][m][n]
+  const int n = n0 + nl;
+  if (n < N) {
+    float* p = part + (int64_t)split * M * N;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + 16 * mt + 4 * j + i;
+        if (m < M) p[(int64_t)m * N + n] = acc[mt][i];
+      }
+  }
+}
+
+// y[e] = f16( ((part[0][e] + part[1][e]) + ...) ), four outputs per thread
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int64_t total, int S,
+                                                           uint16_t* __restrict__ y) {
+  const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (e0 >= total) return;
+  if (e0 + 4 <= total && (total & 3) == 0) {
+    float4_t s = *reinterpret_cast<const float4_t*>(part + e0);
+    for (int k = 1; k < S; ++k) {
+      const float4_t v = *reinterpret_cast<const float4_t*>(part + (int64_t)k * total + e0);
+      s += v;
+    }
+    const uint32_t lo = (uint32_t)float_to_half_bits(s[0]) | ((uint32_t)float_to_half_bits(s[1]) << 16);
+    const uint32_t hi = (uint32_t)float_to_half_bits(s[2]) | ((uint32_t)float_to_half_bits(s[3]) << 16);
+    if ((reinterpret_cast<uintptr_t>(y + e0) & 7) == 0) {
+      *reinterpret_cast<uint2*>(y + e0) = make_uint2(lo, hi);
+      return;
+    }
+    y[e0] = (uint16_t)(lo & 0xFFFFu);
+    y[e0 + 1] = (uint16_t)(lo >> 16);
+    y[e0 + 2] = (uint16_t)(hi & 0xFFFFu);
+    y[e0 + 3] = (uint16_t)(hi >> 16);
+    return;
+  }
+  for (int64_t e = e0; e < min(e0 + 4, total); ++e) {
+    float s = part[e];
+    for (int k = 1; k < S; ++k) s += part[(int64_t)k * total + e];
+    y[e] = float_to_half_bits(s);
+  }
+}
+
+int64_t tiles_of(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+
+}  // namespace
+
+int splitk_max_splits() { return kMaxSplits; }
+
+int splitk_default_splits(int64_t M, int64_t N, int64_t K) {
+  // about two workgroups per CU, at most 4 splits (more cost more in partial traffic and
+  // pipeline fill than they gain: measured on the LLaMA2-7B serving shapes), and at least
+  // four groups per split
+  const int64_t tiles = tiles_of(M, N);
+  const int64_t G = K / 128;
+  int64_t s = (512 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, 4);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, G / 4));
+  return (int)std::max<int64_t>(1, s);
+}
+
+int64_t splitk_workspace_floats(int64_t M, int64_t N, int splits) { return (int64_t)splits * M * N; }
+
+hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                         int64_t M, int64_t N, int64_t K, int splits, float* workspace, uint16_t* y,
+                         hipStream_t stream) {
+  const int TM = (int)((M + BM - 1) / BM);
+  const int64_t items = tiles_of(M, N) * splits;
+  hipLaunchKernelGGL(splitk_partial_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, x, qweight, scales,
+                     zeros, (int)M, (int)N, (int)K, splits, TM, workspace);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t total = M * N;
+  const int64_t grid = (total + 1023) / 1024;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, workspace, total, splits, y);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16

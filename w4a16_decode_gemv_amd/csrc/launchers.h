@@ -52,6 +52,15 @@ hipError_t launch_skinny(const uint16_t* x, const uint32_t* qweight, const uint1
                          const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                          hipStream_t stream);
 
+// Split-K MFMA GEMM (4-bit, groups of 128): S partial tiles in a float32 workspace of
+// splitk_workspace_floats(M, N, S) floats, then a fixed-order reduction into y. Needs 1 <= S <= K/128.
+int splitk_max_splits();
+int splitk_default_splits(int64_t M, int64_t N, int64_t K);
+int64_t splitk_workspace_floats(int64_t M, int64_t N, int splits);
+hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                         int64_t M, int64_t N, int64_t K, int splits, float* workspace, uint16_t* y,
+                         hipStream_t stream);
+
 // Tiled MFMA kernel: any M >= 1.
 hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                        const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
