@@ -69,6 +69,10 @@ def parse():
     p.add_argument("--only-gemv", action="store_true", help="time the headline GEMV only (for profilers)")
     p.add_argument("--only-m", type=int, default=0,
                    help="time only the automatic path at this batch M, K = N = 8192 (for profilers)")
+    p.add_argument("--only-serving", default="",
+                   help="time only one LLaMA2-7B serving GEMM, LAYER:M with LAYER in qkvo,gate,down (the 4096->4096, "
+                        "4096->11008, 11008->4096 shapes) and M in 128,256, on the tiled and split-K kernels "
+                        "(for profilers)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the GEMV, run a plain 64 MiB elementwise copy 5 times (counter calibration)")
     return p.parse_args()
@@ -388,6 +392,28 @@ def main():
     w4.load()
     torch.cuda.set_device(0)
     props = torch.cuda.get_device_properties(0)
+
+    if args.only_serving:
+        import synth
+
+        name, mm = args.only_serving.split(":")
+        mm = int(mm)
+        layers = {lname.split("_")[0]: (lid, lname, kk, nn) for lid, (lname, kk, nn) in enumerate(synth.CONFIGS[5]["layers"])}
+        lid, lname, kk, nn = layers[name]
+        b = algorithmic_bytes(mm, nn, kk)
+        L = Layer(w4, torch, 5, lid, nn, kk, mm, copies_for(b))
+        ws = torch.empty(w4.splitk_workspace_bytes(mm, nn, kk, 16) // 4, dtype=torch.float32, device=L.x.device)
+        t_tiled = time_steps_graph(torch, lambda i: L.call(w4, i, 2), args.steps, args.warmup)
+        t_split = time_steps_graph(torch, lambda i: w4.linear_splitk(*L.copies[i % len(L.copies)], workspace=ws,
+                                                                       out=L.y[i % len(L.y)]), args.steps, args.warmup)
+        flop = 2 * mm * nn * kk
+        res = {"layer": lname, "M": mm, "K": kk, "N": nn, "flop": flop, "algorithmic_bytes": b,
+               "tiled_us": t_tiled * 1e3, "splitk_us": t_split * 1e3,
+               "splitk_default_splits": w4.splitk_workspace_bytes(mm, nn, kk, 0) // (4 * mm * nn),
+               "tiled_mfma_util": flop / (t_tiled * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
+               "splitk_mfma_util": flop / (t_split * 1e-3) / 1e12 / PEAK_FP16_TFLOPS}
+        print(json.dumps(res), flush=True)
+        return 0
 
     if args.only_m:
         mm = args.only_m

@@ -211,6 +211,12 @@ def test_splitk_workspace_and_rejects():
     lib = w4.load()
     assert lib.w4a16_linear_splitk_workspace(128, 4096, 4096, 4) == 4 * 128 * 4096 * 4
     assert lib.w4a16_linear_splitk_workspace(128, 4096, 4096, 0) > 0
+    # the default split count (splits = 0): about 512 workgroups of 64 x 128 tiles, rounded up to
+    # a power of two, at most 4, and at least four groups per split
+    for (m, n, k), s in {(128, 4096, 4096): 4, (128, 11008, 4096): 4, (256, 11008, 4096): 2,
+                         (128, 4096, 11008): 4, (4096, 4096, 4096): 1, (128, 4096, 256): 1,
+                         (128, 4096, 1024): 2}.items():
+        assert lib.w4a16_linear_splitk_workspace(m, n, k, 0) == s * m * n * 4, (m, n, k)
     assert lib.w4a16_linear_splitk_workspace(128, 4096, 256, 3) == -1   # more splits than groups
     assert lib.w4a16_linear_splitk_workspace(128, 4096, 4096, 17) == -1
     assert lib.w4a16_linear_splitk_workspace(0, 4096, 4096, 2) == -1

@@ -82,15 +82,6 @@ __device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t c_lo, half2_
   return __builtin_bit_cast(half8_t, v);
 }
 
-// Tiles are numbered so that each of the eight XCDs (workgroups are dealt to them
-// round-robin) takes a contiguous run: the calibration tiles of one weight tile
-// run on one XCD, which then fetches that weight tile into its L2 once.
-__device__ __forceinline__ int tile_of_block(int id, int nb) {
-  const int xcd = id & 7, slot = id >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  return xcd * per + min(xcd, rem) + slot;
-}
-
 // workgroup barrier that orders LDS only: global loads stay in flight across it
 __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -143,7 +134,8 @@ __global__ __launch_bounds__(kThreads) void alpha_loss_kernel(const uint16_t* __
   __shared__ double wsum[WAVES];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
-  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  // the calibration tiles of one weight tile share an XCD
+  const int tile = xcd_contiguous_item(blockIdx.x, gridDim.x);
   const int m0 = (tile % GT) * BM, n0 = (tile / GT) * BN;
   const int G = K >> 7;
   const int nl = wave * 16 + c;  // this lane's output row within the tile
@@ -291,7 +283,8 @@ __global__ __launch_bounds__(kThreads) void output_reference_kernel(const uint16
   __shared__ Lds lds;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
-  const int tile = tile_of_block(blockIdx.x, gridDim.x);
+  // the calibration tiles of one weight tile share an XCD
+  const int tile = xcd_contiguous_item(blockIdx.x, gridDim.x);
   const int m0 = (tile % GT) * BM, n0 = (tile / GT) * BN;
   const int G = K >> 7;
   const int nl = wave * 16 + c;

@@ -86,4 +86,15 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
+// Workgroups are dealt to the chip's eight XCDs round-robin by linear block id.
+// Renumbering them so that each XCD takes a contiguous run of work items keeps
+// neighbouring items (the m-tiles and K-splits of one weight tile) on one XCD, where
+// they share its L2, instead of fetching the same codes once per XCD. A bijection on
+// [0, nb) for any nb.
+__device__ __forceinline__ int xcd_contiguous_item(int id, int nb) {
+  const int xcd = id & 7, slot = id >> 3;
+  const int per = nb >> 3, rem = nb & 7;
+  return xcd * per + min(xcd, rem) + slot;
+}
+
 }  // namespace w4a16

@@ -82,8 +82,11 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;  // slot group, row within the wave's 16
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  // item = n-tile * TM + m-tile: the m-tiles of one weight tile run on one XCD
+  const int TM = (M + BM - 1) / BM;
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
+  const int m0 = (item % TM) * BM;
+  const int n0 = (item / TM) * BN;
   const int G = K >> 7;
   const int KX = K >> 3;    // 16-byte x chunks per row
   const int KQ = K >> 5;    // 16-byte code chunks per row
@@ -284,8 +287,11 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  // item = n-tile * TM + m-tile: the m-tiles of one weight tile run on one XCD
+  const int TM = (M + BM - 1) / BM;
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
+  const int m0 = (item % TM) * BM;
+  const int n0 = (item / TM) * BN;
   const int S = K >> 7;            // stages
   const int G = K >> (5 + gsh);    // groups per row
   const int KX = K >> 3;
@@ -458,7 +464,7 @@ template <int MB, int BITS>
 hipError_t launch_var(const uint16_t* x, const uint32_t* qweight, const void* scales, const uint16_t* zeros,
                       int64_t M, int64_t N, int64_t K, int gsh, const Nf4Table& table, uint16_t* y,
                       hipStream_t stream) {
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
+  const dim3 grid((unsigned)(((N + BN - 1) / BN) * ((M + 16 * MB - 1) / (16 * MB))));
   hipLaunchKernelGGL((mfma_var_kernel<MB, BITS>), grid, dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(x),
                      qweight, scales, zeros, (int)M, (int)N, (int)K, gsh, table, y);
   return hipGetLastError();
@@ -476,7 +482,7 @@ hipError_t launch_var_m(const uint16_t* x, const uint32_t* qweight, const void* 
 template <int MB>
 hipError_t launch_mb(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                      int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + BN - 1) / BN), (unsigned)((M + 16 * MB - 1) / (16 * MB)));
+  const dim3 grid((unsigned)(((N + BN - 1) / BN) * ((M + 16 * MB - 1) / (16 * MB))));
   hipLaunchKernelGGL(mfma_kernel<MB>, grid, dim3(kThreads), 0, stream, reinterpret_cast<const uint4*>(x),
                      reinterpret_cast<const uint4*>(qweight), scales, zeros, (int)M, (int)N, (int)K, y);
   return hipGetLastError();

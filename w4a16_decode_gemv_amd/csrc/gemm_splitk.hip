@@ -72,14 +72,6 @@ __device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Workgroups are dealt to the eight XCDs round-robin; numbering them so that each
-// XCD takes a contiguous run keeps the m-tiles and splits of one weight tile on one L2.
-__device__ __forceinline__ int item_of_block(int id, int nb) {
-  const int xcd = id & 7, slot = id >> 3;
-  const int per = nb >> 3, rem = nb & 7;
-  return xcd * per + min(xcd, rem) + slot;
-}
-
 struct Stage {
   u32x4_t x[XU];
   u32x4_t q;
@@ -95,7 +87,7 @@ __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t
   __shared__ u32x4_t lx[2][BM][17];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
-  const int item = item_of_block(blockIdx.x, gridDim.x);
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
   const int tm = item % TM;
   const int rest = item / TM;
   const int split = rest % S;
@@ -251,13 +243,15 @@ int64_t tiles_of(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN -
 int splitk_max_splits() { return kMaxSplits; }
 
 int splitk_default_splits(int64_t M, int64_t N, int64_t K) {
-  // about two workgroups per CU, at most 4 splits (more cost more in partial traffic and
-  // pipeline fill than they gain: measured on the LLaMA2-7B serving shapes), and at least
-  // four groups per split
+  // about two workgroups per CU, rounded up to a power of two (3 splits measured slower than
+  // 4 on the 4096 -> 11008 layer at M = 128), at most 4 splits (more cost more in partial
+  // traffic and pipeline fill than they gain: measured on the LLaMA2-7B serving shapes), and
+  // at least four groups per split
   const int64_t tiles = tiles_of(M, N);
   const int64_t G = K / 128;
-  int64_t s = (512 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, 4);
+  const int64_t want = (512 + tiles - 1) / tiles;
+  int64_t s = 1;
+  while (s < want && s < 4) s <<= 1;
   s = std::min<int64_t>(s, std::max<int64_t>(1, G / 4));
   return (int)std::max<int64_t>(1, s);
 }
