@@ -28,9 +28,14 @@ constexpr int64_t kMaxN = int64_t(1) << 24;
 constexpr int64_t kMaxM = int64_t(1) << 16;
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;  // one workgroup per loss tile, 1-D grid
-// automatic dispatch: the GEMV kernel up to this M, the small-batch MFMA kernel up to
-// skinny_max_m(), the tiled MFMA kernel beyond (hand-off points from the M sweep at K = N = 8192)
-constexpr int64_t kAutoGemvMaxM = 1;
+// automatic dispatch, from sweeps on MI355X over the LLaMA projection shapes: the GEMV
+// kernel at M = 1, and at M = 2 on layers of at least 2^25 weights with K <= 16384 (there
+// the GEMV's doubled dot work still hides under the weight stream; on 4096 x 4096 its
+// 2-wave workgroups leave one wave per SIMD, and above K = 16384 its tiles shrink); the
+// small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA kernel beyond
+bool auto_gemv(int64_t M, int64_t N, int64_t K) {
+  return M == 1 || (M == 2 && K <= 16384 && N * K >= (int64_t(1) << 25));
+}
 
 w4a16_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
@@ -133,7 +138,7 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   }
   int32_t kernel = path;
   if (path == 0) {
-    if (M <= kAutoGemvMaxM && w4a16::gemv_supports(M, K))
+    if (auto_gemv(M, N, K) && w4a16::gemv_supports(M, K))
       kernel = 1;
     else if (M <= w4a16::skinny_max_m())
       kernel = 3;

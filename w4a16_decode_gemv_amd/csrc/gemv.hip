@@ -61,11 +61,15 @@ constexpr int kMaxM = 8;
 // Rows per workgroup. Measured on MI355X at K = N = 8192: for M = 1, 8 rows
 // per 4-wave workgroup (1024 workgroups, four per CU) streams better than 16
 // rows (512 workgroups) or 4 rows (2048 workgroups, where the per-workgroup x
-// reads double); for M >= 2 the x reads grow with M, and R * M * PPT <= 16
-// keeps more rows sharing them.
-template <int M, int PPT>
+// reads double): 8.31 against 8.53 us. On smaller layers 8 rows leave fewer
+// than 16 waves per CU (a workgroup has one wave per 2048 inputs of K), and
+// there 4 rows win: 4.08 against 4.75 us at 4096 x 4096, 6.47 against 7.17 at
+// 4096 -> 11008, 6.90 against 7.51 at 11008 -> 4096 ("Narrow" tiles). For
+// M >= 2 the x reads grow with M, and R * M * PPT <= 16 keeps more rows
+// sharing them.
+template <int M, int PPT, bool Narrow = false>
 struct Tile {
-  static constexpr int kBudget = (M == 1) ? 8 : 16;
+  static constexpr int kBudget = (M == 1) ? (Narrow ? 4 : 8) : 16;
   static constexpr int R = (kBudget / (M * PPT)) > 0 ? (kBudget / (M * PPT)) : 1;
   static constexpr int V = R * M;
 };
@@ -81,13 +85,13 @@ __device__ __forceinline__ half2_t q_pair_hi(uint32_t w) {  // nibbles at bits 4
                                    (half2_t){(_Float16)-64.0f, (_Float16)-64.0f});
 }
 
-template <int M, int PPT>
+template <int M, int PPT, bool Narrow>
 __global__ __launch_bounds__(kMaxThreads) void gemv_kernel(const uint4* __restrict__ x, const u32x4_t* __restrict__ qw,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ zeros, int N, int K,
                                                            uint16_t* __restrict__ y) {
-  constexpr int R = Tile<M, PPT>::R;
-  constexpr int V = Tile<M, PPT>::V;
+  constexpr int R = Tile<M, PPT, Narrow>::R;
+  constexpr int V = Tile<M, PPT, Narrow>::V;
   constexpr int E = R * PPT * 16;        // (scale, zero) pairs one wave needs: R rows x PPT slots x 16 groups
   constexpr int NE = (E + 63) / 64;      // ... per lane
   extern __shared__ uint32_t lds[];      // per wave: E staged pairs, then V partial sums
@@ -509,15 +513,15 @@ Launch plan(int64_t K) {
   return {ppt, t};
 }
 
-template <int M, int PPT>
+template <int M, int PPT, bool Narrow = false>
 hipError_t launch_mp(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                      int64_t N, int64_t K, uint16_t* y, int threads, hipStream_t stream) {
-  constexpr int R = Tile<M, PPT>::R;
-  constexpr int V = Tile<M, PPT>::V;
+  constexpr int R = Tile<M, PPT, Narrow>::R;
+  constexpr int V = Tile<M, PPT, Narrow>::V;
   constexpr int E = R * PPT * 16;
   const size_t lds = (size_t)(threads / 64) * (E + V) * 4;
   const int grid = (int)((N + R - 1) / R);
-  hipLaunchKernelGGL((gemv_kernel<M, PPT>), dim3(grid), dim3(threads), lds, stream,
+  hipLaunchKernelGGL((gemv_kernel<M, PPT, Narrow>), dim3(grid), dim3(threads), lds, stream,
                      reinterpret_cast<const uint4*>(x), reinterpret_cast<const u32x4_t*>(qweight), scales, zeros,
                      (int)N, (int)K, y);
   return hipGetLastError();
@@ -528,7 +532,13 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const uint16_t* 
                     int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const Launch l = plan(K);
   switch (l.ppt) {
-    case 1: return launch_mp<M, 1>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+    case 1:
+      if constexpr (M == 1) {
+        // narrow tiles when the default ones would give fewer than 16 waves per CU
+        const int64_t waves = (N + Tile<1, 1>::R - 1) / Tile<1, 1>::R * (l.threads / 64);
+        if (waves < 16 * 256) return launch_mp<1, 1, true>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      }
+      return launch_mp<M, 1>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
     case 2:
       if constexpr (M <= 4) return launch_mp<M, 2>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
       break;

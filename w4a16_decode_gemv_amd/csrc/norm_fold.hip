@@ -16,8 +16,15 @@
 // accumulated in a fixed order (per thread in k order, then a fixed tree), so
 // results are reproducible run to run.
 //
-// One workgroup per row; the row is read twice (the second read is an L2 hit),
-// so registers do not bound K.
+// Work split: a row is cut into S slices of its 16-byte chunks, one workgroup per
+// (row, slice). Every workgroup of a row forms the whole sum of squares in the same
+// fixed order (so r is bit-identical across them) and writes its own slice. Small
+// batches (M < 64) take S = ceil(chunks / 256), one chunk per thread: the float64
+// division and rounding work of a row then spreads over several CUs instead of
+// queueing on one. Larger batches take S = 1 and loop. A thread's first chunk of
+// the second pass, with its gamma and s, is loaded before the reduction, so the
+// latency of those loads overlaps the first pass; that chunk of h is kept from the
+// first pass.
 #include "device_utils.h"
 #include "launchers.h"
 
@@ -26,20 +33,39 @@ namespace w4a16 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int64_t kSplitBelowM = 64;
 
 __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* __restrict__ h,
                                                                 const uint16_t* __restrict__ gamma,
-                                                                const float* __restrict__ s, int K, double eps,
-                                                                u32x4_t* __restrict__ out) {
+                                                                const float* __restrict__ s, int K, int S,
+                                                                double eps, u32x4_t* __restrict__ out) {
   __shared__ double wsum[kThreads / 64];
   __shared__ double rrow;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int row = blockIdx.x / S, slice = blockIdx.x - row * S;
   const int chunks = K >> 3;  // 8 fp16 per 16-byte chunk
-  const int64_t base = (int64_t)blockIdx.x * chunks;
+  // slices are whole multiples of kThreads chunks, so thread t's first chunk c0 + t is one
+  // the first pass below visits (c = t, t + kThreads, ...)
+  const int per = ((chunks + S - 1) / S + kThreads - 1) / kThreads * kThreads;
+  const int c0 = slice * per, c1 = min(chunks, c0 + per);
+  const int64_t base = (int64_t)row * chunks;
+
+  // this thread's first chunk of the second pass: gamma and s now, h from the first pass
+  const int cp = c0 + t;
+  const bool has = cp < c1;
+  uint16_t gp[8];
+  float sp[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    gp[e] = has ? gamma[8 * cp + e] : (uint16_t)0;
+    sp[e] = (has && s != nullptr) ? s[8 * cp + e] : 1.0f;
+  }
+  u32x4_t hp = {0u, 0u, 0u, 0u};
 
   double acc = 0.0;
   for (int c = t; c < chunks; c += kThreads) {
     const u32x4_t v = h[base + c];
+    if (c == cp) hp = v;
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -64,8 +90,23 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* _
   __syncthreads();
   const double r = rrow;
 
-  for (int c = t; c < chunks; c += kThreads) {
-    const u32x4_t v = h[base + c];
+  for (int c = cp; c < c1; c += kThreads) {
+    u32x4_t v = hp;
+    uint16_t g[8];
+    float sv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      g[e] = gp[e];
+      sv[e] = sp[e];
+    }
+    if (c != cp) {
+      v = h[base + c];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        g[e] = gamma[8 * c + e];
+        sv[e] = s != nullptr ? s[8 * c + e] : 1.0f;
+      }
+    }
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
 #pragma unroll
@@ -73,10 +114,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* _
       uint16_t res[2];
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int k = 8 * c + 2 * i + hh;
+        const int e = 2 * i + hh;
         const double hv = (double)half_bits_to_float((uint16_t)(hh ? (w[i] >> 16) : (w[i] & 0xFFFFu)));
-        double val = (hv * r) * (double)half_bits_to_float(gamma[k]);
-        if (s != nullptr) val = val / (double)s[k];
+        double val = (hv * r) * (double)half_bits_to_float(g[e]);
+        if (s != nullptr) val = val / (double)sv[e];
         res[hh] = f64_to_f16_rne(val);
       }
       o[i] = (uint32_t)res[0] | ((uint32_t)res[1] << 16);
@@ -89,8 +130,10 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* _
 
 hipError_t launch_rmsnorm_fold(const uint16_t* h, const uint16_t* gamma, const float* s, int64_t M, int64_t K,
                                double eps, uint16_t* x_s, hipStream_t stream) {
-  hipLaunchKernelGGL(rmsnorm_fold_kernel, dim3((unsigned)M), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const u32x4_t*>(h), gamma, s, (int)K, eps, reinterpret_cast<u32x4_t*>(x_s));
+  const int64_t chunks = K / 8;
+  const int S = M < kSplitBelowM ? (int)((chunks + kThreads - 1) / kThreads) : 1;
+  hipLaunchKernelGGL(rmsnorm_fold_kernel, dim3((unsigned)(M * S)), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const u32x4_t*>(h), gamma, s, (int)K, S, eps, reinterpret_cast<u32x4_t*>(x_s));
   return hipGetLastError();
 }
 
