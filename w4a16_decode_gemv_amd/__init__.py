@@ -108,6 +108,39 @@ def _dev_tensor(t, dtype, name, ndim):
     return t
 
 
+def _out(out, shape, dtype, like, name="out"):
+    """A new output tensor, or the caller's, checked: a contiguous GPU tensor of this dtype
+    and shape on the device of `like` (the kernels write through its pointer)."""
+    torch = _torch()
+    shape = tuple(int(d) for d in shape)
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    out = _dev_tensor(out, dtype, name, len(shape))
+    if tuple(out.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape} (got {tuple(out.shape)})")
+    if out.device != like.device:
+        raise ValueError(f"{name} must be on {like.device} (got {out.device})")
+    return out
+
+
+def _workspace(ws, dtype, like):
+    """A caller's workspace: a contiguous GPU tensor of this dtype on the device of `like`
+    (its size is checked by the library)."""
+    torch = _torch()
+    if not isinstance(ws, torch.Tensor) or ws.device != like.device or ws.dtype != dtype or not ws.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous {dtype} tensor on {like.device}")
+    return ws
+
+
+def _outs(out, count, name):
+    if out is None:
+        return (None,) * count
+    out = tuple(out)
+    if len(out) != count:
+        raise ValueError(f"{name} out must hold {count} tensors")
+    return out
+
+
 def _stream(t):
     torch = _torch()
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
@@ -119,7 +152,7 @@ def channel_scale(x_cal, alpha=0.5, out=None):
     lib = load()
     x_cal = _dev_tensor(x_cal, torch.float16, "x_cal", 2)
     t_, k = x_cal.shape
-    s = torch.empty(k, dtype=torch.float32, device=x_cal.device) if out is None else out
+    s = _out(out, (k,), torch.float32, x_cal)
     _check(lib.awq_channel_scale(x_cal.data_ptr(), t_, k, float(alpha), s.data_ptr(), _stream(x_cal)))
     return s
 
@@ -133,7 +166,7 @@ def scale_input(x, s, out=None):
     m, k = x.shape
     if s.shape[0] != k:
         raise ValueError("s must have K entries")
-    xs = torch.empty_like(x) if out is None else out
+    xs = _out(out, (m, k), torch.float16, x)
     _check(lib.awq_scale_input(x.data_ptr(), s.data_ptr(), m, k, xs.data_ptr(), _stream(x)))
     return xs
 
@@ -153,7 +186,7 @@ def rmsnorm_fold(h, gamma, s=None, eps=1e-5, out=None):
         if s.shape[0] != k:
             raise ValueError("s must have K entries")
         sp = s.data_ptr()
-    xs = torch.empty_like(h) if out is None else out
+    xs = _out(out, (m, k), torch.float16, h)
     _check(lib.awq_rmsnorm_fold(h.data_ptr(), gamma.data_ptr(), sp, m, k, float(eps), xs.data_ptr(), _stream(h)))
     return xs
 
@@ -174,14 +207,12 @@ def quantize_pack(W, s=None, bits=4, group=GROUP, out=None):
         if s.shape[0] != k:
             raise ValueError("s must have K entries")
         sp = s.data_ptr()
-    if out is None:
-        g = max(k // group, 1)
-        words = k // 8 if bits == 4 else 3 * (k // 32)
-        qweight = torch.empty((n, max(words, 1)), dtype=torch.int32, device=W.device)
-        scales = torch.empty((n, g), dtype=torch.float16, device=W.device)
-        zeros = torch.empty((n, g), dtype=torch.float16, device=W.device)
-    else:
-        qweight, scales, zeros = out
+    g = max(k // group, 1)
+    words = k // 8 if bits == 4 else 3 * (k // 32)
+    o = _outs(out, 3, "quantize_pack")
+    qweight = _out(o[0], (n, max(words, 1)), torch.int32, W, "qweight")
+    scales = _out(o[1], (n, g), torch.float16, W, "scales")
+    zeros = _out(o[2], (n, g), torch.float16, W, "zeros")
     _check(lib.awq_quantize_pack(W.data_ptr(), sp, n, k, bits, group, qweight.data_ptr(), scales.data_ptr(),
                                  zeros.data_ptr(), _stream(W)))
     return qweight, scales, zeros
@@ -209,7 +240,8 @@ def linear_splitk(x, qweight, scales, zeros, splits=0, workspace=None, out=None,
         raise ValueError("qweight must be [N][K/8] and scales/zeros [N][K/group]")
     if workspace is None:
         workspace = torch.empty(splitk_workspace_bytes(m, n, k, splits) // 4, dtype=torch.float32, device=x.device)
-    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    workspace = _workspace(workspace, torch.float32, x)
+    y = _out(out, (m, n), torch.float16, x)
     _check(lib.w4a16_linear_splitk(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k,
                                    group, splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    y.data_ptr(), _stream(x)))
@@ -229,13 +261,11 @@ def quantize_pack_sym(W, s=None, bits=4, group=GROUP, out=None):
         if s.shape[0] != k:
             raise ValueError("s must have K entries")
         sp = s.data_ptr()
-    if out is None:
-        words = k // 8 if bits == 4 else 3 * (k // 32)
-        qweight = torch.empty((n, max(words, 1)), dtype=torch.int32, device=W.device)
-        scales = torch.empty((n, max(k // group, 1)), dtype=torch.float16, device=W.device)
-        zeros = torch.empty((n, max(k // group, 1)), dtype=torch.float16, device=W.device)
-    else:
-        qweight, scales, zeros = out
+    words = k // 8 if bits == 4 else 3 * (k // 32)
+    o = _outs(out, 3, "quantize_pack_sym")
+    qweight = _out(o[0], (n, max(words, 1)), torch.int32, W, "qweight")
+    scales = _out(o[1], (n, max(k // group, 1)), torch.float16, W, "scales")
+    zeros = _out(o[2], (n, max(k // group, 1)), torch.float16, W, "zeros")
     _check(lib.awq_quantize_pack_sym(W.data_ptr(), sp, n, k, bits, group, qweight.data_ptr(), scales.data_ptr(),
                                      zeros.data_ptr(), _stream(W)))
     return qweight, scales, zeros
@@ -263,11 +293,9 @@ def nf4_quantize_pack(W, s=None, block=NF4_BLOCK, out=None):
         if s.shape[0] != k:
             raise ValueError("s must have K entries")
         sp = s.data_ptr()
-    if out is None:
-        qweight = torch.empty((n, max(k // 8, 1)), dtype=torch.int32, device=W.device)
-        absmax = torch.empty((n, max(k // block, 1)), dtype=torch.float32, device=W.device)
-    else:
-        qweight, absmax = out
+    o = _outs(out, 2, "nf4_quantize_pack")
+    qweight = _out(o[0], (n, max(k // 8, 1)), torch.int32, W, "qweight")
+    absmax = _out(o[1], (n, max(k // block, 1)), torch.float32, W, "absmax")
     _check(lib.nf4_quantize_pack(W.data_ptr(), sp, n, k, block, qweight.data_ptr(), absmax.data_ptr(), _stream(W)))
     return qweight, absmax
 
@@ -285,7 +313,7 @@ def nf4_linear(x, qweight, absmax, block=NF4_BLOCK, out=None, path=PATH_AUTO):
         raise ValueError("qweight must be [N][K/8]")
     if tuple(absmax.shape) != (n, k // block):
         raise ValueError("absmax must be [N][K/block]")
-    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    y = _out(out, (m, n), torch.float16, x)
     _check(lib.nf4_linear_path(path, x.data_ptr(), qweight.data_ptr(), absmax.data_ptr(), m, n, k, block,
                                y.data_ptr(), _stream(x)))
     return y
@@ -309,7 +337,7 @@ def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO, bit
         raise ValueError("qweight must be [N][K/8] (4-bit) or [N][3K/32] (3-bit)")
     if scales.shape != zeros.shape or scales.shape[0] != n or scales.shape[1] * group != k:
         raise ValueError("scales/zeros must be [N][K/group]")
-    y = torch.empty((m, n), dtype=torch.float16, device=x.device) if out is None else out
+    y = _out(out, (m, n), torch.float16, x)
     args = (x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k, group, y.data_ptr(),
             _stream(x))
     if bits == 4:
@@ -338,7 +366,7 @@ def output_reference(x, W, out=None):
     n = W.shape[0]
     if W.shape[1] != k:
         raise ValueError("x must be [T][K] and W [N][K]")
-    y = torch.empty((t_, n), dtype=torch.float32, device=x.device) if out is None else out
+    y = _out(out, (t_, n), torch.float32, x)
     _check(lib.awq_output_reference(x.data_ptr(), W.data_ptr(), t_, n, k, y.data_ptr(), _stream(x)))
     return y
 
@@ -361,7 +389,8 @@ def alpha_loss(x_s, qweight, scales, zeros, y_ref, group=GROUP, workspace=None, 
         raise ValueError("y_ref must be [T][N]")
     if workspace is None:
         workspace = torch.empty(alpha_loss_workspace(t_, n), dtype=torch.float64, device=x_s.device)
-    loss = torch.empty(1, dtype=torch.float64, device=x_s.device) if out is None else out
+    workspace = _workspace(workspace, torch.float64, x_s)
+    loss = _out(out, (1,), torch.float64, x_s)
     _check(lib.awq_alpha_loss(x_s.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(),
                               y_ref.data_ptr(), t_, n, k, group, workspace.data_ptr(), workspace.numel(),
                               loss.data_ptr(), _stream(x_s)))
