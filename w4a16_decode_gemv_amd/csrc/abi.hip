@@ -29,12 +29,12 @@ constexpr int64_t kMaxM = int64_t(1) << 16;
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;  // one workgroup per loss tile, 1-D grid
 // automatic dispatch, from sweeps on MI355X over the LLaMA projection shapes: the GEMV
-// kernel at M = 1, and at M = 2 on layers of at least 2^25 weights with K <= 16384 (there
+// kernel at M = 1, and at M = 2 on layers of at least 2^25 weights with K <= 32768 (there
 // the GEMV's doubled dot work still hides under the weight stream; on 4096 x 4096 its
-// 2-wave workgroups leave one wave per SIMD, and above K = 16384 its tiles shrink); the
-// small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA kernel beyond
+// 2-wave workgroups leave one wave per SIMD, and above K = 32768 a thread holds several
+// pieces); the small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA kernel beyond
 bool auto_gemv(int64_t M, int64_t N, int64_t K) {
-  return M == 1 || (M == 2 && K <= 16384 && N * K >= (int64_t(1) << 25));
+  return M == 1 || (M == 2 && K <= 32768 && N * K >= (int64_t(1) << 25));
 }
 
 w4a16_status hip_result(hipError_t e, const char* what) {

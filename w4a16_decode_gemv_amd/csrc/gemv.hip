@@ -56,11 +56,12 @@ namespace w4a16 {
 namespace {
 
 constexpr int kMaxThreads = 512;
-// At M = 1 a workgroup may have up to 1024 threads when that gives every thread a single
-// piece (K <= 32768). Measured on MI355X against two pieces per thread in 512 threads:
-// 19.5 against 21.5 us at K = 22016, N = 8192 and 24.5 against 27.2 us at K = 32768
-// (25.9 against 25.5 us at K = 28672).
-constexpr int kMaxThreadsM1 = 1024;
+// At M <= 2 a workgroup may have up to 1024 threads when that gives every thread a
+// single piece (K <= 32768). Measured on MI355X against two pieces per thread in 512
+// threads, N = 8192: at M = 1, 19.5 against 21.5 us at K = 22016 and 24.5 against 27.2
+// us at K = 32768 (25.9 against 25.5 us at K = 28672); at M = 2, 28.8 against 39.8 us at
+// K = 22016 and 34.0 against 41.9 us at K = 28672.
+constexpr int kMaxThreadsOnePiece = 1024;
 constexpr int kMaxM = 8;
 
 // Rows per workgroup. Measured on MI355X at K = N = 8192: for M = 1, 8 rows
@@ -91,7 +92,7 @@ __device__ __forceinline__ half2_t q_pair_hi(uint32_t w) {  // nibbles at bits 4
 }
 
 template <int M, int PPT, bool Narrow>
-__global__ __launch_bounds__(M == 1 && PPT == 1 ? kMaxThreadsM1 : kMaxThreads) void gemv_kernel(const uint4* __restrict__ x, const u32x4_t* __restrict__ qw,
+__global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThreads) void gemv_kernel(const uint4* __restrict__ x, const u32x4_t* __restrict__ qw,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ zeros, int N, int K,
                                                            uint16_t* __restrict__ y) {
@@ -538,7 +539,7 @@ hipError_t launch_mp(const uint16_t* x, const uint32_t* qweight, const uint16_t*
 template <int M>
 hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                     int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  const Launch l = plan(K, M == 1 ? kMaxThreadsM1 : kMaxThreads);
+  const Launch l = plan(K, M <= 2 ? kMaxThreadsOnePiece : kMaxThreads);
   switch (l.ppt) {
     case 1:
       if constexpr (M == 1) {
