@@ -476,6 +476,9 @@ hipError_t launch_var_m(const uint16_t* x, const uint32_t* qweight, const void* 
                         hipStream_t stream) {
   if (M <= 16) return launch_var<1, BITS>(x, qweight, scales, zeros, M, N, K, gsh, table, y, stream);
   if (M <= 32) return launch_var<2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, table, y, stream);
+  // 32-row tiles while 64-row ones would give fewer than two workgroups per CU (as launch_mfma)
+  const int64_t tiles64 = ((M + 63) / 64) * ((N + BN - 1) / BN);
+  if (tiles64 < 512) return launch_var<2, BITS>(x, qweight, scales, zeros, M, N, K, gsh, table, y, stream);
   return launch_var<4, BITS>(x, qweight, scales, zeros, M, N, K, gsh, table, y, stream);
 }
 
