@@ -479,6 +479,22 @@ def main():
         "kernel_us": ms * 1e3,
         "timing": f"HIP events around one graph replay of the {args.steps} timed back-to-back GEMV launches",
     }
+    # the single-launch read floor of the same bytes: one plain read with the GEMV's access
+    # pattern over the same number of rotating copies (a measurement aid of the library)
+    floor_buf = torch.empty((len(layer.copies), nbytes // 4), dtype=torch.int32, device="cuda:0")
+    floor_buf.fill_(0)
+    floor_sink = w4.stream_read(floor_buf[0])
+    floor_ms = time_steps_graph(torch, lambda i: w4.stream_read(floor_buf[i % len(layer.copies)], floor_sink),
+                                args.steps, args.warmup)
+    out["read_floor"] = {
+        "us_per_call": floor_ms * 1e3,
+        "GB_s": nbytes / (floor_ms * 1e-3) / 1e9,
+        "gemv_fraction_of_floor": floor_ms / ms,
+        "bytes": nbytes,
+        "note": "one launch reading the same bytes with the GEMV's access pattern (w4a16_stream_read), "
+                "timed like the GEMV: the practical single-launch ceiling on this device",
+    }
+    del floor_buf
     eager_ms = time_back_to_back(torch, fn, args.steps, args.warmup)
     avg_ms, med_ms = time_per_launch(torch, fn, min(args.steps, 400))
     graph_ms = time_graph(torch, fn, 200)

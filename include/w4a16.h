@@ -380,6 +380,29 @@ w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, c
 /* Largest M that the GEMV kernel (w4a16_linear_path path 1) accepts. */
 int32_t w4a16_gemv_max_m(void);
 
+/*
+ * w4a16_stream_read - a measurement aid, not part of the method. One launch reads
+ * `bytes` of `buf` once, with the access pattern of the GEMV's weight stream (16-byte
+ * non-temporal loads, 1 KB of contiguous memory per wave and load, every load of a
+ * thread issued before any is used), and does no arithmetic beyond an XOR per thread.
+ * Timed beside w4a16_linear on the same number of bytes, it gives the single-launch
+ * floor of the weight stream on the machine at hand (the sources' point that decode is
+ * bound by reading the weights: CMU guide, "where the speed comes from").
+ * Split: with P = bytes / 16 pieces, W = max(min(1024, ceil(P / 256)), ceil(P / 4096)),
+ * chunk = ceil(P / W); workgroup b (of ceil(P / chunk)) reads pieces
+ * [b * chunk, min((b + 1) * chunk, P)), its 256 threads t, t + 256, ... of them.
+ * buf: device memory, 16-byte aligned, bytes > 0 and a multiple of 16. sink: device
+ * memory of w4a16_stream_read_sink_bytes(bytes) bytes, 4-byte aligned; workgroup b
+ * writes sink[b] = W4A16_STREAM_READ_MAGIC only if the XOR of its thread's words equals
+ * that value, and writes nothing otherwise. Errors: W4A16_ERR_NULL, W4A16_ERR_SHAPE
+ * (bytes), W4A16_ERR_ALIGN, W4A16_ERR_HIP; checked before any HIP call.
+ */
+#define W4A16_STREAM_READ_MAGIC 0x5EAD5EADu
+w4a16_status w4a16_stream_read(const void* buf, int64_t bytes, void* sink, void* stream);
+
+/* Bytes of sink that w4a16_stream_read needs for `bytes` (-1 if bytes is not accepted). */
+int64_t w4a16_stream_read_sink_bytes(int64_t bytes);
+
 #ifdef __cplusplus
 }
 #endif

@@ -257,3 +257,24 @@ def test_library_links_no_oracle_and_no_torch():
     out = subprocess.run(["ldd", w4.LIB_PATH], capture_output=True, text=True).stdout
     assert "torch" not in out and "python" not in out
     assert ctypes.CDLL(w4.LIB_PATH) is not None
+
+
+def test_stream_read_sizes_and_rejects():
+    lib = w4.load()
+    vp = ctypes.c_void_p
+    # one word per workgroup: W = max(min(1024, ceil(P/256)), ceil(P/4096)) workgroups of
+    # ceil(P/W) pieces, P = bytes/16
+    assert lib.w4a16_stream_read_sink_bytes(32768) == 4 * 8
+    assert lib.w4a16_stream_read_sink_bytes(32768 + 16) == 4 * 9
+    assert lib.w4a16_stream_read_sink_bytes(16) == 4
+    assert lib.w4a16_stream_read_sink_bytes(35684352) == 4 * 1024  # the headline layer's bytes, 2178 pieces each
+    assert lib.w4a16_stream_read_sink_bytes(1 << 30) == 4 * 16384  # 4096 pieces per workgroup at most
+    assert lib.w4a16_stream_read_sink_bytes(0) == -1
+    assert lib.w4a16_stream_read_sink_bytes(24) == -1
+    buf, sink = vp(1 << 20), vp(1 << 21)
+    assert lib.w4a16_stream_read(None, 4096, sink, None) == w4.ERR_NULL
+    assert lib.w4a16_stream_read(buf, 4096, None, None) == w4.ERR_NULL
+    assert lib.w4a16_stream_read(buf, 0, sink, None) == w4.ERR_SHAPE
+    assert lib.w4a16_stream_read(buf, 4100, sink, None) == w4.ERR_SHAPE
+    assert lib.w4a16_stream_read(vp((1 << 20) + 8), 4096, sink, None) == w4.ERR_ALIGN
+    assert lib.w4a16_stream_read(buf, 4096, vp((1 << 21) + 2), None) == w4.ERR_ALIGN

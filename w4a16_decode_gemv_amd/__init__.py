@@ -64,6 +64,8 @@ def load():
         "nf4_linear_path": ([i32, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_output_reference": ([vp, vp, i64, i64, i64, vp, vp], i32),
         "awq_alpha_loss": ([vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
+        "w4a16_stream_read_sink_bytes": ([i64], i64),
+        "w4a16_stream_read": ([vp, i64, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -78,7 +80,7 @@ def exported_symbols():
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
             "w4a16_linear_path", "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
             "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
-            "awq_alpha_loss"]
+            "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read"]
 
 
 def _check(status):
@@ -426,6 +428,27 @@ def search_alpha(x_cal, W, grid=ALPHA_GRID):
     host = losses.cpu().tolist()
     best = min(range(len(host)), key=lambda i: (host[i], i))  # the first index of the minimum
     return losses, grid[best]
+
+
+STREAM_READ_MAGIC = 0x5EAD5EAD
+
+
+def stream_read(buf, sink=None):
+    """Measurement aid: one launch that reads `buf` once with the GEMV's access pattern.
+    buf: any contiguous GPU tensor whose size is a multiple of 16 bytes. Returns the sink
+    (int32, one word per workgroup; a word is set to STREAM_READ_MAGIC only where a
+    thread's XOR of its words equals it)."""
+    torch = _torch()
+    lib = load()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    words = int(lib.w4a16_stream_read_sink_bytes(nbytes))
+    if words < 0:
+        raise ValueError("buf must hold a positive multiple of 16 bytes")
+    sink = _out(sink, (words // 4,), torch.int32, buf, "sink")
+    _check(lib.w4a16_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)))
+    return sink
 
 
 def gemv_max_m():

@@ -180,6 +180,21 @@ const char* w4a16_last_error(void) { return g_last_error; }
 
 int32_t w4a16_gemv_max_m(void) { return w4a16::gemv_max_m(); }
 
+int64_t w4a16_stream_read_sink_bytes(int64_t bytes) {
+  if (bytes <= 0 || bytes % 16 != 0) return -1;
+  return w4a16::stream_read_blocks(bytes) * 4;
+}
+
+w4a16_status w4a16_stream_read(const void* buf, int64_t bytes, void* sink, void* stream) {
+  if (!buf || !sink) return fail(W4A16_ERR_NULL, "buf and sink are required");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(W4A16_ERR_SHAPE, "bytes must be positive and a multiple of 16");
+  if (w4a16::stream_read_blocks(bytes) > (int64_t(1) << 31) - 1) return fail(W4A16_ERR_SHAPE, "bytes beyond the limit");
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(W4A16_ERR_ALIGN, "buf must be 16-byte and sink 4-byte aligned");
+  return hip_result(w4a16::launch_stream_read(buf, bytes, static_cast<uint32_t*>(sink),
+                                              static_cast<hipStream_t>(stream)),
+                    "stream read launch");
+}
+
 w4a16_status awq_channel_scale(const void* x_cal, int64_t T, int64_t K, double alpha, float* s, void* stream) {
   clear_error();
   if (!x_cal || !s) return fail(W4A16_ERR_NULL, "x_cal and s are required");

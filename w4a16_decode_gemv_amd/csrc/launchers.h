@@ -88,4 +88,8 @@ hipError_t launch_gemv_nf4(const Nf4Table& table, int block, const uint16_t* x, 
 hipError_t launch_mfma_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
                            const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
+// measurement aid: one read of a buffer with the GEMV's access pattern
+int64_t stream_read_blocks(int64_t bytes);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace w4a16
