@@ -178,8 +178,8 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * x: fp16 [M][K], the input after the 1/s fold; qweight/scales/zeros as written
  * by awq_quantize_pack with bits 4; y: fp16 [M][N] (output). group 32, 64 or
  * 128 (as quantized); K % 128 == 0.
- * Dispatch, group 128: M == 1, and M == 2 on layers with K <= 32768 and
- * N * K >= 2^25, run the wave-tile GEMV kernel; other M <= 32 the small-batch
+ * Dispatch, group 128: M == 1, and M == 2 on layers with K <= 24576 and
+ * N * K >= 2^27, run the wave-tile GEMV kernel; other M <= 32 the small-batch
  * MFMA kernel (workgroups own whole rows of y, waves split K); larger M the
  * tiled MFMA kernel. Groups of 32 and 64: M <= 8 (M <= 4 above
  * K = 16384) runs the GEMV kernel's variant, larger M the tiled MFMA kernel's

@@ -29,12 +29,13 @@ constexpr int64_t kMaxM = int64_t(1) << 16;
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;  // one workgroup per loss tile, 1-D grid
 // automatic dispatch, from sweeps on MI355X over the LLaMA projection shapes: the GEMV
-// kernel at M = 1, and at M = 2 on layers of at least 2^25 weights with K <= 32768 (there
-// the GEMV's doubled dot work still hides under the weight stream; on 4096 x 4096 its
-// 2-wave workgroups leave one wave per SIMD, and above K = 32768 a thread holds several
-// pieces); the small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA kernel beyond
+// kernel at M = 1, and at M = 2 on layers of at least 2^27 weights with K <= 24576 (there
+// the GEMV's doubled dot work still hides under the weight stream: 8192 -> 22016,
+// 22016 -> 8192 and 8192 -> 28672; on smaller layers and on 28672 -> 8192 the small-batch
+// kernel is ahead); the small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA
+// kernel beyond
 bool auto_gemv(int64_t M, int64_t N, int64_t K) {
-  return M == 1 || (M == 2 && K <= 32768 && N * K >= (int64_t(1) << 25));
+  return M == 1 || (M == 2 && K <= 24576 && N * K >= (int64_t(1) << 27));
 }
 
 w4a16_status hip_result(hipError_t e, const char* what) {
