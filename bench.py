@@ -63,7 +63,11 @@ def parse():
     p.add_argument("--search", action="store_true",
                    help="also time the AWQ scale search (loss kernel and grid points) on the LLaMA2-7B block")
     p.add_argument("--formats", action="store_true",
-                   help="also time the 3-bit and group-32/64 formats at K = N = 8192 (GEMV M=1, MFMA M=128)")
+                   help="also time the 3-bit, group-32/64 and NF4 formats at K = N = 8192")
+    p.add_argument("--formats-m", default="1,4,128",
+                   help="comma-separated batch sizes of the --formats table")
+    p.add_argument("--formats-paths", action="store_true",
+                   help="in the --formats table, also time every kernel that can take each shape")
     p.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only-gemv", action="store_true", help="time the headline GEMV only (for profilers)")
@@ -165,8 +169,11 @@ def time_per_launch(torch, fn, steps):
     return sum(d) / len(d), d[len(d) // 2]
 
 
-def time_graph(torch, fn, steps, reps=5):
-    """Launches captured into one HIP graph; ms per launch over `reps` replays."""
+def time_graph(torch, fn, steps, reps=5, warm_ms=25.0):
+    """Launches captured into one HIP graph; ms per launch over `reps` replays, after
+    replays that keep the GPU busy for about `warm_ms` (right after host-side set-up the
+    first replays run slower: 11 us kernels measured 1.2-1.4 us high on the first of six
+    back-to-back timings, settling by the fourth)."""
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -177,8 +184,12 @@ def time_graph(torch, fn, steps, reps=5):
     with torch.cuda.graph(g):
         for i in range(steps):
             fn(i)
-    g.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    n = 0
+    while n < 2 or (time.perf_counter() - t0) * 1e3 < warm_ms:
+        g.replay()
+        torch.cuda.synchronize()
+        n += 1
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
@@ -557,29 +568,46 @@ def main():
         out["awq_search_llama2_7b"] = search_leg(w4, torch)
 
     if args.formats:
+        ms_list = [int(v) for v in args.formats_m.split(",")]
+
+        def paths_for(mm, bits, group):
+            # the kernels that take this shape: GEMV (M <= 8), small-batch MFMA (4-bit, M <= 32), tiled
+            if not args.formats_paths:
+                return []
+            return ([1] if mm <= 8 else []) + ([3] if bits == 4 and mm <= 32 else []) + [2]
+
+        def row(fmt, mm, b, call, paths):
+            t = time_graph(torch, lambda i: call(i, 0), 100)
+            r = dict(fmt, M=mm, us=t * 1e3, bytes=b, GB_s=b / (t * 1e-3) / 1e9,
+                     TFLOP_s=2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12)
+            if paths:
+                r["us_by_path"] = {str(p): time_graph(torch, lambda i, p=p: call(i, p), 100) * 1e3 for p in paths}
+            return r
+
         rows = []
         for bits, group in ((4, 128), (4, 64), (4, 32), (3, 128), (3, 64), (3, 32)):
-            for mm in (1, 4, 128):
+            for mm in ms_list:
                 b = algorithmic_bytes(mm, 8192, 8192, group, bits)
                 L = Layer(w4, torch, 3, 0, 8192, 8192, mm, copies_for(b), bits=bits, group=group)
-                t = time_graph(torch, lambda i: L.call(w4, i), 100)
-                rows.append({"bits": bits, "group": group, "M": mm, "us": t * 1e3, "bytes": b,
-                             "GB_s": b / (t * 1e-3) / 1e9, "TFLOP_s": 2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12})
+                rows.append(row({"bits": bits, "group": group}, mm, b, lambda i, p: L.call(w4, i, path=p),
+                                paths_for(mm, bits, group)))
+                print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
                 del L
                 torch.cuda.empty_cache()
         # NF4 (blocks of 64, float32 absmax) on the same layer
         import synth
 
         W = torch.from_numpy(synth.weights(3, 0, 8192, 8192)).to("cuda:0")
-        for mm in (1, 4, 128):
+        for mm in ms_list:
             b = 8192 * 8192 // 2 + 4 * 8192 * (8192 // 64) + 2 * mm * 8192 * 2
             copies = copies_for(b)
             packs = [w4.nf4_quantize_pack(W, None, block=64) for _ in range(copies)]
             xq = torch.from_numpy(synth.activations(3, 0, mm, 8192)).to("cuda:0")
             yq = torch.empty((mm, 8192), dtype=torch.float16, device="cuda:0")
-            t = time_graph(torch, lambda i: w4.nf4_linear(xq, *packs[i % copies], block=64, out=yq), 100)
-            rows.append({"format": "nf4", "group": 64, "M": mm, "us": t * 1e3, "bytes": b,
-                         "GB_s": b / (t * 1e-3) / 1e9, "TFLOP_s": 2 * mm * 8192 * 8192 / (t * 1e-3) / 1e12})
+            rows.append(row({"format": "nf4", "group": 64}, mm, b,
+                            lambda i, p: w4.nf4_linear(xq, *packs[i % copies], block=64, out=yq, path=p),
+                            paths_for(mm, 4, 64)))
+            print(json.dumps(rows[-1]), file=sys.stderr, flush=True)
             del packs
             torch.cuda.empty_cache()
         del W

@@ -181,10 +181,12 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * Dispatch, group 128: M == 1, and M == 2 on layers with K <= 24576 and
  * N * K >= 2^27, run the wave-tile GEMV kernel; other M <= 32 the small-batch
  * MFMA kernel (workgroups own whole rows of y, waves split K); larger M the
- * tiled MFMA kernel. Groups of 32 and 64: M <= 8 (M <= 4 above
- * K = 16384) runs the GEMV kernel's variant, larger M the tiled MFMA kernel's
- * variant (one (scale, zero) per 32-input MFMA step). Alignment: x and qweight
- * 16 bytes, scales/zeros/y 2 bytes.
+ * tiled MFMA kernel. Groups of 32 and 64: M == 1, and M == 2 on layers with
+ * K <= 16384 and N * K >= 2^27, run the GEMV kernel's variant; other M <= 32
+ * the small-batch MFMA kernel (which needs scales and zeros 4-byte aligned;
+ * otherwise the GEMV variant takes M <= 8, M <= 4 above K = 16384); larger M
+ * the tiled MFMA kernel's variant (one (scale, zero) per 32-input MFMA step).
+ * Alignment: x and qweight 16 bytes, scales/zeros/y 2 bytes.
  */
 w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
@@ -193,9 +195,10 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
  * w4a16_linear_path - w4a16_linear with the kernel chosen by the caller, for
  * measuring the GEMV/MFMA hand-off: path 0 = automatic (same as w4a16_linear),
  * 1 = GEMV kernel (needs M <= w4a16_gemv_max_m() and M * ceil(K / 16384) <= 8),
- * 2 = tiled MFMA kernel (any M), 3 = small-batch MFMA kernel (needs M <= 32).
- * A path that cannot take the shape returns W4A16_ERR_UNSUPPORTED before any
- * HIP call (path 3 takes groups of 128 only). Same contract otherwise.
+ * 2 = tiled MFMA kernel (any M), 3 = small-batch MFMA kernel (needs M <= 32;
+ * with groups of 32 or 64, scales and zeros 4-byte aligned, else
+ * W4A16_ERR_ALIGN). A path that cannot take the shape returns
+ * W4A16_ERR_UNSUPPORTED before any HIP call. Same contract otherwise.
  */
 w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,
@@ -366,14 +369,20 @@ w4a16_status nf4_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * with the fp16 codebook of nf4_codebook, float32 accumulation, and the
  * accuracy contract of w4a16_linear (B = sum_k |x * w_hat|). x: fp16 [M][K];
  * qweight, absmax as nf4_quantize_pack writes them; y: fp16 [M][N]; block 32,
- * 64 or 128; K % 128 == 0. Dispatch: M <= 8 (M <= 4 above K = 16384, K <=
- * 32768) the GEMV kernel's NF4 variant (the codebook in LDS), larger M the
- * tiled MFMA kernel's. Alignment: x and qweight 16 bytes, absmax 4, y 2.
+ * 64 or 128; K % 128 == 0. Dispatch: M == 1, and M == 2 on layers with
+ * K <= 16384 and N * K >= 2^27, the GEMV kernel's NF4 variant (the codebook in
+ * LDS); other M <= 32 the small-batch MFMA kernel's; larger M the tiled MFMA
+ * kernel's. Alignment: x and qweight 16 bytes, absmax 4, y 2.
  */
 w4a16_status nf4_linear(const void* x, const void* qweight, const float* absmax, int64_t M, int64_t N,
                         int64_t K, int32_t block, void* y, void* stream);
 
-/* nf4_linear_path - nf4_linear with the kernel chosen: 0 auto, 1 GEMV, 2 tiled MFMA. */
+/*
+ * nf4_linear_path - nf4_linear with the kernel chosen: 0 auto, 1 GEMV (M <= 8,
+ * M <= 4 above K = 16384, K <= 32768), 2 tiled MFMA (any M), 3 small-batch
+ * MFMA (M <= 32). Other paths, or a shape the chosen kernel cannot take, return
+ * W4A16_ERR_UNSUPPORTED before any HIP call.
+ */
 w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, const float* absmax,
                              int64_t M, int64_t N, int64_t K, int32_t block, void* y, void* stream);
 

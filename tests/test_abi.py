@@ -168,10 +168,13 @@ def test_alpha_loss_workspace_and_rejects():
 
 def test_format_variants_reject():
     lib = w4.load()
-    # groups other than 32/64/128; K not a multiple of 128; small-batch path with other formats
+    # groups other than 32/64/128; K not a multiple of 128
     assert lib.w4a16_linear(A16, A16, A16, A16, 1, 64, 256, 16, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w4a16_linear(A16, A16, A16, A16, 1, 64, 96, 32, A16, None) == w4.ERR_SHAPE
-    assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 4, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    # the small-batch path with groups of 32/64: M <= 32, scales and zeros 4-byte aligned
+    assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 33, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear_path(3, A16, A16, A16 + 2, A16, 4, 64, 256, 64, A16, None) == w4.ERR_ALIGN
+    assert lib.w4a16_linear_path(3, A16, A16, A16, A16 + 2, 4, 64, 256, 32, A16, None) == w4.ERR_ALIGN
     assert lib.w3a16_linear(A16, A16, A16, A16, 1, 64, 256, 256, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w3a16_linear(None, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_NULL
     assert lib.w3a16_linear(A16, A16, A16, A16, 1, 64, 200, 128, A16, None) == w4.ERR_SHAPE
@@ -200,7 +203,8 @@ def test_nf4_and_sym_reject():
     assert lib.nf4_linear(A16, A16, A16, 1, 64, 256, 48, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.nf4_linear(A16, A16, A16, 1, 64, 192, 64, A16, None) == w4.ERR_SHAPE
     assert lib.nf4_linear(A16, A16, A16 + 2, 1, 64, 256, 64, A16, None) == w4.ERR_ALIGN
-    assert lib.nf4_linear_path(3, A16, A16, A16, 1, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.nf4_linear_path(4, A16, A16, A16, 1, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.nf4_linear_path(3, A16, A16, A16, 33, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.nf4_linear_path(1, A16, A16, A16, 9, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.awq_quantize_pack_sym(A16, None, 4, 256, 2, 128, A16, A16, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.awq_quantize_pack_sym(A16, None, 4, 200, 4, 128, A16, A16, A16, None) == w4.ERR_SHAPE

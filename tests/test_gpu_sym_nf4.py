@@ -50,7 +50,7 @@ def test_sym_quantize_pack_edge_tensors(lib, kind):
         _sym_compare(lib, W, None, bits, group, kind)
 
 
-@pytest.mark.parametrize("bits,group", [(4, 128), (4, 32), (3, 128)])
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 64), (4, 32), (3, 128)])
 @pytest.mark.parametrize("m", [1, 3, 8, 17, 64])
 def test_sym_linear_all_paths(lib, bits, group, m):
     g = _gpu()
@@ -59,7 +59,7 @@ def test_sym_linear_all_paths(lib, bits, group, m):
     packed = oracle.quantize_pack_sym(synth.weights(2, 8, n, k), s, bits=bits, group=group)
     x = oracle.scale_input(synth.activations(2, 8, m, k), s)
     y_ref, b = oracle.linear(x, *packed, group=group, bits=bits)
-    paths = [0, 2] + ([1] if m <= 8 else []) + ([3] if bits == 4 and group == 128 and m <= 32 else [])
+    paths = [0, 2] + ([1] if m <= 8 else []) + ([3] if bits == 4 and m <= 32 else [])
     for path in paths:
         print(f"sym linear bits={bits} group={group} M={m} path={path}", flush=True)
         y = g.host(lib.linear(g.dev(x), *[g.dev(t) for t in packed], group=group, path=path, bits=bits))
@@ -133,6 +133,26 @@ def test_nf4_mfma(lib, block, m, n, k):
     qw, a = oracle.quantize_pack_nf4(synth.weights(3, 5, n, k), None, block)
     x = synth.activations(3, 5, m, k)
     _nf4_linear_check(lib, x, qw, a, block, 2, "mfma")
+
+
+@pytest.mark.parametrize("block", [128, 64, 32])
+@pytest.mark.parametrize("m", [2, 3, 5, 8, 9, 16, 17, 32])
+@pytest.mark.parametrize("n,k", [(1, 128), (37, 384), (300, 2048), (97, 11008), (40, 32768)])
+def test_nf4_skinny(lib, block, m, n, k):
+    # the small-batch MFMA kernel with the codebook in LDS and 1, 2 or 4 float32 absmax
+    # values per 128 inputs
+    qw, a = oracle.quantize_pack_nf4(synth.weights(3, 6, n, k), None, block)
+    x = synth.activations(3, 6, m, k)
+    _nf4_linear_check(lib, x, qw, a, block, 3, "skinny")
+
+
+@pytest.mark.parametrize("block", [64, 32])
+@pytest.mark.parametrize("m", [2, 8, 32])
+def test_nf4_skinny_wide_layer(lib, block, m):
+    # N = 8200: two 16-column tiles per wave where they fit in registers
+    qw, a = oracle.quantize_pack_nf4(synth.weights(3, 7, 8200, 1024), None, block)
+    x = synth.activations(3, 7, m, 1024)
+    _nf4_linear_check(lib, x, qw, a, block, 3, "skinny-wide")
 
 
 @pytest.mark.parametrize("m", [1, 4, 128])

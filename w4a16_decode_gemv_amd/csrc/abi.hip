@@ -30,12 +30,21 @@ constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;  // one workgroup per loss tile, 1-D grid
 // automatic dispatch, from sweeps on MI355X over the LLaMA projection shapes: the GEMV
 // kernel at M = 1, and at M = 2 on layers of at least 2^27 weights with K <= 24576 (there
-// the GEMV's doubled dot work still hides under the weight stream: 8192 -> 22016,
-// 22016 -> 8192 and 8192 -> 28672; on smaller layers and on 28672 -> 8192 the small-batch
-// kernel is ahead); the small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA
-// kernel beyond
+// the GEMV's doubled dot work still hides under the weight stream: 21.8 against 24.0 us at
+// 8192 -> 22016, 28.7 against 29.9 at 22016 -> 8192, 26.9 against 28.9 at 8192 -> 28672; on
+// smaller layers and on 28672 -> 8192 the small-batch kernel is ahead: 9.9 against 10.3 us
+// at 8192 -> 8192, 29.5 against 33.8 at 28672 -> 8192); the small-batch MFMA kernel up to
+// skinny_max_m(); the tiled MFMA kernel beyond
 bool auto_gemv(int64_t M, int64_t N, int64_t K) {
   return M == 1 || (M == 2 && K <= 24576 && N * K >= (int64_t(1) << 27));
+}
+
+// the same hand-off for groups of 32 and 64 and for NF4, whose GEMV variant has no long-row
+// plan: at M = 2 it keeps the large layers with K <= 16384 (8192 -> 22016, groups of 64:
+// 23.2 against 25.1 us; NF4: 26.7 against 29.3) and loses the long rows (22016 -> 8192:
+// 47.7 against 29.5 us)
+bool auto_gemv_variant(int64_t M, int64_t N, int64_t K) {
+  return M == 1 || (M == 2 && K <= 16384 && N * K >= (int64_t(1) << 27));
 }
 
 w4a16_status hip_result(hipError_t e, const char* what) {
@@ -124,17 +133,28 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   uint16_t* yh = static_cast<uint16_t*>(y);
   if (bits != 4 || group != 128) {
     const bool gemv_ok = w4a16::gemv_variant_supports(M, K, group);
+    // the small-batch kernel loads a row's scales (zeros) of 128 inputs in one 4- or 8-byte load
+    const bool skinny_ok = bits == 4 && M <= w4a16::skinny_max_m() && aligned(scales, 4) && aligned(zeros, 4);
     int32_t kernel = path;
     if (path == 0) {
-      kernel = gemv_ok ? 1 : 2;
+      kernel = auto_gemv_variant(M, N, K) && gemv_ok ? 1 : skinny_ok ? 3 : gemv_ok ? 1 : 2;
     } else if (path == 1 && !gemv_ok) {
       return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel for this format takes M <= %d and K <= 32768 "
                   "(M <= 4 above K = 16384); got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
     } else if (path == 3) {
-      return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes 4-bit codes with groups of 128 only");
+      if (bits != 4) return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes 4-bit codes only");
+      if (M > w4a16::skinny_max_m())
+        return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes M <= %d; got M=%lld",
+                    w4a16::skinny_max_m(), (long long)M);
+      if (!skinny_ok)
+        return fail(W4A16_ERR_ALIGN, "the small-batch MFMA kernel needs scales and zeros 4-byte aligned "
+                    "for groups of 32 and 64");
     }
     if (kernel == 1)
       return hip_result(w4a16::launch_gemv_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
+    if (kernel == 3)
+      return hip_result(w4a16::launch_skinny_variant(group, xh, qw, sc, zr, M, N, K, yh, stream),
+                        "small-batch MFMA launch");
     return hip_result(w4a16::launch_mfma_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
   }
   int32_t kernel = path;
@@ -357,19 +377,29 @@ w4a16_status nf4_quantize_pack(const void* w, const float* s, int64_t N, int64_t
 w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, const float* absmax, int64_t M,
                              int64_t N, int64_t K, int32_t block, void* y, void* stream) {
   clear_error();
-  if (path < 0 || path > 2) return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV) or 2 (tiled MFMA)");
+  if (path < 0 || path > 3)
+    return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA) or 3 (small-batch MFMA)");
   const w4a16_status st = check_nf4_linear(x, qweight, absmax, M, N, K, block, y);
   if (st != W4A16_OK) return st;
   const bool gemv_ok = w4a16::gemv_variant_supports(M, K, block);
   if (path == 1 && !gemv_ok)
     return fail(W4A16_ERR_UNSUPPORTED, "the NF4 GEMV kernel takes M <= %d and K <= 32768 (M <= 4 above K = 16384); "
                 "got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
+  if (path == 3 && M > w4a16::skinny_max_m())
+    return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes M <= %d; got M=%lld", w4a16::skinny_max_m(),
+                (long long)M);
   const uint16_t* xh = static_cast<const uint16_t*>(x);
   const uint32_t* qw = static_cast<const uint32_t*>(qweight);
   uint16_t* yh = static_cast<uint16_t*>(y);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (path == 1 || (path == 0 && gemv_ok))
+  int32_t kernel = path;
+  if (path == 0)
+    kernel = auto_gemv_variant(M, N, K) && gemv_ok ? 1 : M <= w4a16::skinny_max_m() ? 3 : gemv_ok ? 1 : 2;
+  if (kernel == 1)
     return hip_result(w4a16::launch_gemv_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs), "NF4 GEMV launch");
+  if (kernel == 3)
+    return hip_result(w4a16::launch_skinny_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs),
+                      "NF4 small-batch MFMA launch");
   return hip_result(w4a16::launch_mfma_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs), "NF4 MFMA launch");
 }
 

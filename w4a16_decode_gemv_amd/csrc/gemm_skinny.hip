@@ -42,6 +42,16 @@
 // lane (j, n) needs words j, 4+j, 8+j, 12+j of row n's group: the LDS area is
 // written in that order, one 16-byte slot per (row, group, j), XOR-swizzled by
 // row so that neither the writes nor the reads collide in LDS banks.
+//
+// Groups of 64 or 32 (and NF4 blocks of 128, 64 or 32) use the same code stream:
+// the code layout does not depend on the group. Step q covers inputs 32q..32q+31
+// of a 128-input group, which lie inside one group of 32 or 64, so the steps of
+// one group chain into one MFMA accumulator that is scaled once (and its zero
+// applied once, through the sum of x over the same steps). The SUB = 128 / group
+// (scale, zero) pairs of a row's 128 inputs are contiguous in memory and arrive
+// in one load. NF4 codes become fp16 levels through a 16-entry codebook in LDS
+// (16 fp16 values: 8 banks, so every lookup is conflict-free or a broadcast) and
+// are scaled by the float32 absmax of the block; there is no zero.
 #include "device_utils.h"
 #include "launchers.h"
 
@@ -77,22 +87,66 @@ __device__ __forceinline__ half8_t codes_word(uint32_t w) {
   return __builtin_bit_cast(half8_t, v);
 }
 
+// the eight NF4 codes of one code word as their fp16 levels, in k order
+__device__ __forceinline__ half8_t nf4_word(uint32_t w, const _Float16* lut) {
+  uint32_t v[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t n = w >> (4 * i);
+    v[i] = __builtin_bit_cast(uint32_t, (half2_t){lut[n & 15u], lut[(n >> 16) & 15u]});
+  }
+  return as_half8((u32x4_t){v[0], v[1], v[2], v[3]});
+}
+
+// the scale-side bytes of one (row, 128-input group) item: SUB fp16 scales (or zeros), or
+// SUB float32 absmax values, contiguous in memory; one load, little-endian words
+template <int BYTES>
+__device__ __forceinline__ void load_item(__amdgpu_buffer_rsrc_t r, int off, uint32_t (&v)[BYTES >= 4 ? BYTES / 4 : 1]) {
+  if constexpr (BYTES == 2) {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else if constexpr (BYTES == 4) {
+    v[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  } else if constexpr (BYTES == 8) {
+    const auto t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    v[0] = t[0];
+    v[1] = t[1];
+  } else {
+    static_assert(BYTES == 16, "items of 2, 4, 8 or 16 bytes");
+    const u32x4_t t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+    v[0] = t.x;
+    v[1] = t.y;
+    v[2] = t.z;
+    v[3] = t.w;
+  }
+}
+
 // NS stages (2 * NS groups) per wave and chunk; K beyond one chunk per wave loops over chunks
 // XI > 0 (M <= 2 XI <= 8, MT = 1): a stage's x rows arrive in XI full-width loads (lane l of
 // load i takes row 2i + l/32, 16-byte piece l%32 of the stage's 512 bytes) and reach the A
-// fragments through a wave-private LDS area; XI = 0: A fragments loaded straight from L2
-template <int NTW, int MT, int NS, int XI>
+// fragments through a wave-private LDS area; XI = 0: A fragments loaded straight from L2.
+// "Group" below is a 128-input group of the code stream; SUB = 128 / (quantization group)
+// scales per row and group (NF4: float32 absmax values passed through `scales`, no zeros).
+template <int NTW, int MT, int NS, int XI, int SUB, bool NF4>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
-                                                         const uint16_t* __restrict__ scales,
+                                                         const void* __restrict__ scales,
                                                          const uint16_t* __restrict__ zeros, int M, int N, int K,
-                                                         uint16_t* __restrict__ y) {
+                                                         Nf4Table table, uint16_t* __restrict__ y) {
   constexpr int ROWS = 16 * NTW;
   constexpr int CG = 2 * NS;                       // groups per wave and chunk
-  constexpr int SZL = (ROWS * CG + 63) / 64;       // (scale, zero) pairs per lane and chunk
+  constexpr int SZL = (ROWS * CG + 63) / 64;       // (row, group) scale items per lane and chunk
+  constexpr int QS = 4 / SUB;                      // MFMA steps per quantization group
+  constexpr int IB = (NF4 ? 4 : 2) * SUB;          // bytes of one scale item (per tensor)
+  constexpr int IW = IB >= 4 ? IB / 4 : 1;         // 32-bit words holding it
+  static_assert(SUB == 1 || SUB == 2 || SUB == 4, "groups of 128, 64 or 32");
   static_assert(ROWS * 8 >= NTW * MT * 64, "the final combine reuses the code staging area");
-  __shared__ u32x4_t lds_b[KS][ROWS * 8];          // one stage of codes: ROWS x (2 groups x 4 slots)
-  __shared__ uint32_t lds_sz[KS][ROWS][CG + 1];    // one chunk of (scale | zero << 16)
+  __shared__ u32x4_t lds_b[KS][ROWS * 8];            // one stage of codes: ROWS x (2 groups x 4 slots)
+  __shared__ uint32_t lds_sz[KS][ROWS][CG * SUB + 1];  // one chunk of (scale | zero << 16), or absmax
   __shared__ u32x4_t lds_x[XI > 0 ? KS : 1][XI > 0 ? D : 1][XI > 0 ? 2 * XI : 1][33];  // x rows, padded
+  __shared__ __align__(16) _Float16 lut[NF4 ? 16 : 2];
+  if constexpr (NF4) {
+    if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(lut)[threadIdx.x] = table.pairs[threadIdx.x];
+    __syncthreads();
+  }
 
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int j = lane >> 4, c = lane & 15;   // fragment slot group, fragment row
@@ -107,10 +161,10 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
   // buffer views: this workgroup's code, scale and zero rows, and all of x
   const __amdgpu_buffer_rsrc_t q_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)(qw + (int64_t)n0 * (K >> 3)), (short)0, rows * (K >> 1), kBufferFlags);
-  const __amdgpu_buffer_rsrc_t s_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(scales + (int64_t)n0 * G), (short)0, rows * G * 2, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t z_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(zeros + (int64_t)n0 * G), (short)0, rows * G * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const uint8_t*>(scales) + (int64_t)n0 * G * IB), (short)0, rows * G * IB, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(NF4 ? nullptr : zeros + (int64_t)n0 * G * SUB), (short)0, NF4 ? 0 : rows * G * IB, kBufferFlags);
   const __amdgpu_buffer_rsrc_t x_rsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, M * K * 2, kBufferFlags);
 
@@ -130,15 +184,15 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
     // plain arithmetic, not a select: a select would let the compiler split each load in two
     auto bias = [&](int gi) { return (int)(gi >= nv) * kOutOfRange; };
 
-    // (scale, zero) of the chunk: lane -> (row, SZL consecutive groups)
-    uint16_t sv[SZL], zv[SZL];
+    // scales (and zeros) of the chunk: lane -> (row, SZL consecutive groups)
+    uint32_t sv[SZL][IW], zv[NF4 ? 1 : SZL][IW];
     const int sz_row = (lane * SZL) / CG, sz_g = (lane * SZL) % CG;
 #pragma unroll
     for (int e = 0; e < SZL; ++e) {
       const int gi = sz_g + e;
-      const int o = min(sz_row, ROWS - 1) * G * 2 + (g0 + gi) * 2 + bias(gi) + (int)(sz_row >= ROWS) * kOutOfRange;
-      sv[e] = __builtin_amdgcn_raw_buffer_load_b16(s_rsrc, o, 0, 0);
-      zv[e] = __builtin_amdgcn_raw_buffer_load_b16(z_rsrc, o, 0, 0);
+      const int o = min(sz_row, ROWS - 1) * G * IB + (g0 + gi) * IB + bias(gi) + (int)(sz_row >= ROWS) * kOutOfRange;
+      load_item<IB>(s_rsrc, o, sv[e]);
+      if constexpr (!NF4) load_item<IB>(z_rsrc, o, zv[e]);
     }
 
     u32x4_t cr[D][NTW][2];
@@ -185,7 +239,17 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
 
 #pragma unroll
     for (int e = 0; e < SZL; ++e)
-      if (sz_row < ROWS) lds_sz[w][sz_row][sz_g + e] = (uint32_t)sv[e] | ((uint32_t)zv[e] << 16);
+#pragma unroll
+      for (int sub = 0; sub < SUB; ++sub) {
+        uint32_t v;
+        if constexpr (NF4) {
+          v = sv[e][sub];
+        } else {
+          const int sh = 16 * (sub & 1);
+          v = ((sv[e][sub >> 1] >> sh) & 0xFFFFu) | (((zv[e][sub >> 1] >> sh) & 0xFFFFu) << 16);
+        }
+        if (sz_row < ROWS) lds_sz[w][sz_row][(sz_g + e) * SUB + sub] = v;
+      }
 
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
@@ -226,34 +290,67 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
 #pragma unroll
           for (int q = 0; q < 4; ++q) xr[u][gs][0][q] = lds_x[w][u][xrow][16 * gs + 4 * q + j];
         }
-        float4_t sx[MT];
+        // sum of x over each quantization group's steps (for the zero)
+        float4_t sx[NF4 ? 1 : MT][SUB];
+        if constexpr (!NF4) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          sx[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+          for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
-            sx[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xr[u][gs][mt][q]), ones, sx[mt], 0, 0, 0);
+            for (int sub = 0; sub < SUB; ++sub) {
+              sx[mt][sub] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int q = sub * QS; q < (sub + 1) * QS; ++q)
+                sx[mt][sub] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xr[u][gs][mt][q]), ones, sx[mt][sub], 0, 0, 0);
+            }
         }
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           const int row = 16 * nt + c;
           const u32x4_t wq = lds_b[w][row * 8 + ((gs * 4 + j) ^ ((row >> 1) & 7))];
-          const uint32_t szv = lds_sz[w][row][gi];
-          const float d = half_bits_to_float((uint16_t)(szv & 0xFFFFu));
-          const float zf = half_bits_to_float((uint16_t)(szv >> 16));
-          const half8_t b0 = codes_word(wq.x), b1 = codes_word(wq.y), b2 = codes_word(wq.z), b3 = codes_word(wq.w);
+          float d[SUB], zf[SUB];
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            float4_t a4 = {0.f, 0.f, 0.f, 0.f};
-            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xr[u][gs][mt][0]), b0, a4, 0, 0, 0);
-            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xr[u][gs][mt][1]), b1, a4, 0, 0, 0);
-            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xr[u][gs][mt][2]), b2, a4, 0, 0, 0);
-            a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xr[u][gs][mt][3]), b3, a4, 0, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[nt][mt][i] = __builtin_fmaf(d, __builtin_fmaf(-zf, sx[mt][i], a4[i]), acc[nt][mt][i]);
+          for (int sub = 0; sub < SUB; ++sub) {
+            const uint32_t szv = lds_sz[w][row][gi * SUB + sub];
+            if constexpr (NF4) {
+              d[sub] = __builtin_bit_cast(float, szv);
+              zf[sub] = 0.f;
+            } else {
+              d[sub] = half_bits_to_float((uint16_t)(szv & 0xFFFFu));
+              zf[sub] = half_bits_to_float((uint16_t)(szv >> 16));
+            }
           }
+          half8_t b[4];
+          if constexpr (NF4) {
+            b[0] = nf4_word(wq.x, lut);
+            b[1] = nf4_word(wq.y, lut);
+            b[2] = nf4_word(wq.z, lut);
+            b[3] = nf4_word(wq.w, lut);
+          } else {
+            b[0] = codes_word(wq.x);
+            b[1] = codes_word(wq.y);
+            b[2] = codes_word(wq.z);
+            b[3] = codes_word(wq.w);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int sub = 0; sub < SUB; ++sub) {
+              float4_t a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int q = sub * QS; q < (sub + 1) * QS; ++q)
+                a4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xr[u][gs][mt][q]), b[q], a4, 0, 0, 0);
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                if constexpr (NF4)
+                  acc[nt][mt][i] = __builtin_fmaf(d[sub], a4[i], acc[nt][mt][i]);
+                else
+                  acc[nt][mt][i] = __builtin_fmaf(d[sub], __builtin_fmaf(-zf[sub], sx[mt][sub][i], a4[i]), acc[nt][mt][i]);
+              }
+            }
         }
+        // with several scales per group, keep the two groups' work apart: interleaved, their
+        // per-group sums and scales no longer fit in registers
+        if constexpr (SUB > 1) __builtin_amdgcn_sched_barrier(0);
       }
       if constexpr (XI == 0) {
         if (s + D < NS) load_x(s + D, u);
@@ -282,34 +379,87 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
   }
 }
 
-template <int NTW, int MT, int NS, int XI>
-hipError_t launch_tile_x(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                         int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  const dim3 grid((unsigned)((N + 16 * NTW - 1) / (16 * NTW)));
-  hipLaunchKernelGGL((skinny_kernel<NTW, MT, NS, XI>), grid, dim3(kThreads), 0, stream, x, qweight, scales, zeros,
-                     (int)M, (int)N, (int)K, y);
+struct Args {
+  const uint16_t* x;
+  const uint32_t* qweight;
+  const void* scales;  // fp16 scales, or float32 absmax (NF4)
+  const uint16_t* zeros;
+  int64_t M, N, K;
+  Nf4Table table;
+  uint16_t* y;
+  hipStream_t stream;
+};
+
+template <int NTW, int MT, int NS, int XI, int SUB, bool NF4>
+hipError_t launch_tile_x(const Args& a) {
+  const dim3 grid((unsigned)((a.N + 16 * NTW - 1) / (16 * NTW)));
+  hipLaunchKernelGGL((skinny_kernel<NTW, MT, NS, XI, SUB, NF4>), grid, dim3(kThreads), 0, a.stream, a.x, a.qweight,
+                     a.scales, a.zeros, (int)a.M, (int)a.N, (int)a.K, a.table, a.y);
   return hipGetLastError();
 }
 
-template <int NTW, int MT, int NS>
-hipError_t launch_tile(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                       int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  if constexpr (MT == 1) {
-    if (M <= 2) return launch_tile_x<NTW, MT, NS, 1>(x, qweight, scales, zeros, M, N, K, y, stream);
-    if (M <= 4) return launch_tile_x<NTW, MT, NS, 2>(x, qweight, scales, zeros, M, N, K, y, stream);
-    if (M <= 8) return launch_tile_x<NTW, MT, NS, 4>(x, qweight, scales, zeros, M, N, K, y, stream);
+// M <= 8 (MT = 1): x rows through LDS in M/2 full-width loads; otherwise 16-row fragment loads
+// (two column tiles with groups of 32 meet M <= 8 in two-stage chunks only)
+template <int NTW, int MT, int NS, int SUB, bool NF4>
+hipError_t launch_tile(const Args& a) {
+  if constexpr (MT == 1 && !(NTW == 2 && SUB == 4 && NS > 2)) {
+    if (a.M <= 2) return launch_tile_x<NTW, MT, NS, 1, SUB, NF4>(a);
+    if (a.M <= 4) return launch_tile_x<NTW, MT, NS, 2, SUB, NF4>(a);
+    if (a.M <= 8) return launch_tile_x<NTW, MT, NS, 4, SUB, NF4>(a);
   }
-  return launch_tile_x<NTW, MT, NS, 0>(x, qweight, scales, zeros, M, N, K, y, stream);
+  return launch_tile_x<NTW, MT, NS, 0, SUB, NF4>(a);
 }
 
-template <int NTW, int MT>
-hipError_t launch_stages(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
-                         int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  const int64_t stages = ((K / 128 + KS - 1) / KS + 1) / 2;  // per wave
-  if (stages <= 2) return launch_tile<NTW, MT, 2>(x, qweight, scales, zeros, M, N, K, y, stream);
-  if (stages <= 4) return launch_tile<NTW, MT, 4>(x, qweight, scales, zeros, M, N, K, y, stream);
-  if (stages <= 6) return launch_tile<NTW, MT, 6>(x, qweight, scales, zeros, M, N, K, y, stream);
-  return launch_tile<NTW, MT, kMaxStages>(x, qweight, scales, zeros, M, N, K, y, stream);
+// stages per chunk: enough for the wave's whole share, up to CAP (2 or 8; 4 at most with
+// groups of 32, whose chunk of scales is four times as large)
+template <int NTW, int MT, int SUB, bool NF4, int CAP>
+hipError_t launch_stages(const Args& a) {
+  const int64_t stages = ((a.K / 128 + KS - 1) / KS + 1) / 2;  // per wave
+  if constexpr (CAP == 2) {
+    return launch_tile<NTW, MT, 2, SUB, NF4>(a);
+  } else if constexpr (SUB == 4) {
+    return stages <= 2 ? launch_tile<NTW, MT, 2, SUB, NF4>(a) : launch_tile<NTW, MT, 4, SUB, NF4>(a);
+  } else {
+    if (stages <= 2) return launch_tile<NTW, MT, 2, SUB, NF4>(a);
+    if (stages <= 4) return launch_tile<NTW, MT, 4, SUB, NF4>(a);
+    if (stages <= 6) return launch_tile<NTW, MT, 6, SUB, NF4>(a);
+    return launch_tile<NTW, MT, kMaxStages, SUB, NF4>(a);
+  }
+}
+
+// Column tiles per wave (NTW) and the stage cap, measured on MI355X at K = N = 8192,
+// K = 4096 -> N = 11008 and K = 11008 -> N = 4096 for every format and M = 2..32:
+//   * one column tile while M <= 4, on layers too narrow for 256 two-tile workgroups, and on
+//     K <= 4096 up to M = 8: twice the workgroups and waves in flight (K = N = 8192, M = 2:
+//     10.2 against 10.9 us; 4096 -> 11008, M = 2: 8.3 against 9.5 us); beyond, two column
+//     tiles halve the x reads from L2, which then dominate (M = 8: 11.8 against 13.5 us);
+//   * a two-stage cap where the longer chunk costs too many registers: groups of 32 always
+//     (their four scales, zeros and x sums per group), groups of 64 with one column tile when
+//     the grid needs two workgroups per CU (10.9 against 12.5 us at M = 4), groups of 64
+//     at two m-tiles (M = 32: 25.2 against 27.0 us), NF4 at M = 5..8 (15.2 against
+//     16.6 us) and NF4 blocks of 32 with one column tile at M <= 4;
+//   * groups of 128 at two m-tiles keep two column tiles only up to 4 stages per wave (beyond
+//     that the two-tile variant runs out of registers).
+template <int SUB, bool NF4>
+hipError_t launch_format(const Args& a) {
+  constexpr bool zp = !NF4;
+  const int64_t M = a.M;
+  const bool wide = (a.N + 31) / 32 >= 256;
+  if (M <= 4 || !wide || (a.K <= 4096 && M <= 8)) {
+    const bool many = (a.N + 15) / 16 > 256;  // more than one one-tile workgroup per CU
+    if (M > 16) return launch_stages<1, 2, SUB, NF4, zp && SUB == 4 ? 2 : 8>(a);
+    if ((zp && SUB == 4) || (zp && SUB == 2 && M <= 4 && many) || (NF4 && SUB == 4 && M <= 4))
+      return launch_stages<1, 1, SUB, NF4, 2>(a);
+    return launch_stages<1, 1, SUB, NF4, 8>(a);
+  }
+  if (M <= 8) return launch_stages<2, 1, SUB, NF4, SUB == 4 || NF4 ? 2 : 8>(a);
+  if (M <= 16) return launch_stages<2, 1, SUB, NF4, 8>(a);
+  if constexpr (SUB == 1 && zp) {
+    const bool short_k = ((a.K / 128 + KS - 1) / KS + 1) / 2 <= 4;
+    return short_k ? launch_stages<2, 2, SUB, NF4, 8>(a) : launch_stages<1, 2, SUB, NF4, 8>(a);
+  } else {
+    return launch_stages<2, 2, SUB, NF4, zp ? 2 : 8>(a);
+  }
 }
 
 }  // namespace
@@ -318,16 +468,26 @@ int skinny_max_m() { return 32; }
 
 hipError_t launch_skinny(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  // two column tiles per wave halve the x traffic per code byte, as long as that still leaves
-  // one workgroup for each of the 256 compute units
-  // (with two m-tiles, only up to 4 stages per wave: beyond that the two-tile variant runs out
-  // of registers)
-  const bool wide = (N + 31) / 32 >= 256;
-  if (M <= 16) return wide ? launch_stages<2, 1>(x, qweight, scales, zeros, M, N, K, y, stream)
-                           : launch_stages<1, 1>(x, qweight, scales, zeros, M, N, K, y, stream);
-  const bool short_k = ((K / 128 + KS - 1) / KS + 1) / 2 <= 4;
-  return wide && short_k ? launch_stages<2, 2>(x, qweight, scales, zeros, M, N, K, y, stream)
-                         : launch_stages<1, 2>(x, qweight, scales, zeros, M, N, K, y, stream);
+  return launch_format<1, false>({x, qweight, scales, zeros, M, N, K, {}, y, stream});
+}
+
+hipError_t launch_skinny_variant(int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                                 const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
+                                 hipStream_t stream) {
+  const Args a = {x, qweight, scales, zeros, M, N, K, {}, y, stream};
+  if (group == 128) return launch_format<1, false>(a);
+  if (group == 64) return launch_format<2, false>(a);
+  if (group == 32) return launch_format<4, false>(a);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_skinny_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
+                             const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  const Args a = {x, qweight, absmax, nullptr, M, N, K, table, y, stream};
+  if (block == 128) return launch_format<1, true>(a);
+  if (block == 64) return launch_format<2, true>(a);
+  if (block == 32) return launch_format<4, true>(a);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace w4a16
