@@ -571,10 +571,10 @@ def main():
         ms_list = [int(v) for v in args.formats_m.split(",")]
 
         def paths_for(mm, bits, group):
-            # the kernels that take this shape: GEMV (M <= 8), small-batch MFMA (4-bit, M <= 32), tiled
+            # the kernels that take this shape: GEMV (M <= 8), small-batch MFMA (M <= 32), tiled
             if not args.formats_paths:
                 return []
-            return ([1] if mm <= 8 else []) + ([3] if bits == 4 and mm <= 32 else []) + [2]
+            return ([1] if mm <= 8 else []) + ([3] if mm <= 32 else []) + [2]
 
         def row(fmt, mm, b, call, paths):
             t = time_graph(torch, lambda i: call(i, 0), 100)

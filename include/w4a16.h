@@ -236,8 +236,10 @@ w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void*
  * packed 3-bit layout (awq_quantize_pack with bits 3). Lab 4 setup: 3-bit
  * weights, groups of 128; L13 TinyChat kernel fusion. Same formula, accuracy
  * contract, arguments and alignment as w4a16_linear; group 32, 64 or 128;
- * K % 128 == 0. Dispatch: M <= 8 (M <= 4 above K = 16384) the GEMV kernel's
- * 3-bit variant, larger M the tiled MFMA kernel's 3-bit variant.
+ * K % 128 == 0. Dispatch: M <= 2 the GEMV kernel's 3-bit variant (M == 2 up
+ * to K = 32768); other M <= 32 the small-batch MFMA kernel's (scales and zeros
+ * 4-byte aligned below groups of 128, else the GEMV variant up to M = 8, M = 4
+ * above K = 16384); larger M the tiled MFMA kernel's 3-bit variant.
  */
 w4a16_status w3a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
@@ -245,8 +247,10 @@ w4a16_status w3a16_linear(const void* x, const void* qweight, const void* scales
 /*
  * w3a16_linear_path - w3a16_linear with the kernel chosen by the caller: path
  * 0 = automatic, 1 = GEMV variant (needs M <= 8, and M <= 4 above K = 16384,
- * K <= 32768), 2 = tiled MFMA variant (any M). Other paths, or a shape the
- * chosen kernel cannot take, return W4A16_ERR_UNSUPPORTED before any HIP call.
+ * K <= 32768), 2 = tiled MFMA variant (any M), 3 = small-batch MFMA variant
+ * (M <= 32; W4A16_ERR_ALIGN when scales or zeros are not 4-byte aligned below
+ * groups of 128). Other paths, or a shape the chosen kernel cannot take, return
+ * W4A16_ERR_UNSUPPORTED before any HIP call.
  */
 w4a16_status w3a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,

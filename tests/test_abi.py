@@ -179,7 +179,9 @@ def test_format_variants_reject():
     assert lib.w3a16_linear(None, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_NULL
     assert lib.w3a16_linear(A16, A16, A16, A16, 1, 64, 200, 128, A16, None) == w4.ERR_SHAPE
     assert lib.w3a16_linear(A16 + 8, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_ALIGN
-    assert lib.w3a16_linear_path(3, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w3a16_linear_path(4, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w3a16_linear_path(3, A16, A16, A16, A16, 33, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w3a16_linear_path(3, A16, A16, A16 + 2, A16, 4, 64, 256, 64, A16, None) == w4.ERR_ALIGN
     assert lib.w3a16_linear_path(1, A16, A16, A16, A16, 9, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w3a16_linear_path(1, A16, A16, A16, A16, 8, 64, 32768 + 128, 128, A16, None) == w4.ERR_UNSUPPORTED
 

@@ -4,7 +4,7 @@
 * quantize-pack: codes, scales and zeros bit-identical to the oracle's for bits 3/4 and
   groups 32/64/128, on ragged and full-size layers and on the edge tensors;
 * the linear layer: every output within 1e-3 * sum_k |x * w_hat| + 1e-5 of the oracle, on
-  every kernel (the GEMV variant for M <= 8, the small-batch MFMA kernel for 4-bit codes at
+  every kernel (the GEMV variant for M <= 8, the small-batch MFMA kernel at
   M <= 32, the tiled MFMA variant for any M), fed the oracle's packed weights.
 """
 
@@ -111,39 +111,39 @@ def test_mfma_variant(lib, bits, group, m, n, k):
     _linear_check(lib, x, packed, bits, group, 2, "mfma")
 
 
-@pytest.mark.parametrize("group", [64, 32])
+@pytest.mark.parametrize("bits,group", FORMATS)
 @pytest.mark.parametrize("m", [2, 3, 5, 8, 9, 16, 17, 32])
 @pytest.mark.parametrize("n,k", [(1, 128), (37, 384), (300, 2048), (97, 11008), (64, 22016), (40, 32768)])
-def test_skinny_variant(lib, group, m, n, k):
-    # the small-batch MFMA kernel with 2 or 4 (scale, zero) pairs per 128 inputs: every x
-    # path (one, two or four full-width x loads, and 16-row fragment loads), one and two
-    # m-tiles, one chunk and several chunks of stages per wave, ragged N and K
+def test_skinny_variant(lib, bits, group, m, n, k):
+    # the small-batch MFMA kernel with 1, 2 or 4 (scale, zero) pairs per 128 inputs and 4- or
+    # 3-bit codes: every x path (one, two or four full-width x loads, and 16-row fragment
+    # loads), one and two m-tiles, one chunk and several chunks of stages per wave, ragged N, K
     x_cal = synth.calibration(2, 15, k)
     s = oracle.channel_scale(x_cal)
-    packed = oracle.quantize_pack(synth.weights(2, 15, n, k), s, bits=4, group=group)
+    packed = oracle.quantize_pack(synth.weights(2, 15, n, k), s, bits=bits, group=group)
     x = oracle.scale_input(synth.activations(2, 15, m, k), s)
-    _linear_check(lib, x, packed, 4, group, 3, "skinny")
+    _linear_check(lib, x, packed, bits, group, 3, "skinny")
 
 
-@pytest.mark.parametrize("group", [64, 32])
+@pytest.mark.parametrize("bits,group", FORMATS)
 @pytest.mark.parametrize("m", [2, 8, 16, 32])
-def test_skinny_variant_wide_layer(lib, group, m):
-    # N = 8200: 257 two-column tiles, so groups of 64 take two 16-column tiles per wave
+def test_skinny_variant_wide_layer(lib, bits, group, m):
+    # N = 8200: 257 two-column tiles, so M > 4 takes two 16-column tiles per wave
     x_cal = synth.calibration(2, 16, 1024)
     s = oracle.channel_scale(x_cal)
-    packed = oracle.quantize_pack(synth.weights(2, 16, 8200, 1024), s, bits=4, group=group)
+    packed = oracle.quantize_pack(synth.weights(2, 16, 8200, 1024), s, bits=bits, group=group)
     x = oracle.scale_input(synth.activations(2, 16, m, 1024), s)
-    _linear_check(lib, x, packed, 4, group, 3, "skinny-wide")
+    _linear_check(lib, x, packed, bits, group, 3, "skinny-wide")
 
 
-@pytest.mark.parametrize("group", [64, 32])
-def test_skinny_variant_misaligned_scales_fall_back(lib, group):
+@pytest.mark.parametrize("bits,group", [(4, 64), (4, 32), (3, 64), (3, 32)])
+def test_skinny_variant_misaligned_scales_fall_back(lib, bits, group):
     # scales and zeros at a 2-byte but not 4-byte aligned address: the automatic choice takes
     # another kernel, the explicit small-batch path refuses
     torch, g = _torch(), _gpu()
     n, k, m = 64, 1024, 4
     s = oracle.channel_scale(synth.calibration(2, 17, k))
-    packed = oracle.quantize_pack(synth.weights(2, 17, n, k), s, bits=4, group=group)
+    packed = oracle.quantize_pack(synth.weights(2, 17, n, k), s, bits=bits, group=group)
     x = oracle.scale_input(synth.activations(2, 17, m, k), s)
 
     def shifted(a):
@@ -154,12 +154,33 @@ def test_skinny_variant_misaligned_scales_fall_back(lib, group):
         return v
 
     sc, zr = shifted(packed[1]), shifted(packed[2])
-    print(f"linear misaligned scales group={group}", flush=True)
-    y = g.host(lib.linear(g.dev(x), g.dev(packed[0]), sc, zr, group=group))
-    y_ref, b = oracle.linear(x, *packed, group=group)
+    print(f"linear misaligned scales bits={bits} group={group}", flush=True)
+    y = g.host(lib.linear(g.dev(x), g.dev(packed[0]), sc, zr, group=group, bits=bits))
+    y_ref, b = oracle.linear(x, *packed, group=group, bits=bits)
     assert np.all(oracle.within_tolerance(y.astype(np.float64), y_ref, b))
     with pytest.raises(RuntimeError, match="aligned"):
-        lib.linear(g.dev(x), g.dev(packed[0]), sc, zr, group=group, path=3)
+        lib.linear(g.dev(x), g.dev(packed[0]), sc, zr, group=group, path=3, bits=bits)
+
+
+def test_skinny_3bit_group128_takes_2byte_aligned_scales(lib):
+    # with one scale per 128 inputs the small-batch kernel loads scales and zeros 2 bytes at a
+    # time, so 2-byte alignment is enough on the explicit path
+    torch, g = _torch(), _gpu()
+    n, k, m = 64, 1024, 4
+    s = oracle.channel_scale(synth.calibration(2, 18, k))
+    packed = oracle.quantize_pack(synth.weights(2, 18, n, k), s, bits=3, group=128)
+    x = oracle.scale_input(synth.activations(2, 18, m, k), s)
+    bufs = []
+    for a in packed[1:]:
+        buf = torch.empty(a.size + 1, dtype=torch.float16, device="cuda")
+        v = buf[1:].view(a.shape)
+        v.copy_(torch.from_numpy(a).to(v.device))
+        assert v.data_ptr() % 4 == 2
+        bufs.append(v)
+    print("linear 3-bit g128 2-byte aligned scales, path 3", flush=True)
+    y = g.host(lib.linear(g.dev(x), g.dev(packed[0]), *bufs, group=128, path=3, bits=3))
+    y_ref, b = oracle.linear(x, *packed, group=128, bits=3)
+    assert np.all(oracle.within_tolerance(y.astype(np.float64), y_ref, b))
 
 
 @pytest.mark.parametrize("bits,group", FORMATS)
@@ -171,7 +192,7 @@ def test_variants_on_edge_weights(lib, bits, group, kind):
     W = synth.edge_weights(kind, 96, 1024, seed=7)
     packed = oracle.quantize_pack(W, None, bits=bits, group=group)
     x = synth.activations(1, 8, 40, 1024)
-    cases = ((1, 1), (1, 8), (2, 3), (2, 40)) + (((3, 2), (3, 7), (3, 20)) if bits == 4 else ())
+    cases = ((1, 1), (1, 8), (2, 3), (2, 40), (3, 2), (3, 7), (3, 20))
     for path, m in cases:
         _linear_check(lib, x[:m], packed, bits, group, path, kind)
 

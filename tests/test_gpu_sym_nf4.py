@@ -59,7 +59,7 @@ def test_sym_linear_all_paths(lib, bits, group, m):
     packed = oracle.quantize_pack_sym(synth.weights(2, 8, n, k), s, bits=bits, group=group)
     x = oracle.scale_input(synth.activations(2, 8, m, k), s)
     y_ref, b = oracle.linear(x, *packed, group=group, bits=bits)
-    paths = [0, 2] + ([1] if m <= 8 else []) + ([3] if bits == 4 and m <= 32 else [])
+    paths = [0, 2] + ([1] if m <= 8 else []) + ([3] if m <= 32 else [])
     for path in paths:
         print(f"sym linear bits={bits} group={group} M={m} path={path}", flush=True)
         y = g.host(lib.linear(g.dev(x), *[g.dev(t) for t in packed], group=group, path=path, bits=bits))

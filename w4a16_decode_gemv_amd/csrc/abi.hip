@@ -133,16 +133,20 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   uint16_t* yh = static_cast<uint16_t*>(y);
   if (bits != 4 || group != 128) {
     const bool gemv_ok = w4a16::gemv_variant_supports(M, K, group);
-    // the small-batch kernel loads a row's scales (zeros) of 128 inputs in one 4- or 8-byte load
-    const bool skinny_ok = bits == 4 && M <= w4a16::skinny_max_m() && aligned(scales, 4) && aligned(zeros, 4);
+    // the small-batch kernel loads a row's scales (zeros) of 128 inputs in one 2-, 4- or 8-byte load
+    const uintptr_t sz_align = group == 128 ? 2 : 4;
+    const bool skinny_ok = M <= w4a16::skinny_max_m() && aligned(scales, sz_align) && aligned(zeros, sz_align);
     int32_t kernel = path;
     if (path == 0) {
-      kernel = auto_gemv_variant(M, N, K) && gemv_ok ? 1 : skinny_ok ? 3 : gemv_ok ? 1 : 2;
+      // 3-bit codes keep the GEMV variant at M = 2 on every shape: its dequant VALU is shared
+      // by both rows there (8192 -> 8192: 12.5 against 12.8 us for groups of 128, 12.6 against
+      // 13.3 for 64, 12.8 against 15.2 for 32)
+      const bool gemv_first = auto_gemv_variant(M, N, K) || (bits == 3 && M == 2);
+      kernel = gemv_first && gemv_ok ? 1 : skinny_ok ? 3 : gemv_ok ? 1 : 2;
     } else if (path == 1 && !gemv_ok) {
       return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel for this format takes M <= %d and K <= 32768 "
                   "(M <= 4 above K = 16384); got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
     } else if (path == 3) {
-      if (bits != 4) return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes 4-bit codes only");
       if (M > w4a16::skinny_max_m())
         return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes M <= %d; got M=%lld",
                     w4a16::skinny_max_m(), (long long)M);
@@ -153,7 +157,7 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
     if (kernel == 1)
       return hip_result(w4a16::launch_gemv_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
     if (kernel == 3)
-      return hip_result(w4a16::launch_skinny_variant(group, xh, qw, sc, zr, M, N, K, yh, stream),
+      return hip_result(w4a16::launch_skinny_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream),
                         "small-batch MFMA launch");
     return hip_result(w4a16::launch_mfma_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
   }
@@ -305,7 +309,8 @@ w4a16_status w3a16_linear_path(int32_t path, const void* x, const void* qweight,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
                                void* stream) {
   clear_error();
-  if (path < 0 || path > 2) return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV) or 2 (tiled MFMA)");
+  if (path < 0 || path > 3)
+    return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA) or 3 (small-batch MFMA)");
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
   return run_linear(3, path, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));

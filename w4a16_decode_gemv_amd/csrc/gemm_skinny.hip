@@ -52,6 +52,15 @@
 // in one load. NF4 codes become fp16 levels through a 16-entry codebook in LDS
 // (16 fp16 values: 8 banks, so every lookup is conflict-free or a broadcast) and
 // are scaled by the float32 absmax of the block; there is no zero.
+//
+// 3-bit codes (the packed 3-bit layout: per 32-input block, the low two bits of
+// inputs 0..15 and of 16..31 in two words, the high bits of all 32 in a third)
+// keep the k-slot assignment: step q is block q of the group, and slot group j
+// needs the low-bit word j / 2 of that block and its high-bit word. A stage is
+// 96 bytes per row (six 16-byte pieces, spread over the lanes); the LDS area holds
+// each row's two groups transposed, as [group][low word 0 | low word 1 | high
+// word][block], so that a lane reads its four steps' low words and high words in
+// two 16-byte reads.
 #include "device_utils.h"
 #include "launchers.h"
 
@@ -85,6 +94,28 @@ __device__ __forceinline__ half8_t codes_word(uint32_t w) {
   const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
                      __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
   return __builtin_bit_cast(half8_t, v);
+}
+
+// code formats of the kernel
+constexpr int kFmt4 = 0;    // 4-bit codes in layout v1, fp16 scales and zeros
+constexpr int kFmtNf4 = 1;  // 4-bit NF4 codes in layout v1, float32 absmax
+constexpr int kFmt3 = 2;    // 3-bit codes in the packed 3-bit layout, fp16 scales and zeros
+constexpr int kRowStride3 = 28;  // dwords per row of the 3-bit LDS area (24 used; 28 keeps 16 rows apart in banks)
+
+// the eight 3-bit codes q (exact fp16) that slot group j takes from one block: the low bits
+// of pairs 4(j % 2) .. 4(j % 2) + 3 of `lo`, the high bits at bits 4j + e and 16 + 4j + e of
+// `hi` (rotated to bits 2 and 18); OR-ed into 0x6400 and rebased by 1024 like the 4-bit codes
+__device__ __forceinline__ half8_t codes3_word(uint32_t lo, uint32_t hi, int j) {
+  const half2_t c_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
+  const uint32_t l = lo >> (8 * (j & 1));
+  const uint32_t h = __builtin_amdgcn_alignbit(hi, hi, (uint32_t)(4 * j + 30) & 31u);
+  uint32_t v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t t = and_or(h >> e, 0x00040004u, 0x64006400u);
+    v[e] = __builtin_bit_cast(uint32_t, as_half2(and_or(l >> (2 * e), 0x00030003u, t)) + c_lo);
+  }
+  return as_half8((u32x4_t){v[0], v[1], v[2], v[3]});
 }
 
 // the eight NF4 codes of one code word as their fp16 levels, in k order
@@ -126,19 +157,22 @@ __device__ __forceinline__ void load_item(__amdgpu_buffer_rsrc_t r, int off, uin
 // fragments through a wave-private LDS area; XI = 0: A fragments loaded straight from L2.
 // "Group" below is a 128-input group of the code stream; SUB = 128 / (quantization group)
 // scales per row and group (NF4: float32 absmax values passed through `scales`, no zeros).
-template <int NTW, int MT, int NS, int XI, int SUB, bool NF4>
+template <int NTW, int MT, int NS, int XI, int SUB, int FMT>
 __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
                                                          const void* __restrict__ scales,
                                                          const uint16_t* __restrict__ zeros, int M, int N, int K,
                                                          Nf4Table table, uint16_t* __restrict__ y) {
+  constexpr bool NF4 = FMT == kFmtNf4, B3 = FMT == kFmt3;
   constexpr int ROWS = 16 * NTW;
   constexpr int CG = 2 * NS;                       // groups per wave and chunk
+  constexpr int CL = B3 ? (6 * ROWS + 63) / 64 : 2 * NTW;  // 16-byte code loads per lane and stage
   constexpr int SZL = (ROWS * CG + 63) / 64;       // (row, group) scale items per lane and chunk
   constexpr int QS = 4 / SUB;                      // MFMA steps per quantization group
   constexpr int IB = (NF4 ? 4 : 2) * SUB;          // bytes of one scale item (per tensor)
   constexpr int IW = IB >= 4 ? IB / 4 : 1;         // 32-bit words holding it
   static_assert(SUB == 1 || SUB == 2 || SUB == 4, "groups of 128, 64 or 32");
   static_assert(ROWS * 8 >= NTW * MT * 64, "the final combine reuses the code staging area");
+  static_assert(kRowStride3 <= 32, "the 3-bit staging area fits the 4-bit one");
   __shared__ u32x4_t lds_b[KS][ROWS * 8];            // one stage of codes: ROWS x (2 groups x 4 slots)
   __shared__ uint32_t lds_sz[KS][ROWS][CG * SUB + 1];  // one chunk of (scale | zero << 16), or absmax
   __shared__ u32x4_t lds_x[XI > 0 ? KS : 1][XI > 0 ? D : 1][XI > 0 ? 2 * XI : 1][33];  // x rows, padded
@@ -159,8 +193,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
   const int nchunks = (((G + KS - 1) / KS) + CG - 1) / CG;
 
   // buffer views: this workgroup's code, scale and zero rows, and all of x
-  const __amdgpu_buffer_rsrc_t q_rsrc =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(qw + (int64_t)n0 * (K >> 3)), (short)0, rows * (K >> 1), kBufferFlags);
+  const int row_bytes = B3 ? 3 * (K >> 3) : K >> 1;  // code bytes per row
+  const __amdgpu_buffer_rsrc_t q_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const uint8_t*>(qw) + (int64_t)n0 * row_bytes), (short)0, rows * row_bytes, kBufferFlags);
   const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(static_cast<const uint8_t*>(scales) + (int64_t)n0 * G * IB), (short)0, rows * G * IB, kBufferFlags);
   const __amdgpu_buffer_rsrc_t z_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -195,18 +230,30 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
       if constexpr (!NF4) load_item<IB>(z_rsrc, o, zv[e]);
     }
 
-    u32x4_t cr[D][NTW][2];
+    u32x4_t cr[D][CL];
     u32x4_t xr[D][2][MT][4];
     u32x4_t xl[D][XI > 0 ? XI : 1];
     auto load_codes = [&](int s, int slot) {
+      if constexpr (B3) {
+        // piece p = lane + 64 i: row p / 6, 16-byte piece p % 6 of the row's 96 bytes (pieces
+        // 0..2 group 2s, 3..5 group 2s + 1); rows from ROWS on are past the buffer range
+#pragma unroll
+        for (int i = 0; i < CL; ++i) {
+          const int p = lane + 64 * i, row = p / 6, piece = p - 6 * row;
+          const int gi = 2 * s + (int)(piece >= 3);
+          cr[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(
+              q_rsrc, row * row_bytes + (g0 + 2 * s) * 48 + 16 * piece + bias(gi), 0, kNonTemporal);
+        }
+        return;
+      }
       const int gi = 2 * s + (lq >> 2);
       const int off = (g0 + gi) * 64 + 16 * (lq & 3) + bias(gi);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
         for (int h = 0; h < 2; ++h)
-          cr[slot][nt][h] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off + (16 * nt + 8 * h + lr) * (K >> 1), 0,
-                                                                  kNonTemporal);
+          cr[slot][2 * nt + h] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off + (16 * nt + 8 * h + lr) * (K >> 1), 0,
+                                                                       kNonTemporal);
     };
     auto load_x = [&](int s, int slot) {
       if constexpr (XI > 0) {
@@ -254,9 +301,25 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       const int u = s % D;
-      // stage codes -> LDS: piece lq holds words 4(lq%4) .. +3 of group lq/4; word 4p + e goes to
-      // slot (row, group, j = e) at dword p
-      {
+      if constexpr (B3) {
+        // stage codes -> LDS: word 4 piece + e of the row's 24 is word wi = that % 12 of group
+        // that / 12, i.e. kind wi % 3 (low 0, low 1, high) of block wi / 3
+#pragma unroll
+        for (int i = 0; i < CL; ++i) {
+          const int p = lane + 64 * i, row = p / 6, piece = p - 6 * row;
+          const u32x4_t v = cr[u][i];
+          const uint32_t vw[4] = {v.x, v.y, v.z, v.w};
+          if (p < 6 * ROWS) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int wd = 4 * piece + e, gsw = wd / 12, wi = wd - 12 * gsw;
+              lds_words[row * kRowStride3 + gsw * 12 + (wi % 3) * 4 + wi / 3] = vw[e];
+            }
+          }
+        }
+      } else {
+        // stage codes -> LDS: piece lq holds words 4(lq%4) .. +3 of group lq/4; word 4p + e goes
+        // to slot (row, group, j = e) at dword p
         const int gs = lq >> 2, p = lq & 3;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
@@ -264,7 +327,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
           for (int h = 0; h < 2; ++h) {
             const int row = 16 * nt + 8 * h + lr;
             const int swz = (row >> 1) & 7;
-            const u32x4_t v = cr[u][nt][h];
+            const u32x4_t v = cr[u][2 * nt + h];
             lds_words[(row * 8 + ((gs * 4 + 0) ^ swz)) * 4 + p] = v.x;
             lds_words[(row * 8 + ((gs * 4 + 1) ^ swz)) * 4 + p] = v.y;
             lds_words[(row * 8 + ((gs * 4 + 2) ^ swz)) * 4 + p] = v.z;
@@ -306,7 +369,6 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           const int row = 16 * nt + c;
-          const u32x4_t wq = lds_b[w][row * 8 + ((gs * 4 + j) ^ ((row >> 1) & 7))];
           float d[SUB], zf[SUB];
 #pragma unroll
           for (int sub = 0; sub < SUB; ++sub) {
@@ -320,12 +382,21 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
             }
           }
           half8_t b[4];
-          if constexpr (NF4) {
+          if constexpr (B3) {
+            const u32x4_t lo = *reinterpret_cast<const u32x4_t*>(&lds_words[row * kRowStride3 + gs * 12 + (j >> 1) * 4]);
+            const u32x4_t hi = *reinterpret_cast<const u32x4_t*>(&lds_words[row * kRowStride3 + gs * 12 + 8]);
+            b[0] = codes3_word(lo.x, hi.x, j);
+            b[1] = codes3_word(lo.y, hi.y, j);
+            b[2] = codes3_word(lo.z, hi.z, j);
+            b[3] = codes3_word(lo.w, hi.w, j);
+          } else if constexpr (NF4) {
+            const u32x4_t wq = lds_b[w][row * 8 + ((gs * 4 + j) ^ ((row >> 1) & 7))];
             b[0] = nf4_word(wq.x, lut);
             b[1] = nf4_word(wq.y, lut);
             b[2] = nf4_word(wq.z, lut);
             b[3] = nf4_word(wq.w, lut);
           } else {
+            const u32x4_t wq = lds_b[w][row * 8 + ((gs * 4 + j) ^ ((row >> 1) & 7))];
             b[0] = codes_word(wq.x);
             b[1] = codes_word(wq.y);
             b[2] = codes_word(wq.z);
@@ -390,40 +461,40 @@ struct Args {
   hipStream_t stream;
 };
 
-template <int NTW, int MT, int NS, int XI, int SUB, bool NF4>
+template <int NTW, int MT, int NS, int XI, int SUB, int FMT>
 hipError_t launch_tile_x(const Args& a) {
   const dim3 grid((unsigned)((a.N + 16 * NTW - 1) / (16 * NTW)));
-  hipLaunchKernelGGL((skinny_kernel<NTW, MT, NS, XI, SUB, NF4>), grid, dim3(kThreads), 0, a.stream, a.x, a.qweight,
+  hipLaunchKernelGGL((skinny_kernel<NTW, MT, NS, XI, SUB, FMT>), grid, dim3(kThreads), 0, a.stream, a.x, a.qweight,
                      a.scales, a.zeros, (int)a.M, (int)a.N, (int)a.K, a.table, a.y);
   return hipGetLastError();
 }
 
 // M <= 8 (MT = 1): x rows through LDS in M/2 full-width loads; otherwise 16-row fragment loads
 // (two column tiles with groups of 32 meet M <= 8 in two-stage chunks only)
-template <int NTW, int MT, int NS, int SUB, bool NF4>
+template <int NTW, int MT, int NS, int SUB, int FMT>
 hipError_t launch_tile(const Args& a) {
   if constexpr (MT == 1 && !(NTW == 2 && SUB == 4 && NS > 2)) {
-    if (a.M <= 2) return launch_tile_x<NTW, MT, NS, 1, SUB, NF4>(a);
-    if (a.M <= 4) return launch_tile_x<NTW, MT, NS, 2, SUB, NF4>(a);
-    if (a.M <= 8) return launch_tile_x<NTW, MT, NS, 4, SUB, NF4>(a);
+    if (a.M <= 2) return launch_tile_x<NTW, MT, NS, 1, SUB, FMT>(a);
+    if (a.M <= 4) return launch_tile_x<NTW, MT, NS, 2, SUB, FMT>(a);
+    if (a.M <= 8) return launch_tile_x<NTW, MT, NS, 4, SUB, FMT>(a);
   }
-  return launch_tile_x<NTW, MT, NS, 0, SUB, NF4>(a);
+  return launch_tile_x<NTW, MT, NS, 0, SUB, FMT>(a);
 }
 
-// stages per chunk: enough for the wave's whole share, up to CAP (2 or 8; 4 at most with
+// stages per chunk: enough for the wave's whole share, up to CAP (2, 4 or 8; 4 at most with
 // groups of 32, whose chunk of scales is four times as large)
-template <int NTW, int MT, int SUB, bool NF4, int CAP>
+template <int NTW, int MT, int SUB, int FMT, int CAP>
 hipError_t launch_stages(const Args& a) {
   const int64_t stages = ((a.K / 128 + KS - 1) / KS + 1) / 2;  // per wave
   if constexpr (CAP == 2) {
-    return launch_tile<NTW, MT, 2, SUB, NF4>(a);
-  } else if constexpr (SUB == 4) {
-    return stages <= 2 ? launch_tile<NTW, MT, 2, SUB, NF4>(a) : launch_tile<NTW, MT, 4, SUB, NF4>(a);
+    return launch_tile<NTW, MT, 2, SUB, FMT>(a);
+  } else if constexpr (SUB == 4 || CAP == 4) {
+    return stages <= 2 ? launch_tile<NTW, MT, 2, SUB, FMT>(a) : launch_tile<NTW, MT, 4, SUB, FMT>(a);
   } else {
-    if (stages <= 2) return launch_tile<NTW, MT, 2, SUB, NF4>(a);
-    if (stages <= 4) return launch_tile<NTW, MT, 4, SUB, NF4>(a);
-    if (stages <= 6) return launch_tile<NTW, MT, 6, SUB, NF4>(a);
-    return launch_tile<NTW, MT, kMaxStages, SUB, NF4>(a);
+    if (stages <= 2) return launch_tile<NTW, MT, 2, SUB, FMT>(a);
+    if (stages <= 4) return launch_tile<NTW, MT, 4, SUB, FMT>(a);
+    if (stages <= 6) return launch_tile<NTW, MT, 6, SUB, FMT>(a);
+    return launch_tile<NTW, MT, kMaxStages, SUB, FMT>(a);
   }
 }
 
@@ -439,26 +510,44 @@ hipError_t launch_stages(const Args& a) {
 //     at two m-tiles (M = 32: 25.2 against 27.0 us), NF4 at M = 5..8 (15.2 against
 //     16.6 us) and NF4 blocks of 32 with one column tile at M <= 4;
 //   * groups of 128 at two m-tiles keep two column tiles only up to 4 stages per wave (beyond
-//     that the two-tile variant runs out of registers).
-template <int SUB, bool NF4>
+//     that the two-tile variant runs out of registers);
+//   * 3-bit codes have rules of their own (below).
+template <int SUB, int FMT>
 hipError_t launch_format(const Args& a) {
-  constexpr bool zp = !NF4;
+  constexpr bool NF4 = FMT == kFmtNf4, B3 = FMT == kFmt3, zp = !NF4;
   const int64_t M = a.M;
   const bool wide = (a.N + 31) / 32 >= 256;
-  if (M <= 4 || !wide || (a.K <= 4096 && M <= 8)) {
-    const bool many = (a.N + 15) / 16 > 256;  // more than one one-tile workgroup per CU
-    if (M > 16) return launch_stages<1, 2, SUB, NF4, zp && SUB == 4 ? 2 : 8>(a);
-    if ((zp && SUB == 4) || (zp && SUB == 2 && M <= 4 && many) || (NF4 && SUB == 4 && M <= 4))
-      return launch_stages<1, 1, SUB, NF4, 2>(a);
-    return launch_stages<1, 1, SUB, NF4, 8>(a);
-  }
-  if (M <= 8) return launch_stages<2, 1, SUB, NF4, SUB == 4 || NF4 ? 2 : 8>(a);
-  if (M <= 16) return launch_stages<2, 1, SUB, NF4, 8>(a);
-  if constexpr (SUB == 1 && zp) {
-    const bool short_k = ((a.K / 128 + KS - 1) / KS + 1) / 2 <= 4;
-    return short_k ? launch_stages<2, 2, SUB, NF4, 8>(a) : launch_stages<1, 2, SUB, NF4, 8>(a);
+  if constexpr (B3) {
+    // 3-bit codes, measured the same way (their dequant holds more registers and VALU time):
+    // one column tile on narrow layers (full chunks for groups of 128 up to M = 16) and for
+    // groups of 128 on K <= 4096 up to M = 4; otherwise two column tiles, with the two-stage
+    // cap up to M = 8 (groups of 64, M = 4: 13.2 against 17.0 us with one tile) and for
+    // groups of 32 at two m-tiles (groups of 64 there: four stages, as eight spill)
+    if (!wide) {
+      if (M > 16) return launch_stages<1, 2, SUB, FMT, 2>(a);
+      if constexpr (SUB == 1) return launch_stages<1, 1, SUB, FMT, 8>(a);
+      else return launch_stages<1, 1, SUB, FMT, 2>(a);
+    }
+    if (SUB == 1 && a.K <= 4096 && M <= 4) return launch_stages<1, 1, SUB, FMT, 2>(a);
+    if (M <= 8) return launch_stages<2, 1, SUB, FMT, 2>(a);
+    if (M <= 16) return launch_stages<2, 1, SUB, FMT, 8>(a);
+    return launch_stages<2, 2, SUB, FMT, SUB == 4 ? 2 : SUB == 2 ? 4 : 8>(a);
   } else {
-    return launch_stages<2, 2, SUB, NF4, zp ? 2 : 8>(a);
+    if (M <= 4 || !wide || (a.K <= 4096 && M <= 8)) {
+      const bool many = (a.N + 15) / 16 > 256;  // more than one one-tile workgroup per CU
+      if (M > 16) return launch_stages<1, 2, SUB, FMT, zp && SUB == 4 ? 2 : 8>(a);
+      if ((zp && SUB == 4) || (zp && SUB == 2 && M <= 4 && many) || (NF4 && SUB == 4 && M <= 4))
+        return launch_stages<1, 1, SUB, FMT, 2>(a);
+      return launch_stages<1, 1, SUB, FMT, 8>(a);
+    }
+    if (M <= 8) return launch_stages<2, 1, SUB, FMT, SUB == 4 || NF4 ? 2 : 8>(a);
+    if (M <= 16) return launch_stages<2, 1, SUB, FMT, 8>(a);
+    if constexpr (SUB == 1 && FMT == kFmt4) {
+      const bool short_k = ((a.K / 128 + KS - 1) / KS + 1) / 2 <= 4;
+      return short_k ? launch_stages<2, 2, SUB, FMT, 8>(a) : launch_stages<1, 2, SUB, FMT, 8>(a);
+    } else {
+      return launch_stages<2, 2, SUB, FMT, zp ? 2 : 8>(a);
+    }
   }
 }
 
@@ -468,25 +557,31 @@ int skinny_max_m() { return 32; }
 
 hipError_t launch_skinny(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  return launch_format<1, false>({x, qweight, scales, zeros, M, N, K, {}, y, stream});
+  return launch_format<1, kFmt4>({x, qweight, scales, zeros, M, N, K, {}, y, stream});
 }
 
-hipError_t launch_skinny_variant(int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
-                                 const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                                 hipStream_t stream) {
+hipError_t launch_skinny_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight,
+                                 const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, hipStream_t stream) {
   const Args a = {x, qweight, scales, zeros, M, N, K, {}, y, stream};
-  if (group == 128) return launch_format<1, false>(a);
-  if (group == 64) return launch_format<2, false>(a);
-  if (group == 32) return launch_format<4, false>(a);
+  if (bits == 4) {
+    if (group == 128) return launch_format<1, kFmt4>(a);
+    if (group == 64) return launch_format<2, kFmt4>(a);
+    if (group == 32) return launch_format<4, kFmt4>(a);
+  } else if (bits == 3) {
+    if (group == 128) return launch_format<1, kFmt3>(a);
+    if (group == 64) return launch_format<2, kFmt3>(a);
+    if (group == 32) return launch_format<4, kFmt3>(a);
+  }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_skinny_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
                              const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const Args a = {x, qweight, absmax, nullptr, M, N, K, table, y, stream};
-  if (block == 128) return launch_format<1, true>(a);
-  if (block == 64) return launch_format<2, true>(a);
-  if (block == 32) return launch_format<4, true>(a);
+  if (block == 128) return launch_format<1, kFmtNf4>(a);
+  if (block == 64) return launch_format<2, kFmtNf4>(a);
+  if (block == 32) return launch_format<4, kFmtNf4>(a);
   return hipErrorInvalidValue;
 }
 

@@ -46,16 +46,17 @@ hipError_t launch_gemv_variant(int bits, int group, const uint16_t* x, const uin
                                const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream);
 
-// Small-batch MFMA kernel: needs M <= skinny_max_m(). The variant takes 4-bit codes with
-// groups of 32, 64 or 128 (scales and zeros 4-byte aligned below groups of 128), the NF4
-// entry point float32 absmax per block of 32, 64 or 128.
+// Small-batch MFMA kernel: needs M <= skinny_max_m(). The variant takes 4-bit codes (layout
+// v1) or 3-bit codes (the packed 3-bit layout) with groups of 32, 64 or 128 (scales and zeros
+// 4-byte aligned below groups of 128), the NF4 entry point float32 absmax per block of 32, 64
+// or 128.
 int skinny_max_m();
 hipError_t launch_skinny(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                          const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                          hipStream_t stream);
-hipError_t launch_skinny_variant(int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
-                                 const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
-                                 hipStream_t stream);
+hipError_t launch_skinny_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight,
+                                 const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
+                                 uint16_t* y, hipStream_t stream);
 hipError_t launch_skinny_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
                              const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
