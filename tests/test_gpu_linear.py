@@ -76,6 +76,24 @@ def test_skinny_small_shapes(lib, m, n, k):
     _check(lib, xs, qw, sc, zr, path=3, tag="skinny")
 
 
+@pytest.mark.parametrize("m", [33, 40, 48, 63, 64])
+@pytest.mark.parametrize("n,k", [(300, 2048), (97, 11008), (8192, 1024)])
+def test_auto_two_small_batch_passes(lib, m, n, k):
+    # 33 <= M <= 64 on layers with N <= 8192 and K <= 16384: the automatic path runs the
+    # small-batch kernel on rows 0..31 and then on the rest; every row against the oracle, and
+    # the result equals the small-batch kernel run on the two row blocks separately
+    import torch
+
+    g = _gpu()
+    xs, qw, sc, zr = _packed(4, 60 + m, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=0, tag="auto-two-passes")
+    dev = [g.dev(t) for t in (xs, qw, sc, zr)]
+    y = g.host(lib.linear(*dev))
+    y1 = g.host(lib.linear(dev[0][:32].contiguous(), *dev[1:], path=3))
+    y2 = g.host(lib.linear(dev[0][32:].contiguous(), *dev[1:], path=3))
+    assert np.array_equal(y.view(np.uint16), np.concatenate([y1, y2]).view(np.uint16))
+
+
 def test_skinny_long_rows(lib):
     for m, k in [(2, 22016), (9, 65536), (32, 22016)]:
         xs, qw, sc, zr = _packed(4, 41, 70, k, m)

@@ -162,13 +162,22 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
     return hip_result(w4a16::launch_mfma_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
   }
   int32_t kernel = path;
+  bool two_passes = false;
   if (path == 0) {
-    if (auto_gemv(M, N, K) && w4a16::gemv_supports(M, K))
+    if (auto_gemv(M, N, K) && w4a16::gemv_supports(M, K)) {
       kernel = 1;
-    else if (M <= w4a16::skinny_max_m())
+    } else if (M <= w4a16::skinny_max_m()) {
       kernel = 3;
-    else
+    } else if (M <= 2 * w4a16::skinny_max_m() && N <= 8192 && K <= 16384) {
+      // the small-batch kernel twice (rows 0..31, then the rest) against the tiled kernel,
+      // M = 33..64: 14.9-20.9 against 26.0-26.7 us at 4096 -> 4096, 33.1-46.9 against
+      // 47.2-49.2 at 8192 -> 8192, 34.0-51.2 against 61.8-63.8 at 11008 -> 4096; on wider or
+      // longer layers (4096 -> 11008, 8192 -> 22016, 22016 -> 8192) the tiled kernel is ahead
+      kernel = 3;
+      two_passes = true;
+    } else {
       kernel = 2;
+    }
   } else if (path == 1 && !w4a16::gemv_supports(M, K)) {
     return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel takes M <= %d (M * ceil(K / 16384) <= 8); got M=%lld K=%lld",
                 w4a16::gemv_max_m(), (long long)M, (long long)K);
@@ -177,6 +186,12 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
                 w4a16::skinny_max_m(), (long long)M);
   }
   if (kernel == 1) return hip_result(w4a16::launch_gemv(xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
+  if (kernel == 3 && two_passes) {
+    const int64_t m1 = w4a16::skinny_max_m();
+    hipError_t e = w4a16::launch_skinny(xh, qw, sc, zr, m1, N, K, yh, stream);
+    if (e == hipSuccess) e = w4a16::launch_skinny(xh + m1 * K, qw, sc, zr, M - m1, N, K, yh + m1 * N, stream);
+    return hip_result(e, "small-batch MFMA launch");
+  }
   if (kernel == 3)
     return hip_result(w4a16::launch_skinny(xh, qw, sc, zr, M, N, K, yh, stream), "small-batch MFMA launch");
   return hip_result(w4a16::launch_mfma(xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
