@@ -184,10 +184,11 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * on layers with N <= 8192 and K <= 16384 the small-batch kernel in two
  * launches (rows 0..31, then the rest); other M the tiled MFMA kernel.
  * Groups of 32 and 64: M == 1, and M == 2 on layers with K <= 16384 and
- * N * K >= 2^27, run the GEMV kernel's variant; other M <= 32
- * the small-batch MFMA kernel (which needs scales and zeros 4-byte aligned;
- * otherwise the GEMV variant takes M <= 8, M <= 4 above K = 16384); larger M
- * the tiled MFMA kernel's variant (one (scale, zero) per 32-input MFMA step).
+ * N * K >= 2^27, run the GEMV kernel's variant; other M <= 32 the small-batch
+ * MFMA kernel (which needs scales and zeros 4-byte aligned; otherwise the GEMV
+ * variant takes M <= 8, M <= 4 above K = 16384), and 33 <= M <= 64 the same
+ * two launches as for group 128 on the same layers; other M the tiled MFMA
+ * kernel's variant (one (scale, zero) per 32-input MFMA step).
  * Alignment: x and qweight 16 bytes, scales/zeros/y 2 bytes.
  */
 w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
@@ -241,7 +242,9 @@ w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void*
  * K % 128 == 0. Dispatch: M <= 2 the GEMV kernel's 3-bit variant (M == 2 up
  * to K = 32768); other M <= 32 the small-batch MFMA kernel's (scales and zeros
  * 4-byte aligned below groups of 128, else the GEMV variant up to M = 8, M = 4
- * above K = 16384); larger M the tiled MFMA kernel's 3-bit variant.
+ * above K = 16384); 33 <= M <= 64 on layers with N <= 8192 and K <= 16384
+ * two small-batch launches (rows 0..31, then the rest); other M the tiled MFMA
+ * kernel's 3-bit variant.
  */
 w4a16_status w3a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
@@ -377,8 +380,9 @@ w4a16_status nf4_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * qweight, absmax as nf4_quantize_pack writes them; y: fp16 [M][N]; block 32,
  * 64 or 128; K % 128 == 0. Dispatch: M == 1, and M == 2 on layers with
  * K <= 16384 and N * K >= 2^27, the GEMV kernel's NF4 variant (the codebook in
- * LDS); other M <= 32 the small-batch MFMA kernel's; larger M the tiled MFMA
- * kernel's. Alignment: x and qweight 16 bytes, absmax 4, y 2.
+ * LDS); other M <= 32 the small-batch MFMA kernel's, and 33 <= M <= 64 on
+ * layers with N <= 8192 and K <= 16384 two small-batch launches (rows 0..31,
+ * then the rest); other M the tiled MFMA kernel's. Alignment: x and qweight 16 bytes, absmax 4, y 2.
  */
 w4a16_status nf4_linear(const void* x, const void* qweight, const float* absmax, int64_t M, int64_t N,
                         int64_t K, int32_t block, void* y, void* stream);

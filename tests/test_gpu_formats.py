@@ -228,3 +228,22 @@ def test_auto_dispatch_and_determinism(lib, bits, group):
         assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
         y_ref, b = oracle.linear(x, *packed, group=group, bits=bits)
         assert np.all(oracle.within_tolerance(y1.astype(np.float64), y_ref, b))
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("m", [40, 64])
+@pytest.mark.parametrize("n,k", [(300, 2048), (97, 11008)])
+def test_auto_two_small_batch_passes(lib, bits, group, m, n, k):
+    # 33 <= M <= 64 on layers with N <= 8192 and K <= 16384: the automatic path runs the
+    # small-batch kernel on rows 0..31 and then on the rest
+    g = _gpu()
+    s = oracle.channel_scale(synth.calibration(2, 19, k))
+    packed = oracle.quantize_pack(synth.weights(2, 19, n, k), s, bits=bits, group=group)
+    x = oracle.scale_input(synth.activations(2, 19, m, k), s)
+    _linear_check(lib, x, packed, bits, group, 0, "auto-two-passes")
+    dev = [g.dev(t) for t in packed]
+    xd = g.dev(x)
+    y = g.host(lib.linear(xd, *dev, group=group, bits=bits))
+    y1 = g.host(lib.linear(xd[:32].contiguous(), *dev, group=group, bits=bits, path=3))
+    y2 = g.host(lib.linear(xd[32:].contiguous(), *dev, group=group, bits=bits, path=3))
+    assert np.array_equal(y.view(np.uint16), np.concatenate([y1, y2]).view(np.uint16))

@@ -169,3 +169,18 @@ def test_nf4_full_size_sampled_and_deterministic(lib, m):
     rows = np.linspace(0, 8191, 256).astype(int)
     y_ref, b = oracle.linear_nf4(x, g.host_u32(qw_d), g.host(a_d), 64, rows=rows)
     assert np.all(oracle.within_tolerance(y1[:, rows].astype(np.float64), y_ref, b))
+
+
+@pytest.mark.parametrize("block", [64, 32])
+@pytest.mark.parametrize("m", [40, 64])
+def test_nf4_auto_two_small_batch_passes(lib, block, m):
+    # 33 <= M <= 64 on a layer with N <= 8192 and K <= 16384: two small-batch launches
+    g = _gpu()
+    qw, a = oracle.quantize_pack_nf4(synth.weights(3, 8, 300, 2048), None, block)
+    x = synth.activations(3, 8, m, 2048)
+    _nf4_linear_check(lib, x, qw, a, block, 0, "auto-two-passes")
+    qd, ad, xd = g.dev(qw), g.dev(a), g.dev(x)
+    y = g.host(lib.nf4_linear(xd, qd, ad, block=block))
+    y1 = g.host(lib.nf4_linear(xd[:32].contiguous(), qd, ad, block=block, path=3))
+    y2 = g.host(lib.nf4_linear(xd[32:].contiguous(), qd, ad, block=block, path=3))
+    assert np.array_equal(y.view(np.uint16), np.concatenate([y1, y2]).view(np.uint16))

@@ -47,6 +47,15 @@ bool auto_gemv_variant(int64_t M, int64_t N, int64_t K) {
   return M == 1 || (M == 2 && K <= 16384 && N * K >= (int64_t(1) << 27));
 }
 
+// 33 <= M <= 64 on layers with N <= 8192 and K <= 16384: the small-batch kernel twice (rows
+// 0..31, then the rest) beats the tiled kernel there, for every code format (group 128:
+// 14.9-20.9 against 26.0-26.7 us at 4096 -> 4096, 33.1-46.9 against 47.2-49.2 at 8192 -> 8192,
+// 34.0-51.2 against 61.8-63.8 at 11008 -> 4096); on wider or longer layers (4096 -> 11008,
+// 8192 -> 22016, 22016 -> 8192) the tiled kernel is ahead
+bool two_small_batch_passes(int64_t M, int64_t N, int64_t K) {
+  return M > w4a16::skinny_max_m() && M <= 2 * w4a16::skinny_max_m() && N <= 8192 && K <= 16384;
+}
+
 w4a16_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return W4A16_OK;
@@ -135,14 +144,17 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
     const bool gemv_ok = w4a16::gemv_variant_supports(M, K, group);
     // the small-batch kernel loads a row's scales (zeros) of 128 inputs in one 2-, 4- or 8-byte load
     const uintptr_t sz_align = group == 128 ? 2 : 4;
-    const bool skinny_ok = M <= w4a16::skinny_max_m() && aligned(scales, sz_align) && aligned(zeros, sz_align);
+    const bool sz_aligned = aligned(scales, sz_align) && aligned(zeros, sz_align);
+    const bool skinny_ok = M <= w4a16::skinny_max_m() && sz_aligned;
+    bool two_passes = false;
     int32_t kernel = path;
     if (path == 0) {
       // 3-bit codes keep the GEMV variant at M = 2 on every shape: its dequant VALU is shared
       // by both rows there (8192 -> 8192: 12.5 against 12.8 us for groups of 128, 12.6 against
       // 13.3 for 64, 12.8 against 15.2 for 32)
       const bool gemv_first = auto_gemv_variant(M, N, K) || (bits == 3 && M == 2);
-      kernel = gemv_first && gemv_ok ? 1 : skinny_ok ? 3 : gemv_ok ? 1 : 2;
+      two_passes = sz_aligned && two_small_batch_passes(M, N, K);
+      kernel = gemv_first && gemv_ok ? 1 : skinny_ok || two_passes ? 3 : gemv_ok ? 1 : 2;
     } else if (path == 1 && !gemv_ok) {
       return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel for this format takes M <= %d and K <= 32768 "
                   "(M <= 4 above K = 16384); got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
@@ -156,6 +168,13 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
     }
     if (kernel == 1)
       return hip_result(w4a16::launch_gemv_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream), "GEMV launch");
+    if (kernel == 3 && two_passes) {
+      const int64_t m1 = w4a16::skinny_max_m();
+      hipError_t e = w4a16::launch_skinny_variant(bits, group, xh, qw, sc, zr, m1, N, K, yh, stream);
+      if (e == hipSuccess)
+        e = w4a16::launch_skinny_variant(bits, group, xh + m1 * K, qw, sc, zr, M - m1, N, K, yh + m1 * N, stream);
+      return hip_result(e, "small-batch MFMA launch");
+    }
     if (kernel == 3)
       return hip_result(w4a16::launch_skinny_variant(bits, group, xh, qw, sc, zr, M, N, K, yh, stream),
                         "small-batch MFMA launch");
@@ -168,11 +187,7 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
       kernel = 1;
     } else if (M <= w4a16::skinny_max_m()) {
       kernel = 3;
-    } else if (M <= 2 * w4a16::skinny_max_m() && N <= 8192 && K <= 16384) {
-      // the small-batch kernel twice (rows 0..31, then the rest) against the tiled kernel,
-      // M = 33..64: 14.9-20.9 against 26.0-26.7 us at 4096 -> 4096, 33.1-46.9 against
-      // 47.2-49.2 at 8192 -> 8192, 34.0-51.2 against 61.8-63.8 at 11008 -> 4096; on wider or
-      // longer layers (4096 -> 11008, 8192 -> 22016, 22016 -> 8192) the tiled kernel is ahead
+    } else if (two_small_batch_passes(M, N, K)) {
       kernel = 3;
       two_passes = true;
     } else {
@@ -413,10 +428,17 @@ w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, c
   uint16_t* yh = static_cast<uint16_t*>(y);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   int32_t kernel = path;
+  const bool two_passes = path == 0 && two_small_batch_passes(M, N, K);
   if (path == 0)
-    kernel = auto_gemv_variant(M, N, K) && gemv_ok ? 1 : M <= w4a16::skinny_max_m() ? 3 : gemv_ok ? 1 : 2;
+    kernel = auto_gemv_variant(M, N, K) && gemv_ok ? 1 : M <= w4a16::skinny_max_m() || two_passes ? 3 : gemv_ok ? 1 : 2;
   if (kernel == 1)
     return hip_result(w4a16::launch_gemv_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs), "NF4 GEMV launch");
+  if (kernel == 3 && two_passes) {
+    const int64_t m1 = w4a16::skinny_max_m();
+    hipError_t e = w4a16::launch_skinny_nf4(nf4_table(), block, xh, qw, absmax, m1, N, K, yh, hs);
+    if (e == hipSuccess) e = w4a16::launch_skinny_nf4(nf4_table(), block, xh + m1 * K, qw, absmax, M - m1, N, K, yh + m1 * N, hs);
+    return hip_result(e, "NF4 small-batch MFMA launch");
+  }
   if (kernel == 3)
     return hip_result(w4a16::launch_skinny_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs),
                       "NF4 small-batch MFMA launch");
