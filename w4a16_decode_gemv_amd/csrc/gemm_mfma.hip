@@ -48,7 +48,7 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;          // output columns per workgroup (4 waves x 16)
 constexpr int kThreads = 256;
-constexpr int kRing = 2;        // groups whose global loads are in flight (tuned 4-bit kernel)
+constexpr int kRing = 2;        // stages whose global loads are in flight
 
 __device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   const u32x4_t v = {a, b, c, d};
@@ -288,6 +288,7 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
   constexpr int BM = 16 * MB;
   constexpr int AU = (BM * 16 + kThreads - 1) / kThreads;
   constexpr bool NF4 = BITS == kNF4;
+  constexpr int RING = MB == 4 ? kRing : 1;
   constexpr int WPS = BITS == 3 ? 12 : 16;  // code words per row per stage
   __shared__ VarSmem<MB, BITS> sm;
   __shared__ __align__(16) _Float16 lut[16];
@@ -319,38 +320,41 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
   // (scale, zero) staging: thread t -> row t / 4, step t % 4
   const int s_row = min(n0 + (t >> 2), N - 1), s_st = t & 3;
 
-  uint4 areg[AU];
-  uint4 breg = {0u, 0u, 0u, 0u};
-  // scale and zero stay in separate registers until the LDS store: combining them at
-  // load time would make the wave wait for those loads at once
-  uint32_t sreg = 0;
-  uint16_t zreg = 0;
-  auto load_stage = [&](int g) {
+  // register ring of RING stages, as in the 4-bit kernel, with 64-row tiles only (same-box
+  // medians, outputs bit-identical: 1-5.5 % faster at M = 256 on 8192 -> 8192 and
+  // 4096 -> 11008; with 32-row tiles neutral to 12 % slower, NF4 worst); scale and zero stay in separate
+  // registers until the LDS store: combining them at load time would make the wave wait for
+  // those loads at once
+  u32x4_t areg[RING][AU];
+  u32x4_t breg[RING] = {};
+  uint32_t sreg[RING] = {};
+  uint16_t zreg[RING] = {};
+  auto load_stage = [&](int g, int sl) {
 #pragma unroll
     for (int u = 0; u < AU; ++u) {
       const int i = t + u * kThreads;
       const int r = i >> 4, ch = i & 15;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (i < BM * 16 && m0 + r < M) v = x[(int64_t)(m0 + r) * KX + g * 16 + ch];
-      areg[u] = v;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (i < BM * 16 && m0 + r < M) v = *reinterpret_cast<const u32x4_t*>(&x[(int64_t)(m0 + r) * KX + g * 16 + ch]);
+      areg[sl][u] = v;
     }
-    if (b_act) breg = *reinterpret_cast<const uint4*>(qw + b_src + (int64_t)g * WPS);
+    if (b_act) breg[sl] = *reinterpret_cast<const u32x4_t*>(qw + b_src + (int64_t)g * WPS);
     const int64_t off = (int64_t)s_row * G + (((g << 2) + s_st) >> gsh);
     if constexpr (NF4) {
-      sreg = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
+      sreg[sl] = __builtin_bit_cast(uint32_t, static_cast<const float*>(scales)[off]);
     } else {
-      sreg = static_cast<const uint16_t*>(scales)[off];
-      zreg = zeros[off];
+      sreg[sl] = static_cast<const uint16_t*>(scales)[off];
+      zreg[sl] = zeros[off];
     }
   };
-  auto store_stage = [&](int buf) {
+  auto store_stage = [&](int buf, int sl) {
 #pragma unroll
     for (int u = 0; u < AU; ++u) {
       const int i = t + u * kThreads;
-      if (i < BM * 16) sm.a[buf][i >> 4][i & 15] = areg[u];
+      if (i < BM * 16) *reinterpret_cast<u32x4_t*>(&sm.a[buf][i >> 4][i & 15]) = areg[sl][u];
     }
     if (b_act) {
-      const uint32_t wv[4] = {breg.x, breg.y, breg.z, breg.w};
+      const uint32_t wv[4] = {breg[sl].x, breg[sl].y, breg[sl].z, breg[sl].w};
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int w = 4 * b_q + e;  // word of the stage
@@ -359,22 +363,30 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
         sm.b[buf][b_row][pos] = wv[e];
       }
     }
-    sm.sz[buf][t >> 2][s_st] = NF4 ? sreg : (sreg | ((uint32_t)zreg << 16));
+    sm.sz[buf][t >> 2][s_st] = NF4 ? sreg[sl] : (sreg[sl] | ((uint32_t)zreg[sl] << 16));
   };
 
   float4_t acc[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0);
-  store_stage(0);
+#pragma unroll
+  for (int p = 0; p < RING; ++p)
+    if (p < S) load_stage(p, p);
+  store_stage(0, 0);
   __syncthreads();  // also publishes the codebook
 
   const int n_loc = wave * 16 + c;
   const half8_t ones = as_half8(0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u);
-  for (int g = 0; g < S; ++g) {
+  // unrolled by the ring size so that every ring slot is a compile-time index
+  for (int g0 = 0; g0 < S; g0 += RING)
+#pragma unroll
+  for (int kk = 0; kk < RING; ++kk) {
+    const int g = g0 + kk;
+    if (g >= S) continue;
     const int buf = g & 1;
-    if (g + 1 < S) load_stage(g + 1);
+    // slot kk held stage g, stored to LDS one iteration ago: refill it with stage g + RING
+    if (g + RING < S) load_stage(g + RING, kk);
 
     const uint4 szq = *reinterpret_cast<const uint4*>(&sm.sz[buf][n_loc][0]);
     const uint32_t szs[4] = {szq.x, szq.y, szq.z, szq.w};
@@ -456,7 +468,7 @@ __global__ __launch_bounds__(kThreads) void mfma_var_kernel(const uint4* __restr
 
     if (g + 1 < S) {
       __syncthreads();
-      store_stage(buf ^ 1);
+      store_stage(buf ^ 1, (kk + 1) % RING);
       __syncthreads();
     }
   }
