@@ -11,9 +11,9 @@
 //
 // Tile: 64 output columns n (4 waves x 16) by BM = 16 * MB rows of x, stepping
 // one quantization group (128 inputs) per stage, double-buffered in LDS, with the
-// global loads of two groups in flight in a register ring (group g + 2 is loaded
-// while group g is computed and group g + 1 waits in registers for its LDS store;
-// 3-7 % faster than one group ahead on the LLaMA serving shapes):
+// global loads of two groups in flight in a register ring for 32- and 64-row tiles
+// (group g + 2 is loaded while group g is computed and group g + 1 waits in registers
+// for its LDS store; 3-7 % faster than one group ahead on the LLaMA serving shapes):
 //   * x[m0:m0+BM][128g : 128g+128] and the 64 rows' codes of group g are
 //     copied to LDS (global loads for group g+1 are in flight while group g
 //     is computed), with the 64 (scale, zero) pairs;
@@ -81,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
                                                         uint16_t* __restrict__ y) {
   constexpr int BM = 16 * MB;
   constexpr int AU = (BM * 16 + kThreads - 1) / kThreads;  // x chunks per thread per stage
+  constexpr int RING = MB == 1 ? 1 : kRing;  // 16-row tiles (explicit path only, M <= 16) keep one group ahead
   __shared__ Smem<MB> sm;
 
   const int t = threadIdx.x;
@@ -101,10 +102,10 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
   const int64_t b_src = (int64_t)min(n0 + b_row, N - 1) * KQ + b_q;
   const int s_row = min(n0 + (t & 63), N - 1);
 
-  // register ring of kRing groups; native vectors, so that the ring stays in registers
-  u32x4_t areg[kRing][AU];
-  u32x4_t breg[kRing];
-  uint16_t sreg[kRing] = {}, zreg[kRing] = {};
+  // register ring of RING groups; native vectors, so that the ring stays in registers
+  u32x4_t areg[RING][AU];
+  u32x4_t breg[RING];
+  uint16_t sreg[RING] = {}, zreg[RING] = {};
 
   auto load_stage = [&](int g, int sl) {
 #pragma unroll
@@ -136,21 +137,21 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
   for (int mb = 0; mb < MB; ++mb) acc[mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int p = 0; p < kRing; ++p)
+  for (int p = 0; p < RING; ++p)
     if (p < G) load_stage(p, p);
   store_stage(0, 0);
   __syncthreads();
 
   const int n_loc = wave * 16 + c;  // this lane's output column within the tile
   // unrolled by the ring size so that every ring slot is a compile-time index
-  for (int g0 = 0; g0 < G; g0 += kRing)
+  for (int g0 = 0; g0 < G; g0 += RING)
 #pragma unroll
-  for (int kk = 0; kk < kRing; ++kk) {
+  for (int kk = 0; kk < RING; ++kk) {
     const int g = g0 + kk;
     if (g >= G) continue;
     const int buf = g & 1;
-    // slot kk held group g, stored to LDS one iteration ago: refill it with group g + kRing
-    if (g + kRing < G) load_stage(g + kRing, kk);
+    // slot kk held group g, stored to LDS one iteration ago: refill it with group g + RING
+    if (g + RING < G) load_stage(g + RING, kk);
 
     // ---- this lane's (scale, zero) and the 4 code words (one per MFMA step)
     const uint32_t szv = sm.sz[buf][n_loc];
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void mfma_kernel(const uint4* __restrict_
 
     if (g + 1 < G) {
       __syncthreads();  // every wave is done with the buffer about to be refilled
-      store_stage(buf ^ 1, (kk + 1) % kRing);
+      store_stage(buf ^ 1, (kk + 1) % RING);
       __syncthreads();
     }
   }
