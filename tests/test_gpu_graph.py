@@ -119,3 +119,38 @@ def test_quantize_and_norm_in_graph(lib):
         lambda i: [synth.weights(2, 40 + i, n, k), synth.calibration(2, 40 + i, k),
                    np.random.default_rng(50 + i).standard_normal((m, k)).astype(np.float16)],
         eager)
+
+
+@pytest.mark.parametrize("bits,group", [(4, 64), (3, 32)])
+@pytest.mark.parametrize("m", [1, 4, 40])
+def test_formats_in_graph(lib, bits, group, m):
+    # the GEMV variant (M = 1), the small-batch kernel (M = 4) and its two passes (M = 40)
+    torch, g = _torch(), _gpu()
+    k, n = 2048, 600
+    packed = [g.dev(t) for t in oracle.quantize_pack(synth.weights(2, 15, n, k), None, bits=bits, group=group)]
+    x = g.dev(synth.activations(2, 15, m, k))
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    print(f"graph linear bits={bits} group={group} M={m}", flush=True)
+    _replay_and_compare(
+        torch,
+        lambda: lib.linear(x, *packed, group=group, bits=bits, out=y),
+        [x], [y],
+        lambda i: [synth.activations(2, 60 + i, m, k)],
+        lambda: [lib.linear(x, *packed, group=group, bits=bits)])
+
+
+@pytest.mark.parametrize("m", [4, 40])
+def test_nf4_in_graph(lib, m):
+    torch, g = _torch(), _gpu()
+    k, n = 2048, 600
+    qw, a = oracle.quantize_pack_nf4(synth.weights(2, 16, n, k), None, 64)
+    qd, ad = g.dev(qw), g.dev(a)
+    x = g.dev(synth.activations(2, 16, m, k))
+    y = torch.empty((m, n), dtype=torch.float16, device=x.device)
+    print(f"graph nf4 M={m}", flush=True)
+    _replay_and_compare(
+        torch,
+        lambda: lib.nf4_linear(x, qd, ad, block=64, out=y),
+        [x], [y],
+        lambda i: [synth.activations(2, 70 + i, m, k)],
+        lambda: [lib.nf4_linear(x, qd, ad, block=64)])
