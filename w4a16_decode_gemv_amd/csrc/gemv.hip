@@ -91,21 +91,23 @@ __device__ __forceinline__ half2_t q_pair_hi(uint32_t w) {  // nibbles at bits 4
                                    (half2_t){(_Float16)-64.0f, (_Float16)-64.0f});
 }
 
-template <int M, int PPT, bool Narrow>
+// PSH: 2^PSH 32-input pieces per quantization group (2: groups of 128, 1: 64, 0: 32)
+template <int M, int PPT, bool Narrow, int PSH>
 __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThreads) void gemv_kernel(const uint4* __restrict__ x, const u32x4_t* __restrict__ qw,
                                                            const uint16_t* __restrict__ scales,
                                                            const uint16_t* __restrict__ zeros, int N, int K,
                                                            uint16_t* __restrict__ y) {
   constexpr int R = Tile<M, PPT, Narrow>::R;
   constexpr int V = Tile<M, PPT, Narrow>::V;
-  constexpr int E = R * PPT * 16;        // (scale, zero) pairs one wave needs: R rows x PPT slots x 16 groups
+  constexpr int GPW = 64 >> PSH;         // groups one wave's 64 pieces of a slot span
+  constexpr int E = R * PPT * GPW;       // (scale, zero) pairs one wave needs: R rows x PPT slots x GPW groups
   constexpr int NE = (E + 63) / 64;      // ... per lane
   extern __shared__ uint32_t lds[];      // per wave: E staged pairs, then V partial sums
 
   const int T = blockDim.x;
   const int t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
-  const int G = K >> 7;   // groups per row
+  const int G = K >> (5 + PSH);  // groups per row
   const int P = K >> 5;   // 16-byte code pieces per row
   const int KX = K >> 3;  // 16-byte x chunks per input row
   const int row0 = blockIdx.x * R;
@@ -125,13 +127,13 @@ __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThre
   // stored.
 
   // (1) the (scale, zero) pairs this wave needs: lanes of piece slot pp cover
-  //     16 consecutive groups starting at 16 * wave + pp * T / 4
+  //     GPW consecutive groups starting at GPW * wave + pp * T / 2^PSH
   uint16_t sreg[NE], zreg[NE];
 #pragma unroll
   for (int u = 0; u < NE; ++u) {
     const int e = min(lane + 64 * u, E - 1);
-    const int r = e / (16 * PPT), pp = (e >> 4) % PPT, gl = e & 15;
-    const int g = min(16 * wave + pp * (T >> 2) + gl, G - 1);
+    const int r = e / (GPW * PPT), pp = (e / GPW) % PPT, gl = e % GPW;
+    const int g = min(GPW * wave + pp * (T >> PSH) + gl, G - 1);
     const int64_t off = (int64_t)min(row_of(r), N - 1) * G + g;
     sreg[u] = scales[off];
     zreg[u] = zeros[off];
@@ -222,7 +224,7 @@ __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThre
 #pragma unroll
     for (int pp = 0; pp < PPT; ++pp) {
       const int p_raw = t + pp * T;
-      const uint32_t szv = wsz[(r * PPT + pp) * 16 + (lane >> 2)];
+      const uint32_t szv = wsz[(r * PPT + pp) * GPW + (lane >> PSH)];
       const float d = (p_raw < P) ? half_bits_to_float((uint16_t)(szv & 0xFFFFu)) : 0.f;
       const float z = half_bits_to_float((uint16_t)(szv >> 16));
       const uint32_t wd[4] = {cw[r][pp].x, cw[r][pp].y, cw[r][pp].z, cw[r][pp].w};
@@ -522,21 +524,21 @@ Launch plan(int64_t K, int one_piece_max = kMaxThreads) {
   return {ppt, t};
 }
 
-template <int M, int PPT, bool Narrow = false>
+template <int M, int PPT, bool Narrow, int PSH>
 hipError_t launch_mp(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                      int64_t N, int64_t K, uint16_t* y, int threads, hipStream_t stream) {
   constexpr int R = Tile<M, PPT, Narrow>::R;
   constexpr int V = Tile<M, PPT, Narrow>::V;
-  constexpr int E = R * PPT * 16;
+  constexpr int E = R * PPT * (64 >> PSH);
   const size_t lds = (size_t)(threads / 64) * (E + V) * 4;
   const int grid = (int)((N + R - 1) / R);
-  hipLaunchKernelGGL((gemv_kernel<M, PPT, Narrow>), dim3(grid), dim3(threads), lds, stream,
+  hipLaunchKernelGGL((gemv_kernel<M, PPT, Narrow, PSH>), dim3(grid), dim3(threads), lds, stream,
                      reinterpret_cast<const uint4*>(x), reinterpret_cast<const u32x4_t*>(qweight), scales, zeros,
                      (int)N, (int)K, y);
   return hipGetLastError();
 }
 
-template <int M>
+template <int M, int PSH = 2>
 hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                     int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const Launch l = plan(K, M <= 2 ? kMaxThreadsOnePiece : kMaxThreads);
@@ -545,17 +547,17 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const uint16_t* 
       if constexpr (M == 1) {
         // narrow tiles when the default ones would give fewer than 16 waves per CU
         const int64_t waves = (N + Tile<1, 1>::R - 1) / Tile<1, 1>::R * (l.threads / 64);
-        if (waves < 16 * 256) return launch_mp<1, 1, true>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+        if (waves < 16 * 256) return launch_mp<1, 1, true, PSH>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
       }
-      return launch_mp<M, 1>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      return launch_mp<M, 1, false, PSH>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
     case 2:
-      if constexpr (M <= 4) return launch_mp<M, 2>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      if constexpr (M <= 4) return launch_mp<M, 2, false, PSH>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
       break;
     case 4:
-      if constexpr (M <= 2) return launch_mp<M, 4>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      if constexpr (M <= 2) return launch_mp<M, 4, false, PSH>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
       break;
     case 8:
-      if constexpr (M <= 1) return launch_mp<M, 8>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
+      if constexpr (M <= 1) return launch_mp<M, 8, false, PSH>(x, qweight, scales, zeros, N, K, y, l.threads, stream);
       break;
     default: break;
   }
@@ -612,10 +614,31 @@ bool gemv_variant_supports(int64_t M, int64_t K, int group) {
   return ppt == 1 || (ppt == 2 && mt <= 4);
 }
 
+template <int PSH>
+hipError_t launch_gemv_groups(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                              int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
+  switch (M) {
+    case 1: return launch_m<1, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    case 2: return launch_m<2, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    case 3: return launch_m<3, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    case 4: return launch_m<4, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    case 5: return launch_m<5, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    case 6: return launch_m<6, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    case 7: return launch_m<7, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    case 8: return launch_m<8, PSH>(x, qweight, scales, zeros, N, K, y, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 hipError_t launch_gemv_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                                const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   const int gsh = group == 32 ? 0 : group == 64 ? 1 : 2;
   const Nf4Table none = {};
+  // 4-bit codes with groups of 64 or 32: the tuned kernel with two or one pieces per group
+  if (bits == 4 && gemv_supports(M, K)) {
+    if (gsh == 1) return launch_gemv_groups<1>(x, qweight, scales, zeros, M, N, K, y, stream);
+    if (gsh == 0) return launch_gemv_groups<0>(x, qweight, scales, zeros, M, N, K, y, stream);
+  }
   if (bits == 4) return launch_var_fmt<4>(x, qweight, scales, zeros, M, N, K, gsh, none, y, stream);
   return launch_var_fmt<3>(x, qweight, scales, zeros, M, N, K, gsh, none, y, stream);
 }
