@@ -209,7 +209,7 @@ def block_leg(w4, torch):
     import synth
 
     dev = "cuda:0"
-    layers = synth.CONFIGS[2]["layers"]
+    layers = synth.CONFIGS[synth.LLAMA2_7B_BLOCK]["layers"]
     k = layers[0][1]
     eps = 1e-5
     groups = [("qkv", [0, 1, 2]), ("o", [3]), ("gate_up", [4, 5]), ("down", [6])]
@@ -282,7 +282,7 @@ def search_leg(w4, torch):
     dev = "cuda:0"
     rows = []
     total_search_us = 0.0
-    for lid, (name, kk, nn) in enumerate(synth.CONFIGS[2]["layers"]):
+    for lid, (name, kk, nn) in enumerate(synth.CONFIGS[synth.LLAMA2_7B_BLOCK]["layers"]):
         x_cal = torch.from_numpy(synth.calibration(2, lid, kk)).to(dev)
         W = torch.from_numpy(synth.weights(2, lid, nn, kk)).to(dev)
         t_cal = x_cal.shape[0]
@@ -409,7 +409,7 @@ def main():
 
         name, mm = args.only_serving.split(":")
         mm = int(mm)
-        layers = {lname.split("_")[0]: (lid, lname, kk, nn) for lid, (lname, kk, nn) in enumerate(synth.CONFIGS[5]["layers"])}
+        layers = {lname.split("_")[0]: (lid, lname, kk, nn) for lid, (lname, kk, nn) in enumerate(synth.CONFIGS[synth.LLAMA2_7B_SERVING]["layers"])}
         lid, lname, kk, nn = layers[name]
         b = algorithmic_bytes(mm, nn, kk)
         L = Layer(w4, torch, 5, lid, nn, kk, mm, copies_for(b))
@@ -529,7 +529,7 @@ def main():
         import synth
 
         total_bytes, total_us, per = 0, 0.0, []
-        for lid, (name, kk, nn) in enumerate(synth.CONFIGS[3]["layers"]):
+        for lid, (name, kk, nn) in enumerate(synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"]):
             if name in ("k", "v", "o"):
                 continue
             b = algorithmic_bytes(1, nn, kk)
@@ -617,7 +617,7 @@ def main():
         import synth
 
         rows = []
-        for lid, (name, kk, nn) in enumerate(synth.CONFIGS[5]["layers"]):
+        for lid, (name, kk, nn) in enumerate(synth.CONFIGS[synth.LLAMA2_7B_SERVING]["layers"]):
             for mm in (128, 256):
                 b = algorithmic_bytes(mm, nn, kk)
                 L = Layer(w4, torch, 5, lid, nn, kk, mm, copies_for(b))

@@ -27,23 +27,30 @@ OUTLIER_GAIN = 20.0
 # tensor ids inside one layer's seed sequence
 _T_W, _T_OUTL, _T_XCAL, _T_X = 0, 1, 2, 3
 
-# The five workloads: name -> list of (layer name, K, N) and the M values.
+# The five workloads, each under a named id that also enters the seed sequence of its
+# tensors (so the ids keep these values): list of (layer name, K, N) and the M values.
+SINGLE_2048 = 1
+LLAMA2_7B_BLOCK = 2
+LLAMA65B_DECODE = 3
+SWEEP_8192 = 4
+LLAMA2_7B_SERVING = 5
+
 CONFIGS = {
-    1: {"name": "single layer 2048->2048", "layers": [("single", 2048, 2048)], "M": [1]},
-    2: {
+    SINGLE_2048: {"name": "single layer 2048->2048", "layers": [("single", 2048, 2048)], "M": [1]},
+    LLAMA2_7B_BLOCK: {
         "name": "LLaMA2-7B decoder block",
         "layers": [("q", 4096, 4096), ("k", 4096, 4096), ("v", 4096, 4096), ("o", 4096, 4096),
                    ("gate", 4096, 11008), ("up", 4096, 11008), ("down", 11008, 4096)],
         "M": [1],
     },
-    3: {
+    LLAMA65B_DECODE: {
         "name": "LLaMA-65B decode set",
         "layers": [("q", 8192, 8192), ("k", 8192, 8192), ("v", 8192, 8192), ("o", 8192, 8192),
                    ("gate", 8192, 22016), ("up", 8192, 22016), ("down", 22016, 8192)],
         "M": [1],
     },
-    4: {"name": "small-batch sweep 8192->8192", "layers": [("sweep", 8192, 8192)], "M": [2, 4, 8, 16, 32]},
-    5: {
+    SWEEP_8192: {"name": "small-batch sweep 8192->8192", "layers": [("sweep", 8192, 8192)], "M": [2, 4, 8, 16, 32]},
+    LLAMA2_7B_SERVING: {
         "name": "LLaMA2-7B batched serving",
         "layers": [("qkvo", 4096, 4096), ("gate_up", 4096, 11008), ("down", 11008, 4096)],
         "M": [128, 256],

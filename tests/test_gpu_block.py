@@ -104,9 +104,9 @@ def _stacked_vs_separate(lib, cfg, names, m):
 
 @pytest.mark.parametrize("m", [1, 4])
 def test_qkv_as_one_launch(lib, m):
-    _stacked_vs_separate(lib, 2, ["q", "k", "v"], m)
+    _stacked_vs_separate(lib, synth.LLAMA2_7B_BLOCK, ["q", "k", "v"], m)
 
 
 @pytest.mark.parametrize("m", [1, 4])
 def test_gate_up_as_one_launch(lib, m):
-    _stacked_vs_separate(lib, 2, ["gate", "up"], m)
+    _stacked_vs_separate(lib, synth.LLAMA2_7B_BLOCK, ["gate", "up"], m)

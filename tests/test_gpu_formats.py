@@ -202,7 +202,7 @@ def test_variants_on_edge_weights(lib, bits, group, kind):
 def test_full_size_layers_sampled(lib, bits, group, m):
     # LLaMA-65B projections: 8192 -> 8192 and 8192 -> 22016, 256 sampled output rows
     g = _gpu()
-    for lid, (name, k, n) in enumerate(synth.CONFIGS[3]["layers"][3:5]):
+    for lid, (name, k, n) in enumerate(synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"][3:5]):
         x_cal = synth.calibration(3, lid, k)
         s = oracle.channel_scale(x_cal)
         W = synth.weights(3, lid, n, k)

@@ -121,7 +121,7 @@ def test_config1_single_layer(lib):
 
 @pytest.mark.parametrize("layer_id", [0, 4, 6])
 def test_config2_llama2_7b_block(lib, layer_id):
-    name, k, n = synth.CONFIGS[2]["layers"][layer_id]
+    name, k, n = synth.CONFIGS[synth.LLAMA2_7B_BLOCK]["layers"][layer_id]
     xs, qw, sc, zr = _packed(2, layer_id, n, k, 1)
     _check(lib, xs, qw, sc, zr, path=0, tag=f"config2-{name}")
 
@@ -134,7 +134,7 @@ def _sampled_rows(n, seed, count=256):
 
 @pytest.mark.parametrize("layer_id", [0, 4, 6])
 def test_config3_llama65b_full_size_sampled(lib, layer_id):
-    name, k, n = synth.CONFIGS[3]["layers"][layer_id]
+    name, k, n = synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"][layer_id]
     xs, qw, sc, zr = _packed(3, layer_id, n, k, 1)
     _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id), tag=f"config3-{name}")
 
@@ -152,7 +152,7 @@ def test_config4_batch_sweep_both_paths(lib, m):
 @pytest.mark.parametrize("m", [128, 256])
 @pytest.mark.parametrize("layer_id", [0, 1, 2])
 def test_config5_batched_serving(lib, m, layer_id):
-    name, k, n = synth.CONFIGS[5]["layers"][layer_id]
+    name, k, n = synth.CONFIGS[synth.LLAMA2_7B_SERVING]["layers"][layer_id]
     xs, qw, sc, zr = _packed(5, layer_id, n, k, m)
     _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id, 128), tag=f"config5-{name}")
 

@@ -29,12 +29,12 @@ def _qp_compare(lib, W, s, rows=None):
     assert np.array_equal(zr, g.bits16(zo)), g.report_mismatch("zeros", zr, g.bits16(zo))
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [synth.SINGLE_2048, synth.LLAMA2_7B_BLOCK])
 def test_quantize_pack_full_layers(lib, cfg):
     for layer_id, (name, k, n) in enumerate(synth.CONFIGS[cfg]["layers"]):
-        if cfg == 2 and name in ("k", "v", "o", "up"):
+        if cfg == synth.LLAMA2_7B_BLOCK and name in ("k", "v", "o", "up"):
             continue  # same shapes as q / gate
-        print(f"config {cfg} layer {name} K={k} N={n}", flush=True)
+        print(f"workload {synth.CONFIGS[cfg]['name']} layer {name} K={k} N={n}", flush=True)
         L = synth.layer(cfg, layer_id, n, k, 1)
         s = oracle.channel_scale(L["x_cal"])
         _qp_compare(lib, L["W"], s)
@@ -42,7 +42,7 @@ def test_quantize_pack_full_layers(lib, cfg):
 
 @pytest.mark.parametrize("layer_id", [0, 4, 6])
 def test_quantize_pack_llama65b_sampled_rows(lib, layer_id):
-    name, k, n = synth.CONFIGS[3]["layers"][layer_id]
+    name, k, n = synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"][layer_id]
     print(f"config 3 layer {name} K={k} N={n}", flush=True)
     W = synth.weights(3, layer_id, n, k)
     s = oracle.channel_scale(synth.calibration(3, layer_id, k))

@@ -47,7 +47,7 @@ def test_splitk_ragged_shapes(lib, m, n, k, splits):
 @pytest.mark.parametrize("m", [128, 256])
 def test_splitk_serving_shapes(lib, m):
     g = _gpu()
-    for lid, (name, k, n) in enumerate(synth.CONFIGS[5]["layers"]):
+    for lid, (name, k, n) in enumerate(synth.CONFIGS[synth.LLAMA2_7B_SERVING]["layers"]):
         s = oracle.channel_scale(synth.calibration(5, lid, k))
         W = synth.weights(5, lid, n, k)
         packed = tuple(g.host(t) for t in lib.quantize_pack(g.dev(W), g.dev(s)))

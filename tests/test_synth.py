@@ -33,7 +33,7 @@ def test_distributions():
 
 
 def test_configs_shapes():
-    assert synth.CONFIGS[3]["layers"][0] == ("q", 8192, 8192)
+    assert synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"][0] == ("q", 8192, 8192)
     for cfg in synth.CONFIGS.values():
         for _, k, n in cfg["layers"]:
             assert k % 128 == 0 and n > 0
