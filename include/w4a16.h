@@ -179,7 +179,9 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * by awq_quantize_pack with bits 4; y: fp16 [M][N] (output). group 32, 64 or
  * 128 (as quantized); K % 128 == 0.
  * Dispatch, group 128: M == 1, and M == 2 on layers with K <= 24576 and
- * N * K >= 2^27, run the wave-tile GEMV kernel; other M <= 32 the small-batch
+ * N * K >= 2^27 or on layers small enough that the GEMV takes 4-row tiles
+ * (K <= 32768 and ceil(N / 8) * ceil(K / 2048) < 4096 waves, under 16 per CU),
+ * run the wave-tile GEMV kernel; other M <= 32 the small-batch
  * MFMA kernel (workgroups own whole rows of y, waves split K); 33 <= M <= 64
  * on layers with N <= 8192 and K <= 16384 the small-batch kernel in two
  * launches (rows 0..31, then the rest); other M the tiled MFMA kernel.

@@ -32,11 +32,14 @@ constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;  // one workgroup per loss
 // kernel at M = 1, and at M = 2 on layers of at least 2^27 weights with K <= 24576 (there
 // the GEMV's doubled dot work still hides under the weight stream: 21.8 against 24.0 us at
 // 8192 -> 22016, 28.7 against 29.9 at 22016 -> 8192, 26.9 against 28.9 at 8192 -> 28672; on
-// smaller layers and on 28672 -> 8192 the small-batch kernel is ahead: 9.9 against 10.3 us
-// at 8192 -> 8192, 29.5 against 33.8 at 28672 -> 8192); the small-batch MFMA kernel up to
-// skinny_max_m(); the tiled MFMA kernel beyond
+// 8192 -> 8192 and on 28672 -> 8192 the small-batch kernel is ahead: 9.9 against 10.3 us at
+// 8192 -> 8192, 29.5 against 33.8 at 28672 -> 8192), and at M = 2 on the small layers where
+// the GEMV takes narrow tiles (8.1 against 8.3 us at 4096 -> 11008, 8.7 against 9.0 at
+// 11008 -> 4096, 8.4 against 8.6 at 4096 -> 12288, 4.8 both at 4096 -> 4096); the
+// small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA kernel beyond
 bool auto_gemv(int64_t M, int64_t N, int64_t K) {
-  return M == 1 || (M == 2 && K <= 24576 && N * K >= (int64_t(1) << 27));
+  return M == 1 || (M == 2 && K <= 24576 && N * K >= (int64_t(1) << 27)) ||
+         (M == 2 && w4a16::gemv_narrow(M, N, K));
 }
 
 // the same hand-off for groups of 32 and 64 and for NF4, whose GEMV variant has no long-row

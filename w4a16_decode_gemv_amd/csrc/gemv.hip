@@ -72,10 +72,13 @@ constexpr int kMaxM = 8;
 // there 4 rows win: 4.08 against 4.75 us at 4096 x 4096, 6.47 against 7.17 at
 // 4096 -> 11008, 6.90 against 7.51 at 11008 -> 4096 ("Narrow" tiles). For
 // M >= 2 the x reads grow with M, and R * M * PPT <= 16 keeps more rows
-// sharing them.
+// sharing them. M = 2 takes narrow tiles (4 rows) on the same small layers:
+// 4.8 against 6.0 us at 4096 x 4096, 8.1 against 8.9 at 4096 -> 11008, 8.7
+// against 9.6 at 11008 -> 4096; at 8192 x 8192 8 rows stay ahead (10.3
+// against 10.7).
 template <int M, int PPT, bool Narrow = false>
 struct Tile {
-  static constexpr int kBudget = (M == 1) ? (Narrow ? 4 : 8) : 16;
+  static constexpr int kBudget = (M == 1) ? (Narrow ? 4 : 8) : (M == 2 && Narrow) ? 8 : 16;
   static constexpr int R = (kBudget / (M * PPT)) > 0 ? (kBudget / (M * PPT)) : 1;
   static constexpr int V = R * M;
 };
@@ -558,6 +561,13 @@ Launch plan(int64_t K, int one_piece_max = kMaxThreads) {
   return {ppt, t};
 }
 
+// narrow tiles (M <= 2, one piece per thread) when the default ones would give fewer than
+// 16 waves per CU
+bool narrow_tiles(int64_t M, int64_t N, int threads) {
+  const int R = M == 1 ? Tile<1, 1>::R : Tile<2, 1>::R;
+  return M <= 2 && (N + R - 1) / R * (threads / 64) < 16 * 256;
+}
+
 template <int M, int PPT, bool Narrow, int PSH, bool NF4>
 hipError_t launch_mp(const uint16_t* x, const uint32_t* qweight, const void* scales, const uint16_t* zeros,
                      int64_t N, int64_t K, uint16_t* y, int threads, const Nf4Table& table, hipStream_t stream) {
@@ -578,10 +588,9 @@ hipError_t launch_m(const uint16_t* x, const uint32_t* qweight, const void* scal
   const Launch l = plan(K, M <= 2 ? kMaxThreadsOnePiece : kMaxThreads);
   switch (l.ppt) {
     case 1:
-      if constexpr (M == 1) {
-        // narrow tiles when the default ones would give fewer than 16 waves per CU
-        const int64_t waves = (N + Tile<1, 1>::R - 1) / Tile<1, 1>::R * (l.threads / 64);
-        if (waves < 16 * 256) return launch_mp<1, 1, true, PSH, NF4>(x, qweight, scales, zeros, N, K, y, l.threads, table, stream);
+      if constexpr (M <= 2) {
+        if (narrow_tiles(M, N, l.threads))
+          return launch_mp<M, 1, true, PSH, NF4>(x, qweight, scales, zeros, N, K, y, l.threads, table, stream);
       }
       return launch_mp<M, 1, false, PSH, NF4>(x, qweight, scales, zeros, N, K, y, l.threads, table, stream);
     case 2:
@@ -691,6 +700,12 @@ hipError_t launch_gemv_nf4(const Nf4Table& table, int block, const uint16_t* x, 
     return launch_m<1, 0, true>(x, qweight, absmax, nullptr, N, K, y, stream, table);
   }
   return launch_var_fmt<kNF4>(x, qweight, absmax, nullptr, M, N, K, gsh, table, y, stream);
+}
+
+bool gemv_narrow(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > 2 || K <= 0) return false;
+  const Launch l = plan(K, kMaxThreadsOnePiece);
+  return l.ppt == 1 && narrow_tiles(M, N, l.threads);
 }
 
 bool gemv_supports(int64_t M, int64_t K) {

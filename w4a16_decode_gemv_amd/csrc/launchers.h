@@ -35,6 +35,9 @@ hipError_t launch_nf4_quantize_pack(const uint16_t* w, const float* s, int64_t N
 // GEMV kernel: needs M <= gemv_max_m() and gemv_supports(M, K).
 int gemv_max_m();
 bool gemv_supports(int64_t M, int64_t K);
+// whether the GEMV takes narrow (4-row) tiles for this shape: M <= 2, one 32-input
+// piece per thread, and fewer than 16 waves per CU with the default tiles
+bool gemv_narrow(int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                        const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                        hipStream_t stream);
