@@ -186,7 +186,8 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * on layers with N <= 8192 and K <= 16384 the small-batch kernel in two
  * launches (rows 0..31, then the rest); other M the tiled MFMA kernel.
  * Groups of 32 and 64: M == 1, and M == 2 on layers with K <= 24576 and
- * N * K >= 2^26, run the GEMV kernel (two or one 32-input pieces per group);
+ * N * K >= 2^26 or small enough for 4-row tiles (as for group 128), run the
+ * GEMV kernel (two or one 32-input pieces per group);
  * other M <= 32 the small-batch MFMA kernel (which needs scales and zeros
  * 4-byte aligned; otherwise the GEMV takes M <= 8 where it can), and
  * 33 <= M <= 64 the same two launches as for group 128 on the same layers;

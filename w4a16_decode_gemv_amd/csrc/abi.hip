@@ -156,9 +156,12 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
       // by both rows there (8192 -> 8192: 12.5 against 12.8 us for groups of 128, 12.6 against
       // 13.3 for 64, 12.8 against 15.2 for 32). 4-bit groups of 64 and 32 run the tuned GEMV,
       // which at M = 2 stays ahead from 2^26 weights (8192 -> 8192: 10.5 against 11.1 us for
-      // 64, 10.7 against 12.4 for 32; 8192 -> 22016: 21.1 against 25.1)
-      const bool gemv_first = bits == 4 ? M == 1 || (M == 2 && K <= 24576 && N * K >= (int64_t(1) << 26))
-                                        : auto_gemv_variant(M, N, K) || (bits == 3 && M == 2);
+      // 64, 10.7 against 12.4 for 32; 8192 -> 22016: 21.1 against 25.1) and on the small layers
+      // where it takes 4-row tiles (4096 -> 11008: 8.3 against 8.6 us for 64, 8.5 against 9.4
+      // for 32; 11008 -> 4096: 8.9 against 9.4, 9.1 against 11.4; 4096 -> 4096: 4.8 against 4.9)
+      const bool gemv_first =
+          bits == 4 ? M == 1 || (M == 2 && ((K <= 24576 && N * K >= (int64_t(1) << 26)) || w4a16::gemv_narrow(M, N, K)))
+                    : auto_gemv_variant(M, N, K) || (bits == 3 && M == 2);
       two_passes = sz_aligned && two_small_batch_passes(M, N, K);
       kernel = gemv_first && gemv_ok ? 1 : skinny_ok || two_passes ? 3 : gemv_ok ? 1 : 2;
     } else if (path == 1 && !gemv_ok) {
