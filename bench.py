@@ -54,7 +54,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=2000)
     p.add_argument("--warmup", type=int, default=200)
-    p.add_argument("--sweep", action="store_true", help="also time the config-4 batch sweep on both kernels")
+    p.add_argument("--sweep", action="store_true", help="also time the M = 1..64 batch sweep at K = N = 8192 on every kernel")
     p.add_argument("--set", dest="llama_set", action="store_true", help="also time the 7-projection LLaMA-65B set")
     p.add_argument("--block", action="store_true",
                    help="also time a LLaMA2-7B decoder block at M=1: separate projections vs q/k/v and gate/up fused")

@@ -113,17 +113,17 @@ def test_skinny_rejects_large_batches(lib):
         lib.linear(x, qw, sz, sz, path=3)
 
 
-def test_config1_single_layer(lib):
+def test_single_layer_2048(lib):
     xs, qw, sc, zr = _packed(1, 0, 2048, 2048, 1)
     for path in (0, 1, 2, 3):
-        _check(lib, xs, qw, sc, zr, path=path, tag="config1")
+        _check(lib, xs, qw, sc, zr, path=path, tag="single-2048")
 
 
 @pytest.mark.parametrize("layer_id", [0, 4, 6])
-def test_config2_llama2_7b_block(lib, layer_id):
+def test_llama2_7b_block(lib, layer_id):
     name, k, n = synth.CONFIGS[synth.LLAMA2_7B_BLOCK]["layers"][layer_id]
     xs, qw, sc, zr = _packed(2, layer_id, n, k, 1)
-    _check(lib, xs, qw, sc, zr, path=0, tag=f"config2-{name}")
+    _check(lib, xs, qw, sc, zr, path=0, tag=f"llama2-7b-{name}")
 
 
 def _sampled_rows(n, seed, count=256):
@@ -133,28 +133,28 @@ def _sampled_rows(n, seed, count=256):
 
 
 @pytest.mark.parametrize("layer_id", [0, 4, 6])
-def test_config3_llama65b_full_size_sampled(lib, layer_id):
+def test_llama65b_full_size_sampled(lib, layer_id):
     name, k, n = synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"][layer_id]
     xs, qw, sc, zr = _packed(3, layer_id, n, k, 1)
-    _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id), tag=f"config3-{name}")
+    _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id), tag=f"llama65b-{name}")
 
 
 @pytest.mark.parametrize("m", [2, 4, 8, 16, 32])
-def test_config4_batch_sweep_both_paths(lib, m):
+def test_batch_sweep_8192_all_paths(lib, m):
     xs, qw, sc, zr = _packed(4, 0, 8192, 8192, m)
     rows = _sampled_rows(8192, m)
     paths = (1, 2, 3) if m <= 8 else (2, 3)
     for path in paths:
-        _check(lib, xs, qw, sc, zr, path=path, rows=rows, tag="config4")
-    _check(lib, xs, qw, sc, zr, path=0, rows=rows, tag="config4-auto")
+        _check(lib, xs, qw, sc, zr, path=path, rows=rows, tag="sweep-8192")
+    _check(lib, xs, qw, sc, zr, path=0, rows=rows, tag="sweep-8192-auto")
 
 
 @pytest.mark.parametrize("m", [128, 256])
 @pytest.mark.parametrize("layer_id", [0, 1, 2])
-def test_config5_batched_serving(lib, m, layer_id):
+def test_llama2_7b_batched_serving(lib, m, layer_id):
     name, k, n = synth.CONFIGS[synth.LLAMA2_7B_SERVING]["layers"][layer_id]
     xs, qw, sc, zr = _packed(5, layer_id, n, k, m)
-    _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id, 128), tag=f"config5-{name}")
+    _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id, 128), tag=f"serving-{name}")
 
 
 @pytest.mark.parametrize("kind", ["positive", "negative", "constant", "ties", "mixed"])
@@ -215,7 +215,7 @@ def test_deterministic_and_writes_only_its_output(lib, path, m):
     assert np.all(b[:pad] == canary) and np.all(b[pad + m * n:] == canary)
 
 
-def test_gpu_pipeline_end_to_end_config1(lib):
+def test_gpu_pipeline_end_to_end_single_2048(lib):
     """channel scale -> fold -> quantize-pack -> linear, all on the GPU, against
     the oracle doing the same steps."""
     g = _gpu()

@@ -43,7 +43,7 @@ def test_quantize_pack_full_layers(lib, cfg):
 @pytest.mark.parametrize("layer_id", [0, 4, 6])
 def test_quantize_pack_llama65b_sampled_rows(lib, layer_id):
     name, k, n = synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"][layer_id]
-    print(f"config 3 layer {name} K={k} N={n}", flush=True)
+    print(f"LLaMA-65B layer {name} K={k} N={n}", flush=True)
     W = synth.weights(3, layer_id, n, k)
     s = oracle.channel_scale(synth.calibration(3, layer_id, k))
     rows = np.sort(np.random.default_rng(layer_id).choice(n, size=96, replace=False))
