@@ -10,10 +10,11 @@ from 512 calibration tokens, the 1/s fold of x, and the RTN g128 quantize-pack
 packed layer (>= 512 MiB) so the 256 MB Infinity Cache cannot serve them.
 
 Prints ONE JSON line (metric, value = achieved GB/s over the timed steps,
-ms_per_step = time per call including launch gaps, roofline of the GEMV kernel,
-CPU-oracle baseline, and extra legs). The timed steps are back-to-back launches
-captured into one HIP graph, as a decode loop runs them; the eager Python loop
-is reported beside it.
+ms_per_step = time per call including the gaps between launches, roofline of the
+GEMV kernel, read floors of the same bytes, CPU-oracle baseline, and extra legs).
+The timed steps are back-to-back launches queued on one stream behind a device-side
+delay that outlasts their submission, so the HIP events around them time the GPU,
+not the host.
 """
 
 import argparse
@@ -127,33 +128,45 @@ def time_back_to_back(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per call
 
 
-def time_steps_graph(torch, fn, steps, warmup):
-    """The timed region: `warmup` untimed eager calls, then exactly `steps` calls captured
-    into one HIP graph and replayed once between two HIP events on the current stream (the
-    stream the kernels run on), synchronized on both sides. The graph keeps the GPU fed:
-    from Python, one eager launch costs the host about as long as the kernel runs, so an
-    eager loop measures the host as well. Returns ms per call."""
+def time_steps_queued(torch, fn, steps, warmup):
+    """The timed region: `warmup` untimed calls, then exactly `steps` calls launched back to
+    back on the current stream (the stream the kernels run on) and bracketed by two HIP
+    events on it, synchronized on both sides. The launches are queued behind a bounded
+    device-side delay that lasts longer than the host needs to submit them, so the GPU runs
+    them back to back from its queue: the events bracket the kernels and the gaps between
+    them, not the host's launch cost (about as long as the kernel from Python) and not a
+    graph replay's fixed start-up cost (several microseconds per replay, measured). The delay
+    is sized from the host's measured submission rate and checked against its own measured
+    length; a run whose submission outlasted the delay is timed again with a longer one.
+    Returns ms per call."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        fn(0)
-    torch.cuda.current_stream().wait_stream(s)
+    probe = max(1, min(steps, 50))
+    torch.cuda._sleep(50_000_000)  # keeps the probe's launches from draining while they are timed
+    t0 = time.perf_counter()
+    for i in range(probe):
+        fn(i)
+    host_us = (time.perf_counter() - t0) / probe * 1e6
     torch.cuda.synchronize()
-    with torch.cuda.graph(g):
+    delay_us = 3.0 * steps * host_us + 1000.0
+    for _ in range(6):
+        es = torch.cuda.Event(enable_timing=True)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        es.record()
+        torch.cuda._sleep(int(delay_us * 2400))  # cycles of the <= 2.4 GHz shader clock
+        e0.record()
+        t0 = time.perf_counter()
         for i in range(steps):
             fn(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    g.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps
+        e1.record()
+        submit_us = (time.perf_counter() - t0) * 1e6
+        torch.cuda.synchronize()
+        if submit_us < 0.8 * es.elapsed_time(e0) * 1e3:
+            return e0.elapsed_time(e1) / steps
+        delay_us *= 2.0
+    raise RuntimeError("the host could not queue the timed launches ahead of the GPU")
 
 
 def time_per_launch(torch, fn, steps):
@@ -198,6 +211,57 @@ def time_graph(torch, fn, steps, reps=5, warm_ms=25.0):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / (reps * steps)
+
+
+# grid-stride read shapes (threads, workgroups, 16-byte loads in flight per thread) timed
+# beside the GEMV's own pattern: fewer and larger workgroups, persistent grids, other depths
+GRID_READS = ((256, 1024, 8), (256, 2048, 4), (256, 4096, 2), (512, 1024, 4), (1024, 256, 8), (1024, 512, 4),
+              (256, 512, 16), (64, 8192, 4))
+
+
+def read_floor_leg(torch, w4, nbytes, copies, gemv_ms, steps, warmup):
+    """Single-launch read floors of `nbytes`, each timed like the GEMV (one uploaded graph
+    replay of back-to-back launches over `copies` rotating buffers): the GEMV's own access
+    pattern (w4a16_stream_read), grid-stride reads of other shapes (w4a16_stream_read_grid),
+    and a device-to-device copy of the same bytes (hipMemcpyAsync through torch, which also
+    writes them). The same read and copy of 1 GiB show the streaming rate once launch costs
+    are amortised."""
+    dev = "cuda:0"
+    res = {"bytes": nbytes}
+    buf = torch.zeros((copies, nbytes // 4), dtype=torch.int32, device=dev)
+    sink = w4.stream_read(buf[0])
+    t = time_steps_queued(torch, lambda i: w4.stream_read(buf[i % copies], sink), steps, warmup)
+    res["gemv_pattern"] = {"us_per_call": t * 1e3, "GB_s": nbytes / (t * 1e-3) / 1e9}
+    best = t
+    rows = []
+    gsink = torch.empty(8192, dtype=torch.int32, device=dev)
+    for threads, blocks, unroll in GRID_READS:
+        tg = time_steps_queued(torch, lambda i: w4.stream_read_grid(buf[i % copies], threads, blocks, unroll,
+                                                                   gsink[:blocks]), min(steps, 500), 20)
+        rows.append({"threads": threads, "workgroups": blocks, "loads_in_flight": unroll, "us_per_call": tg * 1e3,
+                     "GB_s": nbytes / (tg * 1e-3) / 1e9})
+        best = min(best, tg)
+    res["grid_stride"] = rows
+    dst = torch.empty_like(buf[0])
+    tc = time_steps_queued(torch, lambda i: dst.copy_(buf[i % copies]), min(steps, 500), 20)
+    res["copy_d2d"] = {"us_per_call": tc * 1e3, "GB_s_read_plus_write": 2 * nbytes / (tc * 1e-3) / 1e9,
+                       "note": "reads and writes the bytes once each"}
+    del buf, dst
+    big = torch.zeros(1 << 28, dtype=torch.int32, device=dev)  # 1 GiB
+    big_dst = torch.empty_like(big)
+    tb = time_steps_queued(torch, lambda i: w4.stream_read_grid(big, 256, 2048, 8, gsink[:2048]), 20, 3)
+    tbc = time_steps_queued(torch, lambda i: big_dst.copy_(big), 20, 3)
+    res["read_1gib"] = {"us_per_call": tb * 1e3, "GB_s": (1 << 30) / (tb * 1e-3) / 1e9,
+                        "pattern": "grid-stride, 256 threads x 2048 workgroups x 8 loads"}
+    res["copy_1gib"] = {"us_per_call": tbc * 1e3, "GB_s_read_plus_write": 2 * (1 << 30) / (tbc * 1e-3) / 1e9}
+    del big, big_dst
+    torch.cuda.empty_cache()
+    res["best_single_launch_read"] = {"us_per_call": best * 1e3, "GB_s": nbytes / (best * 1e-3) / 1e9,
+                                      "frac_of_peak": nbytes / (best * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    res["gemv_fraction_of_best_read"] = best / gemv_ms
+    res["note"] = ("single-launch reads of the GEMV's bytes by several patterns, timed like the GEMV; the best of "
+                   "them is the practical ceiling of one launch of this size on this device")
+    return res
 
 
 def block_leg(w4, torch):
@@ -336,7 +400,9 @@ def copy_probe(torch, out):
 
 
 def cpu_baseline(layer, seconds):
-    """The oracle's linear (NumPy float64) on the host, timed on whole-layer calls."""
+    """The oracle on the host: its linear (O-L, NumPy float64) on whole-layer calls for
+    about `seconds`, and its quantize-pack (O-Q) of the same layer for about half as long,
+    each reported separately. `value` is O-L, the metric's operation."""
     import numpy as np
 
     import oracle
@@ -348,29 +414,41 @@ def cpu_baseline(layer, seconds):
         blas_threads = max([p.get("num_threads", 1) for p in blas] or [1])
     except Exception:  # threadpoolctl missing: report what numpy would use
         blas_threads = len(os.sched_getaffinity(0))
+
+    def timed(fn, budget):
+        n_calls, t_total = 0, 0.0
+        t0 = time.perf_counter()
+        while True:
+            a = time.perf_counter()
+            fn()
+            t_total += time.perf_counter() - a
+            n_calls += 1
+            if time.perf_counter() - t0 >= budget and n_calls >= 2:
+                return n_calls, t_total
+
     x = layer.x.cpu().numpy()
     qw, sc, zr = (t.cpu().numpy() for t in layer.copies[0][1:])
     qw = qw.view(np.uint32)
-    n_calls, t_total = 0, 0.0
-    t0 = time.perf_counter()
-    while True:
-        a = time.perf_counter()
-        oracle.linear(x, qw, sc, zr)
-        t_total += time.perf_counter() - a
-        n_calls += 1
-        if time.perf_counter() - t0 >= seconds and n_calls >= 2:
-            break
+    n_calls, t_total = timed(lambda: oracle.linear(x, qw, sc, zr), seconds)
     us = t_total / n_calls * 1e6
     nbytes = algorithmic_bytes(layer.m, layer.n, layer.k)
+    W = layer.W.cpu().numpy()
+    s = layer.s.cpu().numpy()
+    q_calls, q_total = timed(lambda: oracle.quantize_pack(W, s), seconds / 2)
+    q_us = q_total / q_calls * 1e6
+    q_bytes = layer.n * layer.k * 2 + layer.k * 4 + layer.n * layer.k // 2 + 2 * 2 * layer.n * (layer.k // 128)
     return {
         "value": nbytes / (us * 1e-6) / 1e9,
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"{n_calls} whole-layer calls of the float64 NumPy oracle linear (M=1, K=N=8192), "
-                  f"{t_total:.1f} s; {us:.0f} us/call; dequantize is single-threaded NumPy, the matvec uses "
-                  f"{blas_threads} BLAS threads",
+        "sample": f"O-L: {n_calls} whole-layer calls of the float64 NumPy oracle linear (M=1, K=N=8192), "
+                  f"{t_total:.1f} s, {us:.0f} us/call; O-Q: {q_calls} whole-layer quantize-pack calls, "
+                  f"{q_total:.1f} s, {q_us:.0f} us/call. Dequantize and quantize are single-threaded NumPy, the "
+                  f"matvec uses {blas_threads} BLAS threads",
         "us_per_call": us,
+        "quantize_pack": {"us_per_call": q_us, "GB_s": q_bytes / (q_us * 1e-6) / 1e9, "bytes": q_bytes,
+                          "calls": q_calls, "cores": 1},
     }
 
 
@@ -414,8 +492,8 @@ def main():
         b = algorithmic_bytes(mm, nn, kk)
         L = Layer(w4, torch, 5, lid, nn, kk, mm, copies_for(b))
         ws = torch.empty(w4.splitk_workspace_bytes(mm, nn, kk, 16) // 4, dtype=torch.float32, device=L.x.device)
-        t_tiled = time_steps_graph(torch, lambda i: L.call(w4, i, 2), args.steps, args.warmup)
-        t_split = time_steps_graph(torch, lambda i: w4.linear_splitk(*L.copies[i % len(L.copies)], workspace=ws,
+        t_tiled = time_steps_queued(torch, lambda i: L.call(w4, i, 2), args.steps, args.warmup)
+        t_split = time_steps_queued(torch, lambda i: w4.linear_splitk(*L.copies[i % len(L.copies)], workspace=ws,
                                                                        out=L.y[i % len(L.y)]), args.steps, args.warmup)
         flop = 2 * mm * nn * kk
         res = {"layer": lname, "M": mm, "K": kk, "N": nn, "flop": flop, "algorithmic_bytes": b,
@@ -430,7 +508,7 @@ def main():
         mm = args.only_m
         b = algorithmic_bytes(mm, 8192, 8192)
         L = Layer(w4, torch, 4, 0, 8192, 8192, mm, copies_for(b))
-        t = time_steps_graph(torch, lambda i: L.call(w4, i), args.steps, args.warmup)
+        t = time_steps_queued(torch, lambda i: L.call(w4, i), args.steps, args.warmup)
         res = {"M": mm, "K": 8192, "N": 8192, "us_per_call": t * 1e3, "GB_s": b / (t * 1e-3) / 1e9,
                "algorithmic_bytes_per_call": b}
         if args.copy_probe:
@@ -444,8 +522,8 @@ def main():
     layer = Layer(w4, torch, 3, 0, n, k, m, copies_for(nbytes))
     fn = lambda i: layer.call(w4, i)  # noqa: E731
 
-    # ---- the timed region: exactly `steps` calls (one HIP graph), synchronized on both sides
-    ms = time_steps_graph(torch, fn, args.steps, args.warmup)
+    # ---- the timed region: exactly `steps` back-to-back calls, synchronized on both sides
+    ms = time_steps_queued(torch, fn, args.steps, args.warmup)
     value = nbytes / (ms * 1e-3) / 1e9
 
     out = {
@@ -487,25 +565,12 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic_entry(nbytes),
-        "kernel_us": ms * 1e3,
-        "timing": f"HIP events around one graph replay of the {args.steps} timed back-to-back GEMV launches",
+        "us_per_launch": ms * 1e3,
+        "timing": f"HIP events around the {args.steps} timed GEMV launches, queued back to back behind a device-side "
+                  f"delay that outlasts their submission, so that neither host launch cost nor graph start-up is timed",
     }
-    # the single-launch read floor of the same bytes: one plain read with the GEMV's access
-    # pattern over the same number of rotating copies (a measurement aid of the library)
-    floor_buf = torch.empty((len(layer.copies), nbytes // 4), dtype=torch.int32, device="cuda:0")
-    floor_buf.fill_(0)
-    floor_sink = w4.stream_read(floor_buf[0])
-    floor_ms = time_steps_graph(torch, lambda i: w4.stream_read(floor_buf[i % len(layer.copies)], floor_sink),
-                                args.steps, args.warmup)
-    out["read_floor"] = {
-        "us_per_call": floor_ms * 1e3,
-        "GB_s": nbytes / (floor_ms * 1e-3) / 1e9,
-        "gemv_fraction_of_floor": floor_ms / ms,
-        "bytes": nbytes,
-        "note": "one launch reading the same bytes with the GEMV's access pattern (w4a16_stream_read), "
-                "timed like the GEMV: the practical single-launch ceiling on this device",
-    }
-    del floor_buf
+    # the single-launch read floor of the same bytes, by several read patterns
+    out["read_floor"] = read_floor_leg(torch, w4, nbytes, len(layer.copies), ms, args.steps, args.warmup)
     eager_ms = time_back_to_back(torch, fn, args.steps, args.warmup)
     avg_ms, med_ms = time_per_launch(torch, fn, min(args.steps, 400))
     graph_ms = time_graph(torch, fn, 200)

@@ -428,6 +428,25 @@ w4a16_status w4a16_stream_read(const void* buf, int64_t bytes, void* sink, void*
 /* Bytes of sink that w4a16_stream_read needs for `bytes` (-1 if bytes is not accepted). */
 int64_t w4a16_stream_read_sink_bytes(int64_t bytes);
 
+/*
+ * w4a16_stream_read_grid - a measurement aid, not part of the method: a second read
+ * pattern, independent of the GEMV's grid, to test whether the single-launch floor
+ * belongs to the machine or to one access pattern. A grid-stride read of `bytes` of
+ * `buf` in tiles of threads x unroll 16-byte pieces: tile i covers pieces
+ * [i threads unroll, (i + 1) threads unroll); workgroup b (of `blocks`, each of
+ * `threads` threads) takes tiles b, b + blocks, ...; its thread t loads pieces
+ * i threads unroll + t + j threads (j < unroll) non-temporally, all before using any.
+ * threads: 64, 128, 256, 512 or 1024; unroll: 1, 2, 4, 8 or 16; blocks in [1, 2^20].
+ * sink: device memory of blocks 32-bit words, 4-byte aligned; workgroup b writes
+ * sink[b] = W4A16_STREAM_READ_MAGIC only if the XOR of one of its thread's words over
+ * all its tiles equals that value, and nothing otherwise. buf: device memory, 16-byte
+ * aligned, bytes > 0 and a multiple of 16. Errors: W4A16_ERR_NULL, W4A16_ERR_SHAPE,
+ * W4A16_ERR_ARG (threads, unroll, blocks), W4A16_ERR_ALIGN, W4A16_ERR_HIP; checked
+ * before any HIP call.
+ */
+w4a16_status w4a16_stream_read_grid(const void* buf, int64_t bytes, int32_t threads, int32_t blocks, int32_t unroll,
+                                    void* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

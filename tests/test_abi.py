@@ -284,3 +284,18 @@ def test_stream_read_sizes_and_rejects():
     assert lib.w4a16_stream_read(buf, 4100, sink, None) == w4.ERR_SHAPE
     assert lib.w4a16_stream_read(vp((1 << 20) + 8), 4096, sink, None) == w4.ERR_ALIGN
     assert lib.w4a16_stream_read(buf, 4096, vp((1 << 21) + 2), None) == w4.ERR_ALIGN
+
+
+def test_stream_read_grid_rejects():
+    lib = w4.load()
+    vp = ctypes.c_void_p
+    buf, sink = vp(1 << 20), vp(1 << 21)
+    assert lib.w4a16_stream_read_grid(None, 4096, 256, 8, 4, sink, None) == w4.ERR_NULL
+    assert lib.w4a16_stream_read_grid(buf, 4096, 256, 8, 4, None, None) == w4.ERR_NULL
+    assert lib.w4a16_stream_read_grid(buf, 0, 256, 8, 4, sink, None) == w4.ERR_SHAPE
+    assert lib.w4a16_stream_read_grid(buf, 4100, 256, 8, 4, sink, None) == w4.ERR_SHAPE
+    for threads, blocks, unroll in ((32, 8, 4), (384, 8, 4), (2048, 8, 4), (256, 0, 4), (256, (1 << 20) + 1, 4),
+                                    (256, 8, 3), (256, 8, 32), (256, 8, 0)):
+        assert lib.w4a16_stream_read_grid(buf, 4096, threads, blocks, unroll, sink, None) == w4.ERR_ARG
+    assert lib.w4a16_stream_read_grid(vp((1 << 20) + 8), 4096, 256, 8, 4, sink, None) == w4.ERR_ALIGN
+    assert lib.w4a16_stream_read_grid(buf, 4096, 256, 8, 4, vp((1 << 21) + 2), None) == w4.ERR_ALIGN

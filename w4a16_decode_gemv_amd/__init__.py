@@ -66,6 +66,7 @@ def load():
         "awq_alpha_loss": ([vp, vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
         "w4a16_stream_read_sink_bytes": ([i64], i64),
         "w4a16_stream_read": ([vp, i64, vp, vp], i32),
+        "w4a16_stream_read_grid": ([vp, i64, i32, i32, i32, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -80,7 +81,7 @@ def exported_symbols():
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
             "w4a16_linear_path", "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
             "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
-            "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read"]
+            "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read", "w4a16_stream_read_grid"]
 
 
 def _check(status):
@@ -448,6 +449,22 @@ def stream_read(buf, sink=None):
         raise ValueError("buf must hold a positive multiple of 16 bytes")
     sink = _out(sink, (words // 4,), torch.int32, buf, "sink")
     _check(lib.w4a16_stream_read(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(buf)))
+    return sink
+
+
+def stream_read_grid(buf, threads=256, blocks=1024, unroll=4, sink=None):
+    """Measurement aid: a grid-stride read of `buf` in tiles of threads x unroll 16-byte
+    pieces over `blocks` workgroups (a read pattern independent of the GEMV's grid).
+    Returns the sink (int32, one word per workgroup, set to STREAM_READ_MAGIC only where
+    one thread's XOR of its words over all its tiles equals it)."""
+    torch = _torch()
+    lib = load()
+    if not isinstance(buf, torch.Tensor) or buf.device.type != "cuda" or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous GPU tensor")
+    nbytes = buf.numel() * buf.element_size()
+    sink = _out(sink, (int(blocks),), torch.int32, buf, "sink")
+    _check(lib.w4a16_stream_read_grid(buf.data_ptr(), nbytes, int(threads), int(blocks), int(unroll), sink.data_ptr(),
+                                      _stream(buf)))
     return sink
 
 

@@ -259,6 +259,23 @@ w4a16_status w4a16_stream_read(const void* buf, int64_t bytes, void* sink, void*
                     "stream read launch");
 }
 
+w4a16_status w4a16_stream_read_grid(const void* buf, int64_t bytes, int32_t threads, int32_t blocks, int32_t unroll,
+                                    void* sink, void* stream) {
+  clear_error();
+  if (!buf || !sink) return fail(W4A16_ERR_NULL, "buf and sink are required");
+  if (bytes <= 0 || bytes % 16 != 0) return fail(W4A16_ERR_SHAPE, "bytes must be positive and a multiple of 16");
+  if (bytes / 16 > (int64_t(1) << 40)) return fail(W4A16_ERR_SHAPE, "bytes beyond the limit");
+  if (threads != 64 && threads != 128 && threads != 256 && threads != 512 && threads != 1024)
+    return fail(W4A16_ERR_ARG, "threads must be 64, 128, 256, 512 or 1024 (got %d)", (int)threads);
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8 && unroll != 16)
+    return fail(W4A16_ERR_ARG, "unroll must be 1, 2, 4, 8 or 16 (got %d)", (int)unroll);
+  if (blocks <= 0 || blocks > (1 << 20)) return fail(W4A16_ERR_ARG, "blocks must lie in [1, 2^20] (got %d)", (int)blocks);
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(W4A16_ERR_ALIGN, "buf must be 16-byte and sink 4-byte aligned");
+  return hip_result(w4a16::launch_stream_read_grid(buf, bytes, threads, blocks, unroll, static_cast<uint32_t*>(sink),
+                                                   static_cast<hipStream_t>(stream)),
+                    "grid-stride read launch");
+}
+
 w4a16_status awq_channel_scale(const void* x_cal, int64_t T, int64_t K, double alpha, float* s, void* stream) {
   clear_error();
   if (!x_cal || !s) return fail(W4A16_ERR_NULL, "x_cal and s are required");

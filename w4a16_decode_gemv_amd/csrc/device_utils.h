@@ -7,7 +7,13 @@
 namespace w4a16 {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: raw 32-bit data, range-checked
+constexpr int kOutOfRange = 1 << 30;      // added to an offset: past every buffer range used here
+constexpr int kNonTemporal = 2;           // streaming hint for loads of data read once
 
 __device__ __forceinline__ float half_bits_to_float(uint16_t b) {
   return (float)__builtin_bit_cast(_Float16, b);
@@ -18,6 +24,13 @@ __device__ __forceinline__ uint16_t float_to_half_bits(float f) {
 }
 
 __device__ __forceinline__ half2_t as_half2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+
+__device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
+
+__device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4_t v = {a, b, c, d};
+  return __builtin_bit_cast(half8_t, v);
+}
 
 // float64 -> binary16 with a single round-to-nearest-even step (no float32
 // intermediate, which would round twice). Handles signed zero, subnormal
@@ -52,6 +65,44 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t b
   uint32_t d;
   asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(mask), "v"(bits));
   return d;
+}
+
+// The four exact fp16 pairs (q - z) of one layout-v1 code word, in the word's pair order
+// (inputs 0,1 | 2,3 | 4,5 | 6,7): each nibble pair is OR-ed into the mantissa of 0x6400
+// (fp16 1024), giving 1024 + q, or 1024 + 16 q for the upper nibble of a byte, which is
+// rebased by 1/16. c_lo = -(1024 + z) and c_hi = -(64 + z); every step is exact for
+// z in [-2032, 1024], and z = 0 gives the codes q themselves.
+__device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t c_lo, half2_t c_hi) {
+  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
+  const uint32_t w8 = w >> 8;
+  const half2_t p0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + c_lo;
+  const half2_t p1 = __builtin_elementwise_fma(as_half2(and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
+  const half2_t p2 = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) + c_lo;
+  const half2_t p3 = __builtin_elementwise_fma(as_half2(and_or(w8, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
+  return as_half8(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
+                  __builtin_bit_cast(uint32_t, p3));
+}
+
+// the eight codes q of one code word as exact fp16, in k order
+__device__ __forceinline__ half8_t codes_word(uint32_t w) {
+  return dequant_word(w, (half2_t){(_Float16)-1024.0f, (_Float16)-1024.0f},
+                      (half2_t){(_Float16)-64.0f, (_Float16)-64.0f});
+}
+
+// workgroup barrier that orders LDS only: global loads stay in flight across it
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// range-checked buffer resource over [base, base + bytes)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
+}
+
+__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 // The NF4 codebook as kernels take it: the 16 fp16 levels in ascending order, two per

@@ -43,29 +43,11 @@ namespace w4a16 {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int BN = 64;          // output columns per workgroup (4 waves x 16)
 constexpr int kThreads = 256;
 constexpr int kRing = 2;        // stages whose global loads are in flight
 
-__device__ __forceinline__ half8_t as_half8(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  const u32x4_t v = {a, b, c, d};
-  return __builtin_bit_cast(half8_t, v);
-}
-
-// the four exact fp16 pairs (q - z) of one code word; c_lo = -(1024 + z), c_hi = -(64 + z)
-__device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t c_lo, half2_t c_hi) {
-  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const uint32_t w8 = w >> 8;
-  const half2_t p0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + c_lo;
-  const half2_t p1 = __builtin_elementwise_fma(as_half2(and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
-  const half2_t p2 = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) + c_lo;
-  const half2_t p3 = __builtin_elementwise_fma(as_half2(and_or(w8, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
-  return as_half8(__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
-                  __builtin_bit_cast(uint32_t, p3));
-}
 
 template <int MB>
 struct Smem {

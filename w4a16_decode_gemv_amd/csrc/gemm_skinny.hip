@@ -68,33 +68,12 @@ namespace w4a16 {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int KS = 8;               // waves per workgroup, splitting K
 constexpr int kThreads = KS * 64;
 constexpr int D = 2;                // stages in flight per wave
 constexpr int kMaxStages = 8;       // stages per chunk of the largest kernel variant
-constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit raw data, range-checked
-constexpr int kOutOfRange = 1 << 30;      // added to an offset: past every buffer range used here
-constexpr int kNonTemporal = 2;           // streaming hint for the code loads (read once)
 
-__device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
-
-// the eight codes q of one code word as exact fp16, in k order
-__device__ __forceinline__ half8_t codes_word(uint32_t w) {
-  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const half2_t c_lo = {(_Float16)-1024.0f, (_Float16)-1024.0f};
-  const half2_t c_hi = {(_Float16)-64.0f, (_Float16)-64.0f};
-  const uint32_t w8 = w >> 8;
-  const half2_t p0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + c_lo;
-  const half2_t p1 = __builtin_elementwise_fma(as_half2(and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
-  const half2_t p2 = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) + c_lo;
-  const half2_t p3 = __builtin_elementwise_fma(as_half2(and_or(w8, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
-  const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-  return __builtin_bit_cast(half8_t, v);
-}
 
 // code formats of the kernel
 constexpr int kFmt4 = 0;    // 4-bit codes in layout v1, fp16 scales and zeros
@@ -450,7 +429,9 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
   }
 }
 
-struct Args {
+}  // namespace
+
+struct SkinnyArgs {
   const uint16_t* x;
   const uint32_t* qweight;
   const void* scales;  // fp16 scales, or float32 absmax (NF4)
@@ -460,6 +441,10 @@ struct Args {
   uint16_t* y;
   hipStream_t stream;
 };
+
+namespace {
+
+using Args = SkinnyArgs;
 
 template <int NTW, int MT, int NS, int XI, int SUB, int FMT>
 hipError_t launch_tile_x(const Args& a) {
@@ -553,36 +538,88 @@ hipError_t launch_format(const Args& a) {
 
 }  // namespace
 
+// One launcher per (SUB, FMT) pair. The build compiles this file once per part
+// (W4A16_SKINNY_PART = 0..4), each part holding some of the formats, so that the
+// kernel instances compile in parallel; without the macro one object holds them all.
+template <int SUB, int FMT>
+hipError_t skinny_format(const SkinnyArgs& a);
+template <> hipError_t skinny_format<1, kFmt4>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<2, kFmt4>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<4, kFmt4>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<1, kFmt3>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<2, kFmt3>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<4, kFmt3>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<1, kFmtNf4>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<2, kFmtNf4>(const SkinnyArgs& a);
+template <> hipError_t skinny_format<4, kFmtNf4>(const SkinnyArgs& a);
+
+#ifdef W4A16_SKINNY_PART
+#define W4A16_SKINNY_IN_PART(p) (W4A16_SKINNY_PART == (p))
+#else
+#define W4A16_SKINNY_IN_PART(p) 1
+#endif
+
+#if W4A16_SKINNY_IN_PART(0)
+template <>
+hipError_t skinny_format<1, kFmt4>(const SkinnyArgs& a) { return launch_format<1, kFmt4>(a); }
+#endif
+#if W4A16_SKINNY_IN_PART(1)
+template <>
+hipError_t skinny_format<2, kFmt4>(const SkinnyArgs& a) { return launch_format<2, kFmt4>(a); }
+template <>
+hipError_t skinny_format<4, kFmt4>(const SkinnyArgs& a) { return launch_format<4, kFmt4>(a); }
+#endif
+#if W4A16_SKINNY_IN_PART(2)
+template <>
+hipError_t skinny_format<1, kFmt3>(const SkinnyArgs& a) { return launch_format<1, kFmt3>(a); }
+template <>
+hipError_t skinny_format<2, kFmt3>(const SkinnyArgs& a) { return launch_format<2, kFmt3>(a); }
+#endif
+#if W4A16_SKINNY_IN_PART(3)
+template <>
+hipError_t skinny_format<4, kFmt3>(const SkinnyArgs& a) { return launch_format<4, kFmt3>(a); }
+template <>
+hipError_t skinny_format<1, kFmtNf4>(const SkinnyArgs& a) { return launch_format<1, kFmtNf4>(a); }
+#endif
+#if W4A16_SKINNY_IN_PART(4)
+template <>
+hipError_t skinny_format<2, kFmtNf4>(const SkinnyArgs& a) { return launch_format<2, kFmtNf4>(a); }
+template <>
+hipError_t skinny_format<4, kFmtNf4>(const SkinnyArgs& a) { return launch_format<4, kFmtNf4>(a); }
+#endif
+
+#if W4A16_SKINNY_IN_PART(0)
 int skinny_max_m() { return 32; }
 
 hipError_t launch_skinny(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                          int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  return launch_format<1, kFmt4>({x, qweight, scales, zeros, M, N, K, {}, y, stream});
+  return skinny_format<1, kFmt4>({x, qweight, scales, zeros, M, N, K, {}, y, stream});
 }
 
 hipError_t launch_skinny_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight,
                                  const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
                                  uint16_t* y, hipStream_t stream) {
-  const Args a = {x, qweight, scales, zeros, M, N, K, {}, y, stream};
+  const SkinnyArgs a = {x, qweight, scales, zeros, M, N, K, {}, y, stream};
   if (bits == 4) {
-    if (group == 128) return launch_format<1, kFmt4>(a);
-    if (group == 64) return launch_format<2, kFmt4>(a);
-    if (group == 32) return launch_format<4, kFmt4>(a);
+    if (group == 128) return skinny_format<1, kFmt4>(a);
+    if (group == 64) return skinny_format<2, kFmt4>(a);
+    if (group == 32) return skinny_format<4, kFmt4>(a);
   } else if (bits == 3) {
-    if (group == 128) return launch_format<1, kFmt3>(a);
-    if (group == 64) return launch_format<2, kFmt3>(a);
-    if (group == 32) return launch_format<4, kFmt3>(a);
+    if (group == 128) return skinny_format<1, kFmt3>(a);
+    if (group == 64) return skinny_format<2, kFmt3>(a);
+    if (group == 32) return skinny_format<4, kFmt3>(a);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_skinny_nf4(const Nf4Table& table, int block, const uint16_t* x, const uint32_t* qweight,
                              const float* absmax, int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
-  const Args a = {x, qweight, absmax, nullptr, M, N, K, table, y, stream};
-  if (block == 128) return launch_format<1, kFmtNf4>(a);
-  if (block == 64) return launch_format<2, kFmtNf4>(a);
-  if (block == 32) return launch_format<4, kFmtNf4>(a);
+  const SkinnyArgs a = {x, qweight, absmax, nullptr, M, N, K, table, y, stream};
+  if (block == 128) return skinny_format<1, kFmtNf4>(a);
+  if (block == 64) return skinny_format<2, kFmtNf4>(a);
+  if (block == 32) return skinny_format<4, kFmtNf4>(a);
   return hipErrorInvalidValue;
 }
+#endif
 
 }  // namespace w4a16

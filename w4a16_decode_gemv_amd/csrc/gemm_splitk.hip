@@ -32,8 +32,6 @@ namespace w4a16 {
 
 namespace {
 
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
-typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int MT = 4;                  // 16-row MFMA tiles of m per workgroup
 constexpr int WAVES = 8;
@@ -42,37 +40,10 @@ constexpr int BN = 16 * WAVES;         // 128 rows n
 constexpr int kThreads = 64 * WAVES;
 constexpr int XU = BM * 16 / kThreads;  // 16-byte x chunks per thread per stage
 constexpr int R = 2;                   // stages of loads in flight
-constexpr int kBufferFlags = 0x00020000;
-constexpr int kOutOfRange = 1 << 30;
 constexpr int kMaxSplits = 16;
 
-__device__ __forceinline__ half8_t as_half8(u32x4_t v) { return __builtin_bit_cast(half8_t, v); }
 
-__device__ __forceinline__ half8_t dequant_word(uint32_t w, half2_t c_lo, half2_t c_hi) {
-  const half2_t sixteenth = {(_Float16)0.0625f, (_Float16)0.0625f};
-  const uint32_t w8 = w >> 8;
-  const half2_t p0 = as_half2(and_or(w, 0x000F000Fu, 0x64006400u)) + c_lo;
-  const half2_t p1 = __builtin_elementwise_fma(as_half2(and_or(w, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
-  const half2_t p2 = as_half2(and_or(w8, 0x000F000Fu, 0x64006400u)) + c_lo;
-  const half2_t p3 = __builtin_elementwise_fma(as_half2(and_or(w8, 0x00F000F0u, 0x64006400u)), sixteenth, c_hi);
-  const u32x4_t v = {__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
-                     __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
-  return __builtin_bit_cast(half8_t, v);
-}
 
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, kBufferFlags);
-}
-
-__device__ __forceinline__ u32x4_t load16(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 
 struct Stage {
   u32x4_t x[XU];

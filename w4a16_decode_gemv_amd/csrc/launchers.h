@@ -102,5 +102,8 @@ hipError_t launch_mfma_nf4(const Nf4Table& table, int block, const uint16_t* x, 
 // measurement aid: one read of a buffer with the GEMV's access pattern
 int64_t stream_read_blocks(int64_t bytes);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+// grid-stride read in tiles of threads x unroll pieces (threads 64..1024, unroll 1..16, powers of two)
+hipError_t launch_stream_read_grid(const void* buf, int64_t bytes, int threads, int blocks, int unroll, uint32_t* sink,
+                                   hipStream_t stream);
 
 }  // namespace w4a16

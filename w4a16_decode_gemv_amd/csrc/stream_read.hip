@@ -71,9 +71,64 @@ hipError_t launch_u(const void* buf, int64_t pieces, const Split& sp, uint32_t* 
   }
 }
 
+// A second read pattern that shares nothing with the GEMV's grid: a grid-stride
+// read in tiles of THREADS x U pieces. Tile i is pieces [i T U, (i + 1) T U); thread t
+// of the workgroup that takes it loads pieces i T U + t + j T (j < U), all U loads
+// issued before any is used. Workgroup b takes tiles b, b + grid, b + 2 grid, ...
+// (a persistent loop when the grid is smaller than the tile count).
+template <int THREADS, int U>
+__global__ __launch_bounds__(THREADS) void stream_read_grid_kernel(const u32x4_t* __restrict__ buf, int64_t pieces,
+                                                                   uint32_t* __restrict__ sink) {
+  constexpr int64_t kTile = (int64_t)THREADS * U;
+  const int64_t tiles = (pieces + kTile - 1) / kTile;
+  uint32_t acc = 0;
+  for (int64_t tile = blockIdx.x; tile < tiles; tile += gridDim.x) {
+    const int64_t base = tile * kTile + threadIdx.x;
+    u32x4_t v[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t p = base + (int64_t)j * THREADS;
+      v[j] = __builtin_nontemporal_load(&buf[p < pieces ? p : pieces - 1]);
+    }
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int64_t p = base + (int64_t)j * THREADS;
+      if (p < pieces) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+  }
+  if (acc == kMagic) sink[blockIdx.x] = acc;
+}
+
+template <int THREADS>
+hipError_t launch_grid_t(const void* buf, int64_t pieces, int blocks, int unroll, uint32_t* sink, hipStream_t stream) {
+  const u32x4_t* b = static_cast<const u32x4_t*>(buf);
+  switch (unroll) {
+    case 1: hipLaunchKernelGGL((stream_read_grid_kernel<THREADS, 1>), dim3(blocks), dim3(THREADS), 0, stream, b, pieces, sink); break;
+    case 2: hipLaunchKernelGGL((stream_read_grid_kernel<THREADS, 2>), dim3(blocks), dim3(THREADS), 0, stream, b, pieces, sink); break;
+    case 4: hipLaunchKernelGGL((stream_read_grid_kernel<THREADS, 4>), dim3(blocks), dim3(THREADS), 0, stream, b, pieces, sink); break;
+    case 8: hipLaunchKernelGGL((stream_read_grid_kernel<THREADS, 8>), dim3(blocks), dim3(THREADS), 0, stream, b, pieces, sink); break;
+    case 16: hipLaunchKernelGGL((stream_read_grid_kernel<THREADS, 16>), dim3(blocks), dim3(THREADS), 0, stream, b, pieces, sink); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int64_t stream_read_blocks(int64_t bytes) { return split_of(bytes).blocks; }
+
+hipError_t launch_stream_read_grid(const void* buf, int64_t bytes, int threads, int blocks, int unroll, uint32_t* sink,
+                                   hipStream_t stream) {
+  const int64_t pieces = bytes / 16;
+  switch (threads) {
+    case 64: return launch_grid_t<64>(buf, pieces, blocks, unroll, sink, stream);
+    case 128: return launch_grid_t<128>(buf, pieces, blocks, unroll, sink, stream);
+    case 256: return launch_grid_t<256>(buf, pieces, blocks, unroll, sink, stream);
+    case 512: return launch_grid_t<512>(buf, pieces, blocks, unroll, sink, stream);
+    case 1024: return launch_grid_t<1024>(buf, pieces, blocks, unroll, sink, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream) {
   return launch_u<1>(buf, bytes / 16, split_of(bytes), sink, stream);
