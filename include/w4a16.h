@@ -239,6 +239,25 @@ w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void*
                                  void* workspace, int64_t workspace_bytes, void* y, void* stream);
 
 /*
+ * w4a16_linear_splitk_noalloc - w4a16_linear_splitk for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels, launched with the same
+ * arguments minus the workspace. The float32 partials go to the library's own
+ * scratch, a static device array of 2^23 floats (32 MiB) on each GPU the library
+ * runs on, held until the process ends; the call allocates and frees nothing.
+ * Every call on one GPU uses that GPU's array and overwrites it (the kernels write
+ * every partial they read, so nothing needs clearing): calls that overlap on one
+ * GPU (other streams, other threads) race and must be serialised by the caller.
+ * The first call on a device resolves the array's address there (HIP calls, no
+ * allocation). Errors: those of w4a16_linear_splitk except the workspace ones;
+ * W4A16_ERR_SHAPE when splits * M * N (splits after the library's choice for 0)
+ * exceeds 2^23; checked before any HIP call.
+ */
+w4a16_status w4a16_linear_splitk_noalloc(const void* x, const void* qweight, const void* scales, const void* zeros,
+                                         int64_t M, int64_t N, int64_t K, int32_t group, int32_t splits,
+                                         void* y, void* stream);
+
+/*
  * w3a16_linear - the fused dequantize + matrix multiply for 3-bit codes in the
  * packed 3-bit layout (awq_quantize_pack with bits 3). Lab 4 setup: 3-bit
  * weights, groups of 128; L13 TinyChat kernel fusion. Same formula, accuracy

@@ -299,3 +299,20 @@ def test_stream_read_grid_rejects():
         assert lib.w4a16_stream_read_grid(buf, 4096, threads, blocks, unroll, sink, None) == w4.ERR_ARG
     assert lib.w4a16_stream_read_grid(vp((1 << 20) + 8), 4096, 256, 8, 4, sink, None) == w4.ERR_ALIGN
     assert lib.w4a16_stream_read_grid(buf, 4096, 256, 8, 4, vp((1 << 21) + 2), None) == w4.ERR_ALIGN
+
+
+def test_splitk_noalloc_rejects_before_any_hip_call():
+    lib = w4.load()
+
+    def call(group=128, splits=2, M=128, N=4096, K=4096, x=A16):
+        return lib.w4a16_linear_splitk_noalloc(x, A16, A16, A16, M, N, K, group, splits, A16, None)
+
+    assert call(x=None) == w4.ERR_NULL
+    assert call(group=64) == w4.ERR_UNSUPPORTED
+    assert call(splits=-1) == w4.ERR_ARG
+    assert call(splits=17) == w4.ERR_ARG
+    assert call(splits=3, K=256) == w4.ERR_ARG
+    assert call(K=200) == w4.ERR_SHAPE
+    # the library's scratch holds 2^23 float partials: splits * M * N beyond that is refused
+    assert call(M=256, N=11008, splits=4) == w4.ERR_SHAPE
+    assert call(M=2049, N=4096, splits=1) == w4.ERR_SHAPE  # 2048 x 4096 x 1 = 2^23 fits exactly

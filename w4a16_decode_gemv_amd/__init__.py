@@ -55,6 +55,7 @@ def load():
         "awq_alpha_loss_workspace": ([i64, i64], i64),
         "w4a16_linear_splitk_workspace": ([i64, i64, i64, i32], i64),
         "w4a16_linear_splitk": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, i64, vp, vp], i32),
+        "w4a16_linear_splitk_noalloc": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp], i32),
         "w3a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w3a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_quantize_pack_sym": ([vp, vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
@@ -79,7 +80,7 @@ def load():
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
-            "w4a16_linear_path", "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
+            "w4a16_linear_path", "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w4a16_linear_splitk_noalloc", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
             "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
             "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read", "w4a16_stream_read_grid"]
 
@@ -248,6 +249,28 @@ def linear_splitk(x, qweight, scales, zeros, splits=0, workspace=None, out=None,
     _check(lib.w4a16_linear_splitk(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k,
                                    group, splits, workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    y.data_ptr(), _stream(x)))
+    return y
+
+
+def linear_splitk_noalloc(x, qweight, scales, zeros, out, splits=0, group=GROUP):
+    """``linear_splitk`` with the partials in the library's own static scratch: the call
+    allocates nothing (`out`, the fp16 [M][N] result, is the caller's). Calls that overlap
+    on one GPU share that scratch and race."""
+    torch = _torch()
+    lib = load()
+    x = _dev_tensor(x, torch.float16, "x", 2)
+    qweight = _dev_tensor(qweight, torch.int32, "qweight", 2)
+    scales = _dev_tensor(scales, torch.float16, "scales", 2)
+    zeros = _dev_tensor(zeros, torch.float16, "zeros", 2)
+    m, k = x.shape
+    n = qweight.shape[0]
+    if qweight.shape[1] * 8 != k or scales.shape != zeros.shape or tuple(scales.shape) != (n, k // group):
+        raise ValueError("qweight must be [N][K/8] and scales/zeros [N][K/group]")
+    if out is None:
+        raise ValueError("out is required: this call allocates nothing")
+    y = _out(out, (m, n), torch.float16, x)
+    _check(lib.w4a16_linear_splitk_noalloc(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m,
+                                           n, k, group, splits, y.data_ptr(), _stream(x)))
     return y
 
 

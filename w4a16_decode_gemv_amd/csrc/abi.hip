@@ -402,6 +402,30 @@ w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void*
                     "split-K launch");
 }
 
+w4a16_status w4a16_linear_splitk_noalloc(const void* x, const void* qweight, const void* scales, const void* zeros,
+                                         int64_t M, int64_t N, int64_t K, int32_t group, int32_t splits, void* y,
+                                         void* stream) {
+  clear_error();
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "the split-K kernel takes groups of 128 (got %d)", (int)group);
+  if (splits < 0 || splits > w4a16::splitk_max_splits() || splits > K / 128)
+    return fail(W4A16_ERR_ARG, "splits must lie in [0, min(%d, K/128)] (got %d)", w4a16::splitk_max_splits(), (int)splits);
+  const int s = splits == 0 ? w4a16::splitk_default_splits(M, N, K) : splits;
+  const int64_t need = w4a16::splitk_workspace_floats(M, N, s);
+  if (need > w4a16::kSplitkScratchFloats)
+    return fail(W4A16_ERR_SHAPE, "splits * M * N = %lld float partials exceed the library's scratch of %lld",
+                (long long)need, (long long)w4a16::kSplitkScratchFloats);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  float* scratch = nullptr;
+  const w4a16_status rs = hip_result(w4a16::splitk_scratch(hs, &scratch), "scratch address");
+  if (rs != W4A16_OK) return rs;
+  return hip_result(w4a16::launch_splitk(static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
+                                         static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), M,
+                                         N, K, s, scratch, static_cast<uint16_t*>(y), hs),
+                    "split-K launch");
+}
+
 int64_t awq_alpha_loss_workspace(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0 || T > kMaxT || N > kMaxN) return -1;
   const int64_t tiles = w4a16::alpha_loss_partials(T, N);

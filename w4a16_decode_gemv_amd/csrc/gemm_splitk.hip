@@ -24,9 +24,17 @@
 // m-tile are read from LDS while the current m-tile's MFMAs run (2-12 % faster on
 // the LLaMA2-7B serving shapes than reading each fragment just before its MFMA).
 #include <algorithm>
+#include <mutex>
 
 #include "device_utils.h"
 #include "launchers.h"
+
+// The split-K partials of w4a16_linear_splitk_noalloc, for callers that cannot
+// allocate: one array per GPU the library runs on, held until the process ends.
+// Host code never passes this name to a kernel (on the host it stands for no device
+// address); it resolves the array's address on each device once, with
+// hipGetSymbolAddress, and passes that address.
+static __device__ __align__(256) float scratch[w4a16::kSplitkScratchFloats];
 
 namespace w4a16 {
 
@@ -228,6 +236,35 @@ int splitk_default_splits(int64_t M, int64_t N, int64_t K) {
 }
 
 int64_t splitk_workspace_floats(int64_t M, int64_t N, int splits) { return (int64_t)splits * M * N; }
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float* g_scratch[kMaxDevices];  // device address of `scratch` per device, resolved once
+}  // namespace
+
+hipError_t splitk_scratch(hipStream_t stream, float** ptr) {
+  int dev = 0;
+  hipError_t e = hipStreamGetDevice(stream, &dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch[dev]) {
+    int current = 0;
+    e = hipGetDevice(&current);
+    if (e != hipSuccess) return e;
+    if (current != dev && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = current != dev ? hipSetDevice(current) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch[dev] = static_cast<float*>(p);
+  }
+  *ptr = g_scratch[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                          int64_t M, int64_t N, int64_t K, int splits, float* workspace, uint16_t* y,

@@ -71,6 +71,11 @@ int64_t splitk_workspace_floats(int64_t M, int64_t N, int splits);
 hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                          int64_t M, int64_t N, int64_t K, int splits, float* workspace, uint16_t* y,
                          hipStream_t stream);
+// The library's own split-K partials for callers that cannot allocate: a static device
+// array of kSplitkScratchFloats floats per GPU. splitk_scratch returns its address on the
+// device of `stream` (resolved once per device; the first call on a device makes HIP calls).
+constexpr int64_t kSplitkScratchFloats = int64_t(1) << 23;  // 32 MiB
+hipError_t splitk_scratch(hipStream_t stream, float** ptr);
 
 // Tiled MFMA kernel: any M >= 1.
 hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
