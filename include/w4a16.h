@@ -414,7 +414,8 @@ w4a16_status nf4_linear(const void* x, const void* qweight, const float* absmax,
 
 /*
  * nf4_linear_path - nf4_linear with the kernel chosen: 0 auto, 1 GEMV (M <= 8,
- * M <= 4 above K = 16384, K <= 32768), 2 tiled MFMA (any M), 3 small-batch
+ * M <= 4 above K = 16384, K <= 32768; or M == 1 with N * K < 2^26 and
+ * K <= 131072, on the tuned kernel's NF4 form), 2 tiled MFMA (any M), 3 small-batch
  * MFMA (M <= 32). Other paths, or a shape the chosen kernel cannot take, return
  * W4A16_ERR_UNSUPPORTED before any HIP call.
  */

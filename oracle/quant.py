@@ -119,7 +119,7 @@ def quantize_groups(w, bits=4, group=128):
     rng = mx - mn
     rng = np.where(rng == 0.0, 1.0, rng)
     delta = rng / qmax
-    z = np.rint(np.negative(mn) / delta) + 0.0  # a zero offset is stored as +0
+    z = np.rint(np.negative(mn) / delta) + 0.0  # the integer zero offset 0 has one encoding, +0
     q = np.clip(np.rint(wg / delta[:, :, None]) + z[:, :, None], 0.0, qmax)
     return q.astype(np.int64).reshape(n, k), delta, z
 

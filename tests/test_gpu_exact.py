@@ -126,3 +126,28 @@ def test_nf4_every_position(lib, m, path):
         y = g.host(lib.nf4_linear(g.dev(x), g.dev(qw), g.dev(a), block=block, path=path))
         want = _exact_ref(oracle.linear_nf4(x, qw, a, block)[0])
         assert np.array_equal(g.bits16(y), g.bits16(want)), c0
+
+
+@pytest.mark.parametrize("bits,group", [(3, 128), (4, 32), (4, 64), (3, 32), (3, 64)])
+def test_variants_64_row_tiles_every_position(lib, bits, group):
+    # M = 512, N = 4096: 512 tiles of 64 rows, the tiled variant's 64-row tiles and load ring;
+    # row i of x is one-hot at input i % K, so one call rebuilds every input position
+    n, k, m = 4096, 384, 512
+    packed = _weights(7, n, k, bits, group)
+    print(f"exact 64-row tiles bits={bits} group={group}", flush=True)
+    _check(lib, _one_hot([i % k for i in range(m)], k), packed, 2, bits, group, tag="64-row tiles")
+
+
+def test_nf4_64_row_tiles_every_position(lib):
+    g = _gpu()
+    n, k, m, block = 4096, 384, 512, 64
+    rng = np.random.default_rng(8)
+    q = rng.integers(0, 16, size=(n, k))
+    q[:, :16] = np.arange(16)
+    qw = oracle.pack_codes(q)
+    a = (2.0 ** rng.integers(-6, 3, size=(n, k // block))).astype(np.float32)
+    print("exact NF4 64-row tiles", flush=True)
+    x = _one_hot([i % k for i in range(m)], k)
+    y = g.host(lib.nf4_linear(g.dev(x), g.dev(qw), g.dev(a), block=block, path=2))
+    want = _exact_ref(oracle.linear_nf4(x, qw, a, block)[0])
+    assert np.array_equal(g.bits16(y), g.bits16(want))

@@ -247,3 +247,41 @@ def test_auto_two_small_batch_passes(lib, bits, group, m, n, k):
     y1 = g.host(lib.linear(xd[:32].contiguous(), *dev, group=group, bits=bits, path=3))
     y2 = g.host(lib.linear(xd[32:].contiguous(), *dev, group=group, bits=bits, path=3))
     assert np.array_equal(y.view(np.uint16), np.concatenate([y1, y2]).view(np.uint16))
+
+
+@pytest.mark.parametrize("bits,group", FORMATS)
+@pytest.mark.parametrize("k", [384, 512])
+def test_mfma_variant_64_row_tiles(lib, bits, group, k):
+    # M = 512, N = 4096: (512 / 64) * (4096 / 64) = 512 tiles of 64 rows, so the tiled variant
+    # takes its 64-row tiles and their two-stage load ring; K = 384 (3 groups of 128) is not a
+    # multiple of the ring. Every output is compared.
+    m, n = 512, 4096
+    x_cal = synth.calibration(4, 8, k)
+    s = oracle.channel_scale(x_cal)
+    packed = oracle.quantize_pack(synth.weights(4, 8, n, k), s, bits=bits, group=group)
+    x = oracle.scale_input(synth.activations(4, 8, m, k), s)
+    _linear_check(lib, x, packed, bits, group, 2, "mfma-64-row-tiles")
+
+
+@pytest.mark.parametrize("bits,group", [(4, 64), (4, 32)])
+@pytest.mark.parametrize("path", [0, 1])
+def test_gemv_4bit_groups_long_row_one_token(lib, bits, group, path):
+    # M = 1, K = 65536: beyond the GEMV variant's K, but the tuned GEMV takes 4-bit groups of
+    # 64 and 32 there (eight pieces per thread); the automatic path must route it to that GEMV
+    n, k = 40, 65536
+    x_cal = synth.calibration(2, 9, k)
+    s = oracle.channel_scale(x_cal)
+    packed = oracle.quantize_pack(synth.weights(2, 9, n, k), s, bits=bits, group=group)
+    x = oracle.scale_input(synth.activations(2, 9, 1, k), s)
+    _linear_check(lib, x, packed, bits, group, path, "gemv-long-one-token")
+
+
+@pytest.mark.parametrize("bits,group", FORMATS + [(4, 128)])
+def test_skinny_variant_one_row(lib, bits, group):
+    # the small-batch kernel forced at M = 1 (rows past M read as zero)
+    n, k = 97, 11008
+    x_cal = synth.calibration(4, 10, k)
+    s = oracle.channel_scale(x_cal)
+    packed = oracle.quantize_pack(synth.weights(4, 10, n, k), s, bits=bits, group=group)
+    x = oracle.scale_input(synth.activations(4, 10, 1, k), s)
+    _linear_check(lib, x, packed, bits, group, 3, "skinny-one-row")

@@ -54,7 +54,9 @@ def test_gemv_small_shapes(lib, m, n, k):
 
 def test_gemv_long_rows_take_several_pieces_per_thread(lib):
     # K = 22016 (two pieces per thread) and K = 65536 (eight) on M = 1; K = 32768 at M = 4
-    for m, k in [(1, 22016), (1, 65536), (2, 40960), (4, 32768)]:
+    # K = 22016 and 32768 at M = 2: one piece per thread in 688- and 1024-thread workgroups (the
+    # automatic route of the LLaMA-65B down projection at M = 2)
+    for m, k in [(1, 22016), (1, 65536), (2, 22016), (2, 32768), (2, 40960), (4, 32768)]:
         xs, qw, sc, zr = _packed(4, 40, 33, k, m)
         _check(lib, xs, qw, sc, zr, path=1, tag="gemv-long")
 
@@ -132,11 +134,13 @@ def _sampled_rows(n, seed, count=256):
     return rows
 
 
-@pytest.mark.parametrize("layer_id", [0, 4, 6])
-def test_llama65b_full_size_sampled(lib, layer_id):
+@pytest.mark.parametrize("layer_id,m", [(0, 1), (4, 1), (6, 1), (6, 2)])
+def test_llama65b_full_size_all_rows(lib, layer_id, m):
+    # every output of the LLaMA-65B decode layers (8192^2, 8192 -> 22016, 22016 -> 8192) on the
+    # automatic path, as the bench launches them
     name, k, n = synth.CONFIGS[synth.LLAMA65B_DECODE]["layers"][layer_id]
-    xs, qw, sc, zr = _packed(3, layer_id, n, k, 1)
-    _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id), tag=f"llama65b-{name}")
+    xs, qw, sc, zr = _packed(3, layer_id, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=0, tag=f"llama65b-{name}-all-rows")
 
 
 @pytest.mark.parametrize("m", [2, 4, 8, 16, 32])
@@ -146,15 +150,16 @@ def test_batch_sweep_8192_all_paths(lib, m):
     paths = (1, 2, 3) if m <= 8 else (2, 3)
     for path in paths:
         _check(lib, xs, qw, sc, zr, path=path, rows=rows, tag="sweep-8192")
-    _check(lib, xs, qw, sc, zr, path=0, rows=rows, tag="sweep-8192-auto")
+    _check(lib, xs, qw, sc, zr, path=0, tag="sweep-8192-auto-all-rows")
 
 
 @pytest.mark.parametrize("m", [128, 256])
 @pytest.mark.parametrize("layer_id", [0, 1, 2])
 def test_llama2_7b_batched_serving(lib, m, layer_id):
+    # every output of the LLaMA2-7B serving GEMMs on the automatic path
     name, k, n = synth.CONFIGS[synth.LLAMA2_7B_SERVING]["layers"][layer_id]
     xs, qw, sc, zr = _packed(5, layer_id, n, k, m)
-    _check(lib, xs, qw, sc, zr, path=0, rows=_sampled_rows(n, layer_id, 128), tag=f"serving-{name}")
+    _check(lib, xs, qw, sc, zr, path=0, tag=f"serving-{name}-all-rows")
 
 
 @pytest.mark.parametrize("kind", ["positive", "negative", "constant", "ties", "mixed"])

@@ -184,3 +184,21 @@ def test_nf4_auto_two_small_batch_passes(lib, block, m):
     y1 = g.host(lib.nf4_linear(xd[:32].contiguous(), qd, ad, block=block, path=3))
     y2 = g.host(lib.nf4_linear(xd[32:].contiguous(), qd, ad, block=block, path=3))
     assert np.array_equal(y.view(np.uint16), np.concatenate([y1, y2]).view(np.uint16))
+
+
+@pytest.mark.parametrize("block", [64, 32])
+@pytest.mark.parametrize("k", [384, 512])
+def test_nf4_mfma_64_row_tiles(lib, block, k):
+    # M = 512, N = 4096: 512 tiles of 64 rows (the tiled kernel's 64-row tiles and load ring);
+    # K = 384 is not a multiple of the ring; every output compared
+    qw, a = oracle.quantize_pack_nf4(synth.weights(3, 9, 4096, k), None, block)
+    x = synth.activations(3, 9, 512, k)
+    _nf4_linear_check(lib, x, qw, a, block, 2, "mfma-64-row-tiles")
+
+
+@pytest.mark.parametrize("path", [0, 1])
+def test_nf4_gemv_long_row_one_token(lib, path):
+    # M = 1, K = 65536 on a layer under 2^26 weights: the tuned GEMV's NF4 form takes it
+    qw, a = oracle.quantize_pack_nf4(synth.weights(3, 10, 40, 65536), None, 64)
+    x = synth.activations(3, 10, 1, 65536)
+    _nf4_linear_check(lib, x, qw, a, 64, path, "gemv-long-one-token")

@@ -404,6 +404,30 @@ def test_channel_scale_is_correctly_rounded_sqrt_of_mean():
         assert (sv + ulp / 2) ** 2 >= m64 * (1 - Fraction(2) ** -50)
 
 
+def test_channel_scale_on_the_alpha_grid_brackets_the_exact_power():
+    """s = m^(i/20) for every point of the search grid (L13 AWQ section: s = s_X^alpha), pinned
+    in exact rationals: with m the exact mean of |x| (a rational: fp16 magnitudes summed, over
+    T), the float32 s must satisfy (s - ulp/2)^20 <= m^i <= (s + ulp/2)^20, up to the float64
+    arithmetic before the final rounding (a relative 2^-45 after the 20th power)."""
+    import synth
+
+    xc = synth.calibration(2, 5, 1024)
+    t = xc.shape[0]
+    chans = list(range(0, 1024, 61)) + [int(c) for c in synth.outlier_channels(2, 5, 1024)[:4]]
+    eps = Fraction(1, 2 ** 45)
+    for i in range(21):
+        s = oracle.channel_scale(xc, i / 20)
+        for kk in chans:
+            m = sum(abs(Fraction(float(v))) for v in xc[:, kk]) / t
+            sv = Fraction(float(s[kk]))
+            ulp = Fraction(float(np.spacing(np.float32(s[kk]))))
+            target = m ** i
+            assert (sv - ulp / 2) ** 20 <= target * (1 + eps), (i, kk)
+            assert (sv + ulp / 2) ** 20 >= target * (1 - eps), (i, kk)
+    # the oracle's own alpha argument is the float64 i/20; alpha = 0 gives 1 exactly
+    assert np.all(oracle.channel_scale(xc, 0.0) == 1.0)
+
+
 def test_channel_scale_outlier_statistics():
     import synth
 

@@ -144,7 +144,7 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   const uint16_t* zr = static_cast<const uint16_t*>(zeros);
   uint16_t* yh = static_cast<uint16_t*>(y);
   if (bits != 4 || group != 128) {
-    const bool gemv_ok = w4a16::gemv_variant_supports(M, K, group);
+    const bool gemv_ok = w4a16::gemv_format_supports(bits, group, M, N, K);
     // the small-batch kernel loads a row's scales (zeros) of 128 inputs in one 2-, 4- or 8-byte load
     const uintptr_t sz_align = group == 128 ? 2 : 4;
     const bool sz_aligned = aligned(scales, sz_align) && aligned(zeros, sz_align);
@@ -165,8 +165,9 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
       two_passes = sz_aligned && two_small_batch_passes(M, N, K);
       kernel = gemv_first && gemv_ok ? 1 : skinny_ok || two_passes ? 3 : gemv_ok ? 1 : 2;
     } else if (path == 1 && !gemv_ok) {
-      return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernel for this format takes M <= %d and K <= 32768 "
-                  "(M <= 4 above K = 16384); got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
+      return fail(W4A16_ERR_UNSUPPORTED, "the GEMV kernels for this format take M <= %d and K <= 32768 "
+                  "(M <= 4 above K = 16384), or for 4-bit codes M * ceil(K / 16384) <= 8; got M=%lld K=%lld",
+                  w4a16::gemv_max_m(), (long long)M, (long long)K);
     } else if (path == 3) {
       if (M > w4a16::skinny_max_m())
         return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes M <= %d; got M=%lld",
@@ -466,10 +467,11 @@ w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, c
     return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA) or 3 (small-batch MFMA)");
   const w4a16_status st = check_nf4_linear(x, qweight, absmax, M, N, K, block, y);
   if (st != W4A16_OK) return st;
-  const bool gemv_ok = w4a16::gemv_variant_supports(M, K, block);
+  const bool gemv_ok = w4a16::gemv_format_supports(0, block, M, N, K);
   if (path == 1 && !gemv_ok)
-    return fail(W4A16_ERR_UNSUPPORTED, "the NF4 GEMV kernel takes M <= %d and K <= 32768 (M <= 4 above K = 16384); "
-                "got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M, (long long)K);
+    return fail(W4A16_ERR_UNSUPPORTED, "the NF4 GEMV kernels take M <= %d and K <= 32768 (M <= 4 above K = 16384), "
+                "or M = 1 with N * K < 2^26 and K <= 131072; got M=%lld K=%lld", w4a16::gemv_max_m(), (long long)M,
+                (long long)K);
   if (path == 3 && M > w4a16::skinny_max_m())
     return fail(W4A16_ERR_UNSUPPORTED, "the small-batch MFMA kernel takes M <= %d; got M=%lld", w4a16::skinny_max_m(),
                 (long long)M);

@@ -128,9 +128,14 @@ __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThre
   float* wred = reinterpret_cast<float*>(wsz + E);
   _Float16* lut = reinterpret_cast<_Float16*>(wsz + E + V);
   if constexpr (NF4) {
-    // stored and read as fp16 by this wave only: its LDS accesses complete in order
+    // stored and read as fp16 by this wave only; the wave-scope fences and wave barrier
+    // order the other lanes' reads after lanes 0..15's stores for the compiler (they cost
+    // nothing at run time: one wave's LDS accesses complete in order)
     if (lane < 16)
       lut[lane] = __builtin_bit_cast(_Float16, (uint16_t)(table.pairs[lane >> 1] >> (16 * (lane & 1))));
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
   }
 
   // Every load below is unconditional, with indices clamped into the tensors,
@@ -700,6 +705,14 @@ hipError_t launch_gemv_nf4(const Nf4Table& table, int block, const uint16_t* x, 
     return launch_m<1, 0, true>(x, qweight, absmax, nullptr, N, K, y, stream, table);
   }
   return launch_var_fmt<kNF4>(x, qweight, absmax, nullptr, M, N, K, gsh, table, y, stream);
+}
+
+bool gemv_format_supports(int bits, int group, int64_t M, int64_t N, int64_t K) {
+  // the routes launch_gemv_variant and launch_gemv_nf4 take: the tuned kernel for 4-bit
+  // groups of 64/32 (and NF4 rows on small layers) wherever it fits, the variant kernel otherwise
+  if (bits == 4 && gemv_supports(M, K)) return true;
+  if (bits == 0 && M == 1 && N * K < (int64_t{1} << 26) && gemv_supports(M, K)) return true;
+  return gemv_variant_supports(M, K, group);
 }
 
 bool gemv_narrow(int64_t M, int64_t N, int64_t K) {

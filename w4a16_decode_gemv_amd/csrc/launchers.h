@@ -45,6 +45,9 @@ hipError_t launch_gemv(const uint16_t* x, const uint32_t* qweight, const uint16_
 // GEMV for the other code formats (bits 3 or 4, group 32, 64 or 128): needs
 // gemv_variant_supports(M, K, group).
 bool gemv_variant_supports(int64_t M, int64_t K, int group);
+// whether launch_gemv_variant (bits 3 or 4) or launch_gemv_nf4 (bits 0) takes this shape,
+// on whichever GEMV kernel it routes it to
+bool gemv_format_supports(int bits, int group, int64_t M, int64_t N, int64_t K);
 hipError_t launch_gemv_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                                const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                                hipStream_t stream);
