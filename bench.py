@@ -336,6 +336,9 @@ def block_leg(w4, torch):
             "note": "graph-timed; q/k/v (N=12288) and gate/up (N=22016) stacked row-wise share one launch"}
 
 
+SEARCH_GRID = tuple(i / 20 for i in range(21))  # the alphas the library's search visits
+
+
 def search_leg(w4, torch):
     """The AWQ scale search on the LLaMA2-7B block's seven projections with 512 calibration
     tokens: per layer the original output (once per search), the loss kernel alone (one
@@ -354,21 +357,21 @@ def search_leg(w4, torch):
         xs = w4.scale_input(x_cal, s)
         packed = w4.quantize_pack(W, s)
         ws = torch.empty(w4.alpha_loss_workspace(t_cal, nn), dtype=torch.float64, device=dev)
-        loss = torch.empty(len(w4.ALPHA_GRID), dtype=torch.float64, device=dev)
+        loss = torch.empty(len(SEARCH_GRID), dtype=torch.float64, device=dev)
         y_ref = torch.empty((t_cal, nn), dtype=torch.float32, device=dev)
         t_ref = time_graph(torch, lambda i: w4.output_reference(x_cal, W, out=y_ref), 10)
         t_loss = time_graph(torch, lambda i: w4.alpha_loss(xs, *packed, y_ref, workspace=ws,
                                                            out=loss[i % 21:i % 21 + 1]), 21)
 
         def point(i):
-            a = w4.ALPHA_GRID[i % 21]
+            a = SEARCH_GRID[i % 21]
             w4.channel_scale(x_cal, a, out=s)
             w4.scale_input(x_cal, s, out=xs)
             w4.quantize_pack(W, s, out=packed)
             w4.alpha_loss(xs, *packed, y_ref, workspace=ws, out=loss[i % 21:i % 21 + 1])
 
         t_point = time_graph(torch, point, 21)
-        t_scale = time_graph(torch, lambda i: w4.channel_scale(x_cal, w4.ALPHA_GRID[i % 21], out=s), 21)
+        t_scale = time_graph(torch, lambda i: w4.channel_scale(x_cal, SEARCH_GRID[i % 21], out=s), 21)
         t_fold = time_graph(torch, lambda i: w4.scale_input(x_cal, s, out=xs), 21)
         t_quant = time_graph(torch, lambda i: w4.quantize_pack(W, s, out=packed), 21)
         flop = 2 * t_cal * nn * kk  # one product of 2 T N K

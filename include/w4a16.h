@@ -182,9 +182,11 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * N * K >= 2^27 or on layers small enough that the GEMV takes 4-row tiles
  * (K <= 32768 and ceil(N / 8) * ceil(K / 2048) < 4096 waves, under 16 per CU),
  * run the wave-tile GEMV kernel; other M <= 32 the small-batch
- * MFMA kernel (workgroups own whole rows of y, waves split K); 33 <= M <= 64
- * on layers with N <= 8192 and K <= 16384 the small-batch kernel in two
- * launches (rows 0..31, then the rest); other M the tiled MFMA kernel.
+ * MFMA kernel (workgroups own whole rows of y, waves split K); M > 32 the
+ * K-lane MFMA kernel (K split over four waves per workgroup) where the tiled
+ * MFMA kernel would start at most 256 workgroups (ceil(M / 32) * ceil(N / 64)
+ * while ceil(M / 64) * ceil(N / 64) < 512, else the latter), or at most 512 with
+ * K > 8192; the tiled MFMA kernel otherwise.
  * Groups of 32 and 64: M == 1, and M == 2 on layers with K <= 24576 and
  * N * K >= 2^26 or small enough for 4-row tiles (as for group 128), run the
  * GEMV kernel (two or one 32-input pieces per group);
@@ -204,8 +206,9 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
  * 1 = GEMV kernel (needs M <= w4a16_gemv_max_m() and M * ceil(K / 16384) <= 8),
  * 2 = tiled MFMA kernel (any M), 3 = small-batch MFMA kernel (needs M <= 32;
  * with groups of 32 or 64, scales and zeros 4-byte aligned, else
- * W4A16_ERR_ALIGN). A path that cannot take the shape returns
- * W4A16_ERR_UNSUPPORTED before any HIP call. Same contract otherwise.
+ * W4A16_ERR_ALIGN), 4 = K-lane MFMA kernel (any M; groups of 128 only). A path
+ * that cannot take the shape returns W4A16_ERR_UNSUPPORTED before any HIP
+ * call. Same contract otherwise.
  */
 w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group,
@@ -340,6 +343,44 @@ w4a16_status awq_output_reference(const void* x, const void* w, int64_t T, int64
 w4a16_status awq_alpha_loss(const void* x_s, const void* qweight, const void* scales, const void* zeros,
                             const float* y_ref, int64_t T, int64_t N, int64_t K, int32_t group,
                             double* workspace, int64_t workspace_len, double* loss, void* stream);
+
+/* Points of the AWQ scale search's grid: alpha = i / 20, i = 0..20. */
+#define W4A16_ALPHA_GRID_POINTS 21
+
+/*
+ * awq_search_alpha_workspace - bytes of device workspace that awq_search_alpha
+ * needs for T calibration rows, N outputs and K inputs; -1 when the shape is
+ * outside the limits (T <= 65536, N <= 2^24, K <= W4A16_MAX_K, K % 128 == 0).
+ */
+int64_t awq_search_alpha_workspace(int64_t T, int64_t N, int64_t K);
+
+/*
+ * awq_search_alpha - the whole AWQ scale search on the device. L13 guide, AWQ
+ * section (slide 28): alpha* = argmin over alpha of || Q(W s)(s^-1 X) - W X ||
+ * with s = s_X^alpha; "Quantization for LLMs" chapter 11, AWQ section. For the
+ * grid alpha = i / 20 (i = 0..20) it computes, in stream order: the original
+ * output W X once (awq_output_reference), then per grid point s =
+ * awq_channel_scale(x_cal, alpha), x_s = awq_scale_input(x_cal, s),
+ * awq_quantize_pack(w, s, bits 4, group 128) and the loss (awq_alpha_loss) into
+ * losses[i]; finally the choice: best = the first index of the smallest loss
+ * (equal losses keep the smaller alpha), alpha = best / 20, and s = the
+ * candidate scale of that index. Results are bit-identical to running those
+ * calls one by one (the same kernels on the same inputs).
+ * x_cal: fp16 [T][K] calibration activations; w: fp16 [N][K] (nn.Linear
+ * weight); workspace: device memory of workspace_bytes >=
+ * awq_search_alpha_workspace(T, N, K) bytes, 256-byte aligned, overwritten (two
+ * searches in flight at once need two workspaces). Outputs, device memory:
+ * losses float64 [21], best int32 [1], alpha float64 [1], s float32 [K] (or
+ * NULL: the chosen scale is not copied out). All launches are asynchronous on
+ * `stream`; nothing is read back to the host.
+ * Alignment: x_cal and w 16 bytes; losses and alpha 8; best and s 4.
+ * Errors: W4A16_ERR_NULL; W4A16_ERR_SHAPE (a size <= 0, K % 128, T > 65536,
+ * N > 2^24, K > W4A16_MAX_K); W4A16_ERR_ARG (workspace too small);
+ * W4A16_ERR_ALIGN; W4A16_ERR_HIP. Checked before any HIP call.
+ */
+w4a16_status awq_search_alpha(const void* x_cal, const void* w, int64_t T, int64_t N, int64_t K,
+                              void* workspace, int64_t workspace_bytes, double* losses, int32_t* best,
+                              double* alpha, float* s, void* stream);
 
 /*
  * awq_quantize_pack_sym - symmetric absmax group quantization into the same

@@ -80,8 +80,10 @@ def test_linear_rejects_before_any_hip_call(kw, status):
 
 def test_linear_path_rejects_unknown_path_and_big_m_on_gemv():
     lib = w4.load()
-    assert lib.w4a16_linear_path(4, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear_path(5, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w4a16_linear_path(-1, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    # the K-lane MFMA kernel (path 4) takes groups of 128 only
+    assert lib.w4a16_linear_path(4, A16, A16, A16, A16, 64, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w4a16_linear_path(1, A16, A16, A16, A16, 9, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     # the small-batch MFMA kernel takes M <= 32
     assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 33, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
@@ -316,3 +318,30 @@ def test_splitk_noalloc_rejects_before_any_hip_call():
     # the library's scratch holds 2^23 float partials: splits * M * N beyond that is refused
     assert call(M=256, N=11008, splits=4) == w4.ERR_SHAPE
     assert call(M=2049, N=4096, splits=1) == w4.ERR_SHAPE  # 2048 x 4096 x 1 = 2^23 fits exactly
+
+
+def test_search_alpha_workspace_and_rejects():
+    lib = w4.load()
+    vp = ctypes.c_void_p
+    need = lib.awq_search_alpha_workspace(512, 4096, 4096)
+    # y_ref, 21 scales, x_s, codes, scales, zeros, loss partials; each region 256-byte aligned
+    parts = lib.awq_alpha_loss_workspace(512, 4096)
+    r = lambda b: (b + 255) // 256 * 256  # noqa: E731
+    assert need == (r(512 * 4096 * 4) + r(21 * 4096 * 4) + r(512 * 4096 * 2) + r(4096 * 4096 // 2)
+                    + 2 * r(4096 * 32 * 2) + r(parts * 8))
+    assert lib.awq_search_alpha_workspace(0, 4096, 4096) == -1
+    assert lib.awq_search_alpha_workspace(512, 4096, 4100) == -1
+    assert lib.awq_search_alpha_workspace(65537, 64, 128) == -1
+    ws, out = vp(1 << 20), vp(1 << 22)
+
+    def call(x=A16, w=A16, T=512, N=4096, K=4096, ws=ws, wb=need, losses=out, best=out, alpha=out):
+        return lib.awq_search_alpha(x, w, T, N, K, ws, wb, losses, best, alpha, None, None)
+
+    assert call(x=None) == w4.ERR_NULL
+    assert call(ws=None) == w4.ERR_NULL
+    assert call(best=None) == w4.ERR_NULL
+    assert call(K=200) == w4.ERR_SHAPE
+    assert call(T=0) == w4.ERR_SHAPE
+    assert call(wb=need - 1) == w4.ERR_ARG
+    assert call(ws=vp((1 << 20) + 128)) == w4.ERR_ALIGN
+    assert call(losses=vp((1 << 22) + 4)) == w4.ERR_ALIGN

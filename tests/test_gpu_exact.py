@@ -77,7 +77,7 @@ def test_gemv_long_rows(lib, k):
         _check(lib, _one_hot(cols[c0:c0 + m], k), packed, 1, tag=f"K={k} cols {cols[c0:c0 + m]}")
 
 
-@pytest.mark.parametrize("m,path", [(2, 3), (32, 3), (64, 2), (33, 2)])
+@pytest.mark.parametrize("m,path", [(2, 3), (32, 3), (64, 2), (33, 2), (64, 4), (33, 4), (128, 4)])
 def test_mfma_paths_every_position(lib, m, path):
     n, k = 97, 256
     packed = _weights(3, n, k)
@@ -151,3 +151,13 @@ def test_nf4_64_row_tiles_every_position(lib):
     y = g.host(lib.nf4_linear(g.dev(x), g.dev(qw), g.dev(a), block=block, path=2))
     want = _exact_ref(oracle.linear_nf4(x, qw, a, block)[0])
     assert np.array_equal(g.bits16(y), g.bits16(want))
+
+
+@pytest.mark.parametrize("k", [128, 384, 1152])
+def test_klane_every_position_ragged_k_lanes(lib, k):
+    # the K-lane kernel with 1, 3 and 9 groups over its four K-lanes (lanes with no group, and
+    # uneven ranges); row i of x is one-hot at input i % K, so one call rebuilds every input
+    n, m = 97, 192
+    packed = _weights(9, n, k)
+    print(f"exact K-lane K={k}", flush=True)
+    _check(lib, _one_hot([i % k for i in range(m)], k), packed, 4, tag=f"K-lane K={k}")

@@ -80,20 +80,22 @@ def test_skinny_small_shapes(lib, m, n, k):
 
 @pytest.mark.parametrize("m", [33, 40, 48, 63, 64])
 @pytest.mark.parametrize("n,k", [(300, 2048), (97, 11008), (8192, 1024)])
-def test_auto_two_small_batch_passes(lib, m, n, k):
-    # 33 <= M <= 64 on layers with N <= 8192 and K <= 16384: the automatic path runs the
-    # small-batch kernel on rows 0..31 and then on the rest; every row against the oracle, and
-    # the result equals the small-batch kernel run on the two row blocks separately
-    import torch
-
+def test_auto_33_to_64_rows(lib, m, n, k):
+    # 33 <= M <= 64 on layers with N <= 8192: the tiled kernel would start at most 256
+    # workgroups, so the automatic path takes the K-lane kernel (4-bit codes, groups of 128;
+    # the other formats run the small-batch kernel twice there). Every row against the oracle,
+    # and bit-identical to forcing the K-lane kernel; the small-batch kernel run on the two
+    # row blocks separately (path 3) is checked against the oracle too
     g = _gpu()
     xs, qw, sc, zr = _packed(4, 60 + m, n, k, m)
-    _check(lib, xs, qw, sc, zr, path=0, tag="auto-two-passes")
+    _check(lib, xs, qw, sc, zr, path=0, tag="auto-33-64")
     dev = [g.dev(t) for t in (xs, qw, sc, zr)]
     y = g.host(lib.linear(*dev))
-    y1 = g.host(lib.linear(dev[0][:32].contiguous(), *dev[1:], path=3))
-    y2 = g.host(lib.linear(dev[0][32:].contiguous(), *dev[1:], path=3))
-    assert np.array_equal(y.view(np.uint16), np.concatenate([y1, y2]).view(np.uint16))
+    assert np.array_equal(g.bits16(y), g.bits16(g.host(lib.linear(*dev, path=4))))
+    y1 = g.host(lib.linear(dev[0][:32].contiguous(), *dev[1:], path=3)).astype(np.float64)
+    y2 = g.host(lib.linear(dev[0][32:].contiguous(), *dev[1:], path=3)).astype(np.float64)
+    y_ref, b = oracle.linear(xs, qw, sc, zr)
+    assert np.all(oracle.within_tolerance(np.concatenate([y1, y2]), y_ref, b))
 
 
 def test_skinny_long_rows(lib):
@@ -163,7 +165,7 @@ def test_llama2_7b_batched_serving(lib, m, layer_id):
 
 
 @pytest.mark.parametrize("kind", ["positive", "negative", "constant", "ties", "mixed"])
-@pytest.mark.parametrize("path,m", [(1, 1), (1, 3), (2, 1), (2, 20), (3, 2), (3, 32)])
+@pytest.mark.parametrize("path,m", [(1, 1), (1, 3), (2, 1), (2, 20), (3, 2), (3, 32), (4, 20), (4, 70)])
 def test_edge_weights(lib, kind, path, m):
     n, k = 70, 1024
     W = synth.edge_weights(kind, n, k, seed=11)
@@ -172,7 +174,7 @@ def test_edge_weights(lib, kind, path, m):
 
 
 @pytest.mark.parametrize("kind", ["positive", "negative", "mixed"])
-@pytest.mark.parametrize("path,m", [(1, 1), (1, 4), (2, 1), (2, 20), (3, 2), (3, 32)])
+@pytest.mark.parametrize("path,m", [(1, 1), (1, 4), (2, 1), (2, 20), (3, 2), (3, 32), (4, 20), (4, 70)])
 def test_zeros_outside_the_exact_fp16_range(lib, kind, path, m):
     # quantized without the AWQ scale, narrow one-signed groups get |zero| up to ~3400; the MFMA kernels
     # cannot form (q - z) exactly in fp16 beyond [-2032, 1024] and must take their general route there,
@@ -199,7 +201,7 @@ def test_all_zero_rows_give_exact_zeros(lib):
         _check(lib, xs, qw, sc, zr, path=path, tag="zero-rows")
 
 
-@pytest.mark.parametrize("path,m", [(1, 1), (1, 8), (2, 16), (2, 128), (3, 2), (3, 32)])
+@pytest.mark.parametrize("path,m", [(1, 1), (1, 8), (2, 16), (2, 128), (3, 2), (3, 32), (4, 33), (4, 128)])
 def test_deterministic_and_writes_only_its_output(lib, path, m):
     import torch
 
@@ -234,3 +236,25 @@ def test_gpu_pipeline_end_to_end_single_2048(lib):
     qw, sc, zr = oracle.quantize_pack(L["W"], s)
     y_ref, b = oracle.linear(xs, qw, sc, zr)
     assert np.all(oracle.within_tolerance(y, y_ref, b))
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (33, 97, 384), (64, 32, 128), (65, 33, 256), (100, 300, 2048),
+                                   (128, 200, 11008), (257, 64, 4096), (70, 130, 640), (192, 4096, 4096)])
+def test_klane_ragged_shapes(lib, m, n, k):
+    # the K-lane kernel (path 4): rows past M and columns past N, K-lanes with no group
+    # (K = 128, 256) and uneven group ranges (K = 384, 640, 11008)
+    xs, qw, sc, zr = _packed(8, 1, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=4, tag="klane")
+
+
+@pytest.mark.parametrize("m,k,n", [(48, 4096, 4096), (64, 11008, 4096), (128, 4096, 4096), (256, 11008, 4096),
+                                   (64, 8192, 8192), (96, 22016, 8192)])
+def test_auto_klane_route(lib, m, k, n):
+    # shapes the automatic dispatch sends to the K-lane kernel: every output against the oracle,
+    # and bit-identical to forcing path 4
+    g = _gpu()
+    xs, qw, sc, zr = _packed(8, 2, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=0, tag="auto-klane")
+    a = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=0))
+    b = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=4))
+    assert np.array_equal(g.bits16(a), g.bits16(b))

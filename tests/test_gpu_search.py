@@ -147,12 +147,51 @@ def test_search_alpha_matches_oracle(lib, layer):
     W = synth.weights(2, 6, n, k)
     x_cal = synth.calibration(2, 6, k)
     print(f"search {layer} T={x_cal.shape[0]} N={n} K={k}", flush=True)
-    losses_d, best = lib.search_alpha(g.dev(x_cal), g.dev(W))
+    losses_d, best_d, alpha_d, s_d = lib.search_alpha(g.dev(x_cal), g.dev(W))
     losses = g.host(losses_d)
+    best = int(g.host(best_d)[0])
     want, want_best = oracle.search_alpha(x_cal, W)
     tol = np.array([max(RTOL_SEARCH * w, _loss_bound(x_cal, W, a)) for w, a in zip(want, oracle.ALPHA_GRID)])
     assert np.all(np.abs(losses - want) <= tol), (losses, want)
     grid = list(oracle.ALPHA_GRID)
-    assert want[grid.index(best)] <= want.min() * (1 + RTOL_SEARCH), (best, want_best)
-    if best != want_best:
-        print(f"chosen alpha {best} vs oracle {want_best}: losses {want[grid.index(best)]} vs {want.min()}")
+    # the device's own choice is the first minimum of its own losses
+    assert best == int(np.argmin(losses)) and float(g.host(alpha_d)[0]) == grid[best]
+    assert want[best] <= want.min() * (1 + RTOL_SEARCH), (grid[best], want_best)
+    # the chosen scale is the oracle's channel scale at the chosen alpha, bit for bit
+    assert np.array_equal(g.host(s_d).view(np.uint32), oracle.channel_scale(x_cal, grid[best]).view(np.uint32))
+    if grid[best] != want_best:
+        print(f"chosen alpha {grid[best]} vs oracle {want_best}: losses {want[best]} vs {want.min()}")
+
+
+def test_search_alpha_equals_the_steps_one_by_one(lib):
+    """awq_search_alpha runs the same kernels as the separate calls: its losses are bit-identical
+    to output_reference, then per alpha channel_scale, scale_input, quantize_pack, alpha_loss."""
+    import torch
+
+    g = _gpu()
+    k, n = 2048, 300
+    W = g.dev(synth.weights(2, 7, n, k))
+    x_cal = g.dev(synth.calibration(2, 7, k))
+    losses_d, best_d, alpha_d, s_d = lib.search_alpha(x_cal, W)
+    y_ref = lib.output_reference(x_cal, W)
+    step = torch.empty(21, dtype=torch.float64, device=x_cal.device)
+    for i in range(21):
+        s = lib.channel_scale(x_cal, i / 20)
+        xs = lib.scale_input(x_cal, s)
+        lib.alpha_loss(xs, *lib.quantize_pack(W, s), y_ref, out=step[i:i + 1])
+    assert np.array_equal(g.host(losses_d).view(np.uint64), g.host(step).view(np.uint64))
+    best = int(g.host(best_d)[0])
+    assert np.array_equal(g.host(s_d).view(np.uint32), g.host(lib.channel_scale(x_cal, best / 20)).view(np.uint32))
+
+
+def test_search_alpha_first_minimum_on_ties(lib):
+    """Equal losses keep the smaller alpha: with W = 0 every candidate's loss is exactly 0, so
+    the choice is alpha = 0 and the copied scale is all ones."""
+    g = _gpu()
+    k, n = 256, 40
+    W = np.zeros((n, k), dtype=np.float16)
+    x_cal = synth.calibration(2, 8, k)
+    losses_d, best_d, alpha_d, s_d = lib.search_alpha(g.dev(x_cal), g.dev(W))
+    assert np.all(g.host(losses_d) == 0.0)
+    assert int(g.host(best_d)[0]) == 0 and float(g.host(alpha_d)[0]) == 0.0
+    assert np.all(g.host(s_d) == 1.0)

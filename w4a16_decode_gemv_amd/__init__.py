@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP, ERR_ARG = range(7)
-PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_SKINNY = 0, 1, 2, 3
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_SKINNY, PATH_KLANE = 0, 1, 2, 3, 4
 GROUP = 128
 LAYOUT_VERSION = 1
 
@@ -68,6 +68,8 @@ def load():
         "w4a16_stream_read_sink_bytes": ([i64], i64),
         "w4a16_stream_read": ([vp, i64, vp, vp], i32),
         "w4a16_stream_read_grid": ([vp, i64, i32, i32, i32, vp, vp], i32),
+        "awq_search_alpha_workspace": ([i64, i64, i64], i64),
+        "awq_search_alpha": ([vp, vp, i64, i64, i64, vp, i64, vp, vp, vp, vp, vp], i32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -82,7 +84,8 @@ def exported_symbols():
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
             "w4a16_linear_path", "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w4a16_linear_splitk_noalloc", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
             "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
-            "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read", "w4a16_stream_read_grid"]
+            "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read", "w4a16_stream_read_grid",
+            "awq_search_alpha_workspace", "awq_search_alpha"]
 
 
 def _check(status):
@@ -423,35 +426,45 @@ def alpha_loss(x_s, qweight, scales, zeros, y_ref, group=GROUP, workspace=None, 
     return loss
 
 
-ALPHA_GRID = tuple(i / 20 for i in range(21))
+ALPHA_GRID_POINTS = 21
 
 
-def search_alpha(x_cal, W, grid=ALPHA_GRID):
-    """The AWQ grid search on the device: the original output once, then for every alpha
-    s = channel_scale(x_cal, alpha), x_s = scale_input, quantize_pack(W, s) and the output-error loss. Returns (losses float64 [len(grid)] on the device, the alpha
-    of the first minimum)."""
+def search_alpha_workspace(t_, n, k):
+    """Bytes of device workspace that search_alpha needs for T calibration rows, N outputs,
+    K inputs."""
+    nbytes = int(load().awq_search_alpha_workspace(int(t_), int(n), int(k)))
+    if nbytes < 0:
+        raise ValueError(f"T={t_}, N={n}, K={k} outside the limits of the search")
+    return nbytes
+
+
+def search_alpha(x_cal, W, workspace=None, out=None):
+    """The AWQ grid search on the device (awq_search_alpha): the original output once, then
+    for every alpha = i/20 the channel scale, the 1/s fold, the quantize-pack and the
+    output-error loss, then the choice (first minimum). Returns device tensors
+    (losses float64 [21], best int32 [1], alpha float64 [1], s float32 [K]); nothing is read
+    back to the host. out: optional (losses, best, alpha, s) tensors to fill."""
     torch = _torch()
+    lib = load()
     x_cal = _dev_tensor(x_cal, torch.float16, "x_cal", 2)
     W = _dev_tensor(W, torch.float16, "W", 2)
     t_, k = x_cal.shape
     n = W.shape[0]
-    dev = x_cal.device
-    s = torch.empty(k, dtype=torch.float32, device=dev)
-    xs = torch.empty_like(x_cal)
-    packed = (torch.empty((n, k // 8), dtype=torch.int32, device=dev),
-              torch.empty((n, k // GROUP), dtype=torch.float16, device=dev),
-              torch.empty((n, k // GROUP), dtype=torch.float16, device=dev))
-    workspace = torch.empty(alpha_loss_workspace(t_, n), dtype=torch.float64, device=dev)
-    losses = torch.empty(len(grid), dtype=torch.float64, device=dev)
-    y_ref = output_reference(x_cal, W)  # independent of alpha: once per search
-    for i, a in enumerate(grid):
-        channel_scale(x_cal, a, out=s)
-        scale_input(x_cal, s, out=xs)
-        quantize_pack(W, s, out=packed)
-        alpha_loss(xs, *packed, y_ref, workspace=workspace, out=losses[i:i + 1])
-    host = losses.cpu().tolist()
-    best = min(range(len(host)), key=lambda i: (host[i], i))  # the first index of the minimum
-    return losses, grid[best]
+    if W.shape[1] != k:
+        raise ValueError("x_cal must be [T][K] and W [N][K]")
+    need = search_alpha_workspace(t_, n, k)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x_cal.device)
+    workspace = _workspace(workspace, torch.uint8, x_cal)
+    o = _outs(out, 4, "search")
+    losses = _out(o[0], (ALPHA_GRID_POINTS,), torch.float64, x_cal, "losses")
+    best = _out(o[1], (1,), torch.int32, x_cal, "best")
+    alpha = _out(o[2], (1,), torch.float64, x_cal, "alpha")
+    s = _out(o[3], (k,), torch.float32, x_cal, "s")
+    _check(lib.awq_search_alpha(x_cal.data_ptr(), W.data_ptr(), t_, n, k, workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), losses.data_ptr(), best.data_ptr(),
+                                alpha.data_ptr(), s.data_ptr(), _stream(x_cal)))
+    return losses, best, alpha, s
 
 
 STREAM_READ_MAGIC = 0x5EAD5EAD

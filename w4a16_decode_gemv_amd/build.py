@@ -12,9 +12,13 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = ["abi.hip", "awq_quantize.hip", "norm_fold.hip", "gemv.hip", "gemm_skinny.hip", "gemm_mfma.hip", "awq_search.hip", "gemm_splitk.hip", "stream_read.hip"]
+SOURCES = ["abi.hip", "awq_quantize.hip", "norm_fold.hip", "gemv.hip", "gemm_skinny.hip", "gemm_mfma.hip", "awq_search.hip", "gemm_splitk.hip", "stream_read.hip", "gemm_klane.hip"]
 # gemm_skinny.hip holds many kernel instances: it compiles as five parts in parallel
 PARTS = {"gemm_skinny.hip": 5}
+# per-source code generation flags: the tiled MFMA kernels keep their MFMA accumulators in
+# ordinary VGPRs (in AGPRs each accumulator read by the scale FMAs costs a v_accvgpr_read)
+SOURCE_FLAGS = {"gemm_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+                "gemm_klane.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 ARCH = "gfx950"
 
 FLAGS = [
@@ -63,7 +67,8 @@ def build(verbose=False, jobs=None):
         def one(unit):
             src, define, objname = unit
             obj = os.path.join(tmpdir, objname)
-            cmd = [_hipcc(), *compile_flags, *([define] if define else []), "-c", f"-I{INCLUDE}", f"-I{CSRC}",
+            cmd = [_hipcc(), *compile_flags, *SOURCE_FLAGS.get(src, []), *([define] if define else []), "-c",
+                   f"-I{INCLUDE}", f"-I{CSRC}",
                    "-o", obj, os.path.join(CSRC, src)]
             res = subprocess.run(cmd, capture_output=True, text=True)
             return src, obj, res

@@ -59,6 +59,19 @@ bool two_small_batch_passes(int64_t M, int64_t N, int64_t K) {
   return M > w4a16::skinny_max_m() && M <= 2 * w4a16::skinny_max_m() && N <= 8192 && K <= 16384;
 }
 
+// Above the small-batch kernel, 4-bit codes with groups of 128: the K-lane kernel where the
+// tiled kernel has at most one workgroup per CU, or two on long rows (K > 8192); the tiled
+// kernel otherwise. From a sweep of M = 48..512 over nine LLaMA layer shapes (MI355X,
+// graph-timed), e.g. K-lane / tiled: 4096 -> 4096 at M = 128 17.2 / 22.4 us, 11008 -> 4096
+// at M = 256 59.2 / 66.0, 8192 -> 8192 at M = 64 31.9 / 46.4, 22016 -> 8192 at M = 128
+// 118.7 / 130.4; the tiled kernel keeps 4096 -> 4096 at M >= 192 (25.4 / 29.2), every
+// 4096 -> 11008 and 8192 -> 22016 shape and 8192 -> 8192 from M = 96. This also replaces
+// the two small-batch passes at M = 33..64 (11008 -> 4096, M = 64: 38.0 against 51.0 us).
+bool auto_klane(int64_t M, int64_t N, int64_t K) {
+  const int64_t wgs = w4a16::mfma_workgroups(M, N);
+  return M > w4a16::skinny_max_m() && (wgs <= 256 || (K > 8192 && wgs <= 512));
+}
+
 w4a16_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return W4A16_OK;
@@ -197,6 +210,8 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
       kernel = 1;
     } else if (M <= w4a16::skinny_max_m()) {
       kernel = 3;
+    } else if (auto_klane(M, N, K)) {
+      kernel = 4;
     } else if (two_small_batch_passes(M, N, K)) {
       kernel = 3;
       two_passes = true;
@@ -219,7 +234,42 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   }
   if (kernel == 3)
     return hip_result(w4a16::launch_skinny(xh, qw, sc, zr, M, N, K, yh, stream), "small-batch MFMA launch");
+  if (kernel == 4) return hip_result(w4a16::launch_klane(xh, qw, sc, zr, M, N, K, yh, stream), "K-lane MFMA launch");
   return hip_result(w4a16::launch_mfma(xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
+}
+
+}  // namespace
+
+namespace {
+
+// awq_search_alpha's workspace, each region 256-byte aligned: y_ref float32 [T][N], the 21
+// candidate scales float32 [21][K], x_s fp16 [T][K], qweight u32 [N][K/8], scales and zeros
+// fp16 [N][K/128], and the loss partials float64 [awq_alpha_loss_workspace(T, N)]
+struct SearchSpace {
+  int64_t y_ref, s_all, x_s, qweight, scales, zeros, partials, total;
+};
+
+int64_t round256(int64_t b) { return (b + 255) & ~int64_t(255); }
+
+bool search_space(int64_t T, int64_t N, int64_t K, SearchSpace* sp) {
+  if (T <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || T > kMaxM || N > kMaxN || K > W4A16_MAX_K) return false;
+  const int64_t parts = awq_alpha_loss_workspace(T, N);
+  if (parts < 0) return false;
+  int64_t at = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t here = at;
+    at += round256(bytes);
+    return here;
+  };
+  sp->y_ref = take(T * N * 4);
+  sp->s_all = take(int64_t(W4A16_ALPHA_GRID_POINTS) * K * 4);
+  sp->x_s = take(T * K * 2);
+  sp->qweight = take(N * K / 2);
+  sp->scales = take(N * (K / 128) * 2);
+  sp->zeros = take(N * (K / 128) * 2);
+  sp->partials = take(parts * 8);
+  sp->total = at;
+  return true;
 }
 
 }  // namespace
@@ -347,8 +397,11 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
                                void* stream) {
   clear_error();
-  if (path < 0 || path > 3)
-    return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA) or 3 (small-batch MFMA)");
+  if (path < 0 || path > 4)
+    return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA), 3 (small-batch MFMA) or "
+                "4 (K-lane MFMA)");
+  if (path == 4 && group != 128)
+    return fail(W4A16_ERR_UNSUPPORTED, "the K-lane MFMA kernel takes groups of 128 (got %d)", (int)group);
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
   return run_linear(4, path, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
@@ -431,6 +484,56 @@ int64_t awq_alpha_loss_workspace(int64_t T, int64_t N) {
   if (T <= 0 || N <= 0 || T > kMaxT || N > kMaxN) return -1;
   const int64_t tiles = w4a16::alpha_loss_partials(T, N);
   return tiles > kMaxTiles ? -1 : tiles;
+}
+
+int64_t awq_search_alpha_workspace(int64_t T, int64_t N, int64_t K) {
+  SearchSpace sp;
+  return search_space(T, N, K, &sp) ? sp.total : -1;
+}
+
+w4a16_status awq_search_alpha(const void* x_cal, const void* w, int64_t T, int64_t N, int64_t K, void* workspace,
+                              int64_t workspace_bytes, double* losses, int32_t* best, double* alpha, float* s,
+                              void* stream) {
+  clear_error();
+  if (!x_cal || !w || !workspace || !losses || !best || !alpha)
+    return fail(W4A16_ERR_NULL, "x_cal, w, workspace, losses, best and alpha are required");
+  if (T <= 0 || N <= 0 || K <= 0) return fail(W4A16_ERR_SHAPE, "T, N, K must be positive (got %lld, %lld, %lld)",
+                                              (long long)T, (long long)N, (long long)K);
+  if (K % 128 != 0) return fail(W4A16_ERR_SHAPE, "K must be a multiple of 128 (got %lld)", (long long)K);
+  SearchSpace sp;
+  if (!search_space(T, N, K, &sp))
+    return fail(W4A16_ERR_SHAPE, "size beyond the limits (T <= 65536, N <= 2^24, K <= %d)", W4A16_MAX_K);
+  if (workspace_bytes < sp.total)
+    return fail(W4A16_ERR_ARG, "workspace holds %lld bytes, %lld needed", (long long)workspace_bytes,
+                (long long)sp.total);
+  if (!aligned(x_cal, 16) || !aligned(w, 16) || !aligned(workspace, 256))
+    return fail(W4A16_ERR_ALIGN, "x_cal and w must be 16-byte, workspace 256-byte aligned");
+  if (!aligned(losses, 8) || !aligned(alpha, 8) || !aligned(best, 4) || (s && !aligned(s, 4)))
+    return fail(W4A16_ERR_ALIGN, "losses and alpha must be 8-byte, best and s 4-byte aligned");
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* base = static_cast<char*>(workspace);
+  const uint16_t* xc = static_cast<const uint16_t*>(x_cal);
+  const uint16_t* wh = static_cast<const uint16_t*>(w);
+  float* y_ref = reinterpret_cast<float*>(base + sp.y_ref);
+  float* s_all = reinterpret_cast<float*>(base + sp.s_all);
+  uint16_t* x_s = reinterpret_cast<uint16_t*>(base + sp.x_s);
+  uint32_t* qw = reinterpret_cast<uint32_t*>(base + sp.qweight);
+  uint16_t* sc = reinterpret_cast<uint16_t*>(base + sp.scales);
+  uint16_t* zr = reinterpret_cast<uint16_t*>(base + sp.zeros);
+  double* parts = reinterpret_cast<double*>(base + sp.partials);
+  // the original output once, then per grid point: s = s_X^alpha, x_s = f16(x / s),
+  // quantize-pack of W * s, and the output-error loss (L13 guide, AWQ section, slide 28)
+  hipError_t e = w4a16::launch_output_reference(xc, wh, T, N, K, y_ref, hs);
+  for (int i = 0; i < W4A16_ALPHA_GRID_POINTS && e == hipSuccess; ++i) {
+    const double a = (double)i / (double)(W4A16_ALPHA_GRID_POINTS - 1);
+    float* si = s_all + (int64_t)i * K;
+    e = w4a16::launch_channel_scale(xc, T, K, a, si, hs);
+    if (e == hipSuccess) e = w4a16::launch_scale_input(xc, si, T, K, x_s, hs);
+    if (e == hipSuccess) e = w4a16::launch_quantize_pack(wh, si, N, K, 4, 128, qw, sc, zr, hs);
+    if (e == hipSuccess) e = w4a16::launch_alpha_loss(x_s, qw, sc, zr, y_ref, T, N, K, parts, losses + i, hs);
+  }
+  if (e == hipSuccess) e = w4a16::launch_search_select(losses, W4A16_ALPHA_GRID_POINTS, s_all, K, best, alpha, s, hs);
+  return hip_result(e, "alpha-search launch");
 }
 
 void nf4_codebook(uint16_t* levels) {

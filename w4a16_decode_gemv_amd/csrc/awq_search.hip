@@ -44,6 +44,8 @@
 // [n = c]. At step st of a stage, slot group j takes the 8 inputs of chunk
 // 4 j + st, so a lane reads 64 contiguous weight bytes, or one 16-byte chunk of
 // codes, per stage of its row.
+#include <algorithm>
+
 #include "device_utils.h"
 #include "launchers.h"
 
@@ -326,6 +328,45 @@ int64_t tiles(int64_t T, int64_t N) { return ((T + BM - 1) / BM) * ((N + BN - 1)
 }  // namespace
 
 int64_t alpha_loss_partials(int64_t T, int64_t N) { return tiles(T, N); }
+
+namespace {
+
+// The grid search's choice: the first index of the smallest loss (strictly smaller losses
+// replace the best so far, so equal losses keep the smaller alpha), its alpha = index / 20,
+// and the candidate scale of that index copied out. Every workgroup takes the (tiny) argmin
+// itself and copies its slice of the scale.
+__global__ __launch_bounds__(256) void search_select_kernel(const double* __restrict__ losses, int count,
+                                                            const float* __restrict__ s_all, int64_t K,
+                                                            int32_t* __restrict__ best, double* __restrict__ alpha,
+                                                            float* __restrict__ s) {
+  int b = 0;
+  double v = losses[0];
+  for (int i = 1; i < count; ++i) {
+    const double l = losses[i];
+    if (l < v) {
+      v = l;
+      b = i;
+    }
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    *best = b;
+    *alpha = (double)b / (double)(count - 1);
+  }
+  if (s) {
+    const float* src = s_all + (int64_t)b * K;
+    for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < K; k += (int64_t)gridDim.x * 256) s[k] = src[k];
+  }
+}
+
+}  // namespace
+
+hipError_t launch_search_select(const double* losses, int count, const float* s_all, int64_t K, int32_t* best,
+                                double* alpha, float* s, hipStream_t stream) {
+  const int64_t blocks = s ? std::min<int64_t>((K + 255) / 256, 1024) : 1;
+  hipLaunchKernelGGL(search_select_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, losses, count, s_all, K, best,
+                     alpha, s);
+  return hipGetLastError();
+}
 
 hipError_t launch_output_reference(const uint16_t* x, const uint16_t* w, int64_t T, int64_t N, int64_t K, float* y,
                                    hipStream_t stream) {

@@ -501,6 +501,14 @@ hipError_t launch_mb(const uint16_t* x, const uint32_t* qweight, const uint16_t*
 
 }  // namespace
 
+int64_t mfma_workgroups(int64_t M, int64_t N) {
+  const int64_t tn = (N + BN - 1) / BN;
+  if (M <= 16) return tn * M;
+  if (M <= 32) return tn * ((M + 31) / 32);
+  const int64_t tiles64 = ((M + 63) / 64) * tn;
+  return tiles64 < 512 ? ((M + 31) / 32) * tn : tiles64;
+}
+
 hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream) {
   if (M <= 16) return launch_mb<1>(x, qweight, scales, zeros, M, N, K, y, stream);

@@ -80,10 +80,16 @@ hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint1
 constexpr int64_t kSplitkScratchFloats = int64_t(1) << 23;  // 32 MiB
 hipError_t splitk_scratch(hipStream_t stream, float** ptr);
 
-// Tiled MFMA kernel: any M >= 1.
+// Tiled MFMA kernel: any M >= 1. mfma_workgroups: the workgroups launch_mfma starts (for M > 16).
+int64_t mfma_workgroups(int64_t M, int64_t N);
 hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
                        const uint16_t* zeros, int64_t M, int64_t N, int64_t K, uint16_t* y,
                        hipStream_t stream);
+
+// K-lane MFMA kernel (4-bit, groups of 128): any M >= 1; klane_workgroups gives its grid.
+int64_t klane_workgroups(int64_t M, int64_t N);
+hipError_t launch_klane(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                        int64_t M, int64_t N, int64_t K, uint16_t* y, hipStream_t stream);
 
 // AWQ scale search: the original layer's output (float32), and the loss of one
 // candidate scale (number of float64 partials it writes; loss kernel + fixed-order
@@ -94,6 +100,11 @@ int64_t alpha_loss_partials(int64_t T, int64_t N);
 hipError_t launch_alpha_loss(const uint16_t* x_s, const uint32_t* qweight, const uint16_t* scales,
                              const uint16_t* zeros, const float* y_ref, int64_t T, int64_t N, int64_t K,
                              double* partials, double* loss, hipStream_t stream);
+
+// The search's choice on the device: best = first index of the smallest of `count` losses,
+// alpha = best / (count - 1), and (when s is not NULL) s = s_all[best][0..K).
+hipError_t launch_search_select(const double* losses, int count, const float* s_all, int64_t K, int32_t* best,
+                                double* alpha, float* s, hipStream_t stream);
 
 // Tiled MFMA kernel for the other code formats (bits 3 or 4, group 32, 64 or 128); any M >= 1.
 hipError_t launch_mfma_variant(int bits, int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
