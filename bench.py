@@ -73,7 +73,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--only-gemv", action="store_true", help="time the headline GEMV only (for profilers)")
     p.add_argument("--only-m", type=int, default=0,
-                   help="time only the automatic path at this batch M, K = N = 8192 (for profilers)")
+                   help="time only the automatic path (or --path) at this batch M, K = N = 8192 (for profilers)")
+    p.add_argument("--path", type=int, default=0,
+                   help="with --only-m: the kernel (0 auto, 1 GEMV, 2 tiled MFMA, 3 small-batch MFMA, 4 K-lane MFMA)")
     p.add_argument("--only-serving", default="",
                    help="time only one LLaMA2-7B serving GEMM, LAYER:M with LAYER in qkvo,gate,down (the 4096->4096, "
                         "4096->11008, 11008->4096 shapes) and M in 128,256, on the tiled and split-K kernels "
@@ -128,6 +130,25 @@ def time_back_to_back(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps  # ms per call
 
 
+_DELAY_MHZ = []
+
+
+def delay_clock_mhz(torch):
+    """Rate of the counter behind torch.cuda._sleep (its cycles), measured once with HIP events
+    over a short delay (the counter need not run at the shader clock)."""
+    if not _DELAY_MHZ:
+        torch.cuda.synchronize()
+        cycles = 2_000_000
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.cuda._sleep(cycles)
+        e1.record()
+        torch.cuda.synchronize()
+        _DELAY_MHZ.append(cycles / max(e0.elapsed_time(e1) * 1e3, 1.0))
+    return _DELAY_MHZ[0]
+
+
 def time_steps_queued(torch, fn, steps, warmup):
     """The timed region: `warmup` untimed calls, then exactly `steps` calls launched back to
     back on the current stream (the stream the kernels run on) and bracketed by two HIP
@@ -142,8 +163,9 @@ def time_steps_queued(torch, fn, steps, warmup):
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
+    cycles_per_us = delay_clock_mhz(torch)
     probe = max(1, min(steps, 50))
-    torch.cuda._sleep(50_000_000)  # keeps the probe's launches from draining while they are timed
+    torch.cuda._sleep(int(20_000 * cycles_per_us))  # 20 ms: the probe's launches queue behind it
     t0 = time.perf_counter()
     for i in range(probe):
         fn(i)
@@ -155,7 +177,7 @@ def time_steps_queued(torch, fn, steps, warmup):
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         es.record()
-        torch.cuda._sleep(int(delay_us * 2400))  # cycles of the <= 2.4 GHz shader clock
+        torch.cuda._sleep(int(delay_us * cycles_per_us))
         e0.record()
         t0 = time.perf_counter()
         for i in range(steps):
@@ -511,8 +533,8 @@ def main():
         mm = args.only_m
         b = algorithmic_bytes(mm, 8192, 8192)
         L = Layer(w4, torch, 4, 0, 8192, 8192, mm, copies_for(b))
-        t = time_steps_queued(torch, lambda i: L.call(w4, i), args.steps, args.warmup)
-        res = {"M": mm, "K": 8192, "N": 8192, "us_per_call": t * 1e3, "GB_s": b / (t * 1e-3) / 1e9,
+        t = time_steps_queued(torch, lambda i: L.call(w4, i, args.path), args.steps, args.warmup)
+        res = {"M": mm, "K": 8192, "N": 8192, "path": args.path, "us_per_call": t * 1e3, "GB_s": b / (t * 1e-3) / 1e9,
                "algorithmic_bytes_per_call": b}
         if args.copy_probe:
             copy_probe(torch, res)

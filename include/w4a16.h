@@ -182,7 +182,8 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * N * K >= 2^27 or on layers small enough that the GEMV takes 4-row tiles
  * (K <= 32768 and ceil(N / 8) * ceil(K / 2048) < 4096 waves, under 16 per CU),
  * run the wave-tile GEMV kernel; other M <= 32 the small-batch
- * MFMA kernel (workgroups own whole rows of y, waves split K); M > 32 the
+ * MFMA kernel (workgroups own whole rows of y, waves split K), except
+ * 17 <= M <= 32 with K > 16384, which runs the K-lane kernel; M > 32 the
  * K-lane MFMA kernel (K split over four waves per workgroup) where the tiled
  * MFMA kernel would start at most 256 workgroups (ceil(M / 32) * ceil(N / 64)
  * while ceil(M / 64) * ceil(N / 64) < 512, else the latter), or at most 512 with

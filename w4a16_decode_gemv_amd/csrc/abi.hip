@@ -72,6 +72,12 @@ bool auto_klane(int64_t M, int64_t N, int64_t K) {
   return M > w4a16::skinny_max_m() && (wgs <= 256 || (K > 8192 && wgs <= 512));
 }
 
+// 17 <= M <= 32 with K > 16384: the small-batch kernel's two-m-tile variants fall off on
+// such long rows (22016 -> 8192: 91 us at M = 24 and 106 at M = 32, against 44.5 at
+// M = 16), where the K-lane kernel takes 60-69 us; on 8192 -> 22016 it stays ahead
+// (57 / 65 against 73 / 75 us)
+bool auto_klane_small(int64_t M, int64_t K) { return M > 16 && M <= w4a16::skinny_max_m() && K > 16384; }
+
 w4a16_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return W4A16_OK;
@@ -208,6 +214,8 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   if (path == 0) {
     if (auto_gemv(M, N, K) && w4a16::gemv_supports(M, K)) {
       kernel = 1;
+    } else if (auto_klane_small(M, K)) {
+      kernel = 4;
     } else if (M <= w4a16::skinny_max_m()) {
       kernel = 3;
     } else if (auto_klane(M, N, K)) {

@@ -96,19 +96,21 @@ __global__ __launch_bounds__(64 * KL) void klane_kernel(const uint16_t* __restri
   using Stage = KlaneStage<MW, NW>;
   Stage set[R];
   // group g of this K-lane (0 .. gcount-1); groups past the range read as zero
+  // x first: the LDS store of a group's x waits (in issue order) only for the loads issued
+  // before its own, not for that group's codes, which come from HBM and are needed later
   auto issue = [&](int g, Stage& r) {
     const int past = (int)(g >= gcount) * kOutOfRange;
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        r.x[mt][s] = load16(rx, xo + (4 * mt + s) * 4 * K * 2 + g * 256 + past);
 #pragma unroll
     for (int nt = 0; nt < NW; ++nt) {
       r.q[nt] = load16(rq, qo + nt * 16 * (K >> 1) + g * 64 + past);
       r.s[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, so + nt * 16 * G * 2 + g * 2 + past, 0, 0);
       r.z[nt] = __builtin_amdgcn_raw_buffer_load_b16(rz, so + nt * 16 * G * 2 + g * 2 + past, 0, 0);
     }
-#pragma unroll
-    for (int mt = 0; mt < MW; ++mt)
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        r.x[mt][s] = load16(rx, xo + (4 * mt + s) * 4 * K * 2 + g * 256 + past);
   };
   // this wave's LDS area (rows padded to 17 chunks: the 16 lanes of one fragment read hit
   // distinct banks), written by the coalesced loads and read back as A fragments
