@@ -78,7 +78,7 @@ def parse():
                    help="with --only-m: the kernel (0 auto, 1 GEMV, 2 tiled MFMA, 3 small-batch MFMA, 4 K-lane MFMA)")
     p.add_argument("--only-serving", default="",
                    help="time only one LLaMA2-7B serving GEMM, LAYER:M with LAYER in qkvo,gate,down (the 4096->4096, "
-                        "4096->11008, 11008->4096 shapes) and M in 128,256, on the tiled and split-K kernels "
+                        "4096->11008, 11008->4096 shapes) and M in 128,256, on the tiled, K-lane and split-K kernels "
                         "(for profilers)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the GEMV, run a plain 64 MiB elementwise copy 5 times (counter calibration)")
@@ -518,13 +518,15 @@ def main():
         L = Layer(w4, torch, 5, lid, nn, kk, mm, copies_for(b))
         ws = torch.empty(w4.splitk_workspace_bytes(mm, nn, kk, 16) // 4, dtype=torch.float32, device=L.x.device)
         t_tiled = time_steps_queued(torch, lambda i: L.call(w4, i, 2), args.steps, args.warmup)
+        t_klane = time_steps_queued(torch, lambda i: L.call(w4, i, 4), args.steps, args.warmup)
         t_split = time_steps_queued(torch, lambda i: w4.linear_splitk(*L.copies[i % len(L.copies)], workspace=ws,
                                                                        out=L.y[i % len(L.y)]), args.steps, args.warmup)
         flop = 2 * mm * nn * kk
         res = {"layer": lname, "M": mm, "K": kk, "N": nn, "flop": flop, "algorithmic_bytes": b,
-               "tiled_us": t_tiled * 1e3, "splitk_us": t_split * 1e3,
+               "tiled_us": t_tiled * 1e3, "klane_us": t_klane * 1e3, "splitk_us": t_split * 1e3,
                "splitk_default_splits": w4.splitk_workspace_bytes(mm, nn, kk, 0) // (4 * mm * nn),
                "tiled_mfma_util": flop / (t_tiled * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
+               "klane_mfma_util": flop / (t_klane * 1e-3) / 1e12 / PEAK_FP16_TFLOPS,
                "splitk_mfma_util": flop / (t_split * 1e-3) / 1e12 / PEAK_FP16_TFLOPS}
         print(json.dumps(res), flush=True)
         return 0
@@ -712,6 +714,8 @@ def main():
                 b = algorithmic_bytes(mm, nn, kk)
                 L = Layer(w4, torch, 5, lid, nn, kk, mm, copies_for(b))
                 t = time_graph(torch, lambda i: L.call(w4, i), 50)
+                t_tiled = time_graph(torch, lambda i: L.call(w4, i, 2), 50)
+                t_klane = time_graph(torch, lambda i: L.call(w4, i, 4), 50)
                 # dense fp16 reference product of the same shape: y = x @ W^T with W^T stored [K][N]
                 wt = [L.W.t().contiguous() for _ in range(copies_for(nn * kk * 2))]
                 xd = L.x
@@ -737,6 +741,7 @@ def main():
                     split_rows["auto" if sp == 0 else str(sp)] = ts * 1e3
                 t_split = split_rows["auto"]
                 rows.append({"layer": name, "M": mm, "K": kk, "N": nn, "us": t * 1e3,
+                             "tiled_us": t_tiled * 1e3, "klane_us": t_klane * 1e3,
                              "splitk_us": t_split, "splitk_TFLOP_s": flop / (t_split * 1e-6) / 1e12,
                              "splitk_mfma_util": flop / (t_split * 1e-6) / 1e12 / PEAK_FP16_TFLOPS,
                              "splitk_by_splits_us": split_rows,
