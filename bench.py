@@ -242,8 +242,8 @@ GRID_READS = ((256, 1024, 8), (256, 2048, 4), (256, 4096, 2), (512, 1024, 4), (1
 
 
 def read_floor_leg(torch, w4, nbytes, copies, gemv_ms, steps, warmup):
-    """Single-launch read floors of `nbytes`, each timed like the GEMV (one uploaded graph
-    replay of back-to-back launches over `copies` rotating buffers): the GEMV's own access
+    """Single-launch read floors of `nbytes`, each timed like the GEMV (back-to-back launches
+    queued behind a device-side delay, over `copies` rotating buffers): the GEMV's own access
     pattern (w4a16_stream_read), grid-stride reads of other shapes (w4a16_stream_read_grid),
     and a device-to-device copy of the same bytes (hipMemcpyAsync through torch, which also
     writes them). The same read and copy of 1 GiB show the streaming rate once launch costs

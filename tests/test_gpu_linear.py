@@ -248,7 +248,8 @@ def test_klane_ragged_shapes(lib, m, n, k):
 
 
 @pytest.mark.parametrize("m,k,n", [(48, 4096, 4096), (64, 11008, 4096), (128, 4096, 4096), (256, 11008, 4096),
-                                   (64, 8192, 8192), (96, 22016, 8192), (24, 22016, 1024), (32, 22016, 8192)])
+                                   (64, 8192, 8192), (96, 22016, 8192), (24, 22016, 1024), (32, 22016, 8192),
+                                   (96, 8192, 8192), (384, 11008, 4096), (512, 8192, 1024)])
 def test_auto_klane_route(lib, m, k, n):
     # shapes the automatic dispatch sends to the K-lane kernel: every output against the oracle,
     # and bit-identical to forcing path 4

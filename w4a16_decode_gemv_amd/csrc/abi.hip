@@ -60,16 +60,19 @@ bool two_small_batch_passes(int64_t M, int64_t N, int64_t K) {
 }
 
 // Above the small-batch kernel, 4-bit codes with groups of 128: the K-lane kernel where the
-// tiled kernel has at most one workgroup per CU, or two on long rows (K > 8192); the tiled
-// kernel otherwise. From a sweep of M = 48..512 over nine LLaMA layer shapes (MI355X,
-// graph-timed), e.g. K-lane / tiled: 4096 -> 4096 at M = 128 17.2 / 22.4 us, 11008 -> 4096
-// at M = 256 59.2 / 66.0, 8192 -> 8192 at M = 64 31.9 / 46.4, 22016 -> 8192 at M = 128
-// 118.7 / 130.4; the tiled kernel keeps 4096 -> 4096 at M >= 192 (25.4 / 29.2), every
-// 4096 -> 11008 and 8192 -> 22016 shape and 8192 -> 8192 from M = 96. This also replaces
-// the two small-batch passes at M = 33..64 (11008 -> 4096, M = 64: 38.0 against 51.0 us).
+// tiled kernel has at most one workgroup per CU, or where the K-lane grid fills the chip at
+// most once (two workgroups per CU, K >= 8192) or 1.5 times (K > 8192); the tiled kernel
+// otherwise. From a sweep of M = 33..512 over nine layer shapes (MI355X, graph-timed), K-lane /
+// tiled: 4096 -> 4096 at M = 128 16.2 / 24.1 us, 8192 -> 8192 at M = 128 49.3 / 51.2,
+// 11008 -> 4096 at M = 256 55.4 / 66.1 and at M = 384 79.8 / 80.7, 22016 -> 8192 at M = 128
+// 111.5 / 130.1, 8192 -> 1024 at M = 512 24.7 / 39.4; the tiled kernel keeps 4096 -> 4096
+// from M = 192 (25.9 / 26.6), every 4096 -> 11008, 4096 -> 12288 and 8192 -> 22016 shape,
+// 8192 -> 8192 from M = 192 (61.6 / 69.2), 11008 -> 4096 at M = 512 (89.4 / 107.6) and
+// 22016 -> 8192 at M = 256 (175.6 / 208.1). This also replaces the two small-batch passes
+// at M = 33..64 where the tiled grid is short (11008 -> 4096, M = 64: 34.6 against 51.0 us).
 bool auto_klane(int64_t M, int64_t N, int64_t K) {
-  const int64_t wgs = w4a16::mfma_workgroups(M, N);
-  return M > w4a16::skinny_max_m() && (wgs <= 256 || (K > 8192 && wgs <= 512));
+  const int64_t tiled = w4a16::mfma_workgroups(M, N), klane = w4a16::klane_workgroups(M, N);
+  return M > w4a16::skinny_max_m() && (tiled <= 256 || (K >= 8192 && klane <= 512) || (K > 8192 && klane <= 768));
 }
 
 // 17 <= M <= 32 with K > 16384: the small-batch kernel's two-m-tile variants fall off on

@@ -56,7 +56,7 @@ struct KlaneStage {
 };
 
 template <int MW, int NW, int KL, int R>
-__global__ __launch_bounds__(64 * KL) void klane_kernel(const uint16_t* __restrict__ x,
+__global__ __launch_bounds__(64 * KL) __attribute__((amdgpu_waves_per_eu(2, 2))) void klane_kernel(const uint16_t* __restrict__ x,
                                                         const uint32_t* __restrict__ qw,
                                                         const uint16_t* __restrict__ scales,
                                                         const uint16_t* __restrict__ zeros, int M, int N, int K,
