@@ -81,12 +81,16 @@ __global__ __launch_bounds__(64 * KL) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int gcount = base + (kl < extra ? 1 : 0);
 
   const int64_t rows_m = min(M - m0, BM), rows_n = min(N - n0, BN);
-  const __amdgpu_buffer_rsrc_t rx = rsrc(x + (int64_t)m0 * K + (int64_t)g_begin * 128,
-                                         rows_m * K * 2 - (int64_t)g_begin * 256);
-  const __amdgpu_buffer_rsrc_t rq = rsrc(qw + (int64_t)n0 * (K >> 3) + (int64_t)g_begin * 16,
-                                         rows_n * (K >> 1) - (int64_t)g_begin * 64);
-  const __amdgpu_buffer_rsrc_t rs = rsrc(scales + (int64_t)n0 * G + g_begin, rows_n * G * 2 - (int64_t)g_begin * 2);
-  const __amdgpu_buffer_rsrc_t rz = rsrc(zeros + (int64_t)n0 * G + g_begin, rows_n * G * 2 - (int64_t)g_begin * 2);
+  // this K-lane's first group in each tensor, and the bytes from there to the end of the tile's
+  // rows; group g of the K-lane gets views that start g groups further on (scalar arithmetic,
+  // so the per-load offsets below are fixed registers)
+  const uint16_t* x0 = x + (int64_t)m0 * K + (int64_t)g_begin * 128;
+  const uint32_t* q0 = qw + (int64_t)n0 * (K >> 3) + (int64_t)g_begin * 16;
+  const uint16_t* s0 = scales + (int64_t)n0 * G + g_begin;
+  const uint16_t* z0 = zeros + (int64_t)n0 * G + g_begin;
+  const int64_t x_bytes = rows_m * K * 2 - (int64_t)g_begin * 256;
+  const int64_t q_bytes = rows_n * (K >> 1) - (int64_t)g_begin * 64;
+  const int64_t sz_bytes = rows_n * G * 2 - (int64_t)g_begin * 2;
   // x load u takes rows 4u .. 4u+3 of the m-block, 256 contiguous bytes (a group) each:
   // lane l row 4u + l/16 and 16-byte chunk l%16
   const int xo = (lane >> 4) * K * 2 + (lane & 15) * 16;
@@ -99,17 +103,22 @@ __global__ __launch_bounds__(64 * KL) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // x first: the LDS store of a group's x waits (in issue order) only for the loads issued
   // before its own, not for that group's codes, which come from HBM and are needed later
   auto issue = [&](int g, Stage& r) {
-    const int past = (int)(g >= gcount) * kOutOfRange;
+    // views of group g (empty past the K-lane's range: every load reads zero); each view
+    // ends at the tile's last row, so rows past M or N read zero too
+    const bool in = g < gcount;
+    const __amdgpu_buffer_rsrc_t rx = rsrc(x0 + g * 128, in ? x_bytes - g * 256 : 0);
+    const __amdgpu_buffer_rsrc_t rq = rsrc(q0 + g * 16, in ? q_bytes - g * 64 : 0);
+    const __amdgpu_buffer_rsrc_t rs = rsrc(s0 + g, in ? sz_bytes - g * 2 : 0);
+    const __amdgpu_buffer_rsrc_t rz = rsrc(z0 + g, in ? sz_bytes - g * 2 : 0);
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
-      for (int s = 0; s < 4; ++s)
-        r.x[mt][s] = load16(rx, xo + (4 * mt + s) * 4 * K * 2 + g * 256 + past);
+      for (int s = 0; s < 4; ++s) r.x[mt][s] = load16(rx, xo + (4 * mt + s) * 4 * K * 2);
 #pragma unroll
     for (int nt = 0; nt < NW; ++nt) {
-      r.q[nt] = load16(rq, qo + nt * 16 * (K >> 1) + g * 64 + past);
-      r.s[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, so + nt * 16 * G * 2 + g * 2 + past, 0, 0);
-      r.z[nt] = __builtin_amdgcn_raw_buffer_load_b16(rz, so + nt * 16 * G * 2 + g * 2 + past, 0, 0);
+      r.q[nt] = load16(rq, qo + nt * 16 * (K >> 1));
+      r.s[nt] = __builtin_amdgcn_raw_buffer_load_b16(rs, so + nt * 16 * G * 2, 0, 0);
+      r.z[nt] = __builtin_amdgcn_raw_buffer_load_b16(rz, so + nt * 16 * G * 2, 0, 0);
     }
   };
   // this wave's LDS area (rows padded to 17 chunks: the 16 lanes of one fragment read hit
@@ -191,26 +200,25 @@ __global__ __launch_bounds__(64 * KL) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                                           s == 0 ? (float4_t){0.f, 0.f, 0.f, 0.f} : sx[mt], 0, 0, 0);
       }
     }
-    if (fast) {
+    if (!fast) {
+      // the general route's zero term, -z * sum_k x, goes into the group's product first; only
+      // this temporary differs between the routes, so the accumulators are updated in one place
 #pragma unroll
       for (int nt = 0; nt < NW; ++nt) {
-        const float d = half_bits_to_float((uint16_t)r.s[nt]);
-#pragma unroll
-        for (int mt = 0; mt < MW; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mt][nt][i] = __builtin_fmaf(d, p[mt][nt][i], acc[mt][nt][i]);
-      }
-    } else {
-#pragma unroll
-      for (int nt = 0; nt < NW; ++nt) {
-        const float d = half_bits_to_float((uint16_t)r.s[nt]);
         const float zf = half_bits_to_float((uint16_t)r.z[nt]);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[mt][nt][i] = __builtin_fmaf(d, __builtin_fmaf(-zf, sx[mt][i], p[mt][nt][i]), acc[mt][nt][i]);
+          for (int i = 0; i < 4; ++i) p[mt][nt][i] = __builtin_fmaf(-zf, sx[mt][i], p[mt][nt][i]);
       }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NW; ++nt) {
+      const float d = half_bits_to_float((uint16_t)r.s[nt]);
+#pragma unroll
+      for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mt][nt][i] = __builtin_fmaf(d, p[mt][nt][i], acc[mt][nt][i]);
     }
   };
 
