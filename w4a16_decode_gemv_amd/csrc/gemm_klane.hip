@@ -284,8 +284,11 @@ __global__ __launch_bounds__(64 * KL) __attribute__((amdgpu_waves_per_eu(2, 2)))
 }
 
 // the one shape measured best on the LLaMA projection shapes: 64 x 32 tiles, four K-lanes,
-// loads two groups ahead (64 x 64 tiles need AGPR spills of the accumulators, eight K-lanes
-// and one group ahead were slower; a sweep of 48 <= M <= 512 over nine layer shapes)
+// loads two groups ahead (sweeps of 33 <= M <= 512 over nine layer shapes). 64 x 64 tiles
+// need AGPR spills of the accumulators; one group ahead was slower; with two waves per SIMD,
+// eight K-lanes (4096 -> 4096 at M = 128: 18.0 against 15.8 us, slower on every shape) and
+// 32 x 64 tiles (17.7 against 15.8 us; half the x reads per output, twice the dequant per
+// MFMA) were slower too
 constexpr int kMW = 4, kNW = 2, kKL = 4, kR = 2;
 
 }  // namespace
