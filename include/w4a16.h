@@ -184,10 +184,13 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * run the wave-tile GEMV kernel; other M <= 32 the small-batch
  * MFMA kernel (workgroups own whole rows of y, waves split K), except
  * 17 <= M <= 32 with K > 16384, which runs the K-lane kernel; M > 32 the
- * K-lane MFMA kernel (K split over four waves per workgroup) where the tiled
- * MFMA kernel would start at most 256 workgroups (ceil(M / 32) * ceil(N / 64)
- * while ceil(M / 64) * ceil(N / 64) < 512, else the latter), or at most 512 with
- * K > 8192; the tiled MFMA kernel otherwise.
+ * K-lane MFMA kernel (K split over the four waves of a workgroup) where the
+ * tiled MFMA kernel would start at most 256 workgroups (ceil(M / 32) *
+ * ceil(N / 64) while ceil(M / 64) * ceil(N / 64) < 512, else the latter), or
+ * where the K-lane grid (ceil(M / 64) * ceil(N / 32) workgroups) is at most
+ * 512 with K >= 8192 or at most 768 with K > 8192; otherwise the small-batch
+ * kernel twice (rows 0..31, then the rest) for M <= 64 on layers with
+ * N <= 8192 and K <= 16384, and the tiled MFMA kernel for the rest.
  * Groups of 32 and 64: M == 1, and M == 2 on layers with K <= 24576 and
  * N * K >= 2^26 or small enough for 4-row tiles (as for group 128), run the
  * GEMV kernel (two or one 32-input pieces per group);
@@ -200,6 +203,45 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  */
 w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales, const void* zeros,
                           int64_t M, int64_t N, int64_t K, int32_t group, void* y, void* stream);
+
+/*
+ * w4a16_linear_workspace - bytes of float32 workspace that w4a16_linear_ws may
+ * use for this shape and group (0: it will run w4a16_linear's kernels and needs
+ * none); -1 when the shape or group is not accepted. Host only.
+ */
+int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t group);
+
+/*
+ * w4a16_linear_ws_splits - the number of K ranges w4a16_linear_ws splits this
+ * shape into when given its workspace (0: no split, w4a16_linear's kernels);
+ * -1 when the shape or group is not accepted. Host only.
+ */
+int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
+
+/*
+ * w4a16_linear_ws - w4a16_linear whose automatic choice may also take the
+ * split-K kernels (w4a16_linear_splitk) when the caller lends a workspace, for
+ * batched layers with too few output tiles to fill the chip (CMU guide: at
+ * large batch the layer is compute-bound; L13 TinyChat kernel fusion). Same
+ * formula, accuracy contract, arguments and alignment as w4a16_linear, plus
+ * workspace: NULL (then exactly w4a16_linear), or device memory of
+ * workspace_bytes >= w4a16_linear_workspace(M, N, K, group) bytes, 16-byte
+ * aligned, overwritten (two calls in flight at once need two workspaces).
+ * Dispatch, groups of 128 with a workspace (from measured sweeps over the
+ * LLaMA projection shapes): with G = K / 128 and T = ceil(M / 64) *
+ * ceil(N / 128) split-K tiles, for K >= 8192 (M > 16, or M > 32 at K = 8192)
+ * the largest S of 8, 4, 2, 1 with S * T < 1024 and G / S >= 8, unless that is
+ * S = 1 on more than 512 tiles; for 4096 <= K < 8192, S = 2 on 65..128 tiles
+ * and S = 4 on at most 48 tiles at M > 32; otherwise no split
+ * (w4a16_linear_ws_splits reports the choice). With S > 0 the call launches the
+ * two split-K kernels, else w4a16_linear's. Results are reproducible (fixed
+ * summation order for a given shape).
+ * Errors: those of w4a16_linear; W4A16_ERR_ARG (workspace too small for the
+ * split chosen); W4A16_ERR_ALIGN (workspace). Checked before any HIP call.
+ */
+w4a16_status w4a16_linear_ws(const void* x, const void* qweight, const void* scales, const void* zeros,
+                             int64_t M, int64_t N, int64_t K, int32_t group, void* workspace,
+                             int64_t workspace_bytes, void* y, void* stream);
 
 /*
  * w4a16_linear_path - w4a16_linear with the kernel chosen by the caller, for

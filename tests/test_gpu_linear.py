@@ -29,10 +29,10 @@ def _packed(cfg, layer_id, n, k, m, W=None):
     return xs, qw, sc, zr
 
 
-def _check(lib, xs, qw, sc, zr, path, rows=None, tag=""):
+def _check(lib, xs, qw, sc, zr, path, rows=None, tag="", workspace="auto"):
     g = _gpu()
     print(f"linear {tag} M={xs.shape[0]} N={qw.shape[0]} K={xs.shape[1]} path={path}", flush=True)
-    y = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=path)).astype(np.float64)
+    y = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=path, workspace=workspace)).astype(np.float64)
     if rows is not None:
         y = y[:, rows]
     y_ref, b = oracle.linear(xs, qw, sc, zr, rows=rows)
@@ -90,7 +90,7 @@ def test_auto_33_to_64_rows(lib, m, n, k):
     xs, qw, sc, zr = _packed(4, 60 + m, n, k, m)
     _check(lib, xs, qw, sc, zr, path=0, tag="auto-33-64")
     dev = [g.dev(t) for t in (xs, qw, sc, zr)]
-    y = g.host(lib.linear(*dev))
+    y = g.host(lib.linear(*dev, workspace=None))  # w4a16_linear: no workspace, no split-K
     assert np.array_equal(g.bits16(y), g.bits16(g.host(lib.linear(*dev, path=4))))
     y1 = g.host(lib.linear(dev[0][:32].contiguous(), *dev[1:], path=3)).astype(np.float64)
     y2 = g.host(lib.linear(dev[0][32:].contiguous(), *dev[1:], path=3)).astype(np.float64)
@@ -251,11 +251,46 @@ def test_klane_ragged_shapes(lib, m, n, k):
                                    (64, 8192, 8192), (96, 22016, 8192), (24, 22016, 1024), (32, 22016, 8192),
                                    (96, 8192, 8192), (384, 11008, 4096), (512, 8192, 1024)])
 def test_auto_klane_route(lib, m, k, n):
-    # shapes the automatic dispatch sends to the K-lane kernel: every output against the oracle,
-    # and bit-identical to forcing path 4
+    # shapes the automatic dispatch of w4a16_linear (no workspace) sends to the K-lane kernel:
+    # every output against the oracle, and bit-identical to forcing path 4
     g = _gpu()
     xs, qw, sc, zr = _packed(8, 2, n, k, m)
-    _check(lib, xs, qw, sc, zr, path=0, tag="auto-klane")
-    a = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=0))
+    _check(lib, xs, qw, sc, zr, path=0, tag="auto-klane", workspace=None)
+    a = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=0, workspace=None))
     b = g.host(lib.linear(g.dev(xs), g.dev(qw), g.dev(sc), g.dev(zr), path=4))
     assert np.array_equal(g.bits16(a), g.bits16(b))
+
+
+@pytest.mark.parametrize("m,k,n", [(64, 11008, 4096), (256, 4096, 4096), (48, 4096, 11008), (32, 22016, 8192),
+                                   (24, 11008, 4096), (512, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024)])
+def test_auto_with_workspace_takes_split_k(lib, m, k, n):
+    # the automatic path with a workspace (w4a16_linear_ws, the binding's default): shapes where
+    # it splits K (8, 2, 2, 8, 8, 1, 4 and 8 ranges): every output against the oracle, and
+    # bit-identical to the split-K entry point with the same ranges
+    g = _gpu()
+    splits = lib.linear_ws_splits(m, n, k)
+    assert splits > 0
+    xs, qw, sc, zr = _packed(8, 3, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=0, tag=f"auto-ws-S{splits}")
+    dev = [g.dev(t) for t in (xs, qw, sc, zr)]
+    a = g.host(lib.linear(*dev))
+    b = g.host(lib.linear_splitk(*dev, splits=splits))
+    assert np.array_equal(g.bits16(a), g.bits16(b))
+    # a caller's workspace of exactly the size asked for gives the same bits
+    import torch
+
+    ws = torch.empty(lib.linear_workspace_bytes(m, n, k) // 4, dtype=torch.float32, device=g.DEV)
+    c = g.host(lib.linear(*dev, workspace=ws))
+    assert np.array_equal(g.bits16(a), g.bits16(c))
+
+
+def test_auto_with_workspace_refuses_a_short_one(lib):
+    import torch
+
+    g = _gpu()
+    m, k, n = 64, 11008, 4096
+    xs, qw, sc, zr = _packed(8, 4, n, k, m)
+    dev = [g.dev(t) for t in (xs, qw, sc, zr)]
+    short = torch.empty(lib.linear_workspace_bytes(m, n, k) // 4 - 1, dtype=torch.float32, device=g.DEV)
+    with pytest.raises(lib.W4A16Error):
+        lib.linear(*dev, workspace=short)

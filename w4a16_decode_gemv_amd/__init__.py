@@ -52,6 +52,9 @@ def load():
         "awq_quantize_pack": ([vp, vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
         "w4a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w4a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
+        "w4a16_linear_workspace": ([i64, i64, i64, i32], i64),
+        "w4a16_linear_ws_splits": ([i64, i64, i64, i32], i32),
+        "w4a16_linear_ws": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
         "awq_alpha_loss_workspace": ([i64, i64], i64),
         "w4a16_linear_splitk_workspace": ([i64, i64, i64, i32], i64),
         "w4a16_linear_splitk": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, i64, vp, vp], i32),
@@ -82,7 +85,8 @@ def load():
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
-            "w4a16_linear_path", "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w4a16_linear_splitk_noalloc", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
+            "w4a16_linear_path", "w4a16_linear_workspace", "w4a16_linear_ws_splits", "w4a16_linear_ws",
+            "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w4a16_linear_splitk_noalloc", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
             "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
             "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read", "w4a16_stream_read_grid",
             "awq_search_alpha_workspace", "awq_search_alpha"]
@@ -232,6 +236,22 @@ def splitk_workspace_bytes(M, N, K, splits=0):
     return n
 
 
+def linear_workspace_bytes(M, N, K, group=GROUP):
+    """Bytes of float32 workspace the automatic 4-bit path may use (0: none)."""
+    n = int(load().w4a16_linear_workspace(int(M), int(N), int(K), int(group)))
+    if n < 0:
+        raise ValueError(f"M={M}, N={N}, K={K}, group={group} outside the limits of the linear call")
+    return n
+
+
+def linear_ws_splits(M, N, K, group=GROUP):
+    """The K ranges the automatic 4-bit path splits this shape into when given its workspace (0: none)."""
+    n = int(load().w4a16_linear_ws_splits(int(M), int(N), int(K), int(group)))
+    if n < 0:
+        raise ValueError(f"M={M}, N={N}, K={K}, group={group} outside the limits of the linear call")
+    return n
+
+
 def linear_splitk(x, qweight, scales, zeros, splits=0, workspace=None, out=None, group=GROUP):
     """``linear`` (4-bit, groups of 128) on the split-K MFMA kernel; workspace: a float32 device
     tensor of at least splitk_workspace_bytes(M, N, K, splits) bytes (allocated when omitted)."""
@@ -348,10 +368,13 @@ def nf4_linear(x, qweight, absmax, block=NF4_BLOCK, out=None, path=PATH_AUTO):
     return y
 
 
-def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO, bits=4):
+def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO, bits=4, workspace="auto"):
     """y = x @ dequant(qweight, scales, zeros)^T, fp16 [M][N] (float32 accumulation).
 
-    bits 4: qweight in layout v1 [N][K/8]; bits 3: the 3-bit layout [N][3K/32]."""
+    bits 4: qweight in layout v1 [N][K/8]; bits 3: the 3-bit layout [N][3K/32].
+    The automatic path (4-bit) runs w4a16_linear_ws: with workspace "auto" a float32 workspace
+    is allocated from torch when the library asks for one (it may then take the split-K
+    kernels); None runs w4a16_linear (no workspace); a float32 device tensor is used as given."""
     torch = _torch()
     lib = load()
     x = _dev_tensor(x, torch.float16, "x", 2)
@@ -369,7 +392,17 @@ def linear(x, qweight, scales, zeros, group=GROUP, out=None, path=PATH_AUTO, bit
     y = _out(out, (m, n), torch.float16, x)
     args = (x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k, group, y.data_ptr(),
             _stream(x))
-    if bits == 4:
+    if bits == 4 and path == PATH_AUTO and workspace is not None:
+        if isinstance(workspace, str):
+            if workspace != "auto":
+                raise ValueError('workspace must be "auto", None or a float32 device tensor')
+            need = int(lib.w4a16_linear_workspace(m, n, k, group))
+            workspace = torch.empty(need // 4, dtype=torch.float32, device=x.device) if need > 0 else None
+        else:
+            workspace = _workspace(workspace, torch.float32, x)
+        wp, wb = (0, 0) if workspace is None else (workspace.data_ptr(), workspace.numel() * 4)
+        status = lib.w4a16_linear_ws(*args[:8], wp or None, wb, *args[8:])
+    elif bits == 4:
         status = lib.w4a16_linear(*args) if path == PATH_AUTO else lib.w4a16_linear_path(path, *args)
     else:
         status = lib.w3a16_linear(*args) if path == PATH_AUTO else lib.w3a16_linear_path(path, *args)

@@ -81,6 +81,32 @@ bool auto_klane(int64_t M, int64_t N, int64_t K) {
 // (57 / 65 against 73 / 75 us)
 bool auto_klane_small(int64_t M, int64_t K) { return M > 16 && M <= w4a16::skinny_max_m() && K > 16384; }
 
+// The automatic path's split-K choice when the caller lends a workspace (4-bit codes, groups
+// of 128): the number of K ranges, or 0 for the kernels of w4a16_linear. Over K >= 8192 (and
+// M > 16; M > 32 at K = 8192) the largest S of 8, 4, 2, 1 with S * tiles < 1024 and at least
+// 8 groups per range, except S = 1 on more than 512 tiles; over 4096 <= K < 8192, two ranges
+// on 65..128 tiles and four on at most 48 tiles at M > 32. From a sweep of M = 48..512 over
+// nine layer shapes plus M = 16 / 32 (MI355X, graph-timed us, split-K / the automatic path
+// without a workspace): 11008 -> 4096 at M = 64 20.2 (S = 8) / 34.1 and at M = 256 47.9 / 54.0;
+// 22016 -> 8192 at M = 128 90.0 / 109.3 and at M = 512 299.8 (S = 1) / 367.6; 8192 -> 8192 at
+// M = 128 42.3 / 48.0; 8192 -> 1024 at M = 128 15.2 / 23.5; 4096 -> 4096 at M = 256
+// 23.4 (S = 2) / 26.0; 4096 -> 11008 at M = 64 22.7 / 26.8; 11008 -> 4096 at M = 32 19.7 /
+// 25.8. The rule costs up to 4 % where it misjudges (8192 -> 22016 at M = 128: 102.4 / 98.2).
+int auto_splits(int64_t M, int64_t N, int64_t K) {
+  if (M <= 16) return 0;
+  const int64_t tiles = w4a16::splitk_tiles(M, N), G = K / 128;
+  if (K >= 8192 && (M > 32 || K > 8192)) {
+    int s = 8;
+    while (s > 1 && (tiles * s >= 1024 || G / s < 8)) s >>= 1;
+    return s == 1 && tiles > 512 ? 0 : s;
+  }
+  if (K >= 4096 && K < 8192) {
+    if (tiles > 64 && tiles <= 128) return 2;
+    if (M > 32 && tiles <= 48) return 4;
+  }
+  return 0;
+}
+
 w4a16_status hip_result(hipError_t e, const char* what) {
   if (e != hipSuccess) return fail(W4A16_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
   return W4A16_OK;
@@ -402,6 +428,40 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
   return run_linear(4, 0, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
+}
+
+int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
+  if (group != 128 && group != 64 && group != 32) return -1;
+  const int s = group == 128 ? auto_splits(M, N, K) : 0;
+  return s > 0 ? w4a16::splitk_workspace_floats(M, N, s) * 4 : 0;
+}
+
+w4a16_status w4a16_linear_ws(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
+                             int64_t N, int64_t K, int32_t group, void* workspace, int64_t workspace_bytes, void* y,
+                             void* stream) {
+  clear_error();
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  const int s = (group == 128 && workspace) ? auto_splits(M, N, K) : 0;
+  if (s > 0) {
+    const int64_t need = w4a16::splitk_workspace_floats(M, N, s) * 4;
+    if (workspace_bytes < need)
+      return fail(W4A16_ERR_ARG, "workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+    if (!aligned(workspace, 16)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return hip_result(w4a16::launch_splitk(static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
+                                           static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros),
+                                           M, N, K, s, static_cast<float*>(workspace), static_cast<uint16_t*>(y),
+                                           static_cast<hipStream_t>(stream)),
+                      "split-K launch");
+  }
+  return run_linear(4, 0, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));
+}
+
+int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
+  if (group != 128 && group != 64 && group != 32) return -1;
+  return group == 128 ? auto_splits(M, N, K) : 0;
 }
 
 w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,

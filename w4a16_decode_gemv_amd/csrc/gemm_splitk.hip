@@ -221,6 +221,8 @@ int64_t tiles_of(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN -
 
 int splitk_max_splits() { return kMaxSplits; }
 
+int64_t splitk_tiles(int64_t M, int64_t N) { return tiles_of(M, N); }
+
 int splitk_default_splits(int64_t M, int64_t N, int64_t K) {
   // about two workgroups per CU, rounded up to a power of two (3 splits measured slower than
   // 4 on the 4096 -> 11008 layer at M = 128), at most 4 splits (more cost more in partial

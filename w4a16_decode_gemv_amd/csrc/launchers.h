@@ -70,6 +70,7 @@ hipError_t launch_skinny_nf4(const Nf4Table& table, int block, const uint16_t* x
 // splitk_workspace_floats(M, N, S) floats, then a fixed-order reduction into y. Needs 1 <= S <= K/128.
 int splitk_max_splits();
 int splitk_default_splits(int64_t M, int64_t N, int64_t K);
+int64_t splitk_tiles(int64_t M, int64_t N);  // output tiles of the partial kernel (64 x 128)
 int64_t splitk_workspace_floats(int64_t M, int64_t N, int splits);
 hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                          int64_t M, int64_t N, int64_t K, int splits, float* workspace, uint16_t* y,
