@@ -230,8 +230,9 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
  * Dispatch, groups of 128 with a workspace (from measured sweeps over the
  * LLaMA projection shapes): with G = K / 128 and T = ceil(M / 64) *
  * ceil(N / 128) split-K tiles, for K >= 8192 (M > 16, or M > 32 at K = 8192)
- * the largest S of 8, 4, 2, 1 with S * T < 1024 and G / S >= 8, unless that is
- * S = 1 on more than 512 tiles; for 4096 <= K < 8192, S = 2 on 65..128 tiles
+ * the largest S of 8, 4, 2, 1 with S * T < 1024 (S * T <= 256 when T <= 64)
+ * and G / S >= 8, unless that is S = 1 on more than 512 tiles; for
+ * 4096 <= K < 8192, S = 2 on 65..128 tiles
  * and S = 4 on at most 48 tiles at M > 32; otherwise no split
  * (w4a16_linear_ws_splits reports the choice). With S > 0 the call launches the
  * two split-K kernels, else w4a16_linear's. Results are reproducible (fixed
