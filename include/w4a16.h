@@ -228,12 +228,12 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
  * workspace_bytes >= w4a16_linear_workspace(M, N, K, group) bytes, 16-byte
  * aligned, overwritten (two calls in flight at once need two workspaces).
  * Dispatch, groups of 128 with a workspace (from measured sweeps over the
- * LLaMA projection shapes): with G = K / 128 and T = ceil(M / 64) *
- * ceil(N / 128) split-K tiles, for K >= 8192 (M > 16, or M > 32 at K = 8192)
- * the largest S of 8, 4, 2, 1 with S * T < 1024 (S * T <= 256 when T <= 64)
- * and G / S >= 8, unless that is S = 1 on more than 512 tiles; for
- * 4096 <= K < 8192, S = 2 on 65..128 tiles
- * and S = 4 on at most 48 tiles at M > 32; otherwise no split
+ * LLaMA projection shapes): no split for M <= 20; else with G = K / 128 and T
+ * the split-K kernel's tiles (ceil(N / 128) for M <= 32, else ceil(M / 64) *
+ * ceil(N / 128)), for K >= 8192 the largest S of 8, 4, 2, 1 with S * T < 1024
+ * (S * T <= 256 when T <= 64) and G / S >= 8, unless that is S = 1 on more than
+ * 512 tiles; for 4096 <= K < 8192, S = 2 on 65..128 tiles and S = 4 on at most
+ * 48 tiles at M > 32; otherwise no split
  * (w4a16_linear_ws_splits reports the choice). With S > 0 the call launches the
  * two split-K kernels, else w4a16_linear's. Results are reproducible (fixed
  * summation order for a given shape).
@@ -267,7 +267,8 @@ int64_t w4a16_linear_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t s
 
 /*
  * w4a16_linear_splitk - w4a16_linear (4-bit, groups of 128) on the split-K
- * MFMA kernel, for batches whose output has too few tiles to fill the chip
+ * MFMA kernel (output tiles of 64 rows of y by 128 columns, 32 rows when
+ * M <= 32), for batches whose output has too few tiles to fill the chip
  * (CMU guide: at large batch the layer is compute-bound; L13 TinyChat kernel
  * fusion). The K groups are split into `splits` contiguous ranges (0 = the
  * library's choice, else 1 <= splits <= min(16, K/128)); each range's float32

@@ -245,11 +245,13 @@ def test_splitk_workspace_and_rejects():
 def test_linear_ws_split_choice_and_rejects():
     lib = w4.load()
     # the automatic path's split choice with a workspace (4-bit, groups of 128): no split at
-    # M <= 16, at K = 8192 up to M = 32, below K = 4096, and on more than 512 tiles of 64 x 128
-    # with one range; else the largest S of 8, 4, 2, 1 with S * tiles < 1024 (<= 256 on up to
-    # 64 tiles) and >= 8 groups per range (K >= 8192), or two ranges on 65..128 tiles / four on
-    # <= 48 (4096 <= K < 8192)
-    cases = {(1, 8192, 8192): 0, (16, 4096, 11008): 0, (32, 8192, 8192): 0, (32, 4096, 11008): 8, (32, 8192, 22016): 4,
+    # M <= 20, below K = 4096, and on more than 512 tiles (32 x 128 up to M = 32, else
+    # 64 x 128) with one range; else the largest S of 8, 4, 2, 1 with S * tiles < 1024 (<= 256
+    # on up to 64 tiles) and >= 8 groups per range (K >= 8192), or two ranges on 65..128 tiles
+    # / four on <= 48 at M > 32 (4096 <= K < 8192)
+    cases = {(1, 8192, 8192): 0, (16, 4096, 11008): 0, (20, 4096, 11008): 0, (32, 8192, 8192): 4, (24, 8192, 8192): 4,
+             (32, 4096, 11008): 8, (32, 8192, 22016): 4, (24, 22016, 8192): 4, (32, 11008, 4096): 2,
+             (32, 4096, 4096): 0,
              (64, 4096, 11008): 8, (128, 4096, 11008): 4, (256, 4096, 11008): 4, (512, 4096, 11008): 2,
              (128, 8192, 8192): 4, (64, 8192, 8192): 4, (48, 8192, 8192): 4, (256, 8192, 8192): 2, (512, 8192, 8192): 1, (512, 8192, 22016): 1,
              (192, 22016, 8192): 0, (128, 22016, 8192): 2, (64, 1024, 8192): 8,

@@ -82,27 +82,29 @@ bool auto_klane(int64_t M, int64_t N, int64_t K) {
 bool auto_klane_small(int64_t M, int64_t K) { return M > 16 && M <= w4a16::skinny_max_m() && K > 16384; }
 
 // The automatic path's split-K choice when the caller lends a workspace (4-bit codes, groups
-// of 128): the number of K ranges, or 0 for the kernels of w4a16_linear. Over K >= 8192 (and
-// M > 16; M > 32 at K = 8192) the largest S of 8, 4, 2, 1 with S * tiles < 1024 (at most 256
-// on up to 64 tiles) and at least 8 groups per range, except S = 1 on more than 512 tiles;
-// over 4096 <= K < 8192, two ranges on 65..128 tiles and four on at most 48 tiles at M > 32.
-// On 64 tiles four ranges beat eight: 8192 -> 8192 at M = 64 25.8 / 28.8 us, 11008 -> 4096 at
-// M = 128 28.9 / 30.4 (22016 -> 8192 at M = 32 the other way, 50.0 / 47.8). From a sweep of M = 48..512 over
-// nine layer shapes plus M = 16 / 32 (MI355X, graph-timed us, split-K / the automatic path
-// without a workspace): 11008 -> 4096 at M = 64 20.2 (S = 8) / 34.1 and at M = 256 47.9 / 54.0;
-// 22016 -> 8192 at M = 128 90.0 / 109.3 and at M = 512 299.8 (S = 1) / 367.6; 8192 -> 8192 at
-// M = 128 42.3 / 48.0; 8192 -> 1024 at M = 128 15.2 / 23.5; 4096 -> 4096 at M = 256
-// 23.4 (S = 2) / 26.0; 4096 -> 11008 at M = 64 22.7 / 26.8; 11008 -> 4096 at M = 32 19.7 /
-// 25.8. The rule costs up to 4 % where it misjudges (8192 -> 22016 at M = 128: 102.4 / 98.2).
+// of 128): the number of K ranges, or 0 for the kernels of w4a16_linear. No split up to
+// M = 20. Over K >= 8192: the largest S of 8, 4, 2, 1 with S * tiles < 1024 (at most 256 on
+// up to 64 tiles) and at least 8 groups per range, except S = 1 on more than 512 tiles. Over
+// 4096 <= K < 8192: two ranges on 65..128 tiles, four on at most 48 tiles at M > 32. Tiles
+// are the partial kernel's (32 x 128 up to M = 32, else 64 x 128). From sweeps of M = 12..512
+// over nine layer shapes (MI355X, graph-timed us, split-K / the automatic path without a
+// workspace): 11008 -> 4096 at M = 32 17.5 (S = 8) / 25.7, at M = 64 20.2 / 34.1 and at
+// M = 256 47.9 (S = 4) / 54.0; 22016 -> 8192 at M = 32 43.7 / 60.0, at M = 128 90.0 / 109.3 and
+// at M = 512 299.8 (S = 1) / 367.6; 8192 -> 8192 at M = 32 21.7 / 23.5 and at M = 128
+// 42.3 / 48.0; 8192 -> 1024 at M = 32 12.6 / 18.9; 4096 -> 4096 at M = 256 23.4 (S = 2) / 26.0;
+// 4096 -> 11008 at M = 32 19.0 / 24.4. On 64 tiles four ranges beat eight (8192 -> 8192 at
+// M = 64 25.8 / 28.8). Up to M = 16 the small-batch kernel stays ahead on most shapes
+// (8192 -> 8192 at M = 16: 20.8 / 16.2). The rule costs up to 4 % where it misjudges
+// (8192 -> 22016 at M = 128: 102.4 / 98.2; 8192 -> 8192 at M = 24: 21.3 / 20.8).
 int auto_splits(int64_t M, int64_t N, int64_t K) {
-  if (M <= 16) return 0;
+  if (M <= 20) return 0;
   const int64_t tiles = w4a16::splitk_tiles(M, N), G = K / 128;
-  if (K >= 8192 && (M > 32 || K > 8192)) {
+  if (K >= 8192) {
     int s = 8;
     while (s > 1 && (tiles * s >= (tiles <= 64 ? 257 : 1024) || G / s < 8)) s >>= 1;
     return s == 1 && tiles > 512 ? 0 : s;
   }
-  if (K >= 4096 && K < 8192) {
+  if (K >= 4096) {
     if (tiles > 64 && tiles <= 128) return 2;
     if (M > 32 && tiles <= 48) return 4;
   }

@@ -8,12 +8,13 @@
 // Deployment" guide, TinyChat kernel fusion; "CMU 11-868 Model Quantization"
 // guide: at large batch the layer is compute-bound and belongs on the matrix
 // cores). The K groups are split into S contiguous ranges; workgroup (tile, s)
-// computes the float32 partial P_s of its 64 x 128 tile over range s and writes
-// it to the caller's workspace; a second kernel adds the S partials of every
-// output in index order (reproducible) and rounds once to fp16.
+// computes the float32 partial P_s of its 64 x 128 tile (32 x 128 for batches of at
+// most 32 rows) over range s and writes it to the caller's workspace; a second
+// kernel adds the S partials of every output in index order (reproducible) and
+// rounds once to fp16.
 //
 // Partial kernel (same structure as the AWQ-search loss kernel): eight waves,
-// each owning 16 output rows n and all 64 rows m, one group per stage; the x tile
+// each owning 16 output rows n and all 64 (or 32) rows m, one group per stage; the x tile
 // is shared through LDS, a wave's codes and (scale, zero) stay in its registers;
 // loads run two stages ahead in register sets, as buffer loads (rows past M or N
 // and stages past the range read as zero, with no traffic), with an LDS-only
@@ -41,30 +42,33 @@ namespace w4a16 {
 namespace {
 
 
-constexpr int MT = 4;                  // 16-row MFMA tiles of m per workgroup
 constexpr int WAVES = 8;
-constexpr int BM = 16 * MT;            // 64 rows m
 constexpr int BN = 16 * WAVES;         // 128 rows n
 constexpr int kThreads = 64 * WAVES;
-constexpr int XU = BM * 16 / kThreads;  // 16-byte x chunks per thread per stage
 constexpr int R = 2;                   // stages of loads in flight
 constexpr int kMaxSplits = 16;
 
 
 
 
+template <int XU>
 struct Stage {
   u32x4_t x[XU];
   u32x4_t q;
   uint16_t s, z;
 };
 
-// grid: tiles_m * tiles_n * S items; item = (n-tile, split, m-tile) with m-tile fastest
+// grid: tiles_m * tiles_n * S items; item = (n-tile, split, m-tile) with m-tile fastest.
+// MT 16-row MFMA tiles of m per workgroup: 4 (64 rows), or 2 (32 rows) for batches of at
+// most 32 rows, where 64-row tiles would spend half their MFMA and LDS work on absent rows.
+template <int MT>
 __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t* __restrict__ x,
                                                                  const uint32_t* __restrict__ qw,
                                                                  const uint16_t* __restrict__ scales,
                                                                  const uint16_t* __restrict__ zeros, int M, int N,
                                                                  int K, int S, int TM, float* __restrict__ part) {
+  constexpr int BM = 16 * MT;              // rows m per workgroup
+  constexpr int XU = BM * 16 / kThreads;   // 16-byte x chunks per thread per stage
   __shared__ u32x4_t lx[2][BM][17];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
@@ -92,9 +96,9 @@ __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t
   const int qo = nl * (K >> 1) + j * 16;
   const int so = nl * G * 2;
 
-  Stage set[R];
+  Stage<XU> set[R];
   // stage g of this split (0 .. gcount-1); stages past the split read as zero
-  auto issue = [&](int g, Stage& r) {
+  auto issue = [&](int g, Stage<XU>& r) {
     const int past = (int)(g >= gcount) * kOutOfRange;
 #pragma unroll
     for (int u = 0; u < XU; ++u) r.x[u] = load16(rx, xoff[u] + g * 256 + past);
@@ -102,7 +106,7 @@ __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t
     r.s = __builtin_amdgcn_raw_buffer_load_b16(rs, so + g * 2 + past, 0, 0);
     r.z = __builtin_amdgcn_raw_buffer_load_b16(rz, so + g * 2 + past, 0, 0);
   };
-  auto store = [&](const Stage& r, int b) {
+  auto store = [&](const Stage<XU>& r, int b) {
 #pragma unroll
     for (int u = 0; u < XU; ++u) lx[b][(t >> 4) + (kThreads / 16) * u][t & 15] = r.x[u];
   };
@@ -111,7 +115,7 @@ __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Stage& r, int b) {
+  auto compute = [&](const Stage<XU>& r, int b) {
     // x fragments one m-tile ahead: the next tile's LDS reads overlap this tile's MFMAs
     half8_t xa[2][4];
 #pragma unroll
@@ -215,7 +219,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
-int64_t tiles_of(int64_t M, int64_t N) { return ((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+// rows m per workgroup of the partial kernel for a batch of M rows
+int64_t rows_per_tile(int64_t M) { return M <= 32 ? 32 : 64; }
+
+int64_t tiles_of(int64_t M, int64_t N) {
+  const int64_t bm = rows_per_tile(M);
+  return ((M + bm - 1) / bm) * ((N + BN - 1) / BN);
+}
 
 }  // namespace
 
@@ -271,10 +281,15 @@ hipError_t splitk_scratch(hipStream_t stream, float** ptr) {
 hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                          int64_t M, int64_t N, int64_t K, int splits, float* workspace, uint16_t* y,
                          hipStream_t stream) {
-  const int TM = (int)((M + BM - 1) / BM);
+  const int64_t bm = rows_per_tile(M);
+  const int TM = (int)((M + bm - 1) / bm);
   const int64_t items = tiles_of(M, N) * splits;
-  hipLaunchKernelGGL(splitk_partial_kernel, dim3((unsigned)items), dim3(kThreads), 0, stream, x, qweight, scales,
-                     zeros, (int)M, (int)N, (int)K, splits, TM, workspace);
+  if (bm == 32)
+    hipLaunchKernelGGL(splitk_partial_kernel<2>, dim3((unsigned)items), dim3(kThreads), 0, stream, x, qweight, scales,
+                       zeros, (int)M, (int)N, (int)K, splits, TM, workspace);
+  else
+    hipLaunchKernelGGL(splitk_partial_kernel<4>, dim3((unsigned)items), dim3(kThreads), 0, stream, x, qweight, scales,
+                       zeros, (int)M, (int)N, (int)K, splits, TM, workspace);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = M * N;
