@@ -42,6 +42,10 @@ def test_bad_out_and_workspace_tensors_are_refused(lib):
     ws64 = torch.empty(lib.splitk_workspace_bytes(m, n, k, 2) // 8, dtype=torch.float64, device=dev)
     with pytest.raises(ValueError):
         lib.linear_splitk(x, *packed, splits=2, workspace=ws64)
+    # the automatic path's workspace: a float32 tensor on the same device, or "auto" / None
+    for ws in (ws_host, ws64, "scratch"):
+        with pytest.raises(ValueError):
+            lib.linear(x, *packed, workspace=ws)
     torch.cuda.synchronize()
     # nothing was written through the refused tensors' pointers: the accepted output is intact
     want = lib.linear(x, *packed)

@@ -189,16 +189,35 @@ __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t
   }
 }
 
-// y[e] = f16( ((part[0][e] + part[1][e]) + ...) ), four outputs per thread
+// y[e] = f16( ((part[0][e] + part[1][e]) + ...) ), four outputs per thread. With the split
+// count known at compile time (SC > 0) every partial's load is issued before the first add;
+// a runtime count (SC = 0) keeps four loads in flight. A loop over a runtime count with one
+// load per trip waited for each load in turn (one memory round trip per split).
+template <int SC>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int64_t total, int S,
                                                            uint16_t* __restrict__ y) {
   const int64_t e0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (e0 >= total) return;
   if (e0 + 4 <= total && (total & 3) == 0) {
-    float4_t s = *reinterpret_cast<const float4_t*>(part + e0);
-    for (int k = 1; k < S; ++k) {
-      const float4_t v = *reinterpret_cast<const float4_t*>(part + (int64_t)k * total + e0);
-      s += v;
+    float4_t s;
+    if constexpr (SC > 0) {
+      float4_t v[SC];
+#pragma unroll
+      for (int k = 0; k < SC; ++k) v[k] = *reinterpret_cast<const float4_t*>(part + (int64_t)k * total + e0);
+      s = v[0];
+#pragma unroll
+      for (int k = 1; k < SC; ++k) s += v[k];
+    } else {
+      s = *reinterpret_cast<const float4_t*>(part + e0);
+      int k = 1;
+      for (; k + 4 <= S; k += 4) {
+        float4_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float4_t*>(part + (int64_t)(k + u) * total + e0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) s += v[u];
+      }
+      for (; k < S; ++k) s += *reinterpret_cast<const float4_t*>(part + (int64_t)k * total + e0);
     }
     const uint32_t lo = (uint32_t)float_to_half_bits(s[0]) | ((uint32_t)float_to_half_bits(s[1]) << 16);
     const uint32_t hi = (uint32_t)float_to_half_bits(s[2]) | ((uint32_t)float_to_half_bits(s[3]) << 16);
@@ -294,7 +313,22 @@ hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint1
   if (e != hipSuccess) return e;
   const int64_t total = M * N;
   const int64_t grid = (total + 1023) / 1024;
-  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)grid), dim3(256), 0, stream, workspace, total, splits, y);
+  switch (splits) {
+#define W4A16_REDUCE(SC)                                                                                        \
+  case SC:                                                                                                       \
+    hipLaunchKernelGGL(splitk_reduce_kernel<SC>, dim3((unsigned)grid), dim3(256), 0, stream, workspace, total, \
+                       splits, y);                                                                               \
+    break;
+    W4A16_REDUCE(1)
+    W4A16_REDUCE(2)
+    W4A16_REDUCE(4)
+    W4A16_REDUCE(8)
+    W4A16_REDUCE(16)
+#undef W4A16_REDUCE
+    default:
+      hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, workspace, total, splits,
+                         y);
+  }
   return hipGetLastError();
 }
 
