@@ -137,6 +137,91 @@ __device__ __forceinline__ float wave_sum_lane63(float v) {
   return v;
 }
 
+// Sum of the two results of one permlane swap. clang has been seen to fold `p[0] + p[1]` of
+// a single swap into twice its first result; the empty asm statement keeps the two apart.
+__device__ __forceinline__ float swap_pair_sum(uint32_t a, uint32_t b) {
+  asm volatile("" : "+v"(a), "+v"(b));
+  return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+}
+
+// lane l < 32: a[l] + a[l + 32]; lane l >= 32: b[l - 32] + b[l] (the swap exchanges a's upper
+// half with b's lower half)
+__device__ __forceinline__ float permlane32_swap_sum(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                  false, false);
+  return swap_pair_sum(p[0], p[1]);
+}
+
+// lanes of 16-lane rows 0 and 2: a summed over rows (0, 1) and (2, 3) respectively; rows 1 and
+// 3: b summed the same way (the swap exchanges a's odd rows with b's even rows)
+__device__ __forceinline__ float permlane16_swap_sum(float a, float b) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b),
+                                                  false, false);
+  return swap_pair_sum(p[0], p[1]);
+}
+
+// Last three steps of a wave sum, within each group of 8 lanes: lanes l ^ 1, then l ^ 2
+// (quad perms), then j and 7 - j (row_half_mirror, which after the first two steps pairs the
+// group's two quads). Every lane ends with its group's sum.
+__device__ __forceinline__ float dpp_group8_sum(float s) {
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0xB1, 0xF, 0xF, true));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x4E, 0xF, 0xF, true));
+  s += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x141, 0xF, 0xF, true));
+  return s;
+}
+
+// s + s of lane l ^ 8 (row_ror:8 within each 16-lane row)
+__device__ __forceinline__ float dpp_ror8_sum(float s) {
+  return s + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, s), 0x128, 0xF, 0xF, true));
+}
+
+// Sums over the wave of V values at once: out[j] = the sum of v[j] over the 64 lanes, stored
+// by one lane per value. Eight values take three halving steps that leave value j in lanes
+// 8j .. 8j + 7 (swaps across lane halves and 16-lane rows, then a DPP rotate by 8 that pairs
+// lanes l and l ^ 8), then three DPP steps over those 8 lanes: 10 cross-lane adds for 8
+// values, against 6 per value one at a time. Four values take the two swap steps (value j in
+// row j), two take one (value j in lane half j) and a last one none; each then goes on the
+// same way. Every value is summed in one order, pairs of lanes at distance 32, 16, 8, then
+// 1, 2, 4, whatever V and its slot, so a row's result does not depend on how many rows share
+// its wave, and results are deterministic.
+template <int V>
+__device__ __forceinline__ void wave_sums(const float* v, float* out, int lane) {
+  constexpr int V8 = V / 8, V4 = (V % 8) / 4, V2 = (V % 4) / 2, V1 = V % 2;
+#pragma unroll
+  for (int b = 0; b < V8; ++b) {
+    const float* w = v + 8 * b;
+    float s4[4], s2[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s4[j] = permlane32_swap_sum(w[j], w[j + 4]);  // value j + 4 (l >> 5)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) s2[j] = permlane16_swap_sum(s4[j], s4[j + 2]);  // j + 2 ((l >> 4) & 1) + ...
+    const bool up = (lane & 8) != 0;
+    const float keep = up ? s2[1] : s2[0], give = up ? s2[0] : s2[1];
+    const float s = dpp_group8_sum(keep + __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(
+                                              __builtin_bit_cast(int, give), 0x128, 0xF, 0xF, true)));  // value l >> 3
+    if ((lane & 7) == 0) out[8 * b + (lane >> 3)] = s;
+  }
+  int j = 8 * V8;
+  if constexpr (V4) {
+    const float* w = v + j;
+    const float s2a = permlane32_swap_sum(w[0], w[2]), s2b = permlane32_swap_sum(w[1], w[3]);
+    const float s = dpp_group8_sum(dpp_ror8_sum(permlane16_swap_sum(s2a, s2b)));  // value l >> 4
+    if ((lane & 15) == 0) out[j + (lane >> 4)] = s;
+    j += 4;
+  }
+  if constexpr (V2) {
+    const float h = permlane32_swap_sum(v[j], v[j + 1]);  // value l >> 5
+    const float s = dpp_group8_sum(dpp_ror8_sum(permlane16_swap_sum(h, h)));
+    if ((lane & 31) == 0) out[j + (lane >> 5)] = s;
+    j += 2;
+  }
+  if constexpr (V1) {
+    const float h = permlane32_swap_sum(v[j], v[j]);
+    const float s = dpp_group8_sum(dpp_ror8_sum(permlane16_swap_sum(h, h)));
+    if (lane == 0) out[j] = s;
+  }
+}
+
 // Workgroups are dealt to the chip's eight XCDs round-robin by linear block id.
 // Renumbering them so that each XCD takes a contiguous run of work items keeps
 // neighbouring items (the m-tiles and K-splits of one weight tile) on one XCD, where

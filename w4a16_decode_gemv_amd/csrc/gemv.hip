@@ -240,12 +240,12 @@ __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThre
         xp[pp][m][4 * wi + 3] = __builtin_amdgcn_perm(x67, x23, 0x07060302u);
       }
 
-  // (6) slot by slot as the loads land: dequantize, multiply, and sum the row's
-  //     partials across the wave at once (the DPP work of early rows overlaps
-  //     the loads of later ones)
+  // (6) slot by slot as the loads land: dequantize and multiply; then (7) the V partials
+  //     are summed across the wave together (batched swaps and DPP, one pass for all rows)
+  float vsum[V];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float acc[M];
+    float* acc = vsum + r * M;
 #pragma unroll
     for (int m = 0; m < M; ++m) acc[m] = 0.f;
 #pragma unroll
@@ -293,14 +293,10 @@ __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThre
           acc[m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[m]);
       }
     }
-#pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const float s = wave_sum_lane63(acc[m]);
-      if (lane == 63) wred[r * M + m] = s;
-    }
   }
+  wave_sums<V>(vsum, wred, lane);
 
-  // (7) add the waves' sums in a fixed order and store
+  // (8) add the waves' sums in a fixed order and store
   __syncthreads();
   const int nw = T >> 6;
   for (int v = t; v < R * M; v += T) {
