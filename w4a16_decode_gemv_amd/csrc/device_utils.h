@@ -111,32 +111,6 @@ struct Nf4Table {
   uint32_t pairs[8];
 };
 
-// Sum over the 16 lanes of a DPP row; every lane of the row receives the sum.
-__device__ __forceinline__ float dpp_row_sum16(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x141, 0xF, 0xF, true));  // row_half_mirror
-  v += __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x140, 0xF, 0xF, true));  // row_mirror
-  return v;
-}
-
-// Sum over all 64 lanes, valid in lane 63: four in-row DPP steps, then
-// row_bcast15 (rows 1, 3) and row_bcast31 (rows 2, 3).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_add_masked(float v) {
-  return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
-}
-
-__device__ __forceinline__ float wave_sum_lane63(float v) {
-  v = dpp_add_masked<0xB1, 0xF>(v);   // quad_perm 1,0,3,2
-  v = dpp_add_masked<0x4E, 0xF>(v);   // quad_perm 2,3,0,1
-  v = dpp_add_masked<0x141, 0xF>(v);  // row_half_mirror
-  v = dpp_add_masked<0x140, 0xF>(v);  // row_mirror
-  v = dpp_add_masked<0x142, 0xA>(v);  // row_bcast15
-  v = dpp_add_masked<0x143, 0xC>(v);  // row_bcast31
-  return v;
-}
-
 // Sum of the two results of one permlane swap. clang has been seen to fold `p[0] + p[1]` of
 // a single swap into twice its first result; the empty asm statement keeps the two apart.
 __device__ __forceinline__ float swap_pair_sum(uint32_t a, uint32_t b) {

@@ -240,8 +240,10 @@ __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThre
         xp[pp][m][4 * wi + 3] = __builtin_amdgcn_perm(x67, x23, 0x07060302u);
       }
 
-  // (6) slot by slot as the loads land: dequantize and multiply; then (7) the V partials
-  //     are summed across the wave together (batched swaps and DPP, one pass for all rows)
+  // (6) slot by slot as the loads land: dequantize and multiply; then (7) the partials are
+  //     summed across the wave in batches (swaps and DPP): all V of them in one pass at the
+  //     end, or, with 8 inputs, each row's 8 as soon as the row is done (measured on MI355X
+  //     at 8192 x 8192, M = 8: 37.25 against 37.43 us, groups of 64: 35.61 against 36.10)
   float vsum[V];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
@@ -293,8 +295,9 @@ __global__ __launch_bounds__(M <= 2 && PPT == 1 ? kMaxThreadsOnePiece : kMaxThre
           acc[m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[m]);
       }
     }
+    if constexpr (M >= 8) wave_sums<M>(acc, wred + r * M, lane);
   }
-  wave_sums<V>(vsum, wred, lane);
+  if constexpr (M < 8) wave_sums<V>(vsum, wred, lane);
 
   // (8) add the waves' sums in a fixed order and store
   __syncthreads();
@@ -489,10 +492,13 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
       sx[pp][m] = a;
     }
 
-  // (5) per row: dequantize, multiply, wave sum
+  // (5) per row: dequantize, multiply; then the wave sums in batches as in gemv_kernel
+  //     (measured on MI355X at 8192 x 8192 against one wave sum per value: 3-bit groups of
+  //     128, M = 2: 11.15 against 12.35 us, M = 4: 15.37 against 16.79; M = 8 within 1 %)
+  float vsum[V];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    float acc[MT];
+    float* acc = vsum + r * MT;
 #pragma unroll
     for (int m = 0; m < MT; ++m) acc[m] = 0.f;
 #pragma unroll
@@ -525,12 +531,9 @@ __global__ __launch_bounds__(kMaxThreads) void gemv_var_kernel(const uint4* __re
           acc[m] = __builtin_fmaf(d, __builtin_fmaf(-z, sx[pp][m], part[m]), acc[m]);
       }
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      const float sum = wave_sum_lane63(acc[m]);
-      if (lane == 63) wred[r * MT + m] = sum;
-    }
+    if constexpr (MT >= 8) wave_sums<MT>(acc, wred + r * MT, lane);
   }
+  if constexpr (MT < 8) wave_sums<V>(vsum, wred, lane);
 
   // (6) the waves' sums in a fixed order
   __syncthreads();
