@@ -52,6 +52,30 @@ def test_gemv_small_shapes(lib, m, n, k):
     _check(lib, xs, qw, sc, zr, path=1, tag="gemv")
 
 
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 64), (3, 128)])
+@pytest.mark.parametrize("n,k", [(300, 2048), (97, 11008), (4100, 4096)])
+def test_gemv_output_independent_of_batch(lib, bits, group, n, k):
+    # Each thread runs over the same inputs in the same order at any batch size up to 8 (one
+    # piece per thread on these rows), and the wave sums every output's lane partials in one
+    # fixed order however many (row, input) values share the batched reduction (sets of 8, 4,
+    # 2 and single values; M = 3, 5, 6 and 7 reach all four). So an output of a batch of M equals,
+    # bit for bit, that of its x row run alone.
+    g = _gpu()
+    L = synth.layer(4, 70, n, k, 8)
+    s = oracle.channel_scale(L["x_cal"])
+    xs = oracle.scale_input(L["x"], s)
+    packed = oracle.quantize_pack(L["W"], s, bits=bits, group=group)
+    dev = [g.dev(t) for t in packed]
+    print(f"gemv batch independence bits={bits} group={group} N={n} K={k}", flush=True)
+    alone = np.concatenate([g.host(lib.linear(g.dev(np.ascontiguousarray(xs[i:i + 1])), *dev, group=group,
+                                              bits=bits, path=1)) for i in range(8)])
+    y_ref, b = oracle.linear(xs, *packed, group=group, bits=bits)
+    assert np.all(oracle.within_tolerance(alone.astype(np.float64), y_ref, b))
+    for m in range(2, 9):
+        y = g.host(lib.linear(g.dev(np.ascontiguousarray(xs[:m])), *dev, group=group, bits=bits, path=1))
+        assert np.array_equal(y.view(np.uint16), alone[:m].view(np.uint16)), m
+
+
 def test_gemv_long_rows_take_several_pieces_per_thread(lib):
     # K = 22016 (two pieces per thread) and K = 65536 (eight) on M = 1; K = 32768 at M = 4
     # K = 22016 and 32768 at M = 2: one piece per thread in 688- and 1024-thread workgroups (the
