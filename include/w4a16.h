@@ -178,10 +178,10 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * x: fp16 [M][K], the input after the 1/s fold; qweight/scales/zeros as written
  * by awq_quantize_pack with bits 4; y: fp16 [M][N] (output). group 32, 64 or
  * 128 (as quantized); K % 128 == 0.
- * Dispatch, group 128: M == 1, and M == 2 on layers with K <= 24576 and
- * N * K >= 2^27 or on layers small enough that the GEMV takes 4-row tiles
- * (K <= 32768 and ceil(N / 8) * ceil(K / 2048) < 4096 waves, under 16 per CU),
- * run the wave-tile GEMV kernel; other M <= 32 the small-batch
+ * Dispatch, group 128: M == 1, and M == 2 on layers with K <= 24576 or small
+ * enough that the GEMV takes 4-row tiles (K <= 32768 and
+ * ceil(N / 8) * ceil(K / 2048) < 4096 waves, under 16 per CU), run the
+ * wave-tile GEMV kernel; other M <= 32 the small-batch
  * MFMA kernel (workgroups own whole rows of y, waves split K), except
  * 17 <= M <= 32 with K > 16384, which runs the K-lane kernel; M > 32 the
  * K-lane MFMA kernel (K split over the four waves of a workgroup) where the
@@ -191,9 +191,8 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * 512 with K >= 8192 or at most 768 with K > 8192; otherwise the small-batch
  * kernel twice (rows 0..31, then the rest) for M <= 64 on layers with
  * N <= 8192 and K <= 16384, and the tiled MFMA kernel for the rest.
- * Groups of 32 and 64: M == 1, and M == 2 on layers with K <= 24576 and
- * N * K >= 2^26 or small enough for 4-row tiles (as for group 128), run the
- * GEMV kernel (two or one 32-input pieces per group);
+ * Groups of 32 and 64: M == 1, and M == 2 with K <= 32768, run the GEMV
+ * kernel (two or one 32-input pieces per group);
  * other M <= 32 the small-batch MFMA kernel (which needs scales and zeros
  * 4-byte aligned; otherwise the GEMV takes M <= 8 where it can), and
  * 33 <= M <= 64 the same two launches as for group 128 on the same layers;
@@ -310,8 +309,9 @@ w4a16_status w4a16_linear_splitk_noalloc(const void* x, const void* qweight, con
  * packed 3-bit layout (awq_quantize_pack with bits 3). Lab 4 setup: 3-bit
  * weights, groups of 128; L13 TinyChat kernel fusion. Same formula, accuracy
  * contract, arguments and alignment as w4a16_linear; group 32, 64 or 128;
- * K % 128 == 0. Dispatch: M <= 2 the GEMV kernel's 3-bit variant (M == 2 up
- * to K = 32768); other M <= 32 the small-batch MFMA kernel's (scales and zeros
+ * K % 128 == 0. Dispatch: M == 1 the GEMV kernel's 3-bit variant, and M == 2
+ * too where K < N, where K == N with N * K >= 2^26, or where K <= 16384 with
+ * N * K >= 2^27; other M <= 32 the small-batch MFMA kernel's (scales and zeros
  * 4-byte aligned below groups of 128, else the GEMV variant up to M = 8, M = 4
  * above K = 16384); 33 <= M <= 64 on layers with N <= 8192 and K <= 16384
  * two small-batch launches (rows 0..31, then the rest); other M the tiled MFMA

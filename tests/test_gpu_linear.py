@@ -271,6 +271,28 @@ def test_klane_ragged_shapes(lib, m, n, k):
     _check(lib, xs, qw, sc, zr, path=4, tag="klane")
 
 
+@pytest.mark.parametrize("bits,group,n,k,path", [
+    (4, 128, 8192, 8192, 1), (4, 128, 8192, 22016, 1), (4, 128, 8192, 28672, 3), (4, 128, 4096, 4096, 1),
+    (4, 64, 8192, 28672, 1), (4, 32, 4096, 11008, 1),
+    (3, 128, 8192, 8192, 1), (3, 128, 11008, 4096, 1), (3, 128, 4096, 11008, 3), (3, 128, 4096, 4096, 3)])
+def test_auto_m2_route(lib, bits, group, n, k, path):
+    # M = 2: the automatic choice between the GEMV (path 1) and the small-batch kernel (path 3),
+    # bit-identical to forcing the kernel the dispatch rule names for the shape. Random codes,
+    # scales and zeros: this checks the route; parity of each kernel is checked elsewhere.
+    g = _gpu()
+    rng = np.random.default_rng(7)
+    words = k // 8 if bits == 4 else 3 * k // 32
+    qw = rng.integers(-2**31, 2**31, size=(n, words), dtype=np.int64).astype(np.int32)
+    sc = rng.uniform(1e-3, 1e-2, size=(n, k // group)).astype(np.float16)
+    zr = rng.integers(0, 2**bits, size=(n, k // group)).astype(np.float16)
+    x = rng.standard_normal((2, k)).astype(np.float16)
+    dev = [g.dev(t) for t in (x, qw, sc, zr)]
+    print(f"auto M=2 route bits={bits} group={group} N={n} K={k} -> path {path}", flush=True)
+    a = g.host(lib.linear(*dev, group=group, bits=bits, workspace=None))
+    b = g.host(lib.linear(*dev, group=group, bits=bits, path=path))
+    assert np.array_equal(g.bits16(a), g.bits16(b))
+
+
 @pytest.mark.parametrize("m,k,n", [(48, 4096, 4096), (64, 11008, 4096), (128, 4096, 4096), (256, 11008, 4096),
                                    (64, 8192, 8192), (96, 22016, 8192), (24, 22016, 1024), (32, 22016, 8192),
                                    (96, 8192, 8192), (384, 11008, 4096), (512, 8192, 1024)])

@@ -29,17 +29,15 @@ constexpr int64_t kMaxM = int64_t(1) << 16;
 constexpr int64_t kMaxT = int64_t(1) << 20;
 constexpr int64_t kMaxTiles = (int64_t(1) << 31) - 1;  // one workgroup per loss tile, 1-D grid
 // automatic dispatch, from sweeps on MI355X over the LLaMA projection shapes: the GEMV
-// kernel at M = 1, and at M = 2 on layers of at least 2^27 weights with K <= 24576 (there
-// the GEMV's doubled dot work still hides under the weight stream: 21.8 against 24.0 us at
-// 8192 -> 22016, 28.7 against 29.9 at 22016 -> 8192, 26.9 against 28.9 at 8192 -> 28672; on
-// 8192 -> 8192 and on 28672 -> 8192 the small-batch kernel is ahead: 9.9 against 10.3 us at
-// 8192 -> 8192, 29.5 against 33.8 at 28672 -> 8192), and at M = 2 on the small layers where
-// the GEMV takes narrow tiles (8.1 against 8.3 us at 4096 -> 11008, 8.7 against 9.0 at
-// 11008 -> 4096, 8.4 against 8.6 at 4096 -> 12288, 4.8 both at 4096 -> 4096); the
-// small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA kernel beyond
+// kernel at M = 1, and at M = 2 on rows of up to 24576 inputs or where the GEMV takes narrow
+// tiles (its batched cross-lane sums keep the doubled dot work under the weight stream:
+// 9.3 against 9.8 us at 8192 -> 8192, 20.9 against 29.6 at 22016 -> 8192, 19.3 against 23.1
+// at 8192 -> 22016, 7.6 against 8.1 at 4096 -> 11008, 8.4 against 8.8 at 11008 -> 4096, 4.4
+// against 4.8 at 4096 -> 4096; on 28672 -> 8192 the small-batch kernel is ahead, 28.9
+// against 29.2); the small-batch MFMA kernel up to skinny_max_m(); the tiled MFMA kernel
+// beyond
 bool auto_gemv(int64_t M, int64_t N, int64_t K) {
-  return M == 1 || (M == 2 && K <= 24576 && N * K >= (int64_t(1) << 27)) ||
-         (M == 2 && w4a16::gemv_narrow(M, N, K));
+  return M == 1 || (M == 2 && (K <= 24576 || w4a16::gemv_narrow(M, N, K)));
 }
 
 // the same hand-off for groups of 32 and 64 and for NF4, whose GEMV variant has no long-row
@@ -204,16 +202,19 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
     bool two_passes = false;
     int32_t kernel = path;
     if (path == 0) {
-      // 3-bit codes keep the GEMV variant at M = 2 on every shape: its dequant VALU is shared
-      // by both rows there (8192 -> 8192: 12.5 against 12.8 us for groups of 128, 12.6 against
-      // 13.3 for 64, 12.8 against 15.2 for 32). 4-bit groups of 64 and 32 run the tuned GEMV,
-      // which at M = 2 stays ahead from 2^26 weights (8192 -> 8192: 10.5 against 11.1 us for
-      // 64, 10.7 against 12.4 for 32; 8192 -> 22016: 21.1 against 25.1) and on the small layers
-      // where it takes 4-row tiles (4096 -> 11008: 8.3 against 8.6 us for 64, 8.5 against 9.4
-      // for 32; 11008 -> 4096: 8.9 against 9.4, 9.1 against 11.4; 4096 -> 4096: 4.8 against 4.9)
+      // 4-bit groups of 64 and 32 run the tuned GEMV, which at M = 2 is ahead on every
+      // LLaMA shape measured, rows of up to 28672 inputs (8192 -> 8192: 9.5 against 11.0 us for 64, 10.0 against 12.4 for
+      // 32; 28672 -> 8192: 30.0 against 31.9, 31.1 against 33.8; 4096 -> 4096: 4.5 against
+      // 4.9, 4.8 against 5.2). 3-bit codes keep the GEMV variant at M = 2 where rows are no
+      // longer than the layer is wide (its dequant VALU is shared by both rows: 8192 -> 8192
+      // 11.2 against 12.5 us, 8192 -> 22016 24.6 against 28.0, 4096 -> 11008 10.8 against
+      // 11.0) except on square layers below 2^26 weights (4096 -> 4096: 6.9 against 5.9), and
+      // leave longer rows to the small-batch kernel (11008 -> 4096: 11.3 against 10.5,
+      // 22016 -> 8192: 38.6 against 32.6)
       const bool gemv_first =
-          bits == 4 ? M == 1 || (M == 2 && ((K <= 24576 && N * K >= (int64_t(1) << 26)) || w4a16::gemv_narrow(M, N, K)))
-                    : auto_gemv_variant(M, N, K) || (bits == 3 && M == 2);
+          bits == 4 ? M == 1 || (M == 2 && K <= 32768)
+                    : auto_gemv_variant(M, N, K) ||
+                          (bits == 3 && M == 2 && (K < N || (K == N && N * K >= (int64_t(1) << 26))));
       two_passes = sz_aligned && two_small_batch_passes(M, N, K);
       kernel = gemv_first && gemv_ok ? 1 : skinny_ok || two_passes ? 3 : gemv_ok ? 1 : 2;
     } else if (path == 1 && !gemv_ok) {
