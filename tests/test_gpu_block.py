@@ -82,6 +82,28 @@ def test_rmsnorm_fold_edge_rows(lib):
     assert np.all(out[0].view(np.uint16) == 0)   # a zero row stays exactly zero
 
 
+@pytest.mark.parametrize("m,k", [(1, 4096), (3, 11008), (70, 2056)])
+def test_rmsnorm_fold_unaligned_gamma_and_s(lib, m, k):
+    # gamma and s 16-byte aligned take vector loads; at 2 and 4 bytes (the entry's minimum) the
+    # kernel loads them element by element: the same bits either way
+    import torch
+
+    g = _gpu()
+    h, gamma, s = _block_inputs(2, k, m, 11)
+    hd = g.dev(h)
+    gbig = torch.zeros(k + 1, dtype=torch.float16, device=g.DEV)
+    sbig = torch.zeros(k + 1, dtype=torch.float32, device=g.DEV)
+    gbig[1:] = g.dev(gamma)
+    sbig[1:] = g.dev(s)
+    print(f"rmsnorm-fold unaligned M={m} K={k}", flush=True)
+    a = g.host(lib.rmsnorm_fold(hd, g.dev(gamma), g.dev(s), 1e-5))
+    b = g.host(lib.rmsnorm_fold(hd, gbig[1:], sbig[1:], 1e-5))
+    c = g.host(lib.rmsnorm_fold(hd, gbig[1:], None, 1e-5))
+    assert np.array_equal(a.view(np.uint16), b.view(np.uint16))
+    assert np.array_equal(c.view(np.uint16), g.host(lib.rmsnorm_fold(hd, g.dev(gamma), None, 1e-5)).view(np.uint16))
+    assert _check_fold(lib, h, gamma, s, 1e-5, "aligned") <= max(2, h.size // 10000)
+
+
 def _stacked_vs_separate(lib, cfg, names, m):
     g = _gpu()
     layers = {n: (k, nn) for n, k, nn in synth.CONFIGS[cfg]["layers"]}

@@ -24,7 +24,10 @@
 // queueing on one. Larger batches take S = 1 and loop. A thread's first chunk of
 // the second pass, with its gamma and s, is loaded before the reduction, so the
 // latency of those loads overlaps the first pass; that chunk of h is kept from the
-// first pass.
+// first pass. The first pass issues up to four of a thread's chunk loads before it
+// adds any (in k order), and gamma and s arrive in 16-byte loads when aligned:
+// measured on MI355X, one 4096-wide row took 4.0 us against 5.5 us with one chunk
+// load in flight and element-wise gamma and s loads.
 #include "device_utils.h"
 #include "launchers.h"
 
@@ -34,13 +37,16 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int64_t kSplitBelowM = 64;
+constexpr int kInFlight = 4;  // chunks of h each thread has in flight in the first pass
 
+// VEC: gamma and s are 16-byte aligned, so a chunk's eight gamma and eight s values arrive in
+// one and two 16-byte loads instead of eight 2-byte and eight 4-byte ones
+template <bool VEC>
 __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* __restrict__ h,
                                                                 const uint16_t* __restrict__ gamma,
                                                                 const float* __restrict__ s, int K, int S,
                                                                 double eps, u32x4_t* __restrict__ out) {
   __shared__ double wsum[kThreads / 64];
-  __shared__ double rrow;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int row = blockIdx.x / S, slice = blockIdx.x - row * S;
   const int chunks = K >> 3;  // 8 fp16 per 16-byte chunk
@@ -55,24 +61,54 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* _
   const bool has = cp < c1;
   uint16_t gp[8];
   float sp[8];
+  auto load_gs = [&](int c, bool in, uint16_t (&g)[8], float (&sv)[8]) {
+    if constexpr (VEC) {
+      const u32x4_t gz = {0u, 0u, 0u, 0u};
+      const u32x4_t sone = {0x3F800000u, 0x3F800000u, 0x3F800000u, 0x3F800000u};
+      const u32x4_t gw = in ? reinterpret_cast<const u32x4_t*>(gamma)[c] : gz;
+      const bool sin = in && s != nullptr;
+      const u32x4_t s0 = sin ? reinterpret_cast<const u32x4_t*>(s)[2 * c] : sone;
+      const u32x4_t s1 = sin ? reinterpret_cast<const u32x4_t*>(s)[2 * c + 1] : sone;
+      const uint32_t gwv[4] = {gw.x, gw.y, gw.z, gw.w};
+      const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    gp[e] = has ? gamma[8 * cp + e] : (uint16_t)0;
-    sp[e] = (has && s != nullptr) ? s[8 * cp + e] : 1.0f;
-  }
+      for (int e = 0; e < 8; ++e) {
+        g[e] = (uint16_t)(gwv[e >> 1] >> (16 * (e & 1)));
+        sv[e] = __builtin_bit_cast(float, sw[e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        g[e] = in ? gamma[8 * c + e] : (uint16_t)0;
+        sv[e] = (in && s != nullptr) ? s[8 * c + e] : 1.0f;
+      }
+    }
+  };
+  load_gs(cp, has, gp, sp);
   u32x4_t hp = {0u, 0u, 0u, 0u};
 
+  // first pass: kInFlight chunks issued before any is added, added in k order
   double acc = 0.0;
-  for (int c = t; c < chunks; c += kThreads) {
-    const u32x4_t v = h[base + c];
-    if (c == cp) hp = v;
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  for (int cb = t; cb < chunks; cb += kInFlight * kThreads) {
+    u32x4_t v[kInFlight];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const double a = (double)half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
-      const double b = (double)half_bits_to_float((uint16_t)(w[i] >> 16));
-      acc += a * a;
-      acc += b * b;
+    for (int u = 0; u < kInFlight; ++u) {
+      const int c = cb + u * kThreads;
+      v[u] = c < chunks ? h[base + c] : (u32x4_t){0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kInFlight; ++u) {
+      const int c = cb + u * kThreads;
+      if (c >= chunks) break;
+      if (c == cp) hp = v[u];
+      const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const double a = (double)half_bits_to_float((uint16_t)(w[i] & 0xFFFFu));
+        const double b = (double)half_bits_to_float((uint16_t)(w[i] >> 16));
+        acc += a * a;
+        acc += b * b;
+      }
     }
   }
   // fixed-order tree: xor butterfly inside the wave, then the waves in index order
@@ -80,15 +116,12 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* _
   for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
   if (lane == 0) wsum[wave] = acc;
   __syncthreads();
-  if (t == 0) {
-    double ms = 0.0;
+  // every thread forms r from the same four sums in the same order (no second barrier)
+  double ms = 0.0;
 #pragma unroll
-    for (int w = 0; w < kThreads / 64; ++w) ms += wsum[w];
-    ms = ms / (double)K;
-    rrow = 1.0 / sqrt(ms + eps);
-  }
-  __syncthreads();
-  const double r = rrow;
+  for (int w = 0; w < kThreads / 64; ++w) ms += wsum[w];
+  ms = ms / (double)K;
+  const double r = 1.0 / sqrt(ms + eps);
 
   for (int c = cp; c < c1; c += kThreads) {
     u32x4_t v = hp;
@@ -101,11 +134,7 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_fold_kernel(const u32x4_t* _
     }
     if (c != cp) {
       v = h[base + c];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        g[e] = gamma[8 * c + e];
-        sv[e] = s != nullptr ? s[8 * c + e] : 1.0f;
-      }
+      load_gs(c, true, g, sv);
     }
     const uint32_t w[4] = {v.x, v.y, v.z, v.w};
     uint32_t o[4];
@@ -132,8 +161,13 @@ hipError_t launch_rmsnorm_fold(const uint16_t* h, const uint16_t* gamma, const f
                                double eps, uint16_t* x_s, hipStream_t stream) {
   const int64_t chunks = K / 8;
   const int S = M < kSplitBelowM ? (int)((chunks + kThreads - 1) / kThreads) : 1;
-  hipLaunchKernelGGL(rmsnorm_fold_kernel, dim3((unsigned)(M * S)), dim3(kThreads), 0, stream,
-                     reinterpret_cast<const u32x4_t*>(h), gamma, s, (int)K, S, eps, reinterpret_cast<u32x4_t*>(x_s));
+  const bool vec = (reinterpret_cast<uintptr_t>(gamma) & 15) == 0 && (reinterpret_cast<uintptr_t>(s) & 15) == 0;
+  if (vec)
+    hipLaunchKernelGGL(rmsnorm_fold_kernel<true>, dim3((unsigned)(M * S)), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const u32x4_t*>(h), gamma, s, (int)K, S, eps, reinterpret_cast<u32x4_t*>(x_s));
+  else
+    hipLaunchKernelGGL(rmsnorm_fold_kernel<false>, dim3((unsigned)(M * S)), dim3(kThreads), 0, stream,
+                       reinterpret_cast<const u32x4_t*>(h), gamma, s, (int)K, S, eps, reinterpret_cast<u32x4_t*>(x_s));
   return hipGetLastError();
 }
 
