@@ -487,10 +487,9 @@ w4a16_status nf4_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * with the fp16 codebook of nf4_codebook, float32 accumulation, and the
  * accuracy contract of w4a16_linear (B = sum_k |x * w_hat|). x: fp16 [M][K];
  * qweight, absmax as nf4_quantize_pack writes them; y: fp16 [M][N]; block 32,
- * 64 or 128; K % 128 == 0. Dispatch: M == 1, and M == 2 on layers with
- * K <= 16384 and N * K >= 2^27, a GEMV kernel with the codebook in LDS (at
- * M == 1 on layers with N * K < 2^26 the tuned 4-bit GEMV's NF4 form, else the
- * per-piece GEMV's); other M <= 32 the small-batch MFMA kernel's, and
+ * 64 or 128; K % 128 == 0. Dispatch: M == 1 a GEMV kernel with the codebook
+ * in LDS (on layers with N * K < 2^26 the tuned 4-bit GEMV's NF4 form, else
+ * the per-piece GEMV's); other M <= 32 the small-batch MFMA kernel's, and
  * 33 <= M <= 64 on layers with N <= 8192 and K <= 16384 two small-batch
  * launches (rows 0..31, then the rest); other M the tiled MFMA kernel's.
  * Alignment: x and qweight 16 bytes, absmax 4, y 2.

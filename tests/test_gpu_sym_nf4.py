@@ -202,3 +202,19 @@ def test_nf4_gemv_long_row_one_token(lib, path):
     qw, a = oracle.quantize_pack_nf4(synth.weights(3, 10, 40, 65536), None, 64)
     x = synth.activations(3, 10, 1, 65536)
     _nf4_linear_check(lib, x, qw, a, 64, path, "gemv-long-one-token")
+
+
+@pytest.mark.parametrize("n,k,m,path", [(22016, 8192, 2, 3), (8192, 8192, 2, 3), (8192, 22016, 1, 1), (2048, 2048, 1, 1)])
+def test_nf4_auto_route(lib, n, k, m, path):
+    # the automatic choice for NF4: the GEMV at M = 1, the small-batch kernel at M = 2 (bit-identical
+    # to forcing it). Random codes and absmax: this checks the route, not the kernels' parity.
+    g = _gpu()
+    rng = np.random.default_rng(3)
+    qw = rng.integers(-2**31, 2**31, size=(n, k // 8), dtype=np.int64).astype(np.int32)
+    am = rng.uniform(1e-3, 1e-2, size=(n, k // 64)).astype(np.float32)
+    x = rng.standard_normal((m, k)).astype(np.float16)
+    dev = [g.dev(t) for t in (x, qw, am)]
+    print(f"nf4 auto route M={m} N={n} K={k} -> path {path}", flush=True)
+    a = g.host(lib.nf4_linear(*dev, block=64))
+    b = g.host(lib.nf4_linear(*dev, block=64, path=path))
+    assert np.array_equal(g.bits16(a), g.bits16(b))

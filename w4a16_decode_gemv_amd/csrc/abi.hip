@@ -40,13 +40,12 @@ bool auto_gemv(int64_t M, int64_t N, int64_t K) {
   return M == 1 || (M == 2 && (K <= 24576 || w4a16::gemv_narrow(M, N, K)));
 }
 
-// the same hand-off for groups of 32 and 64 and for NF4, whose GEMV variant has no long-row
-// plan: at M = 2 it keeps the large layers with K <= 16384 (8192 -> 22016, groups of 64:
-// 23.2 against 25.1 us; NF4: 26.7 against 29.3) and loses the long rows (22016 -> 8192:
-// 47.7 against 29.5 us)
-bool auto_gemv_variant(int64_t M, int64_t N, int64_t K) {
-  return M == 1 || (M == 2 && K <= 16384 && N * K >= (int64_t(1) << 27));
-}
+// NF4 codes and 3-bit codes at M = 1 take the GEMV on every shape. At M = 2 NF4 goes to the
+// small-batch kernel: its 16-entry lookups cost the GEMV more than the shared x saves (blocks
+// of 64: 8192 -> 8192 14.7 against 12.9 us, 8192 -> 22016 32.6 against 29.4, 8192 -> 28672
+// 40.8 against 37.0, 22016 -> 8192 58.0 against 39.6); 3-bit codes have their own M = 2 rule
+// below
+bool auto_gemv_variant(int64_t M) { return M == 1; }
 
 // 33 <= M <= 64 on layers with N <= 8192 and K <= 16384: the small-batch kernel twice (rows
 // 0..31, then the rest) beats the tiled kernel there, for every code format (group 128:
@@ -202,18 +201,18 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
     bool two_passes = false;
     int32_t kernel = path;
     if (path == 0) {
-      // 4-bit groups of 64 and 32 run the tuned GEMV, which at M = 2 is ahead on every
-      // LLaMA shape measured, rows of up to 28672 inputs (8192 -> 8192: 9.5 against 11.0 us for 64, 10.0 against 12.4 for
-      // 32; 28672 -> 8192: 30.0 against 31.9, 31.1 against 33.8; 4096 -> 4096: 4.5 against
-      // 4.9, 4.8 against 5.2). 3-bit codes keep the GEMV variant at M = 2 where rows are no
-      // longer than the layer is wide (its dequant VALU is shared by both rows: 8192 -> 8192
-      // 11.2 against 12.5 us, 8192 -> 22016 24.6 against 28.0, 4096 -> 11008 10.8 against
-      // 11.0) except on square layers below 2^26 weights (4096 -> 4096: 6.9 against 5.9), and
-      // leave longer rows to the small-batch kernel (11008 -> 4096: 11.3 against 10.5,
-      // 22016 -> 8192: 38.6 against 32.6)
+      // 4-bit groups of 64 and 32 run the tuned GEMV, which at M = 2 is ahead on every LLaMA
+      // shape measured, rows of up to 28672 inputs (8192 -> 8192: 9.5 against 11.0 us for 64,
+      // 10.0 against 12.4 for 32; 28672 -> 8192: 30.0 against 31.9, 31.1 against 33.8;
+      // 4096 -> 4096: 4.5 against 4.9, 4.8 against 5.2). 3-bit codes keep the GEMV variant at
+      // M = 2 where rows are no longer than the layer is wide (its dequant VALU is shared by
+      // both rows: 8192 -> 8192 11.2 against 12.5 us, 8192 -> 22016 24.6 against 28.0,
+      // 4096 -> 11008 10.8 against 11.0) except on square layers below 2^26 weights
+      // (4096 -> 4096: 6.9 against 5.9), and leave longer rows to the small-batch kernel
+      // (11008 -> 4096: 11.3 against 10.5, 22016 -> 8192: 38.6 against 32.6)
       const bool gemv_first =
           bits == 4 ? M == 1 || (M == 2 && K <= 32768)
-                    : auto_gemv_variant(M, N, K) ||
+                    : auto_gemv_variant(M) ||
                           (bits == 3 && M == 2 && (K < N || (K == N && N * K >= (int64_t(1) << 26))));
       two_passes = sz_aligned && two_small_batch_passes(M, N, K);
       kernel = gemv_first && gemv_ok ? 1 : skinny_ok || two_passes ? 3 : gemv_ok ? 1 : 2;
@@ -661,7 +660,7 @@ w4a16_status nf4_linear_path(int32_t path, const void* x, const void* qweight, c
   int32_t kernel = path;
   const bool two_passes = path == 0 && two_small_batch_passes(M, N, K);
   if (path == 0)
-    kernel = auto_gemv_variant(M, N, K) && gemv_ok ? 1 : M <= w4a16::skinny_max_m() || two_passes ? 3 : gemv_ok ? 1 : 2;
+    kernel = auto_gemv_variant(M) && gemv_ok ? 1 : M <= w4a16::skinny_max_m() || two_passes ? 3 : gemv_ok ? 1 : 2;
   if (kernel == 1)
     return hip_result(w4a16::launch_gemv_nf4(nf4_table(), block, xh, qw, absmax, M, N, K, yh, hs), "NF4 GEMV launch");
   if (kernel == 3 && two_passes) {
