@@ -183,9 +183,11 @@ w4a16_status awq_quantize_pack(const void* w, const float* s, int64_t N, int64_t
  * ceil(N / 8) * ceil(K / 2048) < 4096 waves, under 16 per CU), run the
  * wave-tile GEMV kernel; other M <= 32 the small-batch
  * MFMA kernel (workgroups own whole rows of y, waves split K), except
- * 17 <= M <= 32 with K > 16384, which runs the K-lane kernel; M > 32 the
- * K-lane MFMA kernel (K split over the four waves of a workgroup) where the
- * tiled MFMA kernel would start at most 256 workgroups (ceil(M / 32) *
+ * 17 <= M <= 32 with K > 16384, which runs the K-lane kernel; M >= 256 the
+ * one-range split-K kernel (w4a16_linear_path path 5) where its tiles
+ * (ceil(M / 64) * ceil(N / 128)) are a multiple of 256 or at least 1280;
+ * other M > 32 the K-lane MFMA kernel (K split over the four waves of a
+ * workgroup) where the tiled MFMA kernel would start at most 256 workgroups (ceil(M / 32) *
  * ceil(N / 64) while ceil(M / 64) * ceil(N / 64) < 512, else the latter), or
  * where the K-lane grid (ceil(M / 64) * ceil(N / 32) workgroups) is at most
  * 512 with K >= 8192 or at most 768 with K > 8192; otherwise the small-batch
@@ -229,9 +231,10 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
  * Dispatch, groups of 128 with a workspace (from measured sweeps over the
  * LLaMA projection shapes): no split for M <= 20; else with G = K / 128 and T
  * the split-K kernel's tiles (ceil(N / 128) for M <= 32, else ceil(M / 64) *
- * ceil(N / 128)), for K >= 8192 the largest S of 8, 4, 2, 1 with S * T < 1024
- * (S * T <= 256 when T <= 64) and G / S >= 8, unless that is S = 1 on more than
- * 512 tiles; for 4096 <= K < 8192, S = 2 on 65..128 tiles and S = 4 on at most
+ * ceil(N / 128)), for K >= 8192 the largest S of 8, 4, 2 with S * T < 1024
+ * (S * T <= 256 when T <= 64) and G / S >= 8, none if only S = 1 remains (the
+ * automatic choice of w4a16_linear, which needs no workspace, covers those);
+ * for 4096 <= K < 8192, S = 2 on 65..128 tiles and S = 4 on at most
  * 48 tiles at M > 32; otherwise no split
  * (w4a16_linear_ws_splits reports the choice). With S > 0 the call launches the
  * two split-K kernels, else w4a16_linear's. Results are reproducible (fixed
@@ -249,7 +252,9 @@ w4a16_status w4a16_linear_ws(const void* x, const void* qweight, const void* sca
  * 1 = GEMV kernel (needs M <= w4a16_gemv_max_m() and M * ceil(K / 16384) <= 8),
  * 2 = tiled MFMA kernel (any M), 3 = small-batch MFMA kernel (needs M <= 32;
  * with groups of 32 or 64, scales and zeros 4-byte aligned, else
- * W4A16_ERR_ALIGN), 4 = K-lane MFMA kernel (any M; groups of 128 only). A path
+ * W4A16_ERR_ALIGN), 4 = K-lane MFMA kernel (any M; groups of 128 only),
+ * 5 = the split-K kernel with one K range, which writes fp16 y itself (no
+ * workspace, one launch; any M; groups of 128 only). A path
  * that cannot take the shape returns W4A16_ERR_UNSUPPORTED before any HIP
  * call. Same contract otherwise.
  */
@@ -273,13 +278,15 @@ int64_t w4a16_linear_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t s
  * library's choice, else 1 <= splits <= min(16, K/128)); each range's float32
  * partial of every output goes to `workspace`, and a second kernel adds the
  * partials in index order and rounds once to fp16, so results are reproducible.
+ * With one range the partial kernel rounds and writes y itself (the same bits,
+ * one launch; the workspace is still required but not touched).
  * Same formula, accuracy contract, arguments and alignment as w4a16_linear,
  * plus workspace: device memory of workspace_bytes >=
  * w4a16_linear_splitk_workspace(M, N, K, splits) bytes, 16-byte aligned,
  * overwritten (two calls in flight at once need two workspaces).
  * Errors: those of w4a16_linear; W4A16_ERR_UNSUPPORTED (group != 128);
  * W4A16_ERR_NULL (workspace); W4A16_ERR_ARG (splits, workspace too small);
- * W4A16_ERR_ALIGN (workspace). Launches two kernels.
+ * W4A16_ERR_ALIGN (workspace). Launches two kernels (one with one range).
  */
 w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
                                  int64_t M, int64_t N, int64_t K, int32_t group, int32_t splits,

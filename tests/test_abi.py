@@ -80,10 +80,11 @@ def test_linear_rejects_before_any_hip_call(kw, status):
 
 def test_linear_path_rejects_unknown_path_and_big_m_on_gemv():
     lib = w4.load()
-    assert lib.w4a16_linear_path(5, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear_path(6, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w4a16_linear_path(-1, A16, A16, A16, A16, 1, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
-    # the K-lane MFMA kernel (path 4) takes groups of 128 only
+    # the K-lane MFMA kernel (path 4) and the one-range split-K kernel (path 5) take groups of 128 only
     assert lib.w4a16_linear_path(4, A16, A16, A16, A16, 64, 64, 256, 64, A16, None) == w4.ERR_UNSUPPORTED
+    assert lib.w4a16_linear_path(5, A16, A16, A16, A16, 64, 64, 256, 32, A16, None) == w4.ERR_UNSUPPORTED
     assert lib.w4a16_linear_path(1, A16, A16, A16, A16, 9, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
     # the small-batch MFMA kernel takes M <= 32
     assert lib.w4a16_linear_path(3, A16, A16, A16, A16, 33, 64, 256, 128, A16, None) == w4.ERR_UNSUPPORTED
@@ -245,15 +246,16 @@ def test_splitk_workspace_and_rejects():
 def test_linear_ws_split_choice_and_rejects():
     lib = w4.load()
     # the automatic path's split choice with a workspace (4-bit, groups of 128): no split at
-    # M <= 20, below K = 4096, and on more than 512 tiles (32 x 128 up to M = 32, else
-    # 64 x 128) with one range; else the largest S of 8, 4, 2, 1 with S * tiles < 1024 (<= 256
-    # on up to 64 tiles) and >= 8 groups per range (K >= 8192), or two ranges on 65..128 tiles
-    # / four on <= 48 at M > 32 (4096 <= K < 8192)
+    # M <= 20 and below K = 4096; else the largest S of 8, 4, 2 with S * tiles < 1024 (<= 256
+    # on up to 64 tiles; tiles are 32 x 128 up to M = 32, else 64 x 128) and >= 8 groups per
+    # range (K >= 8192), none where only one range would be left (the automatic path without a
+    # workspace takes those), or two ranges on 65..128 tiles / four on <= 48 at M > 32
+    # (4096 <= K < 8192)
     cases = {(1, 8192, 8192): 0, (16, 4096, 11008): 0, (20, 4096, 11008): 0, (32, 8192, 8192): 4, (24, 8192, 8192): 4,
              (32, 4096, 11008): 8, (32, 8192, 22016): 4, (24, 22016, 8192): 4, (32, 11008, 4096): 2,
              (32, 4096, 4096): 0,
              (64, 4096, 11008): 8, (128, 4096, 11008): 4, (256, 4096, 11008): 4, (512, 4096, 11008): 2,
-             (128, 8192, 8192): 4, (64, 8192, 8192): 4, (48, 8192, 8192): 4, (256, 8192, 8192): 2, (512, 8192, 8192): 1, (512, 8192, 22016): 1,
+             (128, 8192, 8192): 4, (64, 8192, 8192): 4, (48, 8192, 8192): 4, (256, 8192, 8192): 2, (512, 8192, 8192): 0, (512, 8192, 22016): 0,
              (192, 22016, 8192): 0, (128, 22016, 8192): 2, (64, 1024, 8192): 8,
              (256, 4096, 4096): 2, (192, 4096, 4096): 2, (128, 4096, 4096): 0, (64, 4096, 4096): 4,
              (48, 11008, 4096): 2, (128, 11008, 4096): 0, (64, 8192, 1024): 0, (64, 64, 2048): 0}

@@ -308,11 +308,11 @@ def test_auto_klane_route(lib, m, k, n):
 
 
 @pytest.mark.parametrize("m,k,n", [(64, 11008, 4096), (256, 4096, 4096), (48, 4096, 11008), (32, 22016, 8192),
-                                   (24, 11008, 4096), (512, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024),
+                                   (24, 11008, 4096), (256, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024),
                                    (32, 8192, 8192), (21, 8192, 22016), (30, 4096, 11008)])
 def test_auto_with_workspace_takes_split_k(lib, m, k, n):
     # the automatic path with a workspace (w4a16_linear_ws, the binding's default): shapes where
-    # it splits K (8, 2, 2, 4, 8, 1, 4, 8, 4, 4 and 2 ranges; the 32-row tiles of the partial
+    # it splits K (8, 2, 2, 4, 8, 2, 4, 8, 4, 4 and 2 ranges; the 32-row tiles of the partial
     # kernel up to M = 32): every output against the oracle, and
     # bit-identical to the split-K entry point with the same ranges
     g = _gpu()
@@ -330,6 +330,34 @@ def test_auto_with_workspace_takes_split_k(lib, m, k, n):
     ws = torch.empty(lib.linear_workspace_bytes(m, n, k) // 4, dtype=torch.float32, device=g.DEV)
     c = g.host(lib.linear(*dev, workspace=ws))
     assert np.array_equal(g.bits16(a), g.bits16(c))
+
+
+@pytest.mark.parametrize("m,k,n", [(512, 4096, 4096), (256, 2048, 16384), (300, 1024, 32768), (512, 8192, 8192)])
+def test_auto_one_range_route(lib, m, k, n):
+    # from M = 256, where the one-range split-K kernel's 64 x 128 tiles fill the 256 CUs a whole
+    # number of times or come to at least 1280, the automatic path (with or without a
+    # workspace) runs it: every output against the oracle, bit-identical to forcing path 5 and
+    # to the split-K entry point with one range
+    g = _gpu()
+    assert lib.linear_ws_splits(m, n, k) == 0
+    assert lib.linear_workspace_bytes(m, n, k) == 0
+    xs, qw, sc, zr = _packed(8, 5, n, k, m)
+    rows = None if n * k <= (1 << 25) else np.linspace(0, n - 1, 384).astype(int)
+    _check(lib, xs, qw, sc, zr, path=0, rows=rows, tag="auto-one-range", workspace=None)
+    dev = [g.dev(t) for t in (xs, qw, sc, zr)]
+    a = g.host(lib.linear(*dev, workspace=None))
+    b = g.host(lib.linear(*dev, path=5))
+    c = g.host(lib.linear(*dev))
+    d = g.host(lib.linear_splitk(*dev, splits=1))
+    for other in (b, c, d):
+        assert np.array_equal(g.bits16(a), g.bits16(other))
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 128, 1), (70, 384, 300), (33, 4096, 1000), (200, 2048, 129)])
+def test_one_range_kernel(lib, m, k, n):
+    # path 5 forced on ragged shapes (rows and columns past the tiles, one group, odd N)
+    xs, qw, sc, zr = _packed(8, 6, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=5, tag="one-range")
 
 
 def test_auto_with_workspace_refuses_a_short_one(lib):

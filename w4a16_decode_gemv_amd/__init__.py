@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_ALIGN, ERR_HIP, ERR_ARG = range(7)
-PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_SKINNY, PATH_KLANE = 0, 1, 2, 3, 4
+PATH_AUTO, PATH_GEMV, PATH_MFMA, PATH_SKINNY, PATH_KLANE, PATH_ONE_RANGE = 0, 1, 2, 3, 4, 5
 GROUP = 128
 LAYOUT_VERSION = 1
 

@@ -56,6 +56,23 @@ bool two_small_batch_passes(int64_t M, int64_t N, int64_t K) {
   return M > w4a16::skinny_max_m() && M <= 2 * w4a16::skinny_max_m() && N <= 8192 && K <= 16384;
 }
 
+// From M = 256, 4-bit codes with groups of 128: the one-range split-K kernel (64 x 128 tiles,
+// fp16 written directly, no workspace) where its tiles fill the chip's 256 CUs a whole number
+// of times or come to at least 1280. Its time follows the rounds of tiles per CU, so a
+// partial last round costs it a whole one. From a sweep of M = 128..1024 over nine layer
+// shapes (MI355X, graph-timed), one-range / the kernel the rules below pick: 8192 -> 8192 at
+// M = 256 64.7 / 68.4 us, M = 512 115.9 / 132.3, M = 1024 228.3 / 259.1; 22016 -> 8192 at
+// M = 512 286.3 / 356.4, M = 1024 566.4 / 714.7; 8192 -> 22016 at M = 512 328.6 / 337.6;
+// 8192 -> 28672 at M = 768 608.8 / 664.0; 4096 -> 4096 at M = 512 29.6 / 35.2;
+// 11008 -> 4096 at M = 512 84.8 / 91.5. With a partial round it loses: 8192 -> 8192 at
+// M = 384 (384 tiles) 113.0 / 97.3, 8192 -> 22016 at M = 384 (1032) 268.6 / 263.9,
+// 4096 -> 11008 at M = 256 (344) 56.6 / 46.8.
+bool auto_one_range(int64_t M, int64_t N) {
+  if (M < 256) return false;
+  const int64_t tiles = w4a16::splitk_tiles(M, N);
+  return tiles % 256 == 0 || tiles >= 1280;
+}
+
 // Above the small-batch kernel, 4-bit codes with groups of 128: the K-lane kernel where the
 // tiled kernel has at most one workgroup per CU, or where the K-lane grid fills the chip at
 // most once (two workgroups per CU, K >= 8192) or 1.5 times (K > 8192); the tiled kernel
@@ -81,17 +98,19 @@ bool auto_klane_small(int64_t M, int64_t K) { return M > 16 && M <= w4a16::skinn
 // The automatic path's split-K choice when the caller lends a workspace (4-bit codes, groups
 // of 128): the number of K ranges, or 0 for the kernels of w4a16_linear. No split up to
 // M = 20. Over K >= 8192: the largest S of 8, 4, 2, 1 with S * tiles < 1024 (at most 256 on
-// up to 64 tiles) and at least 8 groups per range, except S = 1 on more than 512 tiles. Over
+// up to 64 tiles) and at least 8 groups per range (a single range is left to the automatic
+// path without a workspace, which runs the one-range kernel itself where it is ahead). Over
 // 4096 <= K < 8192: two ranges on 65..128 tiles, four on at most 48 tiles at M > 32. Tiles
 // are the partial kernel's (32 x 128 up to M = 32, else 64 x 128). From sweeps of M = 12..512
 // over nine layer shapes (MI355X, graph-timed us, split-K / the automatic path without a
 // workspace): 11008 -> 4096 at M = 32 17.5 (S = 8) / 25.7, at M = 64 20.2 / 34.1 and at
-// M = 256 47.9 (S = 4) / 54.0; 22016 -> 8192 at M = 32 43.7 / 60.0, at M = 128 90.0 / 109.3 and
-// at M = 512 299.8 (S = 1) / 367.6; 8192 -> 8192 at M = 32 21.7 / 23.5 and at M = 128
-// 42.3 / 48.0; 8192 -> 1024 at M = 32 12.6 / 18.9; 4096 -> 4096 at M = 256 23.4 (S = 2) / 26.0;
-// 4096 -> 11008 at M = 32 19.0 / 24.4. On 64 tiles four ranges beat eight (8192 -> 8192 at
-// M = 64 25.8 / 28.8). Up to M = 16 the small-batch kernel stays ahead on most shapes
-// (8192 -> 8192 at M = 16: 20.8 / 16.2). The rule costs up to 4 % where it misjudges
+// M = 256 47.9 (S = 4) / 54.0; 22016 -> 8192 at M = 32 43.7 / 60.0, at M = 128 90.0 / 109.3
+// and at M = 512 299.8 (one range, with a separate reduction then) / 367.6; 8192 -> 8192 at
+// M = 32 21.7 / 23.5 and at M = 128 42.3 / 48.0; 8192 -> 1024 at M = 32 12.6 / 18.9;
+// 4096 -> 4096 at M = 256 23.4 (S = 2) / 26.0; 4096 -> 11008 at M = 32 19.0 / 24.4. On 64
+// tiles four ranges beat eight (8192 -> 8192 at M = 64 25.8 / 28.8). Up to M = 16 the
+// small-batch kernel stays ahead on most shapes (8192 -> 8192 at M = 16: 20.8 / 16.2). The
+// rule costs up to 4 % where it misjudges
 // (8192 -> 22016 at M = 128: 102.4 / 98.2; 8192 -> 8192 at M = 24: 21.3 / 20.8).
 int auto_splits(int64_t M, int64_t N, int64_t K) {
   if (M <= 20) return 0;
@@ -99,7 +118,7 @@ int auto_splits(int64_t M, int64_t N, int64_t K) {
   if (K >= 8192) {
     int s = 8;
     while (s > 1 && (tiles * s >= (tiles <= 64 ? 257 : 1024) || G / s < 8)) s >>= 1;
-    return s == 1 && tiles > 512 ? 0 : s;
+    return s == 1 ? 0 : s;  // one range: the automatic choice without a workspace covers it
   }
   if (K >= 4096) {
     if (tiles > 64 && tiles <= 128) return 2;
@@ -247,6 +266,8 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   if (path == 0) {
     if (auto_gemv(M, N, K) && w4a16::gemv_supports(M, K)) {
       kernel = 1;
+    } else if (auto_one_range(M, N)) {
+      kernel = 5;
     } else if (auto_klane_small(M, K)) {
       kernel = 4;
     } else if (M <= w4a16::skinny_max_m()) {
@@ -276,6 +297,8 @@ w4a16_status run_linear(int32_t bits, int32_t path, const void* x, const void* q
   if (kernel == 3)
     return hip_result(w4a16::launch_skinny(xh, qw, sc, zr, M, N, K, yh, stream), "small-batch MFMA launch");
   if (kernel == 4) return hip_result(w4a16::launch_klane(xh, qw, sc, zr, M, N, K, yh, stream), "K-lane MFMA launch");
+  if (kernel == 5)
+    return hip_result(w4a16::launch_splitk(xh, qw, sc, zr, M, N, K, 1, nullptr, yh, stream), "one-range MFMA launch");
   return hip_result(w4a16::launch_mfma(xh, qw, sc, zr, M, N, K, yh, stream), "MFMA launch");
 }
 
@@ -472,11 +495,11 @@ w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight,
                                const void* zeros, int64_t M, int64_t N, int64_t K, int32_t group, void* y,
                                void* stream) {
   clear_error();
-  if (path < 0 || path > 4)
-    return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA), 3 (small-batch MFMA) or "
-                "4 (K-lane MFMA)");
-  if (path == 4 && group != 128)
-    return fail(W4A16_ERR_UNSUPPORTED, "the K-lane MFMA kernel takes groups of 128 (got %d)", (int)group);
+  if (path < 0 || path > 5)
+    return fail(W4A16_ERR_UNSUPPORTED, "path must be 0 (auto), 1 (GEMV), 2 (tiled MFMA), 3 (small-batch MFMA), "
+                "4 (K-lane MFMA) or 5 (one-range split-K MFMA)");
+  if ((path == 4 || path == 5) && group != 128)
+    return fail(W4A16_ERR_UNSUPPORTED, "the K-lane and one-range MFMA kernels take groups of 128 (got %d)", (int)group);
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
   return run_linear(4, path, x, qweight, scales, zeros, M, N, K, group, y, static_cast<hipStream_t>(stream));

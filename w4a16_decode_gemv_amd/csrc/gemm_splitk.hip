@@ -11,7 +11,8 @@
 // computes the float32 partial P_s of its 64 x 128 tile (32 x 128 for batches of at
 // most 32 rows) over range s and writes it to the caller's workspace; a second
 // kernel adds the S partials of every output in index order (reproducible) and
-// rounds once to fp16.
+// rounds once to fp16. With one range the partial kernel writes y itself (same bits, no
+// workspace, no second kernel).
 //
 // Partial kernel (same structure as the AWQ-search loss kernel): eight waves,
 // each owning 16 output rows n and all 64 (or 32) rows m, one group per stage; the x tile
@@ -61,12 +62,15 @@ struct Stage {
 // grid: tiles_m * tiles_n * S items; item = (n-tile, split, m-tile) with m-tile fastest.
 // MT 16-row MFMA tiles of m per workgroup: 4 (64 rows), or 2 (32 rows) for batches of at
 // most 32 rows, where 64-row tiles would spend half their MFMA and LDS work on absent rows.
-template <int MT>
+// DIRECT (one range, S = 1): the tile's sums are rounded to fp16 and written to y here, with
+// no partials and no second kernel; the same bits as the partial plus a one-range reduction.
+template <int MT, bool DIRECT = false>
 __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t* __restrict__ x,
                                                                  const uint32_t* __restrict__ qw,
                                                                  const uint16_t* __restrict__ scales,
                                                                  const uint16_t* __restrict__ zeros, int M, int N,
-                                                                 int K, int S, int TM, float* __restrict__ part) {
+                                                                 int K, int S, int TM, float* __restrict__ part,
+                                                                 uint16_t* __restrict__ y) {
   constexpr int BM = 16 * MT;              // rows m per workgroup
   constexpr int XU = BM * 16 / kThreads;   // 16-byte x chunks per thread per stage
   __shared__ u32x4_t lx[2][BM][17];
@@ -175,8 +179,20 @@ __global__ __launch_bounds__(kThreads) void splitk_partial_kernel(const uint16_t
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): no load in flight at exit
 
-  // the partial of this split: part[split][m][n]
   const int n = n0 + nl;
+  if constexpr (DIRECT) {
+    if (n < N) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = m0 + 16 * mt + 4 * j + i;
+          if (m < M) y[(int64_t)m * N + n] = float_to_half_bits(acc[mt][i]);
+        }
+    }
+    return;
+  }
+  // the partial of this split: part[split][m][n]
   if (n < N) {
     float* p = part + (int64_t)split * M * N;
 #pragma unroll
@@ -303,12 +319,22 @@ hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint1
   const int64_t bm = rows_per_tile(M);
   const int TM = (int)((M + bm - 1) / bm);
   const int64_t items = tiles_of(M, N) * splits;
+  if (splits == 1) {
+    // one range: the kernel writes y itself (the workspace is not touched)
+    if (bm == 32)
+      hipLaunchKernelGGL((splitk_partial_kernel<2, true>), dim3((unsigned)items), dim3(kThreads), 0, stream, x,
+                         qweight, scales, zeros, (int)M, (int)N, (int)K, 1, TM, nullptr, y);
+    else
+      hipLaunchKernelGGL((splitk_partial_kernel<4, true>), dim3((unsigned)items), dim3(kThreads), 0, stream, x,
+                         qweight, scales, zeros, (int)M, (int)N, (int)K, 1, TM, nullptr, y);
+    return hipGetLastError();
+  }
   if (bm == 32)
     hipLaunchKernelGGL(splitk_partial_kernel<2>, dim3((unsigned)items), dim3(kThreads), 0, stream, x, qweight, scales,
-                       zeros, (int)M, (int)N, (int)K, splits, TM, workspace);
+                       zeros, (int)M, (int)N, (int)K, splits, TM, workspace, nullptr);
   else
     hipLaunchKernelGGL(splitk_partial_kernel<4>, dim3((unsigned)items), dim3(kThreads), 0, stream, x, qweight, scales,
-                       zeros, (int)M, (int)N, (int)K, splits, TM, workspace);
+                       zeros, (int)M, (int)N, (int)K, splits, TM, workspace, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = M * N;
@@ -319,7 +345,6 @@ hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint1
     hipLaunchKernelGGL(splitk_reduce_kernel<SC>, dim3((unsigned)grid), dim3(256), 0, stream, workspace, total, \
                        splits, y);                                                                               \
     break;
-    W4A16_REDUCE(1)
     W4A16_REDUCE(2)
     W4A16_REDUCE(4)
     W4A16_REDUCE(8)
