@@ -342,8 +342,7 @@ def test_auto_one_range_route(lib, m, k, n):
     assert lib.linear_ws_splits(m, n, k) == 0
     assert lib.linear_workspace_bytes(m, n, k) == 0
     xs, qw, sc, zr = _packed(8, 5, n, k, m)
-    rows = None if n * k <= (1 << 25) else np.linspace(0, n - 1, 384).astype(int)
-    _check(lib, xs, qw, sc, zr, path=0, rows=rows, tag="auto-one-range", workspace=None)
+    _check(lib, xs, qw, sc, zr, path=0, tag="auto-one-range", workspace=None)
     dev = [g.dev(t) for t in (xs, qw, sc, zr)]
     a = g.host(lib.linear(*dev, workspace=None))
     b = g.host(lib.linear(*dev, path=5))
