@@ -54,10 +54,11 @@ def _replay_and_compare(torch, capture, inputs, outputs, make_inputs, eager, rep
                                exp.view(torch.int16) if exp.dtype == torch.float16 else exp), i
 
 
-@pytest.mark.parametrize("m", [1, 2, 4, 40, 128])
-def test_linear_in_graph(lib, m):
+@pytest.mark.parametrize("m,n", [(1, 1000), (2, 1000), (4, 1000), (40, 1000), (128, 1000), (512, 4096)])
+def test_linear_in_graph(lib, m, n):
+    # (512, 4096): the automatic path takes the one-range split-K kernel (256 tiles of 64 x 128)
     torch, g = _torch(), _gpu()
-    k, n = 4096, 1000
+    k = 4096
     packed = [g.dev(t) for t in oracle.quantize_pack(synth.weights(2, 11, n, k))]
     x = g.dev(synth.activations(2, 11, m, k))
     y = torch.empty((m, n), dtype=torch.float16, device=x.device)
