@@ -112,11 +112,11 @@ def test_mfma_variant(lib, bits, group, m, n, k):
 
 
 @pytest.mark.parametrize("bits,group", FORMATS)
-@pytest.mark.parametrize("m", [2, 3, 5, 8, 9, 16, 17, 32])
+@pytest.mark.parametrize("m", [2, 3, 5, 8, 9, 13, 16, 17, 32])
 @pytest.mark.parametrize("n,k", [(1, 128), (37, 384), (300, 2048), (97, 11008), (64, 22016), (40, 32768)])
 def test_skinny_variant(lib, bits, group, m, n, k):
     # the small-batch MFMA kernel with 1, 2 or 4 (scale, zero) pairs per 128 inputs and 4- or
-    # 3-bit codes: every x path (one, two or four full-width x loads, and 16-row fragment
+    # 3-bit codes: every x path (one, two, four or eight full-width x loads, and 16-row fragment
     # loads), one and two m-tiles, one chunk and several chunks of stages per wave, ragged N, K
     x_cal = synth.calibration(2, 15, k)
     s = oracle.channel_scale(x_cal)

@@ -92,9 +92,10 @@ def test_mfma_small_shapes(lib, m, n, k):
     _check(lib, xs, qw, sc, zr, path=2, tag="mfma")
 
 
-@pytest.mark.parametrize("m", [1, 2, 3, 7, 16, 17, 31, 32])
+@pytest.mark.parametrize("m", [1, 2, 3, 7, 12, 13, 16, 17, 31, 32])
 @pytest.mark.parametrize("n,k", [(300, 2048), (97, 11008), (64, 384), (1, 128), (40, 1408), (8200, 1024)])
 def test_skinny_small_shapes(lib, m, n, k):
+    # M = 12..16: x rows through LDS (eight full-width loads, rows past M read as zero)
     # K = 384 and 128 leave some of the eight K-splitting waves without a group; K = 1408 (11 groups)
     # and 11008 give uneven splits and half-filled last stages; N = 8200 takes the two-tile-per-wave
     # variant with a ragged last workgroup

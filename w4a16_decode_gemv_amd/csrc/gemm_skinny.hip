@@ -131,7 +131,7 @@ __device__ __forceinline__ void load_item(__amdgpu_buffer_rsrc_t r, int off, uin
 }
 
 // NS stages (2 * NS groups) per wave and chunk; K beyond one chunk per wave loops over chunks
-// XI > 0 (M <= 2 XI <= 8, MT = 1): a stage's x rows arrive in XI full-width loads (lane l of
+// XI > 0 (M <= 2 XI <= 16, MT = 1): a stage's x rows arrive in XI full-width loads (lane l of
 // load i takes row 2i + l/32, 16-byte piece l%32 of the stage's 512 bytes) and reach the A
 // fragments through a wave-private LDS area; XI = 0: A fragments loaded straight from L2.
 // "Group" below is a 128-input group of the code stream; SUB = 128 / (quantization group)
@@ -154,7 +154,10 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
   static_assert(kRowStride3 <= 32, "the 3-bit staging area fits the 4-bit one");
   __shared__ u32x4_t lds_b[KS][ROWS * 8];            // one stage of codes: ROWS x (2 groups x 4 slots)
   __shared__ uint32_t lds_sz[KS][ROWS][CG * SUB + 1];  // one chunk of (scale | zero << 16), or absmax
-  __shared__ u32x4_t lds_x[XI > 0 ? KS : 1][XI > 0 ? D : 1][XI > 0 ? 2 * XI : 1][33];  // x rows, padded
+  // x rows, padded; 16 rows keep one LDS stage per wave (a wave reads its stage before it
+  // stores the next, in program order), which fits the chip's LDS next to two column tiles
+  constexpr int XS = XI > 4 ? 1 : D;
+  __shared__ u32x4_t lds_x[XI > 0 ? KS : 1][XI > 0 ? XS : 1][XI > 0 ? 2 * XI : 1][33];
   __shared__ __align__(16) _Float16 lut[NF4 ? 16 : 2];
   if constexpr (NF4) {
     if (threadIdx.x < 8) reinterpret_cast<uint32_t*>(lut)[threadIdx.x] = table.pairs[threadIdx.x];
@@ -315,7 +318,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
       }
       if constexpr (XI > 0) {
 #pragma unroll
-        for (int i = 0; i < XI; ++i) lds_x[w][u][2 * i + (lane >> 5)][lane & 31] = xl[u][i];
+        for (int i = 0; i < XI; ++i) lds_x[w][u % XS][2 * i + (lane >> 5)][lane & 31] = xl[u][i];
       }
       if (s + D < NS) load_codes(s + D, u);
       if constexpr (XI > 0) {
@@ -330,7 +333,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
           // A fragments from the LDS copy; rows past M read row 0 (their results are never stored)
           const int xrow = c < M ? c : 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) xr[u][gs][0][q] = lds_x[w][u][xrow][16 * gs + 4 * q + j];
+          for (int q = 0; q < 4; ++q) xr[u][gs][0][q] = lds_x[w][u % XS][xrow][16 * gs + 4 * q + j];
         }
         // sum of x over each quantization group's steps (for the zero)
         float4_t sx[NF4 ? 1 : MT][SUB];
@@ -455,13 +458,24 @@ hipError_t launch_tile_x(const Args& a) {
 }
 
 // M <= 8 (MT = 1): x rows through LDS in M/2 full-width loads; otherwise 16-row fragment loads
-// (two column tiles with groups of 32 meet M <= 8 in two-stage chunks only)
+// (two column tiles with groups of 32 meet M <= 8 in two-stage chunks only). 4-bit integer
+// codes take the LDS route for 12 <= M <= 16 too (eight loads for 16 rows), and 3-bit codes at
+// M = 16; measured on MI355X against the fragment loads (same-process interleaved replays,
+// outputs bit-identical), 4-bit groups of 128 at M = 16: 14.5 against 16.1 us at 8192 x 8192,
+// 14.4 against 16.4 at 4096 -> 11008, 13.7 against 15.7 at 11008 -> 4096, 5.9 against 7.1 at
+// 4096 x 4096, 37.9 against 43.7 at 8192 -> 22016, 42.7 against 44.4 at 22016 -> 8192;
+// at M = 12 4-6 % faster on most shapes; at M = 9 up to 5 % slower (eight loads for nine rows);
+// 3-bit codes at M = 16 1-18 % faster, at M = 12 mixed; NF4 at M = 16 from 8 % faster to 4 %
+// slower, so NF4 keeps the fragment loads.
 template <int NTW, int MT, int NS, int SUB, int FMT>
 hipError_t launch_tile(const Args& a) {
   if constexpr (MT == 1 && !(NTW == 2 && SUB == 4 && NS > 2)) {
     if (a.M <= 2) return launch_tile_x<NTW, MT, NS, 1, SUB, FMT>(a);
     if (a.M <= 4) return launch_tile_x<NTW, MT, NS, 2, SUB, FMT>(a);
     if (a.M <= 8) return launch_tile_x<NTW, MT, NS, 4, SUB, FMT>(a);
+    if constexpr (FMT != kFmtNf4) {
+      if (a.M >= (FMT == kFmt3 ? 16 : 12) && a.M <= 16) return launch_tile_x<NTW, MT, NS, 8, SUB, FMT>(a);
+    }
   }
   return launch_tile_x<NTW, MT, NS, 0, SUB, FMT>(a);
 }
