@@ -229,13 +229,15 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
  * workspace_bytes >= w4a16_linear_workspace(M, N, K, group) bytes, 16-byte
  * aligned, overwritten (two calls in flight at once need two workspaces).
  * Dispatch, groups of 128 with a workspace (from measured sweeps over the
- * LLaMA projection shapes): no split for M <= 20; else with G = K / 128 and T
+ * LLaMA projection shapes): no split for M <= 16; else with G = K / 128 and T
  * the split-K kernel's tiles (ceil(N / 128) for M <= 32, else ceil(M / 64) *
- * ceil(N / 128)), for K >= 8192 the largest S of 8, 4, 2 with S * T < 1024
+ * ceil(N / 128)), for K >= 8192: no split up to M = 32 when K <= 16384 and
+ * ceil(N / 32) is a multiple of 256 (the small-batch kernel's grid fills the
+ * chip in whole rounds), else the largest S of 8, 4, 2 with S * T < 1024
  * (S * T <= 256 when T <= 64) and G / S >= 8, none if only S = 1 remains (the
  * automatic choice of w4a16_linear, which needs no workspace, covers those);
- * for 4096 <= K < 8192, S = 2 on 65..128 tiles and S = 4 on at most
- * 48 tiles at M > 32; otherwise no split
+ * for 4096 <= K < 8192 from M = 21, S = 2 on 65..128 tiles and S = 4 on at
+ * most 48 tiles at M > 32; otherwise no split
  * (w4a16_linear_ws_splits reports the choice). With S > 0 the call launches the
  * two split-K kernels, else w4a16_linear's. Results are reproducible (fixed
  * summation order for a given shape).

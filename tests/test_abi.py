@@ -246,12 +246,14 @@ def test_splitk_workspace_and_rejects():
 def test_linear_ws_split_choice_and_rejects():
     lib = w4.load()
     # the automatic path's split choice with a workspace (4-bit, groups of 128): no split at
-    # M <= 20 and below K = 4096; else the largest S of 8, 4, 2 with S * tiles < 1024 (<= 256
-    # on up to 64 tiles; tiles are 32 x 128 up to M = 32, else 64 x 128) and >= 8 groups per
-    # range (K >= 8192), none where only one range would be left (the automatic path without a
-    # workspace takes those), or two ranges on 65..128 tiles / four on <= 48 at M > 32
-    # (4096 <= K < 8192)
-    cases = {(1, 8192, 8192): 0, (16, 4096, 11008): 0, (20, 4096, 11008): 0, (32, 8192, 8192): 4, (24, 8192, 8192): 4,
+    # M <= 16 and below K = 4096; for K >= 8192 none up to M = 32 on rows of at most 16384
+    # where ceil(N / 32) is a multiple of 256, else the largest S of 8, 4, 2 with
+    # S * tiles < 1024 (<= 256 on up to 64 tiles; tiles are 32 x 128 up to M = 32, else
+    # 64 x 128) and >= 8 groups per range, none where only one range would be left (the
+    # automatic path without a workspace takes those); for 4096 <= K < 8192 from M = 21, two
+    # ranges on 65..128 tiles / four on <= 48 at M > 32
+    cases = {(1, 8192, 8192): 0, (16, 4096, 11008): 0, (20, 4096, 11008): 8, (32, 8192, 8192): 0, (24, 8192, 8192): 0,
+             (20, 11008, 4096): 0, (17, 8192, 22016): 4, (32, 16384, 8192): 0,
              (32, 4096, 11008): 8, (32, 8192, 22016): 4, (24, 22016, 8192): 4, (32, 11008, 4096): 2,
              (32, 4096, 4096): 0,
              (64, 4096, 11008): 8, (128, 4096, 11008): 4, (256, 4096, 11008): 4, (512, 4096, 11008): 2,

@@ -310,10 +310,10 @@ def test_auto_klane_route(lib, m, k, n):
 
 @pytest.mark.parametrize("m,k,n", [(64, 11008, 4096), (256, 4096, 4096), (48, 4096, 11008), (32, 22016, 8192),
                                    (24, 11008, 4096), (256, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024),
-                                   (32, 8192, 8192), (21, 8192, 22016), (30, 4096, 11008)])
+                                   (20, 11008, 4096), (21, 8192, 22016), (30, 4096, 11008), (17, 22016, 8192)])
 def test_auto_with_workspace_takes_split_k(lib, m, k, n):
     # the automatic path with a workspace (w4a16_linear_ws, the binding's default): shapes where
-    # it splits K (8, 2, 2, 4, 8, 2, 4, 8, 4, 4 and 2 ranges; the 32-row tiles of the partial
+    # it splits K (8, 2, 2, 4, 8, 2, 4, 8, 8, 4, 2 and 4 ranges; the 32-row tiles of the partial
     # kernel up to M = 32): every output against the oracle, and
     # bit-identical to the split-K entry point with the same ranges
     g = _gpu()

@@ -97,30 +97,36 @@ bool auto_klane_small(int64_t M, int64_t K) { return M > 16 && M <= w4a16::skinn
 
 // The automatic path's split-K choice when the caller lends a workspace (4-bit codes, groups
 // of 128): the number of K ranges, or 0 for the kernels of w4a16_linear. No split up to
-// M = 20. Over K >= 8192: the largest S of 8, 4, 2, 1 with S * tiles < 1024 (at most 256 on
-// up to 64 tiles) and at least 8 groups per range (a single range is left to the automatic
-// path without a workspace, which runs the one-range kernel itself where it is ahead). Over
-// 4096 <= K < 8192: two ranges on 65..128 tiles, four on at most 48 tiles at M > 32. Tiles
-// are the partial kernel's (32 x 128 up to M = 32, else 64 x 128). From sweeps of M = 12..512
-// over nine layer shapes (MI355X, graph-timed us, split-K / the automatic path without a
-// workspace): 11008 -> 4096 at M = 32 17.5 (S = 8) / 25.7, at M = 64 20.2 / 34.1 and at
-// M = 256 47.9 (S = 4) / 54.0; 22016 -> 8192 at M = 32 43.7 / 60.0, at M = 128 90.0 / 109.3
-// and at M = 512 299.8 (one range, with a separate reduction then) / 367.6; 8192 -> 8192 at
-// M = 32 21.7 / 23.5 and at M = 128 42.3 / 48.0; 8192 -> 1024 at M = 32 12.6 / 18.9;
-// 4096 -> 4096 at M = 256 23.4 (S = 2) / 26.0; 4096 -> 11008 at M = 32 19.0 / 24.4. On 64
-// tiles four ranges beat eight (8192 -> 8192 at M = 64 25.8 / 28.8). Up to M = 16 the
-// small-batch kernel stays ahead on most shapes (8192 -> 8192 at M = 16: 20.8 / 16.2). The
-// rule costs up to 4 % where it misjudges
-// (8192 -> 22016 at M = 128: 102.4 / 98.2; 8192 -> 8192 at M = 24: 21.3 / 20.8).
+// M = 16. Over K >= 8192: up to M = 32, none on rows of at most 16384 inputs where the
+// small-batch kernel's grid fills the chip in whole rounds (below); else the largest S of 8,
+// 4, 2 with S * tiles < 1024 (at most 256 on up to 64 tiles) and at least 8 groups per range
+// (a single range is left to the automatic path without a workspace, which runs the one-range
+// kernel itself where it is ahead). Over 4096 <= K < 8192, from M = 21: two ranges on
+// 65..128 tiles, four on at most 48 tiles at M > 32. Tiles are the partial kernel's (32 x 128
+// up to M = 32, else 64 x 128). From sweeps of M = 12..512 over nine layer shapes (MI355X,
+// graph-timed us, split-K / the automatic path without a workspace): 22016 -> 8192 at M = 17
+// 42.1 (S = 4) / 56.8, at M = 32 43.5 / 60.3, at M = 128 90.0 / 109.3; 28672 -> 8192 at
+// M = 17 58.5 / 79.1; 11008 -> 4096 at M = 17 15.2 (S = 8) / 16.8, at M = 64 20.2 / 34.1
+// and at M = 256 47.9 (S = 4) / 54.0; 8192 -> 22016 at M = 20 49.9 / 53.0; 8192 -> 8192 at
+// M = 128 42.3 / 48.0; 8192 -> 1024 at M = 32 11.0 / 14.7; 4096 -> 4096 at M = 256 23.4
+// (S = 2) / 26.0; 4096 -> 11008 at M = 32 19.0 / 20.8. On 64 tiles four ranges beat eight
+// (8192 -> 8192 at M = 64 25.8 / 28.8). Up to M = 16 the small-batch kernel stays ahead on
+// most shapes (8192 -> 8192 at M = 16: 20.8 / 14.5). The rule costs up to 5 % where it
+// misjudges (8192 -> 22016 at M = 128: 102.4 / 98.2; 8192 -> 28672 at M = 32: 68.1 with
+// four ranges against 65.4 with two).
 int auto_splits(int64_t M, int64_t N, int64_t K) {
-  if (M <= 20) return 0;
+  if (M <= 16) return 0;
   const int64_t tiles = w4a16::splitk_tiles(M, N), G = K / 128;
   if (K >= 8192) {
+    // up to M = 32 on rows of at most 16384 inputs, the small-batch kernel wherever its
+    // 32-column workgroups fill the 256 CUs in whole rounds (8192 -> 8192 at M = 21 / 32:
+    // 19.4 / 21.1 against 20.8 / 21.4 us with four ranges)
+    if (M <= 32 && K <= 16384 && ((N + 31) / 32) % 256 == 0) return 0;
     int s = 8;
     while (s > 1 && (tiles * s >= (tiles <= 64 ? 257 : 1024) || G / s < 8)) s >>= 1;
     return s == 1 ? 0 : s;  // one range: the automatic choice without a workspace covers it
   }
-  if (K >= 4096) {
+  if (K >= 4096 && M > 20) {
     if (tiles > 64 && tiles <= 128) return 2;
     if (M > 32 && tiles <= 48) return 4;
   }

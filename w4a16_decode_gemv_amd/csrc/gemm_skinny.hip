@@ -237,26 +237,36 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
           cr[slot][2 * nt + h] = __builtin_amdgcn_raw_buffer_load_b128(q_rsrc, off + (16 * nt + 8 * h + lr) * (K >> 1), 0,
                                                                        kNonTemporal);
     };
-    auto load_x = [&](int s, int slot) {
+    // x rows 0 .. 2 XI - 1 in full-width loads (to LDS, stored before the compute), and the
+    // 16-row fragment loads of the m-tiles not taken through LDS: all of them when XI = 0, the
+    // second when XI > 0 and MT = 2 (those land in the registers the compute reads, so the next
+    // stage's are issued after it)
+    constexpr int MT0 = XI > 0 ? 1 : 0;
+    auto load_x_rows = [&](int s, int slot) {
       if constexpr (XI > 0) {
         const int gi = 2 * s + ((lane & 31) >> 4);
         const int off = (g0 + 2 * s) * 256 + 16 * (lane & 31) + bias(gi);
 #pragma unroll
         for (int i = 0; i < XI; ++i)
           xl[slot][i] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, off + (2 * i + (lane >> 5)) * K * 2, 0, 0);
-        return;
       }
+    };
+    auto load_x_frag = [&](int s, int slot) {
 #pragma unroll
       for (int gs = 0; gs < 2; ++gs) {
         const int gi = 2 * s + gs;
         const int off = (g0 + gi) * 256 + 16 * j + bias(gi);
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
+        for (int mt = MT0; mt < MT; ++mt) {
           const int o = (16 * mt + c) * K * 2 + off;  // rows past M: out of range (buffer size M * K * 2)
 #pragma unroll
           for (int q = 0; q < 4; ++q) xr[slot][gs][mt][q] = __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, o + 64 * q, 0, 0);
         }
       }
+    };
+    auto load_x = [&](int s, int slot) {
+      load_x_rows(s, slot);
+      load_x_frag(s, slot);
     };
 #pragma unroll
     for (int s = 0; s < D && s < NS; ++s) {
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
       }
       if (s + D < NS) load_codes(s + D, u);
       if constexpr (XI > 0) {
-        if (s + D < NS) load_x(s + D, u);
+        if (s + D < NS) load_x_rows(s + D, u);
       }
       __builtin_amdgcn_sched_barrier(0);
 
@@ -405,8 +415,8 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(const uint16_t* __rest
         // per-group sums and scales no longer fit in registers
         if constexpr (SUB > 1) __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (XI == 0) {
-        if (s + D < NS) load_x(s + D, u);
+      if constexpr (MT0 < MT) {
+        if (s + D < NS) load_x_frag(s + D, u);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -473,10 +483,14 @@ hipError_t launch_tile(const Args& a) {
     if (a.M <= 2) return launch_tile_x<NTW, MT, NS, 1, SUB, FMT>(a);
     if (a.M <= 4) return launch_tile_x<NTW, MT, NS, 2, SUB, FMT>(a);
     if (a.M <= 8) return launch_tile_x<NTW, MT, NS, 4, SUB, FMT>(a);
-    if constexpr (FMT != kFmtNf4) {
+    if constexpr (FMT != kFmtNf4 && !(FMT == kFmt3 && NS > 6)) {  // 3-bit eight-stage chunks would spill
       if (a.M >= (FMT == kFmt3 ? 16 : 12) && a.M <= 16) return launch_tile_x<NTW, MT, NS, 8, SUB, FMT>(a);
     }
   }
+  // two m-tiles, 4-bit integer codes: the first m-tile's x rows through LDS, the second's as
+  // fragment loads, wherever the variant fits the registers (one column tile, or two with
+  // two-stage chunks; two tiles with longer chunks spill 200-400 bytes per lane)
+  if constexpr (MT == 2 && FMT == kFmt4 && (NTW == 1 || NS == 2)) return launch_tile_x<NTW, MT, NS, 8, SUB, FMT>(a);
   return launch_tile_x<NTW, MT, NS, 0, SUB, FMT>(a);
 }
 
@@ -543,6 +557,9 @@ hipError_t launch_format(const Args& a) {
     if (M <= 16) return launch_stages<2, 1, SUB, FMT, 8>(a);
     if constexpr (SUB == 1 && FMT == kFmt4) {
       const bool short_k = ((a.K / 128 + KS - 1) / KS + 1) / 2 <= 4;
+      // from M = 24 two-stage chunks, which take the x route above (8192 x 8192 at M = 32:
+      // 20.9 against 23.6 us; at M = 17 the longer chunks stay ahead, 18.1 against 19.2)
+      if (short_k && M >= 24) return launch_stages<2, 2, SUB, FMT, 2>(a);
       return short_k ? launch_stages<2, 2, SUB, FMT, 8>(a) : launch_stages<1, 2, SUB, FMT, 8>(a);
     } else {
       return launch_stages<2, 2, SUB, FMT, zp ? 2 : 8>(a);
