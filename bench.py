@@ -75,7 +75,11 @@ def parse():
     p.add_argument("--only-m", type=int, default=0,
                    help="time only the automatic path (or --path) at this batch M, K = N = 8192 (for profilers)")
     p.add_argument("--path", type=int, default=0,
-                   help="with --only-m: the kernel (0 auto, 1 GEMV, 2 tiled MFMA, 3 small-batch MFMA, 4 K-lane MFMA)")
+                   help="with --only-m: the kernel (0 auto, 1 GEMV, 2 tiled MFMA, 3 small-batch MFMA, 4 K-lane MFMA, "
+                        "6 x-resident MFMA)")
+    p.add_argument("--small-batch-shapes", action="store_true",
+                   help="also time M = 4..32 on nine LLaMA layer shapes: the automatic path, the small-batch MFMA "
+                        "kernel and the x-resident MFMA kernel")
     p.add_argument("--only-serving", default="",
                    help="time only one LLaMA2-7B serving GEMM, LAYER:M with LAYER in qkvo,gate,down (the 4096->4096, "
                         "4096->11008, 11008->4096 shapes) and M in 128,256, on the tiled, K-lane and split-K kernels "
@@ -284,6 +288,32 @@ def read_floor_leg(torch, w4, nbytes, copies, gemv_ms, steps, warmup):
     res["note"] = ("single-launch reads of the GEMV's bytes by several patterns, timed like the GEMV; the best of "
                    "them is the practical ceiling of one launch of this size on this device")
     return res
+
+
+def small_batch_shapes_leg(w4, torch):
+    """M = 4..32 on nine LLaMA projection shapes (4-bit groups of 128), graph-timed: the automatic
+    path with a workspace (the binding's default), the small-batch MFMA kernel and the
+    x-resident MFMA kernel. One JSON row per shape and M, also printed to stderr as it lands."""
+    shapes = [(8192, 8192), (4096, 4096), (4096, 11008), (11008, 4096), (8192, 22016), (22016, 8192),
+              (8192, 28672), (28672, 8192), (8192, 1024)]
+    rows = []
+    for k, n in shapes:
+        for mm in (4, 8, 12, 16, 20, 24, 32):
+            b = algorithmic_bytes(mm, n, k)
+            L = Layer(w4, torch, 4, 0, n, k, mm, copies_for(b))
+            r = {"K": k, "N": n, "M": mm, "bytes": b}
+            r["auto_us"] = time_graph(torch, lambda i: L.call(w4, i, 0), 100) * 1e3
+            r["small_batch_us"] = time_graph(torch, lambda i: L.call(w4, i, 3), 100) * 1e3
+            need = w4.xres_workspace_bytes(mm, n, k)
+            ws = torch.empty(max(1, need // 4), dtype=torch.float32, device=L.x.device)
+            r["xres_us"] = time_graph(torch, lambda i: w4.linear_xres(*L.copies[i % len(L.copies)], workspace=ws,
+                                                                      out=L.y[i % len(L.y)]), 100) * 1e3
+            r["xres_ranges"] = -(-k // 2048)
+            rows.append(r)
+            print(json.dumps(r), file=sys.stderr, flush=True)
+            del L, ws
+            torch.cuda.empty_cache()
+    return rows
 
 
 def block_leg(w4, torch):
@@ -535,7 +565,13 @@ def main():
         mm = args.only_m
         b = algorithmic_bytes(mm, 8192, 8192)
         L = Layer(w4, torch, 4, 0, 8192, 8192, mm, copies_for(b))
-        t = time_steps_queued(torch, lambda i: L.call(w4, i, args.path), args.steps, args.warmup)
+        if args.path == 6:
+            ws = torch.empty(max(1, w4.xres_workspace_bytes(mm, 8192, 8192) // 4), dtype=torch.float32,
+                             device=L.x.device)
+            t = time_steps_queued(torch, lambda i: w4.linear_xres(*L.copies[i % len(L.copies)], workspace=ws,
+                                                                  out=L.y[i % len(L.y)]), args.steps, args.warmup)
+        else:
+            t = time_steps_queued(torch, lambda i: L.call(w4, i, args.path), args.steps, args.warmup)
         res = {"M": mm, "K": 8192, "N": 8192, "path": args.path, "us_per_call": t * 1e3, "GB_s": b / (t * 1e-3) / 1e9,
                "algorithmic_bytes_per_call": b}
         if args.copy_probe:
@@ -652,6 +688,9 @@ def main():
             del L
             torch.cuda.empty_cache()
         out["sweep_k8192_n8192"] = rows
+
+    if args.small_batch_shapes:
+        out["small_batch_shapes"] = small_batch_shapes_leg(w4, torch)
 
     if args.block:
         out["llama2_7b_block"] = block_leg(w4, torch)

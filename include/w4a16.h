@@ -220,7 +220,17 @@ int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t group);
 int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
 
 /*
+ * w4a16_linear_ws_kernel - the kernel w4a16_linear_ws runs for this shape when
+ * given its workspace, with scales and zeros 4-byte aligned: 0 = w4a16_linear's
+ * choice, 1 = the split-K kernels (w4a16_linear_ws_splits ranges), 2 = the
+ * x-resident kernel (w4a16_linear_xres); -1 when the shape or group is not
+ * accepted. Host only.
+ */
+int32_t w4a16_linear_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group);
+
+/*
  * w4a16_linear_ws - w4a16_linear whose automatic choice may also take the
+ * x-resident small-batch kernel (w4a16_linear_xres) and the
  * split-K kernels (w4a16_linear_splitk) when the caller lends a workspace, for
  * batched layers with too few output tiles to fill the chip (CMU guide: at
  * large batch the layer is compute-bound; L13 TinyChat kernel fusion). Same
@@ -229,7 +239,11 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
  * workspace_bytes >= w4a16_linear_workspace(M, N, K, group) bytes, 16-byte
  * aligned, overwritten (two calls in flight at once need two workspaces).
  * Dispatch, groups of 128 with a workspace (from measured sweeps over the
- * LLaMA projection shapes): no split for M <= 16; else with G = K / 128 and T
+ * LLaMA projection shapes): the x-resident kernel when K > 2048, K / 128 is even, scales
+ * and zeros are 4-byte aligned and, with W = ceil(N / 128) * ceil(K / 2048) its
+ * workgroups, 8 <= M <= 32 with W >= 512, 12 <= M <= 32 with N > K and
+ * W >= 160, or 16 <= M <= 32 with W >= 256; otherwise split-K: no split for
+ * M <= 16; else with G = K / 128 and T
  * the split-K kernel's tiles (ceil(N / 128) for M <= 32, else ceil(M / 64) *
  * ceil(N / 128)), for K >= 8192: no split up to M = 32 when K <= 16384 and
  * ceil(N / 32) is a multiple of 256 (the small-batch kernel's grid fills the
@@ -238,9 +252,10 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group);
  * automatic choice of w4a16_linear, which needs no workspace, covers those);
  * for 4096 <= K < 8192 from M = 21, S = 2 on 65..128 tiles and S = 4 on at
  * most 48 tiles at M > 32; otherwise no split
- * (w4a16_linear_ws_splits reports the choice). With S > 0 the call launches the
- * two split-K kernels, else w4a16_linear's. Results are reproducible (fixed
- * summation order for a given shape).
+ * (w4a16_linear_ws_splits reports the split-K choice, w4a16_linear_ws_kernel
+ * the kernel). With S > 0 the call launches the two split-K kernels, else
+ * w4a16_linear's. Results are reproducible (fixed summation order for a given
+ * shape).
  * Errors: those of w4a16_linear; W4A16_ERR_ARG (workspace too small for the
  * split chosen); W4A16_ERR_ALIGN (workspace). Checked before any HIP call.
  */
@@ -293,6 +308,38 @@ int64_t w4a16_linear_splitk_workspace(int64_t M, int64_t N, int64_t K, int32_t s
 w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void* scales, const void* zeros,
                                  int64_t M, int64_t N, int64_t K, int32_t group, int32_t splits,
                                  void* workspace, int64_t workspace_bytes, void* y, void* stream);
+
+/*
+ * w4a16_linear_xres_workspace - bytes of float32 workspace that
+ * w4a16_linear_xres needs for this shape (0 when K <= 2048: one K range, no
+ * workspace); -1 when the shape is not accepted (M > 32, or an odd number of
+ * groups of 128 per row).
+ */
+int64_t w4a16_linear_xres_workspace(int64_t M, int64_t N, int64_t K);
+
+/*
+ * w4a16_linear_xres - w4a16_linear (4-bit, groups of 128) for small batches,
+ * 1 <= M <= 32, on the x-resident MFMA kernel: a workgroup owns 128 output
+ * columns and one range of 2048 inputs; each of its eight waves keeps the x
+ * fragments of its 256 inputs in registers and streams the codes of the 128
+ * columns past them, so x crosses from L2 once per 128 columns instead of once
+ * per 32 (CMU guide, "where the speed comes from": small-batch decode stays
+ * bound by the weight stream; L13 TinyChat kernel fusion). The S = ceil(K / 2048)
+ * ranges' float32 partials go to `workspace` and a second kernel adds them in
+ * index order and rounds once to fp16 (reproducible); with one range the first
+ * kernel writes y itself. Same formula, accuracy contract and arguments as
+ * w4a16_linear, plus workspace: device memory of workspace_bytes >=
+ * w4a16_linear_xres_workspace(M, N, K) bytes, 16-byte aligned, overwritten
+ * (NULL allowed when that is 0; two calls in flight at once need two
+ * workspaces). Needs (K / 128) even; scales and zeros 4-byte aligned.
+ * Errors: those of w4a16_linear; W4A16_ERR_UNSUPPORTED (group != 128, M > 32,
+ * odd group count); W4A16_ERR_NULL (workspace needed); W4A16_ERR_ARG
+ * (workspace too small); W4A16_ERR_ALIGN (workspace, scales, zeros). Checked
+ * before any HIP call.
+ */
+w4a16_status w4a16_linear_xres(const void* x, const void* qweight, const void* scales, const void* zeros,
+                               int64_t M, int64_t N, int64_t K, int32_t group, void* workspace,
+                               int64_t workspace_bytes, void* y, void* stream);
 
 /*
  * w4a16_linear_splitk_noalloc - w4a16_linear_splitk for callers that cannot

@@ -243,6 +243,29 @@ def test_splitk_workspace_and_rejects():
     assert call(K=200) == w4.ERR_SHAPE
 
 
+def test_xres_workspace_and_rejects():
+    lib = w4.load()
+    # ranges of 2048 inputs: S = ceil(K / 2048) float32 partials of M x N, none for one range
+    assert lib.w4a16_linear_xres_workspace(32, 8192, 8192) == 4 * 32 * 8192 * 4
+    assert lib.w4a16_linear_xres_workspace(16, 4096, 11008) == 6 * 16 * 4096 * 4
+    assert lib.w4a16_linear_xres_workspace(32, 4096, 2048) == 0
+    assert lib.w4a16_linear_xres_workspace(33, 4096, 4096) == -1   # M > 32
+    assert lib.w4a16_linear_xres_workspace(8, 4096, 384) == -1     # odd number of groups
+    assert lib.w4a16_linear_xres_workspace(0, 4096, 4096) == -1
+
+    def call(group=128, ws=A16, wb=1 << 30, M=32, K=8192, sc=A16):
+        return lib.w4a16_linear_xres(A16, A16, sc, A16, M, 4096, K, group, ws, wb, A16, None)
+
+    assert call(group=64) == w4.ERR_UNSUPPORTED
+    assert call(M=33) == w4.ERR_UNSUPPORTED
+    assert call(K=384) == w4.ERR_UNSUPPORTED
+    assert call(ws=None) == w4.ERR_NULL
+    assert call(wb=100) == w4.ERR_ARG
+    assert call(ws=A16 + 8) == w4.ERR_ALIGN
+    assert call(sc=A16 + 2) == w4.ERR_ALIGN
+    assert call(K=200) == w4.ERR_SHAPE
+
+
 def test_linear_ws_split_choice_and_rejects():
     lib = w4.load()
     # the automatic path's split choice with a workspace (4-bit, groups of 128): no split at
@@ -261,9 +284,24 @@ def test_linear_ws_split_choice_and_rejects():
              (192, 22016, 8192): 0, (128, 22016, 8192): 2, (64, 1024, 8192): 8,
              (256, 4096, 4096): 2, (192, 4096, 4096): 2, (128, 4096, 4096): 0, (64, 4096, 4096): 4,
              (48, 11008, 4096): 2, (128, 11008, 4096): 0, (64, 8192, 1024): 0, (64, 64, 2048): 0}
+    # the x-resident kernel (8 <= M <= 32, K > 2048; with W = ceil(N / 128) * ceil(K / 2048) its
+    # workgroups: W >= 512, or M >= 12 with N > K and W >= 160, or M >= 16 with W >= 256); the
+    # workspace covers both kernels' needs
+    xres = {(32, 8192, 8192), (24, 8192, 8192), (20, 11008, 4096), (17, 8192, 22016), (32, 16384, 8192),
+            (32, 8192, 22016), (24, 22016, 8192), (32, 11008, 4096), (12, 11008, 4096), (16, 8192, 8192),
+            (8, 8192, 22016), (8, 28672, 8192)}
+    for extra in ((12, 11008, 4096), (12, 8192, 8192), (16, 8192, 8192), (8, 8192, 22016), (8, 28672, 8192),
+                  (4, 8192, 22016), (8, 11008, 4096)):
+        cases[extra] = 0
     for (m, n, k), s in cases.items():
         assert lib.w4a16_linear_ws_splits(m, n, k, 128) == s, (m, n, k)
-        assert lib.w4a16_linear_workspace(m, n, k, 128) == s * m * n * 4, (m, n, k)
+        want_x = (m, n, k) in xres
+        assert lib.w4a16_linear_ws_kernel(m, n, k, 128) == (2 if want_x else 1 if s else 0), (m, n, k)
+        xf = -(-k // 2048) * m * n if want_x and k > 2048 else 0
+        assert lib.w4a16_linear_workspace(m, n, k, 128) == max(s * m * n, xf) * 4, (m, n, k)
+    assert lib.w4a16_linear_ws_kernel(32, 8192, 8192, 64) == 0
+    assert lib.w4a16_linear_ws_kernel(32, 8192, 8320, 128) == 0   # odd number of groups
+    assert lib.w4a16_linear_ws_kernel(16, 20480, 2048, 128) == 0  # one K range: not on this path
     assert lib.w4a16_linear_ws_splits(256, 4096, 11008, 64) == 0   # split-K takes groups of 128 only
     assert lib.w4a16_linear_workspace(256, 4096, 11008, 32) == 0
     assert lib.w4a16_linear_workspace(0, 4096, 4096, 128) == -1

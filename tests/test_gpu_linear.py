@@ -308,17 +308,17 @@ def test_auto_klane_route(lib, m, k, n):
     assert np.array_equal(g.bits16(a), g.bits16(b))
 
 
-@pytest.mark.parametrize("m,k,n", [(64, 11008, 4096), (256, 4096, 4096), (48, 4096, 11008), (32, 22016, 8192),
-                                   (24, 11008, 4096), (256, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024),
-                                   (20, 11008, 4096), (21, 8192, 22016), (30, 4096, 11008), (17, 22016, 8192)])
+@pytest.mark.parametrize("m,k,n", [(64, 11008, 4096), (256, 4096, 4096), (48, 4096, 11008), (24, 11008, 4096),
+                                   (256, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024), (20, 11008, 4096),
+                                   (32, 11008, 4096)])
 def test_auto_with_workspace_takes_split_k(lib, m, k, n):
     # the automatic path with a workspace (w4a16_linear_ws, the binding's default): shapes where
-    # it splits K (8, 2, 2, 4, 8, 2, 4, 8, 8, 4, 2 and 4 ranges; the 32-row tiles of the partial
-    # kernel up to M = 32): every output against the oracle, and
-    # bit-identical to the split-K entry point with the same ranges
+    # it splits K (8, 2, 2, 8, 2, 4, 8, 8 and 2 ranges; the 32-row tiles of the partial kernel up
+    # to M = 32): every output against the oracle, and bit-identical to the split-K entry point
+    # with the same ranges
     g = _gpu()
     splits = lib.linear_ws_splits(m, n, k)
-    assert splits > 0
+    assert splits > 0 and lib.linear_ws_kernel(m, n, k) == 1
     xs, qw, sc, zr = _packed(8, 3, n, k, m)
     _check(lib, xs, qw, sc, zr, path=0, tag=f"auto-ws-S{splits}")
     dev = [g.dev(t) for t in (xs, qw, sc, zr)]
@@ -329,6 +329,28 @@ def test_auto_with_workspace_takes_split_k(lib, m, k, n):
     import torch
 
     ws = torch.empty(lib.linear_workspace_bytes(m, n, k) // 4, dtype=torch.float32, device=g.DEV)
+    c = g.host(lib.linear(*dev, workspace=ws))
+    assert np.array_equal(g.bits16(a), g.bits16(c))
+
+
+@pytest.mark.parametrize("m,k,n", [(32, 22016, 8192), (21, 8192, 22016), (30, 4096, 11008), (17, 22016, 8192),
+                                   (12, 4096, 11008), (24, 8192, 8192), (16, 4096, 20480), (8, 22016, 8192),
+                                   (16, 8192, 8192)])
+def test_auto_with_workspace_takes_x_resident(lib, m, k, n):
+    # shapes where the automatic path with a workspace runs the x-resident small-batch kernel:
+    # every output against the oracle,
+    # bit-identical to its own entry point, and with a workspace of exactly the size asked for
+    g = _gpu()
+    assert lib.linear_ws_kernel(m, n, k) == 2
+    xs, qw, sc, zr = _packed(8, 4, n, k, m)
+    _check(lib, xs, qw, sc, zr, path=0, tag="auto-ws-x-resident")
+    dev = [g.dev(t) for t in (xs, qw, sc, zr)]
+    a = g.host(lib.linear(*dev))
+    b = g.host(lib.linear_xres(*dev))
+    assert np.array_equal(g.bits16(a), g.bits16(b))
+    import torch
+
+    ws = torch.empty(max(1, lib.linear_workspace_bytes(m, n, k) // 4), dtype=torch.float32, device=g.DEV)
     c = g.host(lib.linear(*dev, workspace=ws))
     assert np.array_equal(g.bits16(a), g.bits16(c))
 

@@ -54,11 +54,14 @@ def load():
         "w4a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w4a16_linear_workspace": ([i64, i64, i64, i32], i64),
         "w4a16_linear_ws_splits": ([i64, i64, i64, i32], i32),
+        "w4a16_linear_ws_kernel": ([i64, i64, i64, i32], i32),
         "w4a16_linear_ws": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
         "awq_alpha_loss_workspace": ([i64, i64], i64),
         "w4a16_linear_splitk_workspace": ([i64, i64, i64, i32], i64),
         "w4a16_linear_splitk": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, i64, vp, vp], i32),
         "w4a16_linear_splitk_noalloc": ([vp, vp, vp, vp, i64, i64, i64, i32, i32, vp, vp], i32),
+        "w4a16_linear_xres_workspace": ([i64, i64, i64], i64),
+        "w4a16_linear_xres": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, i64, vp, vp], i32),
         "w3a16_linear": ([vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "w3a16_linear_path": ([i32, vp, vp, vp, vp, i64, i64, i64, i32, vp, vp], i32),
         "awq_quantize_pack_sym": ([vp, vp, i64, i64, i32, i32, vp, vp, vp, vp], i32),
@@ -85,9 +88,10 @@ def load():
 def exported_symbols():
     return ["w4a16_layout_version", "w4a16_status_str", "w4a16_last_error", "w4a16_gemv_max_m",
             "awq_channel_scale", "awq_scale_input", "awq_rmsnorm_fold", "awq_quantize_pack", "w4a16_linear",
-            "w4a16_linear_path", "w4a16_linear_workspace", "w4a16_linear_ws_splits", "w4a16_linear_ws",
-            "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w4a16_linear_splitk_noalloc", "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook",
-            "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
+            "w4a16_linear_path", "w4a16_linear_workspace", "w4a16_linear_ws_splits", "w4a16_linear_ws_kernel",
+            "w4a16_linear_ws",
+            "w4a16_linear_splitk_workspace", "w4a16_linear_splitk", "w4a16_linear_splitk_noalloc", "w4a16_linear_xres_workspace", "w4a16_linear_xres",
+            "w3a16_linear", "w3a16_linear_path", "awq_quantize_pack_sym", "nf4_codebook", "nf4_quantize_pack", "nf4_linear", "nf4_linear_path", "awq_alpha_loss_workspace", "awq_output_reference",
             "awq_alpha_loss", "w4a16_stream_read_sink_bytes", "w4a16_stream_read", "w4a16_stream_read_grid",
             "awq_search_alpha_workspace", "awq_search_alpha"]
 
@@ -252,6 +256,15 @@ def linear_ws_splits(M, N, K, group=GROUP):
     return n
 
 
+def linear_ws_kernel(M, N, K, group=GROUP):
+    """The kernel the automatic 4-bit path runs when given its workspace: 0 the no-workspace
+    choice, 1 split-K, 2 the x-resident kernel."""
+    n = int(load().w4a16_linear_ws_kernel(int(M), int(N), int(K), int(group)))
+    if n < 0:
+        raise ValueError(f"M={M}, N={N}, K={K}, group={group} outside the limits of the linear call")
+    return n
+
+
 def linear_splitk(x, qweight, scales, zeros, splits=0, workspace=None, out=None, group=GROUP):
     """``linear`` (4-bit, groups of 128) on the split-K MFMA kernel; workspace: a float32 device
     tensor of at least splitk_workspace_bytes(M, N, K, splits) bytes (allocated when omitted)."""
@@ -294,6 +307,40 @@ def linear_splitk_noalloc(x, qweight, scales, zeros, out, splits=0, group=GROUP)
     y = _out(out, (m, n), torch.float16, x)
     _check(lib.w4a16_linear_splitk_noalloc(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m,
                                            n, k, group, splits, y.data_ptr(), _stream(x)))
+    return y
+
+
+def xres_workspace_bytes(M, N, K):
+    n = int(load().w4a16_linear_xres_workspace(int(M), int(N), int(K)))
+    if n < 0:
+        raise ValueError(f"shape M={M} N={N} K={K} is not accepted by the x-resident kernel")
+    return n
+
+
+def linear_xres(x, qweight, scales, zeros, workspace=None, out=None, group=GROUP):
+    """``linear`` (4-bit, groups of 128, M <= 32) on the x-resident MFMA kernel; workspace: a
+    float32 device tensor of at least xres_workspace_bytes(M, N, K) bytes (allocated when
+    omitted and needed)."""
+    torch = _torch()
+    lib = load()
+    x = _dev_tensor(x, torch.float16, "x", 2)
+    qweight = _dev_tensor(qweight, torch.int32, "qweight", 2)
+    scales = _dev_tensor(scales, torch.float16, "scales", 2)
+    zeros = _dev_tensor(zeros, torch.float16, "zeros", 2)
+    m, k = x.shape
+    n = qweight.shape[0]
+    if qweight.shape[1] * 8 != k or scales.shape != zeros.shape or tuple(scales.shape) != (n, k // group):
+        raise ValueError("qweight must be [N][K/8] and scales/zeros [N][K/group]")
+    need = xres_workspace_bytes(m, n, k)
+    wp, wbytes = None, 0
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=x.device)
+    if workspace is not None:
+        workspace = _workspace(workspace, torch.float32, x)
+        wp, wbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    y = _out(out, (m, n), torch.float16, x)
+    _check(lib.w4a16_linear_xres(x.data_ptr(), qweight.data_ptr(), scales.data_ptr(), zeros.data_ptr(), m, n, k,
+                                 group, wp, wbytes, y.data_ptr(), _stream(x)))
     return y
 
 

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = ["abi.hip", "awq_quantize.hip", "norm_fold.hip", "gemv.hip", "gemm_skinny.hip", "gemm_mfma.hip", "awq_search.hip", "gemm_splitk.hip", "stream_read.hip", "gemm_klane.hip"]
+SOURCES = ["abi.hip", "awq_quantize.hip", "norm_fold.hip", "gemv.hip", "gemm_skinny.hip", "gemm_mfma.hip", "awq_search.hip", "gemm_splitk.hip", "stream_read.hip", "gemm_klane.hip", "gemm_xres.hip"]
 # gemm_skinny.hip holds many kernel instances: it compiles as five parts in parallel
 PARTS = {"gemm_skinny.hip": 5}
 # per-source code generation flags: the tiled MFMA kernels keep their MFMA accumulators in

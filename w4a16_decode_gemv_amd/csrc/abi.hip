@@ -1,5 +1,6 @@
 // C ABI of the library: argument validation (host only, before any HIP call),
 // status codes and text, and dispatch to the kernel launchers.
+#include <algorithm>
 #include <cmath>
 #include <stdarg.h>
 #include <stdint.h>
@@ -131,6 +132,37 @@ int auto_splits(int64_t M, int64_t N, int64_t K) {
     if (M > 32 && tiles <= 48) return 4;
   }
   return 0;
+}
+
+// The x-resident kernel on the automatic path with a workspace (4-bit, groups of 128, scales
+// and zeros 4-byte aligned, an even number of groups per row, K > 2048), with W = ceil(N / 128) *
+// ceil(K / 2048) its workgroups: from M = 8 where W >= 512, from M = 12 on layers wider than
+// they are long with W >= 160, and from M = 16 where W >= 256. From a sweep of M = 4..32 over
+// nine layer shapes (MI355X, graph-timed us, x-resident / the automatic choice before it):
+// 22016 -> 8192 at M = 8 / 16 / 32 27.7 / 29.4 / 43.5 against 37.2 / 42.4 / 44.2; 8192 -> 28672
+// at M = 8 / 16 / 32 33.5 / 37.2 / 56.8 against 41.2 / 50.4 / 68.2; 28672 -> 8192 at M = 8 / 16
+// 34.7 / 37.6 against 37.7 / 44.2; 8192 -> 22016 at M = 8 / 32 27.4 / 44.2 against 31.7 / 52.5;
+// 4096 -> 11008 at M = 12 / 32 12.5 / 16.0 against 14.0 / 19.1; 8192 -> 8192 at M = 16 / 32
+// 14.3 / 17.2 against 14.8 / 21.1. It loses where its grid is short (4096 -> 4096: 64
+// workgroups, 11.9 against 5.9 at M = 16; 8192 -> 1024: 32; 11008 -> 4096: 192, 16.7 against
+// 16.4 at M = 24 with split-K), at M = 4 (8192 -> 8192: 13.8 against 10.5) and below M = 16 on
+// 8192 -> 8192 (14.0 against 14.0 at M = 12).
+bool auto_xres(int64_t M, int64_t N, int64_t K) {
+  // K > 2048: the kernel then takes its workspace (one range needs none and is not measured here)
+  if (M < 8 || K <= 2048 || !w4a16::xres_supports(M, K)) return false;
+  const int64_t W = ((N + 127) / 128) * w4a16::xres_ranges(K);
+  return W >= 512 || (M >= 12 && N > K && W >= 160) || (M >= 16 && W >= 256);
+}
+
+// float32 workspace the automatic path may use (groups of 128): the larger of the two
+// kernels' needs where both may run (the x-resident kernel falls back to the split-K choice
+// when scales or zeros are not 4-byte aligned)
+int64_t ws_floats(int64_t M, int64_t N, int64_t K) {
+  int64_t f = 0;
+  const int s = auto_splits(M, N, K);
+  if (s > 0) f = w4a16::splitk_workspace_floats(M, N, s);
+  if (auto_xres(M, N, K)) f = std::max(f, w4a16::xres_workspace_floats(M, N, K));
+  return f;
 }
 
 w4a16_status hip_result(hipError_t e, const char* what) {
@@ -466,8 +498,7 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
 int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
   if (group != 128 && group != 64 && group != 32) return -1;
-  const int s = group == 128 ? auto_splits(M, N, K) : 0;
-  return s > 0 ? w4a16::splitk_workspace_floats(M, N, s) * 4 : 0;
+  return group == 128 ? ws_floats(M, N, K) * 4 : 0;
 }
 
 w4a16_status w4a16_linear_ws(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
@@ -476,6 +507,17 @@ w4a16_status w4a16_linear_ws(const void* x, const void* qweight, const void* sca
   clear_error();
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
+  if (group == 128 && workspace && auto_xres(M, N, K) && aligned(scales, 4) && aligned(zeros, 4)) {
+    const int64_t need = w4a16::xres_workspace_floats(M, N, K) * 4;
+    if (workspace_bytes < need)
+      return fail(W4A16_ERR_ARG, "workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+    if (!aligned(workspace, 16)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
+    return hip_result(w4a16::launch_xres(static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
+                                         static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), M,
+                                         N, K, static_cast<float*>(workspace), static_cast<uint16_t*>(y),
+                                         static_cast<hipStream_t>(stream)),
+                      "x-resident MFMA launch");
+  }
   const int s = (group == 128 && workspace) ? auto_splits(M, N, K) : 0;
   if (s > 0) {
     const int64_t need = w4a16::splitk_workspace_floats(M, N, s) * 4;
@@ -495,6 +537,14 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
   if (group != 128 && group != 64 && group != 32) return -1;
   return group == 128 ? auto_splits(M, N, K) : 0;
+}
+
+int32_t w4a16_linear_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
+  if (group != 128 && group != 64 && group != 32) return -1;
+  if (group != 128) return 0;
+  if (auto_xres(M, N, K)) return 2;
+  return auto_splits(M, N, K) > 0 ? 1 : 0;
 }
 
 w4a16_status w4a16_linear_path(int32_t path, const void* x, const void* qweight, const void* scales,
@@ -558,6 +608,38 @@ w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void*
                                          N, K, s, static_cast<float*>(workspace), static_cast<uint16_t*>(y),
                                          static_cast<hipStream_t>(stream)),
                     "split-K launch");
+}
+
+int64_t w4a16_linear_xres_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
+  if (!w4a16::xres_supports(M, K)) return -1;
+  return w4a16::xres_workspace_floats(M, N, K) * 4;
+}
+
+w4a16_status w4a16_linear_xres(const void* x, const void* qweight, const void* scales, const void* zeros, int64_t M,
+                               int64_t N, int64_t K, int32_t group, void* workspace, int64_t workspace_bytes, void* y,
+                               void* stream) {
+  clear_error();
+  const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
+  if (st != W4A16_OK) return st;
+  if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "the x-resident kernel takes groups of 128 (got %d)", (int)group);
+  if (!w4a16::xres_supports(M, K))
+    return fail(W4A16_ERR_UNSUPPORTED, "the x-resident kernel takes M <= %d and an even number of groups per row "
+                "(got M=%lld K=%lld)", w4a16::xres_max_m(), (long long)M, (long long)K);
+  if (!aligned(scales, 4) || !aligned(zeros, 4))
+    return fail(W4A16_ERR_ALIGN, "the x-resident kernel needs scales and zeros 4-byte aligned");
+  const int64_t need = w4a16::xres_workspace_floats(M, N, K) * 4;
+  if (need > 0) {
+    if (!workspace) return fail(W4A16_ERR_NULL, "a workspace of %lld bytes is required", (long long)need);
+    if (workspace_bytes < need)
+      return fail(W4A16_ERR_ARG, "workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
+    if (!aligned(workspace, 16)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
+  }
+  return hip_result(w4a16::launch_xres(static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
+                                       static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), M, N,
+                                       K, static_cast<float*>(workspace), static_cast<uint16_t*>(y),
+                                       static_cast<hipStream_t>(stream)),
+                    "x-resident MFMA launch");
 }
 
 w4a16_status w4a16_linear_splitk_noalloc(const void* x, const void* qweight, const void* scales, const void* zeros,

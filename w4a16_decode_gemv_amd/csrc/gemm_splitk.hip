@@ -337,13 +337,16 @@ hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint1
                        zeros, (int)M, (int)N, (int)K, splits, TM, workspace, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  return launch_splitk_reduce(workspace, M, N, splits, y, stream);
+}
+
+hipError_t launch_splitk_reduce(const float* part, int64_t M, int64_t N, int S, uint16_t* y, hipStream_t stream) {
   const int64_t total = M * N;
   const int64_t grid = (total + 1023) / 1024;
-  switch (splits) {
-#define W4A16_REDUCE(SC)                                                                                        \
-  case SC:                                                                                                       \
-    hipLaunchKernelGGL(splitk_reduce_kernel<SC>, dim3((unsigned)grid), dim3(256), 0, stream, workspace, total, \
-                       splits, y);                                                                               \
+  switch (S) {
+#define W4A16_REDUCE(SC)                                                                                      \
+  case SC:                                                                                                     \
+    hipLaunchKernelGGL(splitk_reduce_kernel<SC>, dim3((unsigned)grid), dim3(256), 0, stream, part, total, S, y); \
     break;
     W4A16_REDUCE(2)
     W4A16_REDUCE(4)
@@ -351,8 +354,7 @@ hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint1
     W4A16_REDUCE(16)
 #undef W4A16_REDUCE
     default:
-      hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, workspace, total, splits,
-                         y);
+      hipLaunchKernelGGL(splitk_reduce_kernel<0>, dim3((unsigned)grid), dim3(256), 0, stream, part, total, S, y);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,268 @@
+// Small-batch W4A16 GEMM (M <= 32, 4-bit codes, groups of 128) with each wave's block of x
+// held in registers for the whole launch and K split across workgroups.
+//
+// y[m][n] = f16( sum_s P_s[m][n] ),
+// P_s[m][n] = sum_{g in range s} d[n][g] * sum_{k in g} x[m][k] (q[n][k] - z[n][g])
+//
+// The fused dequantize + multiply of the other kernels ("MIT 6.5940 L13 LLM Deployment"
+// guide, TinyChat kernel fusion), on the matrix cores because every weight serves up to 32
+// rows of x ("CMU 11-868 Model Quantization" guide, where the speed comes from).
+//
+// Why another small-batch kernel. The small-batch kernel's workgroups own 32 output columns
+// and all of K, so each of them reads all of x: at M = 32 on an 8192 x 8192 layer that is
+// 128 MB of L2-to-L1 traffic beside 34 MB of codes, and that path sets its time. Here a
+// workgroup owns 128 columns and one range of 2048 inputs (16 groups). Each of its eight waves
+// loads the x fragments of its 256 inputs (two groups, 16 or 32 rows) once, keeps them in
+// registers, and streams the codes of all 128 columns past them: x crosses L2 -> L1 once per
+// 128 columns (32 MB at M = 32 on 8192 x 8192). Every x, scale, zero and code load of a wave
+// is issued before its first MFMA (16 KB of codes per wave in flight), so the weight stream
+// keeps the GEMV's depth.
+//
+// Per 16-column n-tile and group the four MFMA steps accumulate sum x (q - z) exactly (fp16
+// (q - z) B fragments while z lies in [-2032, 1024]; a wave meeting another zero takes exact q
+// and z * sum x for that group, sum x from an MFMA against ones), then acc += d * that. The
+// eight waves' float32 tiles are added through LDS in wave order. With one K range (K <= 2048)
+// the sums are rounded to fp16 and written to y; otherwise range s writes its tile to the
+// caller's workspace P[s][m][n] and the split-K reduction kernel adds the ranges in index
+// order and rounds once. Results are reproducible.
+#include "device_utils.h"
+#include "launchers.h"
+
+namespace w4a16 {
+
+namespace {
+
+constexpr int kXrWaves = 8;
+constexpr int kXrThreads = 64 * kXrWaves;
+constexpr int kXrGroups = 2;                           // groups of 128 inputs per wave
+constexpr int kXrTiles = 8;                            // 16-column n-tiles per wave
+constexpr int kXrCols = 16 * kXrTiles;                 // 128 output columns per workgroup
+constexpr int kXrRangeGroups = kXrWaves * kXrGroups;   // 16 groups (2048 inputs) per K range
+
+// grid: ceil(N / 128) * S items, item = n-tile * S + range (ranges of one n-tile adjacent);
+// MT 16-row m-tiles (M <= 16 * MT)
+//
+// Loads are whole 128-byte lines: a code row's two groups (128 bytes) come from 8 lanes, an x
+// row's 512 bytes from 32 lanes. The MFMA fragments need lane (c, j) to hold row c, so codes
+// and x pass through LDS (XOR-swizzled, conflict-free both ways), inside the wave's slice of
+// the reduction area: x once, before that slice holds any partial tile, and each n-tile's codes
+// through the two slots written last (with one m-tile the last n-tile uses the wave's
+// (scale, zero) area for its second half, read before). Each wave keeps its own (scale, zero)
+// pairs: no workgroup barrier before the final sums. With one m-tile the workgroup fits 72 KB
+// of LDS and 128 VGPRs, two per CU. Measured (timing-only copies, 8192 x 8192 at M = 4):
+// half-line code loads cost 2.5 us; on 22016 -> 8192 at M = 16 (three rounds of workgroups)
+// one workgroup per CU cost 6-8 us against two.
+template <int MT, bool DIRECT>
+__global__ __launch_bounds__(kXrThreads) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
+void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
+                 const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int S,
+                 float* __restrict__ part, uint16_t* __restrict__ y) {
+  // red[wave]: first the wave's x rows [16 MT][32 pieces], then the code stage, then its
+  // partial tiles
+  __shared__ float4_t red[kXrWaves][kXrTiles * MT][64];
+  __shared__ u32x4_t wsz[kXrWaves][64];  // the wave's (scale pair) [128] then (zero pair) [128] words
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int j = lane >> 4, c = lane & 15;
+  const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
+  const int range = item % S, tn = item / S;
+  const int n0 = tn * kXrCols;
+  const int G = K >> 7;
+  const int g0 = range * kXrRangeGroups + wave * kXrGroups;  // this wave's first group
+  // G is even and so is g0: a wave holds both of its groups or neither; a wave past the last
+  // group reads zeros everywhere (no traffic) and adds exact zeros
+  const int past = (int)(g0 >= G) * kOutOfRange;
+  const int rows_n = min(N - n0, kXrCols);
+  const __amdgpu_buffer_rsrc_t rx = rsrc(x, (int64_t)M * K * 2);  // rows past M read zero
+  const __amdgpu_buffer_rsrc_t rq = rsrc(qw + (int64_t)n0 * (K >> 3), (int64_t)rows_n * (K >> 1));
+  const __amdgpu_buffer_rsrc_t rs = rsrc(scales + (int64_t)n0 * G, (int64_t)rows_n * G * 2);
+  const __amdgpu_buffer_rsrc_t rz = rsrc(zeros + (int64_t)n0 * G, (int64_t)rows_n * G * 2);
+
+  // (1) the wave's (scale, zero) pairs (groups g0, g0 + 1) of rows lane and lane + 64
+  uint32_t sv[2], zv[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int off = (lane + 64 * u) * G * 2 + g0 * 2 + past;
+    sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+    zv[u] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  // (2) x rows of the wave's 256 inputs: load i takes row 2i + lane / 32, piece lane % 32 (16
+  //     bytes; piece p is input chunk p % 16 of group g0 + p / 16)
+  u32x4_t xl[8 * MT];
+#pragma unroll
+  for (int i = 0; i < 8 * MT; ++i) xl[i] = load16(rx, (2 * i + (lane >> 5)) * K * 2 + g0 * 256 + (lane & 31) * 16 + past);
+  __builtin_amdgcn_sched_barrier(0);
+  // (3) codes: n-tile tt, load i takes row 16 tt + 8i + lane / 8, piece lane % 8 (piece p holds
+  //     words 4 (p % 4) .. + 3 of group g0 + p / 4); non-temporal (read once)
+  //     With one m-tile the last n-tile's codes are issued after the first n-tile's compute (its
+  //     registers then free), which keeps the wave within 128 VGPRs (two workgroups per CU).
+  u32x4_t q[kXrTiles][2];
+  constexpr int kLate = MT == 1 ? kXrTiles - 1 : kXrTiles;  // n-tiles issued up front
+  auto issue_codes = [&](int tt) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      q[tt][i] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                       rq, (16 * tt + 8 * i + (lane >> 3)) * (K >> 1) + g0 * 64 + (lane & 7) * 16 + past, 0,
+                       kNonTemporal));
+  };
+#pragma unroll
+  for (int tt = 0; tt < kLate; ++tt) {
+    issue_codes(tt);
+    __builtin_amdgcn_sched_barrier(0);  // loads stay in compute order: each n-tile waits only for its own
+  }
+
+  // x into the wave's slice of red (row r, piece p at r * 32 + (p ^ (r % 16))), then the
+  // fragments: m-tile mt, group h, step s of lane (c, j) is row 16 mt + c, piece 16 h + 4 j + s
+  u32x4_t* xs = reinterpret_cast<u32x4_t*>(&red[wave][0][0]);
+#pragma unroll
+  for (int i = 0; i < 8 * MT; ++i) {
+    const int r = 2 * i + (lane >> 5);
+    xs[r * 32 + ((lane & 31) ^ (r & 15))] = xl[i];
+  }
+  u32x4_t xf[MT][kXrGroups][4];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int h = 0; h < kXrGroups; ++h)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) xf[mt][h][s] = xs[(16 * mt + c) * 32 + 16 * h + ((4 * j + s) ^ c)];
+  uint32_t* sz = reinterpret_cast<uint32_t*>(&wsz[wave][0]);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    sz[lane + 64 * u] = sv[u];
+    sz[kXrCols + lane + 64 * u] = zv[u];
+  }
+
+  // (4) compute each n-tile as its codes land. Its two loads go to the stage: rows 0..7 to half
+  //     A, rows 8..15 to half B, row r at (r % 8) * 8 + (p ^ ((r % 8) / 2 + 4 (r / 8))) for piece
+  //     p; lane (c, j) reads row c, pieces j and 4 + j: words 4j .. 4j + 3 of each group, the B
+  //     fragments of steps 0..3. A is the wave's last partial-tile slot and B the one before,
+  //     both written after the last n-tile's stage reads; with one m-tile B is the next-to-last
+  //     tile's own slot (written after its stage reads) and, for the last n-tile, the
+  //     (scale, zero) area, whose pairs that tile has read by then.
+  const u32x4_t ones_bits = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
+  const half8_t ones = as_half8(ones_bits);
+  u32x4_t* half_a = reinterpret_cast<u32x4_t*>(&red[wave][kXrTiles * MT - 1][0]);
+  u32x4_t* half_b = reinterpret_cast<u32x4_t*>(&red[wave][kXrTiles * MT - 2][0]);
+#pragma unroll
+  for (int tt = 0; tt < kXrTiles; ++tt) {
+    const uint32_t spair = sz[16 * tt + c], zpair = sz[kXrCols + 16 * tt + c];
+    u32x4_t* hb = (MT == 1 && tt == kXrTiles - 1) ? &wsz[wave][0] : half_b;
+    // the pairs are read through another type than the stage is written with: keep the reads
+    // first where they share the area
+    if (MT == 1 && tt == kXrTiles - 1) asm volatile("" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = lane >> 3;
+      (i ? hb : half_a)[r * 8 + ((lane & 7) ^ ((r >> 1) | (i << 2)))] = q[tt][i];
+    }
+    const int ci = c & 7, cb = c >> 3;
+    const u32x4_t* hc = cb ? hb : half_a;
+    const u32x4_t qc[2] = {hc[ci * 8 + (j ^ ((ci >> 1) | (cb << 2)))], hc[ci * 8 + ((4 + j) ^ ((ci >> 1) | (cb << 2)))]};
+    float4_t acc[MT];
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < kXrGroups; ++h) {
+      const float d = half_bits_to_float((uint16_t)(spair >> (16 * h)));
+      const _Float16 zh = __builtin_bit_cast(_Float16, (uint16_t)(zpair >> (16 * h)));
+      const float zf = (float)zh;
+      const bool exact = zf >= -2032.0f && zf <= 1024.0f;
+      const bool fast = __builtin_amdgcn_ballot_w64(!exact) == 0;
+      const _Float16 clo = fast ? -((_Float16)1024.0f + zh) : (_Float16)-1024.0f;
+      const _Float16 chi = fast ? -((_Float16)64.0f + zh) : (_Float16)-64.0f;
+      const half2_t c_lo = {clo, clo}, c_hi = {chi, chi};
+      const half8_t bq[4] = {dequant_word(qc[h].x, c_lo, c_hi), dequant_word(qc[h].y, c_lo, c_hi),
+                             dequant_word(qc[h].z, c_lo, c_hi), dequant_word(qc[h].w, c_lo, c_hi)};
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float4_t a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][s]), bq[s], a, 0, 0, 0);
+        if (fast) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, a[i], acc[mt][i]);
+        } else {
+          float4_t sx = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s = 0; s < 4; ++s) sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][s]), ones, sx, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, __builtin_fmaf(-zf, sx[i], a[i]), acc[mt][i]);
+        }
+      }
+    }
+    // D fragment: lane (c, j) holds rows 16 mt + 4j + i of column n0 + 16 tt + c
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) red[wave][tt * MT + mt][lane] = acc[mt];
+    if (tt == 0 && kLate < kXrTiles) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_codes(kXrTiles - 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  __syncthreads();
+
+  // (5) the eight waves' tiles added in wave order; each thread takes whole D-fragment slots
+  constexpr int kSlots = kXrTiles * MT * 64;
+  float* p = DIRECT ? nullptr : part + (int64_t)range * M * N;
+#pragma unroll
+  for (int u0 = 0; u0 < kSlots; u0 += kXrThreads) {
+    const int u = u0 + t;
+    const int tile = u >> 6, ln = u & 63;
+    float4_t sum = red[0][tile][ln];
+#pragma unroll
+    for (int w = 1; w < kXrWaves; ++w) sum += red[w][tile][ln];
+    const int tt = tile / MT, mt = tile % MT;
+    const int n = n0 + 16 * tt + (ln & 15);
+    if (n < N) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = 16 * mt + 4 * (ln >> 4) + i;
+        if (m < M) {
+          if constexpr (DIRECT)
+            y[(int64_t)m * N + n] = float_to_half_bits(sum[i]);
+          else
+            p[(int64_t)m * N + n] = sum[i];
+        }
+      }
+    }
+  }
+}
+
+template <int MT>
+hipError_t launch_mt(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, const uint16_t* zr, int64_t M,
+                     int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
+  const int S = xres_ranges(K);
+  const int64_t items = ((N + kXrCols - 1) / kXrCols) * S;
+  if (S == 1)
+    hipLaunchKernelGGL((xres_kernel<MT, true>), dim3((unsigned)items), dim3(kXrThreads), 0, stream, x, qw, sc, zr,
+                       (int)M, (int)N, (int)K, 1, nullptr, y);
+  else
+    hipLaunchKernelGGL((xres_kernel<MT, false>), dim3((unsigned)items), dim3(kXrThreads), 0, stream, x, qw, sc, zr,
+                       (int)M, (int)N, (int)K, S, workspace, nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_splitk_reduce(workspace, M, N, S, y, stream);
+}
+
+}  // namespace
+
+int xres_max_m() { return 32; }
+
+int xres_ranges(int64_t K) { return (int)((K / 128 + kXrRangeGroups - 1) / kXrRangeGroups); }
+
+bool xres_supports(int64_t M, int64_t K) { return M >= 1 && M <= xres_max_m() && (K / 128) % 2 == 0; }
+
+int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K) {
+  const int S = xres_ranges(K);
+  return S == 1 ? 0 : (int64_t)S * M * N;
+}
+
+hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                       int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
+  if (M <= 16) return launch_mt<1>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  return launch_mt<2>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+}
+
+}  // namespace w4a16

@@ -81,6 +81,21 @@ hipError_t launch_splitk(const uint16_t* x, const uint32_t* qweight, const uint1
 constexpr int64_t kSplitkScratchFloats = int64_t(1) << 23;  // 32 MiB
 hipError_t splitk_scratch(hipStream_t stream, float** ptr);
 
+// The split-K reduction alone: y[m][n] = f16(sum over s = 0..S-1, in index order, of
+// part[s][m][n]), part float32 [S][M][N].
+hipError_t launch_splitk_reduce(const float* part, int64_t M, int64_t N, int S, uint16_t* y, hipStream_t stream);
+
+// Small-batch MFMA kernel with x held in registers and K split into xres_ranges(K) ranges of
+// 2048 inputs (4-bit, groups of 128): needs xres_supports(M, K) (M <= 32, an even number of
+// groups per row) and scales and zeros 4-byte aligned; with more than one range, a float32
+// workspace of xres_workspace_floats(M, N, K) floats.
+int xres_max_m();
+int xres_ranges(int64_t K);
+bool xres_supports(int64_t M, int64_t K);
+int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K);
+hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+                       int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream);
+
 // Tiled MFMA kernel: any M >= 1. mfma_workgroups: the workgroups launch_mfma starts (for M > 16).
 int64_t mfma_workgroups(int64_t M, int64_t N);
 hipError_t launch_mfma(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
