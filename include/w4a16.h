@@ -311,20 +311,21 @@ w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void*
 
 /*
  * w4a16_linear_xres_workspace - bytes of float32 workspace that
- * w4a16_linear_xres needs for this shape (0 when K <= 2048: one K range, no
- * workspace); -1 when the shape is not accepted (M > 32, or an odd number of
- * groups of 128 per row).
+ * w4a16_linear_xres needs for this shape (S * M * N floats for its S K ranges,
+ * 0 with one range); -1 when the shape is not accepted (M > 32, or an odd
+ * number of groups of 128 per row).
  */
 int64_t w4a16_linear_xres_workspace(int64_t M, int64_t N, int64_t K);
 
 /*
  * w4a16_linear_xres - w4a16_linear (4-bit, groups of 128) for small batches,
  * 1 <= M <= 32, on the x-resident MFMA kernel: a workgroup owns 128 output
- * columns and one range of 2048 inputs; each of its eight waves keeps the x
- * fragments of its 256 inputs in registers and streams the codes of the 128
- * columns past them, so x crosses from L2 once per 128 columns instead of once
- * per 32 (CMU guide, "where the speed comes from": small-batch decode stays
- * bound by the weight stream; L13 TinyChat kernel fusion). The S = ceil(K / 2048)
+ * columns and one range of 2048 inputs (eight waves; 1024 inputs and four
+ * waves when M > 16 and ceil(N / 128) * ceil(K / 2048) >= 512); each wave
+ * keeps the x fragments of its 256 inputs in registers and streams the codes
+ * of the 128 columns past them, so x crosses from L2 once per 128 columns
+ * instead of once per 32 (CMU guide, "where the speed comes from": small-batch
+ * decode stays bound by the weight stream; L13 TinyChat kernel fusion). The S
  * ranges' float32 partials go to `workspace` and a second kernel adds them in
  * index order and rounds once to fp16 (reproducible); with one range the first
  * kernel writes y itself. Same formula, accuracy contract and arguments as

@@ -249,6 +249,8 @@ def test_xres_workspace_and_rejects():
     assert lib.w4a16_linear_xres_workspace(32, 8192, 8192) == 4 * 32 * 8192 * 4
     assert lib.w4a16_linear_xres_workspace(16, 4096, 11008) == 6 * 16 * 4096 * 4
     assert lib.w4a16_linear_xres_workspace(32, 4096, 2048) == 0
+    assert lib.w4a16_linear_xres_workspace(32, 8192, 22016) == 22 * 32 * 8192 * 4   # four-wave ranges of 1024
+    assert lib.w4a16_linear_xres_workspace(16, 8192, 22016) == 11 * 16 * 8192 * 4
     assert lib.w4a16_linear_xres_workspace(33, 4096, 4096) == -1   # M > 32
     assert lib.w4a16_linear_xres_workspace(8, 4096, 384) == -1     # odd number of groups
     assert lib.w4a16_linear_xres_workspace(0, 4096, 4096) == -1
@@ -297,7 +299,9 @@ def test_linear_ws_split_choice_and_rejects():
         assert lib.w4a16_linear_ws_splits(m, n, k, 128) == s, (m, n, k)
         want_x = (m, n, k) in xres
         assert lib.w4a16_linear_ws_kernel(m, n, k, 128) == (2 if want_x else 1 if s else 0), (m, n, k)
-        xf = -(-k // 2048) * m * n if want_x and k > 2048 else 0
+        # K ranges of 2048 inputs, or 1024 with two m-tiles on at least 512 eight-wave workgroups
+        rng = 1024 if m > 16 and -(-n // 128) * -(-k // 2048) >= 512 else 2048
+        xf = -(-k // rng) * m * n if want_x else 0
         assert lib.w4a16_linear_workspace(m, n, k, 128) == max(s * m * n, xf) * 4, (m, n, k)
     assert lib.w4a16_linear_ws_kernel(32, 8192, 8192, 64) == 0
     assert lib.w4a16_linear_ws_kernel(32, 8192, 8320, 128) == 0   # odd number of groups

@@ -66,6 +66,18 @@ def test_xres_small_batch_layer_every_output(lib):
         assert np.all(ok), (m, np.argwhere(~ok)[:3])
 
 
+@pytest.mark.parametrize("m", [17, 32])
+def test_xres_four_wave_ranges(lib, m):
+    # M > 16 on a grid of at least 512 eight-wave workgroups (ceil(32769 / 128) * ceil(2304 / 2048)
+    # = 514): four-wave workgroups and K ranges of 1024 inputs (8, 8 and 2 groups: the last
+    # range's second wave and above idle); a ragged last column tile; every output
+    n, k = 32769, 2304
+    s, packed = _packed(9, 2, n, k)
+    x = oracle.scale_input(synth.activations(9, 2, m, k), s)
+    assert lib.xres_workspace_bytes(m, n, k) == 3 * m * n * 4
+    _check(lib, x, packed, "four-wave")
+
+
 @pytest.mark.parametrize("kind", ["positive", "negative", "mixed", "wide"])
 def test_xres_edge_weights(lib, kind):
     W = synth.edge_weights(kind, 96, 4096, seed=13)

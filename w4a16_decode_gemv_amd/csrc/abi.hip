@@ -150,7 +150,7 @@ int auto_splits(int64_t M, int64_t N, int64_t K) {
 bool auto_xres(int64_t M, int64_t N, int64_t K) {
   // K > 2048: the kernel then takes its workspace (one range needs none and is not measured here)
   if (M < 8 || K <= 2048 || !w4a16::xres_supports(M, K)) return false;
-  const int64_t W = ((N + 127) / 128) * w4a16::xres_ranges(K);
+  const int64_t W = ((N + 127) / 128) * ((K / 128 + 15) / 16);  // eight-wave workgroups
   return W >= 512 || (M >= 12 && N > K && W >= 160) || (M >= 16 && W >= 256);
 }
 

@@ -11,18 +11,18 @@
 // Why another small-batch kernel. The small-batch kernel's workgroups own 32 output columns
 // and all of K, so each of them reads all of x: at M = 32 on an 8192 x 8192 layer that is
 // 128 MB of L2-to-L1 traffic beside 34 MB of codes, and that path sets its time. Here a
-// workgroup owns 128 columns and one range of 2048 inputs (16 groups). Each of its eight waves
-// loads the x fragments of its 256 inputs (two groups, 16 or 32 rows) once, keeps them in
-// registers, and streams the codes of all 128 columns past them: x crosses L2 -> L1 once per
-// 128 columns (32 MB at M = 32 on 8192 x 8192). Every x, scale, zero and code load of a wave
+// workgroup owns 128 columns and one range of 2048 inputs (16 groups; 1024 inputs with four
+// waves, see xres_waves). Each of its waves loads the x fragments of its 256 inputs (two
+// groups, 16 or 32 rows) once, keeps them in registers, and streams the codes of all 128
+// columns past them: x crosses L2 -> L1 once per 128 columns (8 MB at M = 32 on 8192 x 8192). Every x, scale, zero and code load of a wave
 // is issued before its first MFMA (16 KB of codes per wave in flight), so the weight stream
 // keeps the GEMV's depth.
 //
 // Per 16-column n-tile and group the four MFMA steps accumulate sum x (q - z) exactly (fp16
 // (q - z) B fragments while z lies in [-2032, 1024]; a wave meeting another zero takes exact q
 // and z * sum x for that group, sum x from an MFMA against ones), then acc += d * that. The
-// eight waves' float32 tiles are added through LDS in wave order. With one K range (K <= 2048)
-// the sums are rounded to fp16 and written to y; otherwise range s writes its tile to the
+// waves' float32 tiles are added through LDS in wave order. With one K range the sums are
+// rounded to fp16 and written to y; otherwise range s writes its tile to the
 // caller's workspace P[s][m][n] and the split-K reduction kernel adds the ranges in index
 // order and rounds once. Results are reproducible.
 #include "device_utils.h"
@@ -32,12 +32,9 @@ namespace w4a16 {
 
 namespace {
 
-constexpr int kXrWaves = 8;
-constexpr int kXrThreads = 64 * kXrWaves;
 constexpr int kXrGroups = 2;                           // groups of 128 inputs per wave
 constexpr int kXrTiles = 8;                            // 16-column n-tiles per wave
 constexpr int kXrCols = 16 * kXrTiles;                 // 128 output columns per workgroup
-constexpr int kXrRangeGroups = kXrWaves * kXrGroups;   // 16 groups (2048 inputs) per K range
 
 // grid: ceil(N / 128) * S items, item = n-tile * S + range (ranges of one n-tile adjacent);
 // MT 16-row m-tiles (M <= 16 * MT)
@@ -52,15 +49,17 @@ constexpr int kXrRangeGroups = kXrWaves * kXrGroups;   // 16 groups (2048 inputs
 // of LDS and 128 VGPRs, two per CU. Measured (timing-only copies, 8192 x 8192 at M = 4):
 // half-line code loads cost 2.5 us; on 22016 -> 8192 at M = 16 (three rounds of workgroups)
 // one workgroup per CU cost 6-8 us against two.
-template <int MT, bool DIRECT>
-__global__ __launch_bounds__(kXrThreads) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
+template <int MT, int WV, bool DIRECT>
+__global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
 void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
                  const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int S,
                  float* __restrict__ part, uint16_t* __restrict__ y) {
   // red[wave]: first the wave's x rows [16 MT][32 pieces], then the code stage, then its
   // partial tiles
-  __shared__ float4_t red[kXrWaves][kXrTiles * MT][64];
-  __shared__ u32x4_t wsz[kXrWaves][64];  // the wave's (scale pair) [128] then (zero pair) [128] words
+  constexpr int kXrThreads = 64 * WV;
+  constexpr int kXrRangeGroups = WV * kXrGroups;  // groups per K range
+  __shared__ float4_t red[WV][kXrTiles * MT][64];
+  __shared__ u32x4_t wsz[WV][64];  // the wave's (scale pair) [128] then (zero pair) [128] words
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
   const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
@@ -212,7 +211,7 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
     const int tile = u >> 6, ln = u & 63;
     float4_t sum = red[0][tile][ln];
 #pragma unroll
-    for (int w = 1; w < kXrWaves; ++w) sum += red[w][tile][ln];
+    for (int w = 1; w < WV; ++w) sum += red[w][tile][ln];
     const int tt = tile / MT, mt = tile % MT;
     const int n = n0 + 16 * tt + (ln & 15);
     if (n < N) {
@@ -230,16 +229,16 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   }
 }
 
-template <int MT>
+template <int MT, int WV>
 hipError_t launch_mt(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, const uint16_t* zr, int64_t M,
                      int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
-  const int S = xres_ranges(K);
+  const int S = (int)((K / 128 + WV * kXrGroups - 1) / (WV * kXrGroups));
   const int64_t items = ((N + kXrCols - 1) / kXrCols) * S;
   if (S == 1)
-    hipLaunchKernelGGL((xres_kernel<MT, true>), dim3((unsigned)items), dim3(kXrThreads), 0, stream, x, qw, sc, zr,
+    hipLaunchKernelGGL((xres_kernel<MT, WV, true>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc, zr,
                        (int)M, (int)N, (int)K, 1, nullptr, y);
   else
-    hipLaunchKernelGGL((xres_kernel<MT, false>), dim3((unsigned)items), dim3(kXrThreads), 0, stream, x, qw, sc, zr,
+    hipLaunchKernelGGL((xres_kernel<MT, WV, false>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc, zr,
                        (int)M, (int)N, (int)K, S, workspace, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
@@ -250,19 +249,43 @@ hipError_t launch_mt(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, 
 
 int xres_max_m() { return 32; }
 
-int xres_ranges(int64_t K) { return (int)((K / 128 + kXrRangeGroups - 1) / kXrRangeGroups); }
+// Waves per workgroup (two groups of 128 inputs each; a K range is 256 * waves inputs): eight,
+// or four with two m-tiles where eight-wave workgroups would come to at least 512 (two or more
+// rounds of the chip). Four-wave workgroups of two m-tiles take 68 KB of LDS, so two share a
+// CU and the rounds overlap: 22016 -> 8192 at M = 32 39.0 against 43.8 us, 8192 -> 28672 46.5
+// against 57.8; on one round they lose (8192 -> 8192 at M = 32: 18.1 against 17.3), and with
+// one m-tile (where eight-wave workgroups already pair up) they lose everywhere measured
+// (22016 -> 8192 at M = 16: 31.5 against 29.2).
+int xres_waves(int64_t M, int64_t N, int64_t K) {
+  const int64_t w8 = ((N + kXrCols - 1) / kXrCols) * ((K / 128 + 15) / 16);
+  return M > 16 && w8 >= 512 ? 4 : 8;
+}
+
+int xres_ranges(int64_t M, int64_t N, int64_t K) {
+  const int64_t g = (int64_t)xres_waves(M, N, K) * kXrGroups;
+  return (int)((K / 128 + g - 1) / g);
+}
 
 bool xres_supports(int64_t M, int64_t K) { return M >= 1 && M <= xres_max_m() && (K / 128) % 2 == 0; }
 
 int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K) {
-  const int S = xres_ranges(K);
+  const int S = xres_ranges(M, N, K);
   return S == 1 ? 0 : (int64_t)S * M * N;
+}
+
+hipError_t launch_xres_waves(int waves, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                             const uint16_t* zeros, int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y,
+                             hipStream_t stream) {
+  if (M <= 16)
+    return waves == 4 ? launch_mt<1, 4>(x, qweight, scales, zeros, M, N, K, workspace, y, stream)
+                      : launch_mt<1, 8>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  return waves == 4 ? launch_mt<2, 4>(x, qweight, scales, zeros, M, N, K, workspace, y, stream)
+                    : launch_mt<2, 8>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
 }
 
 hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
-  if (M <= 16) return launch_mt<1>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
-  return launch_mt<2>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  return launch_xres_waves(xres_waves(M, N, K), x, qweight, scales, zeros, M, N, K, workspace, y, stream);
 }
 
 }  // namespace w4a16

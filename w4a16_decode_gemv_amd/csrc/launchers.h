@@ -85,16 +85,22 @@ hipError_t splitk_scratch(hipStream_t stream, float** ptr);
 // part[s][m][n]), part float32 [S][M][N].
 hipError_t launch_splitk_reduce(const float* part, int64_t M, int64_t N, int S, uint16_t* y, hipStream_t stream);
 
-// Small-batch MFMA kernel with x held in registers and K split into xres_ranges(K) ranges of
-// 2048 inputs (4-bit, groups of 128): needs xres_supports(M, K) (M <= 32, an even number of
+// Small-batch MFMA kernel with x held in registers and K split into xres_ranges(M, N, K) ranges
+// of 2048 or 1024 inputs (4-bit, groups of 128): needs xres_supports(M, K) (M <= 32, an even number of
 // groups per row) and scales and zeros 4-byte aligned; with more than one range, a float32
 // workspace of xres_workspace_floats(M, N, K) floats.
 int xres_max_m();
-int xres_ranges(int64_t K);
+int xres_waves(int64_t M, int64_t N, int64_t K);  // waves per workgroup; a K range is 256 * waves inputs
+int xres_ranges(int64_t M, int64_t N, int64_t K);
 bool xres_supports(int64_t M, int64_t K);
 int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K);
 hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream);
+// the same with 4 or 8 waves per workgroup (ranges of 1024 or 2048 inputs; the workspace holds
+// the ranges of that choice)
+hipError_t launch_xres_waves(int waves, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
+                             const uint16_t* zeros, int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y,
+                             hipStream_t stream);
 
 // Tiled MFMA kernel: any M >= 1. mfma_workgroups: the workgroups launch_mfma starts (for M > 16).
 int64_t mfma_workgroups(int64_t M, int64_t N);
