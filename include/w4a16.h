@@ -239,11 +239,12 @@ int32_t w4a16_linear_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group);
  * workspace_bytes >= w4a16_linear_workspace(M, N, K, group) bytes, 16-byte
  * aligned, overwritten (two calls in flight at once need two workspaces).
  * Dispatch, groups of 128 with a workspace (from measured sweeps over the
- * LLaMA projection shapes): the x-resident kernel when K > 2048, K / 128 is even, scales
- * and zeros are 4-byte aligned and, with W = ceil(N / 128) * ceil(K / 2048) its
- * workgroups, 8 <= M <= 32 with W >= 512, 12 <= M <= 32 with N > K and
- * W >= 160, or 16 <= M <= 32 with W >= 256; otherwise split-K: no split for
- * M <= 16; else with G = K / 128 and T
+ * LLaMA projection shapes): the x-resident kernel when K > 2048, K / 128 is even,
+ * scales and zeros are 4-byte aligned and: for 4 <= M <= 16, N * K >= 2^27, or
+ * M >= 8 with N * K >= 2^25 and N > K, or M >= 8 with ceil(N / 32) <= 64 and
+ * K >= 8192, or M >= 12 with N * K >= 2^25; for 17 <= M <= 32, with
+ * W = ceil(N / 128) * ceil(K / 2048), W >= 256, or N > K with W >= 160;
+ * otherwise split-K: no split for M <= 16; else with G = K / 128 and T
  * the split-K kernel's tiles (ceil(N / 128) for M <= 32, else ceil(M / 64) *
  * ceil(N / 128)), for K >= 8192: no split up to M = 32 when K <= 16384 and
  * ceil(N / 32) is a multiple of 256 (the small-batch kernel's grid fills the
@@ -319,12 +320,13 @@ int64_t w4a16_linear_xres_workspace(int64_t M, int64_t N, int64_t K);
 
 /*
  * w4a16_linear_xres - w4a16_linear (4-bit, groups of 128) for small batches,
- * 1 <= M <= 32, on the x-resident MFMA kernel: a workgroup owns 128 output
- * columns and one range of 2048 inputs (eight waves; 1024 inputs and four
- * waves when M > 16 and ceil(N / 128) * ceil(K / 2048) >= 512); each wave
- * keeps the x fragments of its 256 inputs in registers and streams the codes
- * of the 128 columns past them, so x crosses from L2 once per 128 columns
- * instead of once per 32 (CMU guide, "where the speed comes from": small-batch
+ * 1 <= M <= 32, on the x-resident MFMA kernel: a workgroup owns 64 output
+ * columns for M <= 16 (128 above) and one range of 256 inputs per wave (eight
+ * waves, or four where M <= 16 and ceil(N / 64) * ceil(K / 2048) < 512, or
+ * M > 16 and ceil(N / 128) * ceil(K / 2048) >= 512); each wave keeps the x
+ * fragments of its 256 inputs in registers and streams the codes of the
+ * workgroup's columns past them, so x crosses from L2 once per 64 or 128
+ * columns instead of once per 32 (CMU guide, "where the speed comes from": small-batch
  * decode stays bound by the weight stream; L13 TinyChat kernel fusion). The S
  * ranges' float32 partials go to `workspace` and a second kernel adds them in
  * index order and rounds once to fp16 (reproducible); with one range the first

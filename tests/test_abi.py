@@ -243,14 +243,32 @@ def test_splitk_workspace_and_rejects():
     assert call(K=200) == w4.ERR_SHAPE
 
 
+def _xres_ranges(m, n, k):
+    # K ranges of the x-resident kernel: 256 inputs per wave; with M <= 16 workgroups of 64
+    # columns, eight waves where they come to 512 or more (else four); with M > 16 128
+    # columns, four waves where eight-wave workgroups would come to 512 or more (else eight)
+    g = k // 128
+    r8 = -(-g // 16)
+    if m <= 16:
+        waves = 8 if -(-n // 64) * r8 >= 512 else 4
+    else:
+        waves = 4 if -(-n // 128) * r8 >= 512 else 8
+    return -(-g // (2 * waves))
+
+
 def test_xres_workspace_and_rejects():
     lib = w4.load()
-    # ranges of 2048 inputs: S = ceil(K / 2048) float32 partials of M x N, none for one range
+    # S float32 partials of M x N, none for one range
     assert lib.w4a16_linear_xres_workspace(32, 8192, 8192) == 4 * 32 * 8192 * 4
-    assert lib.w4a16_linear_xres_workspace(16, 4096, 11008) == 6 * 16 * 4096 * 4
+    assert lib.w4a16_linear_xres_workspace(16, 8192, 8192) == 4 * 16 * 8192 * 4     # 512 workgroups of 8 waves
+    assert lib.w4a16_linear_xres_workspace(16, 4096, 11008) == 11 * 16 * 4096 * 4   # 4-wave ranges of 1024
     assert lib.w4a16_linear_xres_workspace(32, 4096, 2048) == 0
+    assert lib.w4a16_linear_xres_workspace(16, 4096, 2048) == 2 * 16 * 4096 * 4
     assert lib.w4a16_linear_xres_workspace(32, 8192, 22016) == 22 * 32 * 8192 * 4   # four-wave ranges of 1024
     assert lib.w4a16_linear_xres_workspace(16, 8192, 22016) == 11 * 16 * 8192 * 4
+    for m, n, k in [(4, 1024, 8192), (9, 11008, 4096), (24, 28672, 8192), (17, 4096, 4096), (1, 1, 256)]:
+        s = _xres_ranges(m, n, k)
+        assert lib.w4a16_linear_xres_workspace(m, n, k) == (s * m * n * 4 if s > 1 else 0), (m, n, k)
     assert lib.w4a16_linear_xres_workspace(33, 4096, 4096) == -1   # M > 32
     assert lib.w4a16_linear_xres_workspace(8, 4096, 384) == -1     # odd number of groups
     assert lib.w4a16_linear_xres_workspace(0, 4096, 4096) == -1
@@ -286,12 +304,14 @@ def test_linear_ws_split_choice_and_rejects():
              (192, 22016, 8192): 0, (128, 22016, 8192): 2, (64, 1024, 8192): 8,
              (256, 4096, 4096): 2, (192, 4096, 4096): 2, (128, 4096, 4096): 0, (64, 4096, 4096): 4,
              (48, 11008, 4096): 2, (128, 11008, 4096): 0, (64, 8192, 1024): 0, (64, 64, 2048): 0}
-    # the x-resident kernel (8 <= M <= 32, K > 2048; with W = ceil(N / 128) * ceil(K / 2048) its
-    # workgroups: W >= 512, or M >= 12 with N > K and W >= 160, or M >= 16 with W >= 256); the
-    # workspace covers both kernels' needs
-    xres = {(32, 8192, 8192), (24, 8192, 8192), (20, 11008, 4096), (17, 8192, 22016), (32, 16384, 8192),
-            (32, 8192, 22016), (24, 22016, 8192), (32, 11008, 4096), (12, 11008, 4096), (16, 8192, 8192),
-            (8, 8192, 22016), (8, 28672, 8192)}
+    # the x-resident kernel (K > 2048, an even number of groups; M = 4..16: N K >= 2^27, or
+    # M >= 8 with N K >= 2^25 and N > K, or M >= 8 with ceil(N / 32) <= 64 and K >= 8192, or
+    # M >= 12 with N K >= 2^25; M = 17..32, with W = ceil(N / 128) ceil(K / 2048): W >= 256, or
+    # N > K with W >= 160); the workspace covers both kernels' needs
+    xres = {(4, 8192, 22016), (8, 8192, 22016), (8, 11008, 4096), (8, 28672, 8192), (12, 8192, 8192),
+            (12, 11008, 4096), (16, 4096, 11008), (16, 8192, 8192), (17, 8192, 22016), (20, 11008, 4096),
+            (24, 8192, 8192), (24, 22016, 8192), (32, 8192, 8192), (32, 8192, 22016), (32, 11008, 4096),
+            (32, 16384, 8192)}
     for extra in ((12, 11008, 4096), (12, 8192, 8192), (16, 8192, 8192), (8, 8192, 22016), (8, 28672, 8192),
                   (4, 8192, 22016), (8, 11008, 4096)):
         cases[extra] = 0
@@ -299,9 +319,7 @@ def test_linear_ws_split_choice_and_rejects():
         assert lib.w4a16_linear_ws_splits(m, n, k, 128) == s, (m, n, k)
         want_x = (m, n, k) in xres
         assert lib.w4a16_linear_ws_kernel(m, n, k, 128) == (2 if want_x else 1 if s else 0), (m, n, k)
-        # K ranges of 2048 inputs, or 1024 with two m-tiles on at least 512 eight-wave workgroups
-        rng = 1024 if m > 16 and -(-n // 128) * -(-k // 2048) >= 512 else 2048
-        xf = -(-k // rng) * m * n if want_x else 0
+        xf = _xres_ranges(m, n, k) * m * n if want_x else 0
         assert lib.w4a16_linear_workspace(m, n, k, 128) == max(s * m * n, xf) * 4, (m, n, k)
     assert lib.w4a16_linear_ws_kernel(32, 8192, 8192, 64) == 0
     assert lib.w4a16_linear_ws_kernel(32, 8192, 8320, 128) == 0   # odd number of groups

@@ -335,7 +335,7 @@ def test_auto_with_workspace_takes_split_k(lib, m, k, n):
 
 @pytest.mark.parametrize("m,k,n", [(32, 22016, 8192), (21, 8192, 22016), (30, 4096, 11008), (17, 22016, 8192),
                                    (12, 4096, 11008), (24, 8192, 8192), (16, 4096, 20480), (8, 22016, 8192),
-                                   (16, 8192, 8192)])
+                                   (16, 8192, 8192), (4, 22016, 8192), (8, 8192, 1024), (12, 11008, 4096)])
 def test_auto_with_workspace_takes_x_resident(lib, m, k, n):
     # shapes where the automatic path with a workspace runs the x-resident small-batch kernel:
     # every output against the oracle,

@@ -75,6 +75,10 @@ def test_xres_four_wave_ranges(lib, m):
     s, packed = _packed(9, 2, n, k)
     x = oracle.scale_input(synth.activations(9, 2, m, k), s)
     assert lib.xres_workspace_bytes(m, n, k) == 3 * m * n * 4
+    if m == 17:
+        # and M <= 16 on the same layer: 64-column workgroups of eight waves (514 of them)
+        x16 = oracle.scale_input(synth.activations(9, 2, 16, k), s)
+        _check(lib, x16, packed, "64-column")
     _check(lib, x, packed, "four-wave")
 
 

@@ -135,23 +135,32 @@ int auto_splits(int64_t M, int64_t N, int64_t K) {
 }
 
 // The x-resident kernel on the automatic path with a workspace (4-bit, groups of 128, scales
-// and zeros 4-byte aligned, an even number of groups per row, K > 2048), with W = ceil(N / 128) *
-// ceil(K / 2048) its workgroups: from M = 8 where W >= 512, from M = 12 on layers wider than
-// they are long with W >= 160, and from M = 16 where W >= 256. From a sweep of M = 4..32 over
-// nine layer shapes (MI355X, graph-timed us, x-resident / the automatic choice before it):
-// 22016 -> 8192 at M = 8 / 16 / 32 27.7 / 29.4 / 43.5 against 37.2 / 42.4 / 44.2; 8192 -> 28672
-// at M = 8 / 16 / 32 33.5 / 37.2 / 56.8 against 41.2 / 50.4 / 68.2; 28672 -> 8192 at M = 8 / 16
-// 34.7 / 37.6 against 37.7 / 44.2; 8192 -> 22016 at M = 8 / 32 27.4 / 44.2 against 31.7 / 52.5;
-// 4096 -> 11008 at M = 12 / 32 12.5 / 16.0 against 14.0 / 19.1; 8192 -> 8192 at M = 16 / 32
-// 14.3 / 17.2 against 14.8 / 21.1. It loses where its grid is short (4096 -> 4096: 64
-// workgroups, 11.9 against 5.9 at M = 16; 8192 -> 1024: 32; 11008 -> 4096: 192, 16.7 against
-// 16.4 at M = 24 with split-K), at M = 4 (8192 -> 8192: 13.8 against 10.5) and below M = 16 on
-// 8192 -> 8192 (14.0 against 14.0 at M = 12).
+// and zeros 4-byte aligned, an even number of groups per row, K > 2048). Up to M = 16 (its
+// 64-column workgroups): from M = 4 on layers of at least 2^27 weights, from M = 8 on layers
+// of at least 2^25 weights wider than they are long, or where the small-batch kernel's grid is
+// at most 64 workgroups on rows of 8192 inputs or more, and from M = 12 on layers of at least
+// 2^25 weights. From M = 17 (128-column workgroups), with W = ceil(N / 128) * ceil(K / 2048):
+// where W >= 512, on layers wider than long with W >= 160, and where W >= 256. From sweeps of
+// M = 4..32 over nine layer shapes (MI355X, graph-timed us, x-resident / the automatic choice
+// before it): 22016 -> 8192 at M = 4 / 16 / 32 25.0 / 27.8 / 39.0 against 31.8 / 42.5 / 44.2;
+// 8192 -> 28672 at M = 4 / 16 / 32 29.4 / 34.2 / 46.0 against 31.1 / 50.2 / 68.2; 8192 -> 1024
+// at M = 8 / 16 6.9 / 6.9 against 7.1 / 9.4; 4096 -> 11008 at M = 8 / 32 10.7 / 16.0 against
+// 11.6 / 19.1; 11008 -> 4096 at M = 12 / 16 12.6 / 12.9 against 13.4 / 13.9; 8192 -> 8192 at
+// M = 12 / 16 / 32 13.0 / 13.2 / 17.2 against 14.1 / 14.6 / 21.1. It loses on 4096 -> 4096 at
+// every M (7.4 against 5.9 at M = 16), below the thresholds above (8192 -> 8192 at M = 8: 12.7
+// against 12.1) and from M = 20 on 11008 -> 4096 and 8192 -> 1024 (16.5 against 15.9 with
+// split-K; 14.8 against 12.0).
 bool auto_xres(int64_t M, int64_t N, int64_t K) {
   // K > 2048: the kernel then takes its workspace (one range needs none and is not measured here)
-  if (M < 8 || K <= 2048 || !w4a16::xres_supports(M, K)) return false;
-  const int64_t W = ((N + 127) / 128) * ((K / 128 + 15) / 16);  // eight-wave workgroups
-  return W >= 512 || (M >= 12 && N > K && W >= 160) || (M >= 16 && W >= 256);
+  if (M < 4 || K <= 2048 || !w4a16::xres_supports(M, K)) return false;
+  if (M <= 16) {
+    const int64_t w = N * K;
+    if (w >= (int64_t(1) << 27)) return true;
+    if (M >= 8 && ((N > K && w >= (int64_t(1) << 25)) || ((N + 31) / 32 <= 64 && K >= 8192))) return true;
+    return M >= 12 && w >= (int64_t(1) << 25);
+  }
+  const int64_t W = ((N + 127) / 128) * ((K / 128 + 15) / 16);  // eight-wave 128-column workgroups
+  return W >= 512 || (N > K && W >= 160) || W >= 256;
 }
 
 // float32 workspace the automatic path may use (groups of 128): the larger of the two

@@ -11,12 +11,13 @@
 // Why another small-batch kernel. The small-batch kernel's workgroups own 32 output columns
 // and all of K, so each of them reads all of x: at M = 32 on an 8192 x 8192 layer that is
 // 128 MB of L2-to-L1 traffic beside 34 MB of codes, and that path sets its time. Here a
-// workgroup owns 128 columns and one range of 2048 inputs (16 groups; 1024 inputs with four
-// waves, see xres_waves). Each of its waves loads the x fragments of its 256 inputs (two
-// groups, 16 or 32 rows) once, keeps them in registers, and streams the codes of all 128
-// columns past them: x crosses L2 -> L1 once per 128 columns (8 MB at M = 32 on 8192 x 8192). Every x, scale, zero and code load of a wave
-// is issued before its first MFMA (16 KB of codes per wave in flight), so the weight stream
-// keeps the GEMV's depth.
+// workgroup owns 64 or 128 columns and one range of 256 inputs per wave (eight or four waves,
+// see xres_config). Each of its waves loads the x fragments of its 256 inputs (two groups, 16
+// or 32 rows) once, keeps them in registers, and streams the codes of all the workgroup's
+// columns past them: x crosses L2 -> L1 once per 64 or 128 columns (8 MB at M = 32 on
+// 8192 x 8192). Every x, scale, zero and code load of a wave
+// is issued before its first MFMA (8 or 16 KB of codes per wave in flight), so the weight
+// stream keeps the GEMV's depth.
 //
 // Per 16-column n-tile and group the four MFMA steps accumulate sum x (q - z) exactly (fp16
 // (q - z) B fragments while z lies in [-2032, 1024]; a wave meeting another zero takes exact q
@@ -33,8 +34,6 @@ namespace w4a16 {
 namespace {
 
 constexpr int kXrGroups = 2;                           // groups of 128 inputs per wave
-constexpr int kXrTiles = 8;                            // 16-column n-tiles per wave
-constexpr int kXrCols = 16 * kXrTiles;                 // 128 output columns per workgroup
 
 // grid: ceil(N / 128) * S items, item = n-tile * S + range (ranges of one n-tile adjacent);
 // MT 16-row m-tiles (M <= 16 * MT)
@@ -49,7 +48,7 @@ constexpr int kXrCols = 16 * kXrTiles;                 // 128 output columns per
 // of LDS and 128 VGPRs, two per CU. Measured (timing-only copies, 8192 x 8192 at M = 4):
 // half-line code loads cost 2.5 us; on 22016 -> 8192 at M = 16 (three rounds of workgroups)
 // one workgroup per CU cost 6-8 us against two.
-template <int MT, int WV, bool DIRECT>
+template <int MT, int WV, int NT, bool DIRECT>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
 void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
                  const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int S,
@@ -58,7 +57,11 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   // partial tiles
   constexpr int kXrThreads = 64 * WV;
   constexpr int kXrRangeGroups = WV * kXrGroups;  // groups per K range
-  __shared__ float4_t red[WV][kXrTiles * MT][64];
+  constexpr int kXrTiles = NT;                     // 16-column n-tiles per wave
+  constexpr int kXrCols = 16 * NT;                 // output columns per workgroup
+  constexpr int kSlotTiles = NT < 8 ? 8 : NT;      // slots per m-tile: x needs 8 KB per m-tile
+  constexpr bool kSpare = NT * MT <= kSlotTiles * MT - 2;  // two slots past the partial tiles
+  __shared__ float4_t red[WV][kSlotTiles * MT][64];
   __shared__ u32x4_t wsz[WV][64];  // the wave's (scale pair) [128] then (zero pair) [128] words
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
@@ -77,9 +80,9 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   const __amdgpu_buffer_rsrc_t rz = rsrc(zeros + (int64_t)n0 * G, (int64_t)rows_n * G * 2);
 
   // (1) the wave's (scale, zero) pairs (groups g0, g0 + 1) of rows lane and lane + 64
-  uint32_t sv[2], zv[2];
+  uint32_t sv[NT / 4], zv[NT / 4];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NT / 4; ++u) {
     const int off = (lane + 64 * u) * G * 2 + g0 * 2 + past;
     sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
     zv[u] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
@@ -96,7 +99,7 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   //     With one m-tile the last n-tile's codes are issued after the first n-tile's compute (its
   //     registers then free), which keeps the wave within 128 VGPRs (two workgroups per CU).
   u32x4_t q[kXrTiles][2];
-  constexpr int kLate = MT == 1 ? kXrTiles - 1 : kXrTiles;  // n-tiles issued up front
+  constexpr int kLate = MT == 1 && NT == 8 ? kXrTiles - 1 : kXrTiles;  // n-tiles issued up front
   auto issue_codes = [&](int tt) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -128,7 +131,7 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
       for (int s = 0; s < 4; ++s) xf[mt][h][s] = xs[(16 * mt + c) * 32 + 16 * h + ((4 * j + s) ^ c)];
   uint32_t* sz = reinterpret_cast<uint32_t*>(&wsz[wave][0]);
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
+  for (int u = 0; u < NT / 4; ++u) {
     sz[lane + 64 * u] = sv[u];
     sz[kXrCols + lane + 64 * u] = zv[u];
   }
@@ -142,15 +145,16 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   //     (scale, zero) area, whose pairs that tile has read by then.
   const u32x4_t ones_bits = {0x3C003C00u, 0x3C003C00u, 0x3C003C00u, 0x3C003C00u};
   const half8_t ones = as_half8(ones_bits);
-  u32x4_t* half_a = reinterpret_cast<u32x4_t*>(&red[wave][kXrTiles * MT - 1][0]);
-  u32x4_t* half_b = reinterpret_cast<u32x4_t*>(&red[wave][kXrTiles * MT - 2][0]);
+  u32x4_t* half_a = reinterpret_cast<u32x4_t*>(&red[wave][kSlotTiles * MT - 1][0]);
+  u32x4_t* half_b = reinterpret_cast<u32x4_t*>(&red[wave][kSlotTiles * MT - 2][0]);
 #pragma unroll
   for (int tt = 0; tt < kXrTiles; ++tt) {
     const uint32_t spair = sz[16 * tt + c], zpair = sz[kXrCols + 16 * tt + c];
-    u32x4_t* hb = (MT == 1 && tt == kXrTiles - 1) ? &wsz[wave][0] : half_b;
+    constexpr bool kBorrow = !kSpare && MT == 1;  // the last n-tile's half B is the pairs' area
+    u32x4_t* hb = (kBorrow && tt == kXrTiles - 1) ? &wsz[wave][0] : half_b;
     // the pairs are read through another type than the stage is written with: keep the reads
     // first where they share the area
-    if (MT == 1 && tt == kXrTiles - 1) asm volatile("" ::: "memory");
+    if (kBorrow && tt == kXrTiles - 1) asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = lane >> 3;
@@ -208,6 +212,7 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
 #pragma unroll
   for (int u0 = 0; u0 < kSlots; u0 += kXrThreads) {
     const int u = u0 + t;
+    if (kSlots % kXrThreads != 0 && u >= kSlots) break;
     const int tile = u >> 6, ln = u & 63;
     float4_t sum = red[0][tile][ln];
 #pragma unroll
@@ -229,17 +234,17 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   }
 }
 
-template <int MT, int WV>
+template <int MT, int WV, int NT>
 hipError_t launch_mt(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, const uint16_t* zr, int64_t M,
                      int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
   const int S = (int)((K / 128 + WV * kXrGroups - 1) / (WV * kXrGroups));
-  const int64_t items = ((N + kXrCols - 1) / kXrCols) * S;
+  const int64_t items = ((N + 16 * NT - 1) / (16 * NT)) * S;
   if (S == 1)
-    hipLaunchKernelGGL((xres_kernel<MT, WV, true>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc, zr,
-                       (int)M, (int)N, (int)K, 1, nullptr, y);
+    hipLaunchKernelGGL((xres_kernel<MT, WV, NT, true>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc,
+                       zr, (int)M, (int)N, (int)K, 1, nullptr, y);
   else
-    hipLaunchKernelGGL((xres_kernel<MT, WV, false>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc, zr,
-                       (int)M, (int)N, (int)K, S, workspace, nullptr);
+    hipLaunchKernelGGL((xres_kernel<MT, WV, NT, false>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc,
+                       zr, (int)M, (int)N, (int)K, S, workspace, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
   return launch_splitk_reduce(workspace, M, N, S, y, stream);
@@ -249,16 +254,34 @@ hipError_t launch_mt(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, 
 
 int xres_max_m() { return 32; }
 
-// Waves per workgroup (two groups of 128 inputs each; a K range is 256 * waves inputs): eight,
-// or four with two m-tiles where eight-wave workgroups would come to at least 512 (two or more
-// rounds of the chip). Four-wave workgroups of two m-tiles take 68 KB of LDS, so two share a
-// CU and the rounds overlap: 22016 -> 8192 at M = 32 39.0 against 43.8 us, 8192 -> 28672 46.5
-// against 57.8; on one round they lose (8192 -> 8192 at M = 32: 18.1 against 17.3), and with
-// one m-tile (where eight-wave workgroups already pair up) they lose everywhere measured
-// (22016 -> 8192 at M = 16: 31.5 against 29.2).
+// The workgroup shape: waves (two groups of 128 inputs each; a K range is 256 * waves inputs)
+// and 16-column n-tiles per wave. From timings of the four shapes (graph-timed us, partials and
+// reduction; waves x n-tiles):
+// - one m-tile (M <= 16): four n-tiles (64 columns; 94 VGPRs and 36 or 72 KB of LDS, so 16
+//   waves share a CU), eight waves where such workgroups come to at least 512, else four:
+//   8192 -> 8192 at M = 16 13.3 (8 x 4) against 14.6 (8 x 8) and 13.8 (4 x 4); 22016 -> 8192
+//   at M = 16 28.2 against 29.3; 8192 -> 28672 at M = 8 31.6 against 34.0; 8192 -> 1024 at
+//   M = 16 6.8 (4 x 4) against 8.4 (8 x 4) and 12.2 (8 x 8); 4096 -> 11008 at M = 8 10.7 (4 x 4)
+//   against 11.7 (8 x 4); 11008 -> 4096 at M = 16 13.1 against 13.7;
+// - two m-tiles: eight n-tiles, four waves where eight-wave workgroups would come to at least
+//   512 (two or more rounds of the chip: 68 KB of LDS, two per CU), else eight: 22016 -> 8192 at
+//   M = 32 40.4 (4 x 8) against 45.0 (8 x 8), 8192 -> 28672 at M = 32 47.9 against 59.4;
+//   8192 -> 8192 at M = 32 17.8 (8 x 8) against 18.7 (4 x 8) and 18.0 (4 x 4).
+void xres_config(int64_t M, int64_t N, int64_t K, int* waves, int* tiles) {
+  const int64_t ranges8 = (K / 128 + 15) / 16;
+  if (M <= 16) {
+    *tiles = 4;
+    *waves = ((N + 63) / 64) * ranges8 >= 512 ? 8 : 4;
+  } else {
+    *tiles = 8;
+    *waves = ((N + 127) / 128) * ranges8 >= 512 ? 4 : 8;
+  }
+}
+
 int xres_waves(int64_t M, int64_t N, int64_t K) {
-  const int64_t w8 = ((N + kXrCols - 1) / kXrCols) * ((K / 128 + 15) / 16);
-  return M > 16 && w8 >= 512 ? 4 : 8;
+  int waves, tiles;
+  xres_config(M, N, K, &waves, &tiles);
+  return waves;
 }
 
 int xres_ranges(int64_t M, int64_t N, int64_t K) {
@@ -273,19 +296,25 @@ int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K) {
   return S == 1 ? 0 : (int64_t)S * M * N;
 }
 
-hipError_t launch_xres_waves(int waves, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
-                             const uint16_t* zeros, int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y,
-                             hipStream_t stream) {
-  if (M <= 16)
-    return waves == 4 ? launch_mt<1, 4>(x, qweight, scales, zeros, M, N, K, workspace, y, stream)
-                      : launch_mt<1, 8>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
-  return waves == 4 ? launch_mt<2, 4>(x, qweight, scales, zeros, M, N, K, workspace, y, stream)
-                    : launch_mt<2, 8>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+hipError_t launch_xres_config(int waves, int tiles, const uint16_t* x, const uint32_t* qweight,
+                              const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
+                              float* workspace, uint16_t* y, hipStream_t stream) {
+#define W4A16_XRES(MT, WV, NT) \
+  if (waves == WV && tiles == NT) return launch_mt<MT, WV, NT>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  if (M <= 16) {
+    W4A16_XRES(1, 8, 8) W4A16_XRES(1, 4, 8) W4A16_XRES(1, 4, 4) W4A16_XRES(1, 8, 4)
+  } else {
+    W4A16_XRES(2, 8, 8) W4A16_XRES(2, 4, 8) W4A16_XRES(2, 4, 4) W4A16_XRES(2, 8, 4)
+  }
+#undef W4A16_XRES
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
-  return launch_xres_waves(xres_waves(M, N, K), x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  int waves, tiles;
+  xres_config(M, N, K, &waves, &tiles);
+  return launch_xres_config(waves, tiles, x, qweight, scales, zeros, M, N, K, workspace, y, stream);
 }
 
 }  // namespace w4a16

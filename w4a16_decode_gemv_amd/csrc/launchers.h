@@ -90,17 +90,20 @@ hipError_t launch_splitk_reduce(const float* part, int64_t M, int64_t N, int S, 
 // groups per row) and scales and zeros 4-byte aligned; with more than one range, a float32
 // workspace of xres_workspace_floats(M, N, K) floats.
 int xres_max_m();
-int xres_waves(int64_t M, int64_t N, int64_t K);  // waves per workgroup; a K range is 256 * waves inputs
+// the workgroup shape launch_xres takes: waves (a K range is 256 * waves inputs) and 16-column
+// n-tiles per wave
+void xres_config(int64_t M, int64_t N, int64_t K, int* waves, int* tiles);
+int xres_waves(int64_t M, int64_t N, int64_t K);
 int xres_ranges(int64_t M, int64_t N, int64_t K);
 bool xres_supports(int64_t M, int64_t K);
 int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K);
 hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream);
-// the same with 4 or 8 waves per workgroup (ranges of 1024 or 2048 inputs; the workspace holds
-// the ranges of that choice)
-hipError_t launch_xres_waves(int waves, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales,
-                             const uint16_t* zeros, int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y,
-                             hipStream_t stream);
+// the same with 4 or 8 waves per workgroup (ranges of 1024 or 2048 inputs) and 4 or 8 n-tiles
+// per wave (64 or 128 columns per workgroup); the workspace holds the ranges of that choice
+hipError_t launch_xres_config(int waves, int tiles, const uint16_t* x, const uint32_t* qweight,
+                              const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
+                              float* workspace, uint16_t* y, hipStream_t stream);
 
 // Tiled MFMA kernel: any M >= 1. mfma_workgroups: the workgroups launch_mfma starts (for M > 16).
 int64_t mfma_workgroups(int64_t M, int64_t N);
