@@ -26,6 +26,8 @@
 // rounded to fp16 and written to y; otherwise range s writes its tile to the
 // caller's workspace P[s][m][n] and the split-K reduction kernel adds the ranges in index
 // order and rounds once. Results are reproducible.
+#include <type_traits>
+
 #include "device_utils.h"
 #include "launchers.h"
 
@@ -62,7 +64,7 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   constexpr int kSlotTiles = NT < 8 ? 8 : NT;      // slots per m-tile: x needs 8 KB per m-tile
   constexpr bool kSpare = NT * MT <= kSlotTiles * MT - 2;  // two slots past the partial tiles
   __shared__ float4_t red[WV][kSlotTiles * MT][64];
-  __shared__ u32x4_t wsz[WV][64];  // the wave's (scale pair) [128] then (zero pair) [128] words
+  __shared__ u32x4_t wsz[WV][12 * NT];  // the wave's (scale, zero) table, 3 x 16 NT words  // the wave's (scale pair) [128] then (zero pair) [128] words
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
   const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
@@ -129,11 +131,34 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
     for (int h = 0; h < kXrGroups; ++h)
 #pragma unroll
       for (int s = 0; s < 4; ++s) xf[mt][h][s] = xs[(16 * mt + c) * 32 + 16 * h + ((4 * j + s) ^ c)];
+  // The wave's table: word r the scale pair of row r; then, when every zero of the wave lies in
+  // [-2032, 1024] (one ballot), words kXrCols + r and 2 kXrCols + r the two groups' fp16 pair
+  // (-(1024 + z), -(64 + z)) that rebuilds q - z exactly, else word kXrCols + r the zero pair
+  // (the general route: exact q and z * sum x).
   uint32_t* sz = reinterpret_cast<uint32_t*>(&wsz[wave][0]);
+  bool in_range = true;
+#pragma unroll
+  for (int u = 0; u < NT / 4; ++u)
+#pragma unroll
+    for (int h = 0; h < kXrGroups; ++h) {
+      const float zf = half_bits_to_float((uint16_t)(zv[u] >> (16 * h)));
+      in_range = in_range && zf >= -2032.0f && zf <= 1024.0f;
+    }
+  const bool fast = __builtin_amdgcn_ballot_w64(!in_range) == 0;
 #pragma unroll
   for (int u = 0; u < NT / 4; ++u) {
     sz[lane + 64 * u] = sv[u];
-    sz[kXrCols + lane + 64 * u] = zv[u];
+    if (fast) {
+#pragma unroll
+      for (int h = 0; h < kXrGroups; ++h) {
+        const _Float16 zh = __builtin_bit_cast(_Float16, (uint16_t)(zv[u] >> (16 * h)));
+        const _Float16 clo = -((_Float16)1024.0f + zh), chi = -((_Float16)64.0f + zh);
+        sz[(1 + h) * kXrCols + lane + 64 * u] =
+            (uint32_t)__builtin_bit_cast(uint16_t, clo) | ((uint32_t)__builtin_bit_cast(uint16_t, chi) << 16);
+      }
+    } else {
+      sz[kXrCols + lane + 64 * u] = zv[u];
+    }
   }
 
   // (4) compute each n-tile as its codes land. Its two loads go to the stage: rows 0..7 to half
@@ -147,12 +172,15 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   const half8_t ones = as_half8(ones_bits);
   u32x4_t* half_a = reinterpret_cast<u32x4_t*>(&red[wave][kSlotTiles * MT - 1][0]);
   u32x4_t* half_b = reinterpret_cast<u32x4_t*>(&red[wave][kSlotTiles * MT - 2][0]);
+  auto tiles = [&](auto route) {
+    constexpr bool FAST = decltype(route)::value;
 #pragma unroll
   for (int tt = 0; tt < kXrTiles; ++tt) {
-    const uint32_t spair = sz[16 * tt + c], zpair = sz[kXrCols + 16 * tt + c];
-    constexpr bool kBorrow = !kSpare && MT == 1;  // the last n-tile's half B is the pairs' area
+    const int row = 16 * tt + c;
+    const uint32_t spair = sz[row], w1 = sz[kXrCols + row], w2 = FAST ? sz[2 * kXrCols + row] : 0u;
+    constexpr bool kBorrow = !kSpare && MT == 1;  // the last n-tile's half B is the table's area
     u32x4_t* hb = (kBorrow && tt == kXrTiles - 1) ? &wsz[wave][0] : half_b;
-    // the pairs are read through another type than the stage is written with: keep the reads
+    // the table is read through another type than the stage is written with: keep the reads
     // first where they share the area
     if (kBorrow && tt == kXrTiles - 1) asm volatile("" ::: "memory");
 #pragma unroll
@@ -169,12 +197,9 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
 #pragma unroll
     for (int h = 0; h < kXrGroups; ++h) {
       const float d = half_bits_to_float((uint16_t)(spair >> (16 * h)));
-      const _Float16 zh = __builtin_bit_cast(_Float16, (uint16_t)(zpair >> (16 * h)));
-      const float zf = (float)zh;
-      const bool exact = zf >= -2032.0f && zf <= 1024.0f;
-      const bool fast = __builtin_amdgcn_ballot_w64(!exact) == 0;
-      const _Float16 clo = fast ? -((_Float16)1024.0f + zh) : (_Float16)-1024.0f;
-      const _Float16 chi = fast ? -((_Float16)64.0f + zh) : (_Float16)-64.0f;
+      const uint32_t cw = FAST ? (h ? w2 : w1) : 0xD400E400u;  // (-1024, -64): exact q
+      const _Float16 clo = __builtin_bit_cast(_Float16, (uint16_t)(cw & 0xFFFFu));
+      const _Float16 chi = __builtin_bit_cast(_Float16, (uint16_t)(cw >> 16));
       const half2_t c_lo = {clo, clo}, c_hi = {chi, chi};
       const half8_t bq[4] = {dequant_word(qc[h].x, c_lo, c_hi), dequant_word(qc[h].y, c_lo, c_hi),
                              dequant_word(qc[h].z, c_lo, c_hi), dequant_word(qc[h].w, c_lo, c_hi)};
@@ -183,10 +208,11 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
         float4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][s]), bq[s], a, 0, 0, 0);
-        if (fast) {
+        if constexpr (FAST) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, a[i], acc[mt][i]);
         } else {
+          const float zf = half_bits_to_float((uint16_t)(w1 >> (16 * h)));
           float4_t sx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int s = 0; s < 4; ++s) sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][s]), ones, sx, 0, 0, 0);
@@ -204,6 +230,11 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+  };
+  if (fast)
+    tiles(std::true_type{});
+  else
+    tiles(std::false_type{});
   __syncthreads();
 
   // (5) the eight waves' tiles added in wave order; each thread takes whole D-fragment slots
@@ -301,10 +332,11 @@ hipError_t launch_xres_config(int waves, int tiles, const uint16_t* x, const uin
                               float* workspace, uint16_t* y, hipStream_t stream) {
 #define W4A16_XRES(MT, WV, NT) \
   if (waves == WV && tiles == NT) return launch_mt<MT, WV, NT>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  // the shapes xres_config chooses
   if (M <= 16) {
-    W4A16_XRES(1, 8, 8) W4A16_XRES(1, 4, 8) W4A16_XRES(1, 4, 4) W4A16_XRES(1, 8, 4)
+    W4A16_XRES(1, 4, 4) W4A16_XRES(1, 8, 4)
   } else {
-    W4A16_XRES(2, 8, 8) W4A16_XRES(2, 4, 8) W4A16_XRES(2, 4, 4) W4A16_XRES(2, 8, 4)
+    W4A16_XRES(2, 8, 8) W4A16_XRES(2, 4, 8)
   }
 #undef W4A16_XRES
   return hipErrorInvalidValue;

@@ -99,8 +99,9 @@ bool xres_supports(int64_t M, int64_t K);
 int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K);
 hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream);
-// the same with 4 or 8 waves per workgroup (ranges of 1024 or 2048 inputs) and 4 or 8 n-tiles
-// per wave (64 or 128 columns per workgroup); the workspace holds the ranges of that choice
+// the same with 4 or 8 waves per workgroup (ranges of 1024 or 2048 inputs) and 4 n-tiles per
+// wave (64 columns) for M <= 16, 8 (128 columns) above; the workspace holds the ranges of that
+// choice; another shape returns hipErrorInvalidValue
 hipError_t launch_xres_config(int waves, int tiles, const uint16_t* x, const uint32_t* qweight,
                               const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
                               float* workspace, uint16_t* y, hipStream_t stream);
