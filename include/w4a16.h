@@ -243,8 +243,7 @@ int32_t w4a16_linear_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group);
  * scales and zeros are 4-byte aligned and: for 4 <= M <= 16, N * K >= 2^27, or
  * M >= 8 with N * K >= 2^25 and N > K, or M >= 8 with ceil(N / 32) <= 64 and
  * K >= 8192, or M >= 12 with N * K >= 2^25; for 17 <= M <= 32, with
- * W = ceil(N / 128) * ceil(K / 2048), W >= 256, or N > K with W >= 160;
- * otherwise split-K: no split for M <= 16; else with G = K / 128 and T
+ * W = ceil(N / 128) * ceil(K / 2048), W >= 160; otherwise split-K: no split for M <= 16; else with G = K / 128 and T
  * the split-K kernel's tiles (ceil(N / 128) for M <= 32, else ceil(M / 64) *
  * ceil(N / 128)), for K >= 8192: no split up to M = 32 when K <= 16384 and
  * ceil(N / 32) is a multiple of 256 (the small-batch kernel's grid fills the

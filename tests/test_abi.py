@@ -306,12 +306,12 @@ def test_linear_ws_split_choice_and_rejects():
              (48, 11008, 4096): 2, (128, 11008, 4096): 0, (64, 8192, 1024): 0, (64, 64, 2048): 0}
     # the x-resident kernel (K > 2048, an even number of groups; M = 4..16: N K >= 2^27, or
     # M >= 8 with N K >= 2^25 and N > K, or M >= 8 with ceil(N / 32) <= 64 and K >= 8192, or
-    # M >= 12 with N K >= 2^25; M = 17..32, with W = ceil(N / 128) ceil(K / 2048): W >= 256, or
-    # N > K with W >= 160); the workspace covers both kernels' needs
+    # M >= 12 with N K >= 2^25; M = 17..32, with W = ceil(N / 128) ceil(K / 2048): W >= 160); the
+    # workspace covers both kernels' needs
     xres = {(4, 8192, 22016), (8, 8192, 22016), (8, 11008, 4096), (8, 28672, 8192), (12, 8192, 8192),
             (12, 11008, 4096), (16, 4096, 11008), (16, 8192, 8192), (17, 8192, 22016), (20, 11008, 4096),
             (24, 8192, 8192), (24, 22016, 8192), (32, 8192, 8192), (32, 8192, 22016), (32, 11008, 4096),
-            (32, 16384, 8192)}
+            (32, 16384, 8192), (20, 4096, 11008), (32, 4096, 11008)}
     for extra in ((12, 11008, 4096), (12, 8192, 8192), (16, 8192, 8192), (8, 8192, 22016), (8, 28672, 8192),
                   (4, 8192, 22016), (8, 11008, 4096)):
         cases[extra] = 0

@@ -308,14 +308,13 @@ def test_auto_klane_route(lib, m, k, n):
     assert np.array_equal(g.bits16(a), g.bits16(b))
 
 
-@pytest.mark.parametrize("m,k,n", [(64, 11008, 4096), (256, 4096, 4096), (48, 4096, 11008), (24, 11008, 4096),
-                                   (256, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024), (20, 11008, 4096),
-                                   (32, 11008, 4096)])
+@pytest.mark.parametrize("m,k,n", [(64, 11008, 4096), (256, 4096, 4096), (48, 4096, 11008), (24, 8192, 1024),
+                                   (256, 8192, 8192), (40, 4096, 1000), (128, 8192, 1024), (32, 16384, 1024)])
 def test_auto_with_workspace_takes_split_k(lib, m, k, n):
     # the automatic path with a workspace (w4a16_linear_ws, the binding's default): shapes where
-    # it splits K (8, 2, 2, 8, 2, 4, 8, 8 and 2 ranges; the 32-row tiles of the partial kernel up
-    # to M = 32): every output against the oracle, and bit-identical to the split-K entry point
-    # with the same ranges
+    # it splits K (8, 2, 2, 8, 2, 4, 8 and 8 ranges; the 32-row tiles of the partial kernel up to
+    # M = 32): every output against the oracle, and bit-identical to the split-K entry point with
+    # the same ranges
     g = _gpu()
     splits = lib.linear_ws_splits(m, n, k)
     assert splits > 0 and lib.linear_ws_kernel(m, n, k) == 1
@@ -335,7 +334,8 @@ def test_auto_with_workspace_takes_split_k(lib, m, k, n):
 
 @pytest.mark.parametrize("m,k,n", [(32, 22016, 8192), (21, 8192, 22016), (30, 4096, 11008), (17, 22016, 8192),
                                    (12, 4096, 11008), (24, 8192, 8192), (16, 4096, 20480), (8, 22016, 8192),
-                                   (16, 8192, 8192), (4, 22016, 8192), (8, 8192, 1024), (12, 11008, 4096)])
+                                   (16, 8192, 8192), (4, 22016, 8192), (8, 8192, 1024), (12, 11008, 4096),
+                                   (24, 11008, 4096)])
 def test_auto_with_workspace_takes_x_resident(lib, m, k, n):
     # shapes where the automatic path with a workspace runs the x-resident small-batch kernel:
     # every output against the oracle,

@@ -139,17 +139,16 @@ int auto_splits(int64_t M, int64_t N, int64_t K) {
 // 64-column workgroups): from M = 4 on layers of at least 2^27 weights, from M = 8 on layers
 // of at least 2^25 weights wider than they are long, or where the small-batch kernel's grid is
 // at most 64 workgroups on rows of 8192 inputs or more, and from M = 12 on layers of at least
-// 2^25 weights. From M = 17 (128-column workgroups), with W = ceil(N / 128) * ceil(K / 2048):
-// where W >= 512, on layers wider than long with W >= 160, and where W >= 256. From sweeps of
-// M = 4..32 over nine layer shapes (MI355X, graph-timed us, x-resident / the automatic choice
-// before it): 22016 -> 8192 at M = 4 / 16 / 32 25.0 / 27.8 / 39.0 against 31.8 / 42.5 / 44.2;
-// 8192 -> 28672 at M = 4 / 16 / 32 29.4 / 34.2 / 46.0 against 31.1 / 50.2 / 68.2; 8192 -> 1024
-// at M = 8 / 16 6.9 / 6.9 against 7.1 / 9.4; 4096 -> 11008 at M = 8 / 32 10.7 / 16.0 against
-// 11.6 / 19.1; 11008 -> 4096 at M = 12 / 16 12.6 / 12.9 against 13.4 / 13.9; 8192 -> 8192 at
-// M = 12 / 16 / 32 13.0 / 13.2 / 17.2 against 14.1 / 14.6 / 21.1. It loses on 4096 -> 4096 at
-// every M (7.4 against 5.9 at M = 16), below the thresholds above (8192 -> 8192 at M = 8: 12.7
-// against 12.1) and from M = 20 on 11008 -> 4096 and 8192 -> 1024 (16.5 against 15.9 with
-// split-K; 14.8 against 12.0).
+// 2^25 weights. From M = 17 (128-column workgroups) where W = ceil(N / 128) * ceil(K / 2048)
+// >= 160. From sweeps of M = 4..32 over nine layer shapes (MI355X, graph-timed us, x-resident /
+// the automatic choice before it): 22016 -> 8192 at M = 4 / 16 / 32 23.9 / 27.4 / 36.0 against
+// 31.5 / 42.5 / 44.2; 8192 -> 28672 at M = 4 / 16 / 32 27.5 / 33.4 / 41.6 against 30.4 / 50.0 /
+// 68.2; 8192 -> 1024 at M = 8 / 16 6.5 / 6.6 against 7.1 / 9.4; 4096 -> 11008 at M = 8 / 32
+// 10.3 / 14.4 against 11.6 / 19.1; 11008 -> 4096 at M = 12 / 32 12.3 / 15.4 against 13.5 /
+// 17.2; 8192 -> 8192 at M = 12 / 16 / 32 12.6 / 12.9 / 15.5 against 14.0 / 14.6 / 21.1. It
+// loses on 4096 -> 4096 at every M (7.1 against 6.0 at M = 16), below the thresholds above
+// (8192 -> 8192 at M = 8: 12.3 against 12.1; 4096 -> 11008 at M = 4: 9.8 against 8.6) and from
+// M = 20 on 8192 -> 1024 (13.3 against 12.6).
 bool auto_xres(int64_t M, int64_t N, int64_t K) {
   // K > 2048: the kernel then takes its workspace (one range needs none and is not measured here)
   if (M < 4 || K <= 2048 || !w4a16::xres_supports(M, K)) return false;
@@ -160,7 +159,7 @@ bool auto_xres(int64_t M, int64_t N, int64_t K) {
     return M >= 12 && w >= (int64_t(1) << 25);
   }
   const int64_t W = ((N + 127) / 128) * ((K / 128 + 15) / 16);  // eight-wave 128-column workgroups
-  return W >= 512 || (N > K && W >= 160) || W >= 256;
+  return W >= 160;
 }
 
 // float32 workspace the automatic path may use (groups of 128): the larger of the two
