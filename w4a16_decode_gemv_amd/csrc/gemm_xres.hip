@@ -15,14 +15,13 @@
 // see xres_config). Each of its waves loads the x fragments of its 256 inputs (two groups, 16
 // or 32 rows) once, keeps them in registers, and streams the codes of all the workgroup's
 // columns past them: x crosses L2 -> L1 once per 64 or 128 columns (8 MB at M = 32 on
-// 8192 x 8192). Every x, scale, zero and code load of a wave
-// is issued before its first MFMA (8 or 16 KB of codes per wave in flight), so the weight
-// stream keeps the GEMV's depth.
+// 8192 x 8192). Every x, scale, zero and code load of a wave is issued before its first MFMA
+// (8 or 16 KB of codes per wave in flight), so the weight stream keeps the GEMV's depth.
 //
 // Per 16-column n-tile and group the four MFMA steps accumulate sum x (q - z) exactly (fp16
-// (q - z) B fragments while z lies in [-2032, 1024]; a wave meeting another zero takes exact q
-// and z * sum x for that group, sum x from an MFMA against ones), then acc += d * that. The
-// waves' float32 tiles are added through LDS in wave order. With one K range the sums are
+// (q - z) B fragments while every zero of the wave lies in [-2032, 1024]; otherwise the wave
+// takes exact q and z * sum x for all its groups, sum x from an MFMA against ones), then
+// acc += d * that. The waves' float32 tiles are added through LDS in wave order. With one K range the sums are
 // rounded to fp16 and written to y; otherwise range s writes its tile to the
 // caller's workspace P[s][m][n] and the split-K reduction kernel adds the ranges in index
 // order and rounds once. Results are reproducible.
@@ -37,19 +36,20 @@ namespace {
 
 constexpr int kXrGroups = 2;                           // groups of 128 inputs per wave
 
-// grid: ceil(N / 128) * S items, item = n-tile * S + range (ranges of one n-tile adjacent);
-// MT 16-row m-tiles (M <= 16 * MT)
+// grid: ceil(N / (16 NT)) * S items, item = n-tile * S + range (ranges of one n-tile
+// adjacent); WV waves, each with NT 16-column n-tiles and MT 16-row m-tiles (M <= 16 * MT)
 //
 // Loads are whole 128-byte lines: a code row's two groups (128 bytes) come from 8 lanes, an x
 // row's 512 bytes from 32 lanes. The MFMA fragments need lane (c, j) to hold row c, so codes
 // and x pass through LDS (XOR-swizzled, conflict-free both ways), inside the wave's slice of
 // the reduction area: x once, before that slice holds any partial tile, and each n-tile's codes
-// through the two slots written last (with one m-tile the last n-tile uses the wave's
-// (scale, zero) area for its second half, read before). Each wave keeps its own (scale, zero)
-// pairs: no workgroup barrier before the final sums. With one m-tile the workgroup fits 72 KB
-// of LDS and 128 VGPRs, two per CU. Measured (timing-only copies, 8192 x 8192 at M = 4):
-// half-line code loads cost 2.5 us; on 22016 -> 8192 at M = 16 (three rounds of workgroups)
-// one workgroup per CU cost 6-8 us against two.
+// through two slots that hold no partial tile yet (with one m-tile and eight n-tiles the last
+// n-tile uses the wave's (scale, zero) table for its second half, read before). Each wave keeps
+// its own (scale, zero) table: no workgroup barrier before the final sums. With one m-tile and
+// four n-tiles a workgroup needs 35 or 70 KB of LDS and at most 128 VGPRs, so 16 waves share a
+// CU. Measured (timing-only copies, 8192 x 8192 at M = 4): half-line code loads cost 2.5 us;
+// on 22016 -> 8192 at M = 16 (three rounds of workgroups) one workgroup per CU cost 6-8 us
+// against two.
 template <int MT, int WV, int NT, bool DIRECT>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
 void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
@@ -64,7 +64,7 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   constexpr int kSlotTiles = NT < 8 ? 8 : NT;      // slots per m-tile: x needs 8 KB per m-tile
   constexpr bool kSpare = NT * MT <= kSlotTiles * MT - 2;  // two slots past the partial tiles
   __shared__ float4_t red[WV][kSlotTiles * MT][64];
-  __shared__ u32x4_t wsz[WV][12 * NT];  // the wave's (scale, zero) table, 3 x 16 NT words  // the wave's (scale pair) [128] then (zero pair) [128] words
+  __shared__ u32x4_t wsz[WV][12 * NT];  // the wave's (scale, zero) table: 3 x 16 NT words
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
   const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
