@@ -102,3 +102,31 @@ def test_xres_nan_workspace_and_reproducible(lib):
     y1 = _check(lib, x, packed, "nan workspace", workspace=ws)
     y2 = g.host(lib.linear_xres(g.dev(x), *[g.dev(t) for t in packed]))
     assert np.array_equal(y1.view(np.uint16), y2.view(np.uint16))
+
+
+def test_auto_path_falls_back_on_two_byte_aligned_scales(lib):
+    # scales and zeros only 2-byte aligned: the automatic path with a workspace declines the
+    # x-resident kernel (which loads (scale, zero) pairs as 4-byte words) and takes the earlier
+    # choice within the same workspace; the kernel's own entry point refuses them
+    import torch
+
+    g = _gpu()
+    m, n, k = 16, 8192, 8192
+    assert lib.linear_ws_kernel(m, n, k) == 2
+    s, (qw, sc, zr) = _packed(4, 3, n, k)
+    x = oracle.scale_input(synth.activations(4, 3, m, k), s)
+    G = k // 128
+
+    def shifted(a):
+        buf = torch.zeros(a.size + 1, dtype=torch.float16, device=g.DEV)
+        buf[1:] = torch.from_numpy(np.ascontiguousarray(a).reshape(-1)).to(g.DEV)
+        return buf[1:].view(n, G)
+
+    sc_d, zr_d = shifted(sc), shifted(zr)
+    assert sc_d.data_ptr() % 4 == 2 and zr_d.data_ptr() % 4 == 2
+    print("x-resident fallback on 2-byte aligned scales", flush=True)
+    y = g.host(lib.linear(g.dev(x), g.dev(qw), sc_d, zr_d)).astype(np.float64)
+    y_ref, b = oracle.linear(x, qw, sc, zr)
+    assert np.all(oracle.within_tolerance(y, y_ref, b))
+    with pytest.raises(lib.W4A16Error):
+        lib.linear_xres(g.dev(x), g.dev(qw), sc_d, zr_d)
