@@ -238,12 +238,13 @@ int32_t w4a16_linear_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group);
  * workspace: NULL (then exactly w4a16_linear), or device memory of
  * workspace_bytes >= w4a16_linear_workspace(M, N, K, group) bytes, 16-byte
  * aligned, overwritten (two calls in flight at once need two workspaces).
- * Dispatch, groups of 128 with a workspace (from measured sweeps over the
- * LLaMA projection shapes): the x-resident kernel when K > 2048, K / 128 is even,
+ * Dispatch with a workspace (from measured sweeps over the LLaMA projection
+ * shapes), groups of 128 or 64: the x-resident kernel when K > 2048, K / 128 is even,
  * scales and zeros are 4-byte aligned and: for 4 <= M <= 16, N * K >= 2^27, or
  * M >= 8 with N * K >= 2^25 and N > K, or M >= 8 with ceil(N / 32) <= 64 and
  * K >= 8192, or M >= 12 with N * K >= 2^25; for 17 <= M <= 32, with
- * W = ceil(N / 128) * ceil(K / 2048), W >= 160; otherwise split-K: no split for M <= 16; else with G = K / 128 and T
+ * W = ceil(N / 128) * ceil(K / 2048), W >= 160; otherwise, groups of 128 only,
+ * split-K: no split for M <= 16; else with G = K / 128 and T
  * the split-K kernel's tiles (ceil(N / 128) for M <= 32, else ceil(M / 64) *
  * ceil(N / 128)), for K >= 8192: no split up to M = 32 when K <= 16384 and
  * ceil(N / 32) is a multiple of 256 (the small-batch kernel's grid fills the
@@ -318,7 +319,7 @@ w4a16_status w4a16_linear_splitk(const void* x, const void* qweight, const void*
 int64_t w4a16_linear_xres_workspace(int64_t M, int64_t N, int64_t K);
 
 /*
- * w4a16_linear_xres - w4a16_linear (4-bit, groups of 128) for small batches,
+ * w4a16_linear_xres - w4a16_linear (4-bit, groups of 128 or 64) for small batches,
  * 1 <= M <= 32, on the x-resident MFMA kernel: a workgroup owns 64 output
  * columns for M <= 16 (128 above) and one range of 256 inputs per wave (eight
  * waves, or four where M <= 16 and ceil(N / 64) * ceil(K / 2048) < 512, or
@@ -333,8 +334,10 @@ int64_t w4a16_linear_xres_workspace(int64_t M, int64_t N, int64_t K);
  * w4a16_linear, plus workspace: device memory of workspace_bytes >=
  * w4a16_linear_xres_workspace(M, N, K) bytes, 16-byte aligned, overwritten
  * (NULL allowed when that is 0; two calls in flight at once need two
- * workspaces). Needs (K / 128) even; scales and zeros 4-byte aligned.
- * Errors: those of w4a16_linear; W4A16_ERR_UNSUPPORTED (group != 128, M > 32,
+ * workspaces). Needs (K / 128) even; scales and zeros 4-byte aligned. With
+ * groups of 64 each MFMA step takes 32 contiguous inputs, so a group is two
+ * steps and is scaled after them (groups of 128: four).
+ * Errors: those of w4a16_linear; W4A16_ERR_UNSUPPORTED (group other than 128 or 64, M > 32,
  * odd group count); W4A16_ERR_NULL (workspace needed); W4A16_ERR_ARG
  * (workspace too small); W4A16_ERR_ALIGN (workspace, scales, zeros). Checked
  * before any HIP call.

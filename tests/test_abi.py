@@ -276,7 +276,7 @@ def test_xres_workspace_and_rejects():
     def call(group=128, ws=A16, wb=1 << 30, M=32, K=8192, sc=A16):
         return lib.w4a16_linear_xres(A16, A16, sc, A16, M, 4096, K, group, ws, wb, A16, None)
 
-    assert call(group=64) == w4.ERR_UNSUPPORTED
+    assert call(group=32) == w4.ERR_UNSUPPORTED   # groups of 128 and 64 only
     assert call(M=33) == w4.ERR_UNSUPPORTED
     assert call(K=384) == w4.ERR_UNSUPPORTED
     assert call(ws=None) == w4.ERR_NULL
@@ -321,7 +321,12 @@ def test_linear_ws_split_choice_and_rejects():
         assert lib.w4a16_linear_ws_kernel(m, n, k, 128) == (2 if want_x else 1 if s else 0), (m, n, k)
         xf = _xres_ranges(m, n, k) * m * n if want_x else 0
         assert lib.w4a16_linear_workspace(m, n, k, 128) == max(s * m * n, xf) * 4, (m, n, k)
-    assert lib.w4a16_linear_ws_kernel(32, 8192, 8192, 64) == 0
+        # groups of 64: the x-resident kernel on the same shapes, else w4a16_linear's kernels
+        assert lib.w4a16_linear_ws_kernel(m, n, k, 64) == (2 if want_x else 0), (m, n, k)
+        assert lib.w4a16_linear_workspace(m, n, k, 64) == xf * 4, (m, n, k)
+        assert lib.w4a16_linear_ws_splits(m, n, k, 64) == 0, (m, n, k)
+    assert lib.w4a16_linear_ws_kernel(32, 8192, 8192, 32) == 0
+    assert lib.w4a16_linear_ws_kernel(32, 8192, 8320, 64) == 0    # odd number of 128-input blocks
     assert lib.w4a16_linear_ws_kernel(32, 8192, 8320, 128) == 0   # odd number of groups
     assert lib.w4a16_linear_ws_kernel(16, 20480, 2048, 128) == 0  # one K range: not on this path
     assert lib.w4a16_linear_ws_splits(256, 4096, 11008, 64) == 0   # split-K takes groups of 128 only

@@ -355,6 +355,28 @@ def test_auto_with_workspace_takes_x_resident(lib, m, k, n):
     assert np.array_equal(g.bits16(a), g.bits16(c))
 
 
+@pytest.mark.parametrize("m,k,n", [(16, 22016, 8192), (32, 8192, 8192), (21, 8192, 22016), (12, 4096, 11008),
+                                   (8, 8192, 1024), (32, 11008, 4096)])
+def test_auto_with_workspace_takes_x_resident_groups_of_64(lib, m, k, n):
+    # groups of 64 follow the same rule: every output against the oracle, bit-identical to the
+    # kernel's own entry point, with a workspace of exactly the size asked for
+    import torch
+
+    g = _gpu()
+    assert lib.linear_ws_kernel(m, n, k, group=64) == 2
+    s = oracle.channel_scale(synth.calibration(8, 5, k))
+    packed = oracle.quantize_pack(synth.weights(8, 5, n, k), s, group=64)
+    x = oracle.scale_input(synth.activations(8, 5, m, k), s)
+    print(f"auto-ws-x-resident groups of 64 M={m} K={k} N={n}", flush=True)
+    dev = [g.dev(t) for t in (x, *packed)]
+    ws = torch.empty(lib.linear_workspace_bytes(m, n, k, group=64) // 4, dtype=torch.float32, device=g.DEV)
+    a = g.host(lib.linear(*dev, group=64, workspace=ws))
+    y_ref, b = oracle.linear(x, *packed, group=64)
+    assert np.all(oracle.within_tolerance(a.astype(np.float64), y_ref, b))
+    c = g.host(lib.linear_xres(*dev, group=64))
+    assert np.array_equal(g.bits16(a), g.bits16(c))
+
+
 @pytest.mark.parametrize("m,k,n", [(512, 4096, 4096), (256, 2048, 16384), (300, 1024, 32768), (512, 8192, 8192)])
 def test_auto_one_range_route(lib, m, k, n):
     # from M = 256, where the one-range split-K kernel's 64 x 128 tiles fill the 256 CUs a whole

@@ -82,6 +82,53 @@ def test_xres_four_wave_ranges(lib, m):
     _check(lib, x, packed, "four-wave")
 
 
+@pytest.mark.parametrize("m", [1, 5, 16, 17, 32])
+@pytest.mark.parametrize("n,k", [(97, 2048), (300, 4352), (129, 11008)])
+def test_xres_groups_of_64(lib, m, n, k):
+    # groups of 64: each MFMA step takes 32 contiguous inputs (codes word-transposed through
+    # the stage, x fragments in the same order), two steps per group, each group scaled after
+    # its steps; ragged rows, columns and K ranges as above
+    g = _gpu()
+    s = oracle.channel_scale(synth.calibration(9, 2, k))
+    packed = oracle.quantize_pack(synth.weights(9, 2, n, k), s, group=64)
+    x = oracle.scale_input(synth.activations(9, 2, m, k), s)
+    print(f"x-resident groups of 64 M={m} N={n} K={k}", flush=True)
+    y = g.host(lib.linear_xres(g.dev(x), *[g.dev(t) for t in packed], group=64))
+    y_ref, b = oracle.linear(x, *packed, group=64)
+    ok = oracle.within_tolerance(y.astype(np.float64), y_ref, b)
+    assert np.all(ok), np.argwhere(~ok)[:3]
+
+
+@pytest.mark.parametrize("kind", ["positive", "negative", "wide"])
+def test_xres_groups_of_64_edge_weights(lib, kind):
+    # one-signed and wide groups: zeros outside [-2032, 1024] send their waves to the general
+    # route (exact q and z * sum x per group of 64)
+    g = _gpu()
+    packed = oracle.quantize_pack(synth.edge_weights(kind, 96, 4096, seed=13), None, group=64)
+    for m in (3, 32):
+        x = synth.activations(1, 14, m, 4096)
+        print(f"x-resident groups of 64 {kind} M={m}", flush=True)
+        y = g.host(lib.linear_xres(g.dev(x), *[g.dev(t) for t in packed], group=64))
+        y_ref, b = oracle.linear(x, *packed, group=64)
+        assert np.all(oracle.within_tolerance(y.astype(np.float64), y_ref, b)), (kind, m)
+
+
+def test_xres_groups_of_64_full_layer(lib):
+    # K = N = 8192 with groups of 64: every output at M = 16 and 32
+    g = _gpu()
+    k = n = 8192
+    s = oracle.channel_scale(synth.calibration(4, 0, k))
+    packed = oracle.quantize_pack(synth.weights(4, 0, n, k), s, group=64)
+    x = oracle.scale_input(synth.activations(4, 0, 32, k), s)
+    y_ref, b = oracle.linear(x, *packed, group=64)
+    dev = [g.dev(t) for t in packed]
+    for m in (16, 32):
+        print(f"x-resident groups of 64 8192^2 M={m}", flush=True)
+        y = g.host(lib.linear_xres(g.dev(x[:m]), *dev, group=64))
+        ok = oracle.within_tolerance(y.astype(np.float64), y_ref[:m], b[:m])
+        assert np.all(ok), (m, np.argwhere(~ok)[:3])
+
+
 @pytest.mark.parametrize("kind", ["positive", "negative", "mixed", "wide"])
 def test_xres_edge_weights(lib, kind):
     W = synth.edge_weights(kind, 96, 4096, seed=13)

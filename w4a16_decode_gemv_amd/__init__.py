@@ -318,7 +318,7 @@ def xres_workspace_bytes(M, N, K):
 
 
 def linear_xres(x, qweight, scales, zeros, workspace=None, out=None, group=GROUP):
-    """``linear`` (4-bit, groups of 128, M <= 32) on the x-resident MFMA kernel; workspace: a
+    """``linear`` (4-bit, groups of 128 or 64, M <= 32) on the x-resident MFMA kernel; workspace: a
     float32 device tensor of at least xres_workspace_bytes(M, N, K) bytes (allocated when
     omitted and needed)."""
     torch = _torch()

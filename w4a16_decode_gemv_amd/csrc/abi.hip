@@ -506,6 +506,7 @@ w4a16_status w4a16_linear(const void* x, const void* qweight, const void* scales
 int64_t w4a16_linear_workspace(int64_t M, int64_t N, int64_t K, int32_t group) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
   if (group != 128 && group != 64 && group != 32) return -1;
+  if (group == 64) return auto_xres(M, N, K) ? w4a16::xres_workspace_floats(M, N, K) * 4 : 0;
   return group == 128 ? ws_floats(M, N, K) * 4 : 0;
 }
 
@@ -515,12 +516,15 @@ w4a16_status w4a16_linear_ws(const void* x, const void* qweight, const void* sca
   clear_error();
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
-  if (group == 128 && workspace && auto_xres(M, N, K) && aligned(scales, 4) && aligned(zeros, 4)) {
+  // groups of 64 take the x-resident kernel on the same shapes (measured ahead of the small-batch
+  // kernel on each of them: 22016 -> 8192 at M = 16 44.4 -> 28.2 us, 8192 -> 28672 at M = 32
+  // 79.8 -> 46.1, 8192 x 8192 at M = 32 21.9 -> 17.0) and behind it on the others tried
+  if ((group == 128 || group == 64) && workspace && auto_xres(M, N, K) && aligned(scales, 4) && aligned(zeros, 4)) {
     const int64_t need = w4a16::xres_workspace_floats(M, N, K) * 4;
     if (workspace_bytes < need)
       return fail(W4A16_ERR_ARG, "workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
     if (!aligned(workspace, 16)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
-    return hip_result(w4a16::launch_xres(static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
+    return hip_result(w4a16::launch_xres(group, static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
                                          static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), M,
                                          N, K, static_cast<float*>(workspace), static_cast<uint16_t*>(y),
                                          static_cast<hipStream_t>(stream)),
@@ -550,7 +554,7 @@ int32_t w4a16_linear_ws_splits(int64_t M, int64_t N, int64_t K, int32_t group) {
 int32_t w4a16_linear_ws_kernel(int64_t M, int64_t N, int64_t K, int32_t group) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 128 != 0 || M > kMaxM || N > kMaxN || K > W4A16_MAX_K) return -1;
   if (group != 128 && group != 64 && group != 32) return -1;
-  if (group != 128) return 0;
+  if (group != 128) return group == 64 && auto_xres(M, N, K) ? 2 : 0;
   if (auto_xres(M, N, K)) return 2;
   return auto_splits(M, N, K) > 0 ? 1 : 0;
 }
@@ -630,7 +634,8 @@ w4a16_status w4a16_linear_xres(const void* x, const void* qweight, const void* s
   clear_error();
   const w4a16_status st = check_linear(x, qweight, scales, zeros, M, N, K, group, y);
   if (st != W4A16_OK) return st;
-  if (group != 128) return fail(W4A16_ERR_UNSUPPORTED, "the x-resident kernel takes groups of 128 (got %d)", (int)group);
+  if (group != 128 && group != 64)
+    return fail(W4A16_ERR_UNSUPPORTED, "the x-resident kernel takes groups of 128 or 64 (got %d)", (int)group);
   if (!w4a16::xres_supports(M, K))
     return fail(W4A16_ERR_UNSUPPORTED, "the x-resident kernel takes M <= %d and an even number of groups per row "
                 "(got M=%lld K=%lld)", w4a16::xres_max_m(), (long long)M, (long long)K);
@@ -643,7 +648,7 @@ w4a16_status w4a16_linear_xres(const void* x, const void* qweight, const void* s
       return fail(W4A16_ERR_ARG, "workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)need);
     if (!aligned(workspace, 16)) return fail(W4A16_ERR_ALIGN, "workspace must be 16-byte aligned");
   }
-  return hip_result(w4a16::launch_xres(static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
+  return hip_result(w4a16::launch_xres(group, static_cast<const uint16_t*>(x), static_cast<const uint32_t*>(qweight),
                                        static_cast<const uint16_t*>(scales), static_cast<const uint16_t*>(zeros), M, N,
                                        K, static_cast<float*>(workspace), static_cast<uint16_t*>(y),
                                        static_cast<hipStream_t>(stream)),

@@ -50,7 +50,7 @@ constexpr int kXrGroups = 2;                           // groups of 128 inputs p
 // CU. Measured (timing-only copies, 8192 x 8192 at M = 4): half-line code loads cost 2.5 us;
 // on 22016 -> 8192 at M = 16 (three rounds of workgroups) one workgroup per CU cost 6-8 us
 // against two.
-template <int MT, int WV, int NT, bool DIRECT>
+template <int MT, int WV, int NT, int GS, bool DIRECT>
 __global__ __launch_bounds__(64 * WV) __attribute__((amdgpu_waves_per_eu(MT == 1 ? 4 : 2)))
 void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw,
                  const uint16_t* __restrict__ scales, const uint16_t* __restrict__ zeros, int M, int N, int K, int S,
@@ -63,32 +63,37 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   constexpr int kXrCols = 16 * NT;                 // output columns per workgroup
   constexpr int kSlotTiles = NT < 8 ? 8 : NT;      // slots per m-tile: x needs 8 KB per m-tile
   constexpr bool kSpare = NT * MT <= kSlotTiles * MT - 2;  // two slots past the partial tiles
+  constexpr int kGB = 128 / GS;                     // groups per 128 inputs
+  constexpr int kSPG = 4 / kGB;                     // MFMA steps per group
+  constexpr int kGSh = GS == 128 ? 7 : (GS == 64 ? 6 : 5);
   __shared__ float4_t red[WV][kSlotTiles * MT][64];
-  __shared__ u32x4_t wsz[WV][12 * NT];  // the wave's (scale, zero) table: 3 x 16 NT words
+  __shared__ u32x4_t wsz[WV][12 * NT * kGB];  // the wave's (scale, zero) table: 3 kGB x 16 NT words
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int j = lane >> 4, c = lane & 15;
   const int item = xcd_contiguous_item(blockIdx.x, gridDim.x);
   const int range = item % S, tn = item / S;
   const int n0 = tn * kXrCols;
-  const int G = K >> 7;
-  const int g0 = range * kXrRangeGroups + wave * kXrGroups;  // this wave's first group
+  const int G = K >> kGSh;
+  const int g0 = range * kXrRangeGroups + wave * kXrGroups;  // this wave's first 128 inputs, in 128s
   // G is even and so is g0: a wave holds both of its groups or neither; a wave past the last
   // group reads zeros everywhere (no traffic) and adds exact zeros
-  const int past = (int)(g0 >= G) * kOutOfRange;
+  const int past = (int)(g0 >= (K >> 7)) * kOutOfRange;
   const int rows_n = min(N - n0, kXrCols);
   const __amdgpu_buffer_rsrc_t rx = rsrc(x, (int64_t)M * K * 2);  // rows past M read zero
   const __amdgpu_buffer_rsrc_t rq = rsrc(qw + (int64_t)n0 * (K >> 3), (int64_t)rows_n * (K >> 1));
   const __amdgpu_buffer_rsrc_t rs = rsrc(scales + (int64_t)n0 * G, (int64_t)rows_n * G * 2);
   const __amdgpu_buffer_rsrc_t rz = rsrc(zeros + (int64_t)n0 * G, (int64_t)rows_n * G * 2);
 
-  // (1) the wave's (scale, zero) pairs (groups g0, g0 + 1) of rows lane and lane + 64
-  uint32_t sv[NT / 4], zv[NT / 4];
+  // (1) the wave's (scale, zero) pairs (its 2 kGB groups, two per word) of rows lane and lane + 64
+  uint32_t sv[NT / 4][kGB], zv[NT / 4][kGB];
 #pragma unroll
-  for (int u = 0; u < NT / 4; ++u) {
-    const int off = (lane + 64 * u) * G * 2 + g0 * 2 + past;
-    sv[u] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
-    zv[u] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
-  }
+  for (int u = 0; u < NT / 4; ++u)
+#pragma unroll
+    for (int w = 0; w < kGB; ++w) {
+      const int off = (lane + 64 * u) * G * 2 + g0 * kGB * 2 + 4 * w + past;
+      sv[u][w] = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+      zv[u][w] = __builtin_amdgcn_raw_buffer_load_b32(rz, off, 0, 0);
+    }
   __builtin_amdgcn_sched_barrier(0);
   // (2) x rows of the wave's 256 inputs: load i takes row 2i + lane / 32, piece lane % 32 (16
   //     bytes; piece p is input chunk p % 16 of group g0 + p / 16)
@@ -130,34 +135,39 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
 #pragma unroll
     for (int h = 0; h < kXrGroups; ++h)
 #pragma unroll
-      for (int s = 0; s < 4; ++s) xf[mt][h][s] = xs[(16 * mt + c) * 32 + 16 * h + ((4 * j + s) ^ c)];
+      for (int s = 0; s < 4; ++s)
+        xf[mt][h][s] = xs[(16 * mt + c) * 32 + 16 * h + ((GS == 128 ? 4 * j + s : 4 * s + j) ^ c)];
   // The wave's table: word r the scale pair of row r; then, when every zero of the wave lies in
   // [-2032, 1024] (one ballot), words kXrCols + r and 2 kXrCols + r the two groups' fp16 pair
   // (-(1024 + z), -(64 + z)) that rebuilds q - z exactly, else word kXrCols + r the zero pair
   // (the general route: exact q and z * sum x).
+  //   With groups of 64 or 32 the table holds kGB scale words, then 2 kGB pair words (one per
+  //   group) or kGB zero words; group gg of the wave is half gg % 2 of scale (zero) word gg / 2.
   uint32_t* sz = reinterpret_cast<uint32_t*>(&wsz[wave][0]);
   bool in_range = true;
 #pragma unroll
   for (int u = 0; u < NT / 4; ++u)
 #pragma unroll
-    for (int h = 0; h < kXrGroups; ++h) {
-      const float zf = half_bits_to_float((uint16_t)(zv[u] >> (16 * h)));
+    for (int gg = 0; gg < 2 * kGB; ++gg) {
+      const float zf = half_bits_to_float((uint16_t)(zv[u][gg >> 1] >> (16 * (gg & 1))));
       in_range = in_range && zf >= -2032.0f && zf <= 1024.0f;
     }
   const bool fast = __builtin_amdgcn_ballot_w64(!in_range) == 0;
 #pragma unroll
   for (int u = 0; u < NT / 4; ++u) {
-    sz[lane + 64 * u] = sv[u];
+#pragma unroll
+    for (int w = 0; w < kGB; ++w) sz[w * kXrCols + lane + 64 * u] = sv[u][w];
     if (fast) {
 #pragma unroll
-      for (int h = 0; h < kXrGroups; ++h) {
-        const _Float16 zh = __builtin_bit_cast(_Float16, (uint16_t)(zv[u] >> (16 * h)));
+      for (int gg = 0; gg < 2 * kGB; ++gg) {
+        const _Float16 zh = __builtin_bit_cast(_Float16, (uint16_t)(zv[u][gg >> 1] >> (16 * (gg & 1))));
         const _Float16 clo = -((_Float16)1024.0f + zh), chi = -((_Float16)64.0f + zh);
-        sz[(1 + h) * kXrCols + lane + 64 * u] =
+        sz[(kGB + gg) * kXrCols + lane + 64 * u] =
             (uint32_t)__builtin_bit_cast(uint16_t, clo) | ((uint32_t)__builtin_bit_cast(uint16_t, chi) << 16);
       }
     } else {
-      sz[kXrCols + lane + 64 * u] = zv[u];
+#pragma unroll
+      for (int w = 0; w < kGB; ++w) sz[(kGB + w) * kXrCols + lane + 64 * u] = zv[u][w];
     }
   }
 
@@ -177,17 +187,34 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
 #pragma unroll
   for (int tt = 0; tt < kXrTiles; ++tt) {
     const int row = 16 * tt + c;
-    const uint32_t spair = sz[row], w1 = sz[kXrCols + row], w2 = FAST ? sz[2 * kXrCols + row] : 0u;
+    // scale words, then the pair words (fast route) or the zero words (general route)
+    uint32_t sw[kGB], cws[2 * kGB];
+#pragma unroll
+    for (int w = 0; w < kGB; ++w) sw[w] = sz[w * kXrCols + row];
+#pragma unroll
+    for (int gg = 0; gg < 2 * kGB; ++gg) cws[gg] = FAST || gg < kGB ? sz[(kGB + gg) * kXrCols + row] : 0u;
     constexpr bool kBorrow = !kSpare && MT == 1;  // the last n-tile's half B is the table's area
     u32x4_t* hb = (kBorrow && tt == kXrTiles - 1) ? &wsz[wave][0] : half_b;
     // the table is read through another type than the stage is written with: keep the reads
     // first where they share the area
     if (kBorrow && tt == kXrTiles - 1) asm volatile("" ::: "memory");
+    // groups of 64 or 32: word e of piece p goes to slot 4 (p / 4) + e, element p % 4, so that
+    // lane (c, j) reads words j, 4 + j, 8 + j, 12 + j of each 128 inputs: step s then spans the
+    // 32 inputs 32 s .. 32 s + 31 (x fragments read in the same order), one group or half of one
+    if constexpr (GS != 128) asm volatile("" ::: "memory");
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int r = lane >> 3;
-      (i ? hb : half_a)[r * 8 + ((lane & 7) ^ ((r >> 1) | (i << 2)))] = q[tt][i];
+      const int r = lane >> 3, swz = (r >> 1) | (i << 2);
+      if constexpr (GS == 128) {
+        (i ? hb : half_a)[r * 8 + ((lane & 7) ^ swz)] = q[tt][i];
+      } else {
+        uint32_t* dst = reinterpret_cast<uint32_t*>(i ? hb : half_a);
+        const int pc = lane & 7;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[(r * 8 + ((4 * (pc >> 2) + e) ^ swz)) * 4 + (pc & 3)] = q[tt][i][e];
+      }
     }
+    if constexpr (GS != 128) asm volatile("" ::: "memory");
     const int ci = c & 7, cb = c >> 3;
     const u32x4_t* hc = cb ? hb : half_a;
     const u32x4_t qc[2] = {hc[ci * 8 + (j ^ ((ci >> 1) | (cb << 2)))], hc[ci * 8 + ((4 + j) ^ ((ci >> 1) | (cb << 2)))]};
@@ -195,27 +222,33 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[mt] = (float4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < kXrGroups; ++h) {
-      const float d = half_bits_to_float((uint16_t)(spair >> (16 * h)));
-      const uint32_t cw = FAST ? (h ? w2 : w1) : 0xD400E400u;  // (-1024, -64): exact q
+    for (int h = 0; h < kXrGroups; ++h)
+#pragma unroll
+      for (int gi = 0; gi < kGB; ++gi) {
+      const int gg = h * kGB + gi;  // the wave's group; its steps are gi kSPG .. (gi + 1) kSPG - 1
+      const float d = half_bits_to_float((uint16_t)(sw[gg >> 1] >> (16 * (gg & 1))));
+      const uint32_t cw = FAST ? cws[gg] : 0xD400E400u;  // (-1024, -64): exact q
       const _Float16 clo = __builtin_bit_cast(_Float16, (uint16_t)(cw & 0xFFFFu));
       const _Float16 chi = __builtin_bit_cast(_Float16, (uint16_t)(cw >> 16));
       const half2_t c_lo = {clo, clo}, c_hi = {chi, chi};
-      const half8_t bq[4] = {dequant_word(qc[h].x, c_lo, c_hi), dequant_word(qc[h].y, c_lo, c_hi),
-                             dequant_word(qc[h].z, c_lo, c_hi), dequant_word(qc[h].w, c_lo, c_hi)};
+      half8_t bq[kSPG];
+#pragma unroll
+      for (int s = 0; s < kSPG; ++s) bq[s] = dequant_word(qc[h][gi * kSPG + s], c_lo, c_hi);
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         float4_t a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][s]), bq[s], a, 0, 0, 0);
+        for (int s = 0; s < kSPG; ++s)
+          a = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][gi * kSPG + s]), bq[s], a, 0, 0, 0);
         if constexpr (FAST) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, a[i], acc[mt][i]);
         } else {
-          const float zf = half_bits_to_float((uint16_t)(w1 >> (16 * h)));
+          const float zf = half_bits_to_float((uint16_t)(cws[gg >> 1] >> (16 * (gg & 1))));
           float4_t sx = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int s = 0; s < 4; ++s) sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][s]), ones, sx, 0, 0, 0);
+          for (int s = 0; s < kSPG; ++s)
+            sx = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(xf[mt][h][gi * kSPG + s]), ones, sx, 0, 0, 0);
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[mt][i] = __builtin_fmaf(d, __builtin_fmaf(-zf, sx[i], a[i]), acc[mt][i]);
         }
@@ -265,16 +298,16 @@ void xres_kernel(const uint16_t* __restrict__ x, const uint32_t* __restrict__ qw
   }
 }
 
-template <int MT, int WV, int NT>
+template <int MT, int WV, int NT, int GS>
 hipError_t launch_mt(const uint16_t* x, const uint32_t* qw, const uint16_t* sc, const uint16_t* zr, int64_t M,
                      int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
   const int S = (int)((K / 128 + WV * kXrGroups - 1) / (WV * kXrGroups));
   const int64_t items = ((N + 16 * NT - 1) / (16 * NT)) * S;
   if (S == 1)
-    hipLaunchKernelGGL((xres_kernel<MT, WV, NT, true>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc,
+    hipLaunchKernelGGL((xres_kernel<MT, WV, NT, GS, true>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc,
                        zr, (int)M, (int)N, (int)K, 1, nullptr, y);
   else
-    hipLaunchKernelGGL((xres_kernel<MT, WV, NT, false>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc,
+    hipLaunchKernelGGL((xres_kernel<MT, WV, NT, GS, false>), dim3((unsigned)items), dim3(64 * WV), 0, stream, x, qw, sc,
                        zr, (int)M, (int)N, (int)K, S, workspace, nullptr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return e;
@@ -327,11 +360,15 @@ int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K) {
   return S == 1 ? 0 : (int64_t)S * M * N;
 }
 
-hipError_t launch_xres_config(int waves, int tiles, const uint16_t* x, const uint32_t* qweight,
+hipError_t launch_xres_config(int waves, int tiles, int group, const uint16_t* x, const uint32_t* qweight,
                               const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
                               float* workspace, uint16_t* y, hipStream_t stream) {
 #define W4A16_XRES(MT, WV, NT) \
-  if (waves == WV && tiles == NT) return launch_mt<MT, WV, NT>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  if (waves == WV && tiles == NT) {                                                                                   \
+    if (group == 128) return launch_mt<MT, WV, NT, 128>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);  \
+    if (group == 64) return launch_mt<MT, WV, NT, 64>(x, qweight, scales, zeros, M, N, K, workspace, y, stream);    \
+    return hipErrorInvalidValue;                                                                                      \
+  }
   // the shapes xres_config chooses
   if (M <= 16) {
     W4A16_XRES(1, 4, 4) W4A16_XRES(1, 8, 4)
@@ -342,11 +379,11 @@ hipError_t launch_xres_config(int waves, int tiles, const uint16_t* x, const uin
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+hipError_t launch_xres(int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream) {
   int waves, tiles;
   xres_config(M, N, K, &waves, &tiles);
-  return launch_xres_config(waves, tiles, x, qweight, scales, zeros, M, N, K, workspace, y, stream);
+  return launch_xres_config(waves, tiles, group, x, qweight, scales, zeros, M, N, K, workspace, y, stream);
 }
 
 }  // namespace w4a16

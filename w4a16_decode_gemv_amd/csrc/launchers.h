@@ -86,7 +86,7 @@ hipError_t splitk_scratch(hipStream_t stream, float** ptr);
 hipError_t launch_splitk_reduce(const float* part, int64_t M, int64_t N, int S, uint16_t* y, hipStream_t stream);
 
 // Small-batch MFMA kernel with x held in registers and K split into xres_ranges(M, N, K) ranges
-// of 2048 or 1024 inputs (4-bit, groups of 128): needs xres_supports(M, K) (M <= 32, an even number of
+// of 2048 or 1024 inputs (4-bit, groups of 128 or 64): needs xres_supports(M, K) (M <= 32, an even number of
 // groups per row) and scales and zeros 4-byte aligned; with more than one range, a float32
 // workspace of xres_workspace_floats(M, N, K) floats.
 int xres_max_m();
@@ -97,12 +97,12 @@ int xres_waves(int64_t M, int64_t N, int64_t K);
 int xres_ranges(int64_t M, int64_t N, int64_t K);
 bool xres_supports(int64_t M, int64_t K);
 int64_t xres_workspace_floats(int64_t M, int64_t N, int64_t K);
-hipError_t launch_xres(const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
+hipError_t launch_xres(int group, const uint16_t* x, const uint32_t* qweight, const uint16_t* scales, const uint16_t* zeros,
                        int64_t M, int64_t N, int64_t K, float* workspace, uint16_t* y, hipStream_t stream);
 // the same with 4 or 8 waves per workgroup (ranges of 1024 or 2048 inputs) and 4 n-tiles per
 // wave (64 columns) for M <= 16, 8 (128 columns) above; the workspace holds the ranges of that
-// choice; another shape returns hipErrorInvalidValue
-hipError_t launch_xres_config(int waves, int tiles, const uint16_t* x, const uint32_t* qweight,
+// choice; another shape or group returns hipErrorInvalidValue
+hipError_t launch_xres_config(int waves, int tiles, int group, const uint16_t* x, const uint32_t* qweight,
                               const uint16_t* scales, const uint16_t* zeros, int64_t M, int64_t N, int64_t K,
                               float* workspace, uint16_t* y, hipStream_t stream);
 
