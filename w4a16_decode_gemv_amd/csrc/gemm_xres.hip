@@ -1,5 +1,5 @@
-// Small-batch W4A16 GEMM (M <= 32, 4-bit codes, groups of 128) with each wave's block of x
-// held in registers for the whole launch and K split across workgroups.
+// Small-batch W4A16 GEMM (M <= 32, 4-bit codes, groups of 128 or 64) with each wave's block of
+// x held in registers for the whole launch and K split across workgroups.
 //
 // y[m][n] = f16( sum_s P_s[m][n] ),
 // P_s[m][n] = sum_{g in range s} d[n][g] * sum_{k in g} x[m][k] (q[n][k] - z[n][g])
@@ -18,7 +18,8 @@
 // 8192 x 8192). Every x, scale, zero and code load of a wave is issued before its first MFMA
 // (8 or 16 KB of codes per wave in flight), so the weight stream keeps the GEMV's depth.
 //
-// Per 16-column n-tile and group the four MFMA steps accumulate sum x (q - z) exactly (fp16
+// Per 16-column n-tile and group the group's MFMA steps (four for groups of 128; two for
+// groups of 64, where each step takes 32 contiguous inputs) accumulate sum x (q - z) exactly (fp16
 // (q - z) B fragments while every zero of the wave lies in [-2032, 1024]; otherwise the wave
 // takes exact q and z * sum x for all its groups, sum x from an MFMA against ones), then
 // acc += d * that. The waves' float32 tiles are added through LDS in wave order. With one K range the sums are
