@@ -74,31 +74,31 @@ def test_linear_in_graph(lib, m, n):
     assert np.all(oracle.within_tolerance(g.host(y).astype(np.float64), y_ref, b))
 
 
-@pytest.mark.parametrize("m", [8, 24])
-def test_x_resident_in_graph(lib, m):
+@pytest.mark.parametrize("m,group", [(8, 128), (24, 128), (16, 64)])
+def test_x_resident_in_graph(lib, m, group):
     # 4096 -> 11008: the automatic path with the binding's workspace (allocated inside the
     # capture) runs the x-resident kernel and its range reduction; its own entry point with a
     # caller workspace too. 64-column four-wave workgroups at M = 8, 128-column eight-wave ones
-    # at M = 24
+    # at M = 24; groups of 64 at M = 16
     torch, g = _torch(), _gpu()
     k, n = 4096, 11008
-    assert lib.linear_ws_kernel(m, n, k) == 2
-    packed = [g.dev(t) for t in oracle.quantize_pack(synth.weights(2, 13, n, k))]
+    assert lib.linear_ws_kernel(m, n, k, group=group) == 2
+    packed = [g.dev(t) for t in oracle.quantize_pack(synth.weights(2, 13, n, k), group=group)]
     x = g.dev(synth.activations(2, 13, m, k))
     y = torch.empty((m, n), dtype=torch.float16, device=x.device)
     y2 = torch.empty((m, n), dtype=torch.float16, device=x.device)
     ws = torch.empty(lib.xres_workspace_bytes(m, n, k) // 4, dtype=torch.float32, device=x.device)
-    print(f"graph x-resident M={m}", flush=True)
+    print(f"graph x-resident M={m} group={group}", flush=True)
 
     def capture():
-        lib.linear(x, *packed, out=y)
-        lib.linear_xres(x, *packed, workspace=ws, out=y2)
+        lib.linear(x, *packed, out=y, group=group)
+        lib.linear_xres(x, *packed, workspace=ws, out=y2, group=group)
 
     _replay_and_compare(
         torch, capture, [x], [y, y2],
         lambda i: [synth.activations(2, 40 + i, m, k)],
-        lambda: [lib.linear(x, *packed), lib.linear_xres(x, *packed)])
-    y_ref, b = oracle.linear(g.host(x), g.host_u32(packed[0]), g.host(packed[1]), g.host(packed[2]))
+        lambda: [lib.linear(x, *packed, group=group), lib.linear_xres(x, *packed, group=group)])
+    y_ref, b = oracle.linear(g.host(x), g.host_u32(packed[0]), g.host(packed[1]), g.host(packed[2]), group=group)
     assert np.all(oracle.within_tolerance(g.host(y).astype(np.float64), y_ref, b))
 
 
