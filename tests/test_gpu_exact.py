@@ -100,19 +100,20 @@ def test_splitk_every_position(lib):
             assert np.array_equal(g.bits16(y), g.bits16(want)), (c0, splits)
 
 
-@pytest.mark.parametrize("m", [16, 32])
-def test_xres_every_position(lib, m):
-    # the x-resident kernel: K = 4352 is three K ranges (the last one of two groups, its other
-    # waves idle); every input position of the first range, and the last range's
+@pytest.mark.parametrize("m,group", [(16, 128), (32, 128), (16, 64), (32, 64)])
+def test_xres_every_position(lib, m, group):
+    # the x-resident kernel: K = 4352 is three K ranges (the last one of two 128-input blocks,
+    # its other waves idle); every input position of the first range, and the last range's.
+    # Groups of 64 pin the other k-to-lane order (each MFMA step 32 contiguous inputs)
     g = _gpu()
     n, k = 131, 4352
-    packed = _weights(7, n, k)
+    packed = _weights(7, n, k, 4, group)
     dev = [g.dev(t) for t in packed]
-    print(f"exact x-resident M={m}", flush=True)
+    print(f"exact x-resident M={m} group={group}", flush=True)
     for c0 in list(range(0, 2048, m)) + list(range(4096, k, m)):
         x = _one_hot([min(c, k - 1) for c in range(c0, c0 + m)], k)
-        y = g.host(lib.linear_xres(g.dev(x), *dev))
-        want = _exact_ref(oracle.linear(x, *packed)[0])
+        y = g.host(lib.linear_xres(g.dev(x), *dev, group=group))
+        want = _exact_ref(oracle.linear(x, *packed, group=group)[0])
         assert np.array_equal(g.bits16(y), g.bits16(want)), c0
 
 
